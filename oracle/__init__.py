@@ -1,0 +1,264 @@
+"""CPU oracle for Kimi Delta Attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library never loads it,
+and it imports nothing from the product package: the two share no code.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, token by token).  This
+module only marshals numpy arrays into it.  Every array is converted to
+float64 before the call, so bf16 inputs are widened exactly.
+
+Page labels used in docstrings: [kda.rs] is the "atlas_core/kimi_k3/kda.rs"
+Kimi K3 KDA CPU reference page, [api.py] the "K3/kda/ops/api.py" chunk_kda
+boundary page.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+
+GATE_LOGDECAY, GATE_SAFE, GATE_SOFTPLUS = 0, 1, 2
+L2_EPS = 1e-6  # [kda.rs] KDA_L2_EPS: the in-kernel q/k normalisation epsilon
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc into ``oracle/libkda_oracle.so``."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC",
+                               "-shared", "-o", tmp, _SRC, "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+        ("K", ctypes.c_int), ("V", ctypes.c_int),
+        ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)), ("N", ctypes.c_int),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("scale", ctypes.c_double), ("lower_bound", ctypes.c_double),
+        ("gate_mode", ctypes.c_int), ("use_qk_l2norm", ctypes.c_int),
+        ("use_beta_sigmoid", ctypes.c_int), ("l2_eps", ctypes.c_double),
+        ("initial_state", ctypes.c_void_p),
+    ]
+
+
+class _Decode(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int), ("H", ctypes.c_int), ("D", ctypes.c_int), ("W", ctypes.c_int),
+        ("x", ctypes.c_void_p), ("conv_w", ctypes.c_void_p), ("conv_state", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("lower_bound", ctypes.c_double),
+        ("gate_mode", ctypes.c_int), ("use_qk_l2norm", ctypes.c_int),
+        ("use_beta_sigmoid", ctypes.c_int),
+        ("scale", ctypes.c_double), ("l2_eps", ctypes.c_double),
+        ("state", ctypes.c_void_p), ("o", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        lib = ctypes.CDLL(build())
+        P = ctypes.POINTER(_Problem)
+        dp = ctypes.c_void_p
+        lib.or_chunk_fwd.argtypes = [P, dp, dp, ctypes.c_int]
+        lib.or_chunk_fwd_chunked.argtypes = [P, ctypes.c_int, dp, dp, ctypes.c_int]
+        lib.or_chunk_bwd.argtypes = [P, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+        lib.or_decode_step.argtypes = [ctypes.POINTER(_Decode), ctypes.c_int]
+        lib.or_gate_values.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp,
+                                       ctypes.c_double, dp]
+        lib.or_l2norm_rows.argtypes = [dp, ctypes.c_int, ctypes.c_int, ctypes.c_double, dp]
+        _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor: widen exactly on the CPU
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class _Args:
+    """Holds the converted arrays alive for the duration of one call."""
+
+    def __init__(self, q, k, v, g, beta, A_log, dt_bias, scale, initial_state, use_qk_l2norm,
+                 gate_mode, use_beta_sigmoid, lower_bound, cu_seqlens):
+        self.q, self.k, self.v, self.g, self.beta = map(_f64, (q, k, v, g, beta))
+        self.A_log, self.dt_bias, self.h0 = _f64(A_log), _f64(dt_bias), _f64(initial_state)
+        B, T, H, K = self.q.shape
+        V = self.v.shape[-1]
+        self.shape = (B, T, H, K, V)
+        if cu_seqlens is not None:
+            if hasattr(cu_seqlens, "detach"):
+                cu_seqlens = cu_seqlens.detach().cpu().numpy()
+            self.cu = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+            assert B == 1 and self.cu[-1] == T
+            self.N = len(self.cu) - 1
+        else:
+            self.cu = None
+            self.N = B
+        if gate_mode != GATE_LOGDECAY and self.A_log is None:
+            raise ValueError("A_log is required for the in-kernel gate")  # [api.py] chunk_kda
+        if gate_mode == GATE_SAFE and lower_bound is None:
+            raise ValueError("lower_bound is required for the safe gate")  # [api.py] chunk_kda
+        p = _Problem()
+        p.B, p.T, p.H, p.K, p.V = B, T, H, K, V
+        p.cu_seqlens = (self.cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+                        if self.cu is not None else None)
+        p.N = self.N
+        p.q, p.k, p.v, p.g, p.beta = map(_ptr, (self.q, self.k, self.v, self.g, self.beta))
+        p.A_log, p.dt_bias = _ptr(self.A_log), _ptr(self.dt_bias)
+        p.scale = float(K ** -0.5 if scale is None else scale)
+        p.lower_bound = float("nan") if lower_bound is None else float(lower_bound)
+        p.gate_mode = int(gate_mode)
+        p.use_qk_l2norm = int(bool(use_qk_l2norm))
+        p.use_beta_sigmoid = int(bool(use_beta_sigmoid))
+        p.l2_eps = L2_EPS
+        p.initial_state = _ptr(self.h0)
+        self.p = p
+
+
+def chunk_fwd(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
+              use_qk_l2norm=False, gate_mode=GATE_LOGDECAY, use_beta_sigmoid=False,
+              lower_bound=None, cu_seqlens=None, threads=None):
+    """The KDA forward as the plain token recurrence ([kda.rs] module doc
+    "Recurrence"; boundary and flag order of [api.py] chunk_kda).
+
+    Shapes: q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H];
+    initial_state [N, H, K, V].  Returns (o [B, T, H, V], final_state [N, H, K, V]),
+    both float64."""
+    a = _Args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, use_qk_l2norm, gate_mode,
+              use_beta_sigmoid, lower_bound, cu_seqlens)
+    B, T, H, K, V = a.shape
+    o = np.zeros((B, T, H, V))
+    fs = np.zeros((a.N, H, K, V))
+    _load().or_chunk_fwd(ctypes.byref(a.p), _ptr(o), _ptr(fs), threads or default_threads())
+    return o, fs
+
+
+def chunk_fwd_chunked(q, k, v, g, beta, *, chunk_size, A_log=None, dt_bias=None, scale=None,
+                      initial_state=None, use_qk_l2norm=False, gate_mode=GATE_LOGDECAY,
+                      use_beta_sigmoid=False, lower_bound=None, cu_seqlens=None, threads=None):
+    """The same forward evaluated in chunkwise WY/UT form with any chunk size
+    (a tail chunk allowed).  An independent derivation, used only to pin
+    ``chunk_fwd``."""
+    a = _Args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, use_qk_l2norm, gate_mode,
+              use_beta_sigmoid, lower_bound, cu_seqlens)
+    B, T, H, K, V = a.shape
+    o = np.zeros((B, T, H, V))
+    fs = np.zeros((a.N, H, K, V))
+    _load().or_chunk_fwd_chunked(ctypes.byref(a.p), int(chunk_size), _ptr(o), _ptr(fs),
+                                 threads or default_threads())
+    return o, fs
+
+
+def chunk_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bias=None, scale=None,
+              initial_state=None, use_qk_l2norm=False, gate_mode=GATE_LOGDECAY,
+              use_beta_sigmoid=False, lower_bound=None, cu_seqlens=None, threads=None):
+    """Gradients of <o, dO> + <final_state, d_final_state> w.r.t. every input as
+    passed (reverse mode through the token recurrence, checkpointed every 64
+    tokens).  Returns a dict with dq, dk, dv, dg, dbeta, dh0, and dA_log /
+    ddt_bias for the in-kernel gate modes."""
+    a = _Args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, use_qk_l2norm, gate_mode,
+              use_beta_sigmoid, lower_bound, cu_seqlens)
+    B, T, H, K, V = a.shape
+    dO = _f64(dO)
+    dSf = _f64(d_final_state)
+    out = {
+        "dq": np.zeros((B, T, H, K)), "dk": np.zeros((B, T, H, K)), "dv": np.zeros((B, T, H, V)),
+        "dg": np.zeros((B, T, H, K)), "dbeta": np.zeros((B, T, H)),
+        "dh0": np.zeros((a.N, H, K, V)), "dA_log": np.zeros(H), "ddt_bias": np.zeros(H * K),
+    }
+    _load().or_chunk_bwd(ctypes.byref(a.p), _ptr(dO), _ptr(dSf), _ptr(out["dq"]), _ptr(out["dk"]),
+                         _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"]),
+                         _ptr(out["dA_log"]), _ptr(out["ddt_bias"]), threads or default_threads())
+    if gate_mode == GATE_LOGDECAY:
+        out["dA_log"] = None
+        out["ddt_bias"] = None
+    return out
+
+
+def decode_step(x, conv_w, conv_state, g, beta, state, *, A_log=None, dt_bias=None, scale=None,
+                use_qk_l2norm=True, gate_mode=GATE_LOGDECAY, use_beta_sigmoid=True,
+                lower_bound=None, threads=None):
+    """One decode token per sequence ([kda.rs] kda_decode_token): the causal
+    depthwise short-conv update with SiLU over the [q|k|v] channels
+    ([kda.rs] conv_update), then one recurrent step ([kda.rs] kda_recurrent_step).
+
+    x [N, 3*H*D]; conv_w [3*H*D, W]; conv_state [N, 3*H*D, W]; g [N, H*D];
+    beta [N, H]; state [N, H, D, D].  Returns (o [N, H*D], new conv_state,
+    new state), all float64; the inputs are not modified."""
+    x = _f64(x)
+    conv_w = _f64(conv_w)
+    cs = _f64(conv_state).copy()
+    st = _f64(state).copy()
+    g = _f64(g)
+    beta = _f64(beta)
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    N, H, D, _ = st.shape
+    W = conv_w.shape[-1]
+    assert x.shape == (N, 3 * H * D) and cs.shape == (N, 3 * H * D, W)
+    if gate_mode != GATE_LOGDECAY and A_log is None:
+        raise ValueError("A_log is required for the in-kernel gate")
+    if gate_mode == GATE_SAFE and lower_bound is None:
+        raise ValueError("lower_bound is required for the safe gate")
+    o = np.zeros((N, H * D))
+    d = _Decode()
+    d.N, d.H, d.D, d.W = N, H, D, W
+    d.x, d.conv_w, d.conv_state = _ptr(x), _ptr(conv_w), _ptr(cs)
+    d.g, d.beta, d.A_log, d.dt_bias = _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias)
+    d.lower_bound = float("nan") if lower_bound is None else float(lower_bound)
+    d.gate_mode, d.use_qk_l2norm, d.use_beta_sigmoid = int(gate_mode), int(use_qk_l2norm), int(use_beta_sigmoid)
+    d.scale = float(D ** -0.5 if scale is None else scale)
+    d.l2_eps = L2_EPS
+    d.state, d.o = _ptr(st), _ptr(o)
+    _load().or_decode_step(ctypes.byref(d), threads or default_threads())
+    return o, cs, st
+
+
+def gate(x, *, gate_mode, A_log=None, dt_bias=None, lower_bound=None):
+    """Per-channel log-decay from the raw gate input x [H, K] ([kda.rs] bounded_gate)."""
+    x = _f64(x)
+    H, K = x.shape
+    out = np.zeros((H, K))
+    A_log, dt_bias = _f64(A_log), _f64(dt_bias)
+    _load().or_gate_values(int(gate_mode), H, K, _ptr(x), _ptr(A_log), _ptr(dt_bias),
+                           float("nan") if lower_bound is None else float(lower_bound), _ptr(out))
+    return out
+
+
+def l2norm(x):
+    """Row L2 normalisation with the in-kernel epsilon ([kda.rs] l2norm_rows)."""
+    x = _f64(x)
+    out = np.zeros_like(x)
+    d = x.shape[-1]
+    _load().or_l2norm_rows(_ptr(x), int(x.size // d), d, L2_EPS, _ptr(out))
+    return out
