@@ -1,0 +1,182 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library.
+ *
+ * The operation is the gated delta rule with a per-channel decay on the key
+ * axis ("atlas_core/kimi_k3/kda.rs" page, module doc "Recurrence"), per
+ * sequence n and head h, with a K x V fp32 state S:
+ *     S <- diag(exp(g_t)) S
+ *     d <- beta_t * (v_t - S^T k_t)
+ *     S <- S + k_t d^T
+ *     o_t <- scale * S^T q_t
+ * with q, k optionally L2-normalised (eps 1e-6), beta optionally a logit and
+ * g optionally computed in kernel from a raw gate input.  The argument set
+ * follows the chunk_kda operator boundary of the "K3/kda/ops/api.py" page
+ * (q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
+ * output_final_state, use_qk_l2norm_in_kernel, use_gate_in_kernel,
+ * use_beta_sigmoid_in_kernel, safe_gate, lower_bound, chunk_size) without its
+ * backend switch, plus packed variable-length sequences.
+ *
+ * Conventions shared by every entry point
+ *   - Plain C types only.  Every tensor pointer is a DEVICE pointer unless
+ *     stated otherwise; the args structs themselves live on the host and are
+ *     read during the call only.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     device memory and keeps no global mutable state; scratch memory is a
+ *     caller-provided workspace whose size the *_workspace queries return.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL is the default
+ *     stream) and the call returns without synchronising.
+ *   - Every argument is validated on the host before anything is launched;
+ *     on any error nothing is launched.  Device-resident index data
+ *     (cu_seqlens) cannot be checked on the host: kernels clamp it so that
+ *     no access leaves the tensors, but results for malformed offsets are
+ *     unspecified.
+ *   - Outputs must not alias inputs, except the documented in/out states of
+ *     kda_recurrent_step.
+ *   - Layouts are row-major with the last index fastest:
+ *       q, k, g [rows, H, K]   v, o [rows, H, V]   beta [rows, H]
+ *       states  [N, H, K, V]   (key index major)
+ *     rows = B*T for dense input (sequence n is rows n*T .. n*T+T-1), or the
+ *     packed token count T with B = 1 for variable-length input (sequence n is
+ *     rows cu_seqlens[n] .. cu_seqlens[n+1]-1).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad flag value */
+    KDA_ERR_UNSUPPORTED = 2,   /* dtype, chunk size, K/V/D outside the built set */
+    KDA_ERR_MISSING_PARAM = 3, /* A_log absent with an in-kernel gate, or lower_bound
+                                  absent with the safe gate (the two ValueErrors of
+                                  the api.py boundary) */
+    KDA_ERR_WORKSPACE = 4,     /* workspace pointer NULL or smaller than required */
+    KDA_ERR_HIP = 5            /* a kernel launch reported an error */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* How g is turned into the per-channel log-decay (api.py chunk_kda gate
+ * branch; kda.rs bounded_gate):
+ *   KDA_GATE_LOGDECAY  g is the log-decay itself (use_gate_in_kernel=False).
+ *   KDA_GATE_SAFE      g_eff = lower_bound * sigmoid(exp(A_log_h) * (g + dt_bias))
+ *                      (use_gate_in_kernel=True, safe_gate=True).
+ *   KDA_GATE_SOFTPLUS  g_eff = -exp(A_log_h) * softplus(g + dt_bias)
+ *                      (use_gate_in_kernel=True, safe_gate=False). */
+typedef enum { KDA_GATE_LOGDECAY = 0, KDA_GATE_SAFE = 1, KDA_GATE_SOFTPLUS = 2 } kda_gate_mode;
+
+/* Arguments of the chunked forward / backward. */
+typedef struct {
+    /* sizes */
+    int B, T, H, K, V;
+    /* Variable-length packing: device int32 [N+1] prefix offsets with
+     * cu_seqlens[0] = 0 and cu_seqlens[N] = T, non-decreasing; requires B = 1.
+     * NULL means dense input with N = B sequences of length T. */
+    const int32_t *cu_seqlens;
+    int N;
+    /* inputs */
+    kda_dtype qkv_dtype;     /* dtype of q, k, v (and o, dq, dk, dv, dO) */
+    const void *q, *k, *v;
+    const float *g;          /* [rows, H, K] log-decay or raw gate input (see gate_mode) */
+    const float *beta;       /* [rows, H] value, or logit when use_beta_sigmoid */
+    const float *A_log;      /* [H]; required for SAFE / SOFTPLUS, ignored otherwise */
+    const float *dt_bias;    /* [H*K] or NULL (= 0); SAFE / SOFTPLUS only */
+    float scale;             /* <= 0 or NaN means K^-1/2 */
+    float lower_bound;       /* NaN means "none".  Required for SAFE.  In LOGDECAY
+                                mode a finite value promises g >= lower_bound on
+                                every element; kernels may use it to pick a
+                                faster overflow-safe factorisation. */
+    int gate_mode;           /* kda_gate_mode */
+    int use_qk_l2norm;       /* q <- q (sum q^2 + 1e-6)^-1/2, same for k.  With 0 the
+                                caller must supply well-scaled keys: the api.py
+                                boundary warns that un-normalised keys can drive the
+                                exact result to inf. */
+    int use_beta_sigmoid;    /* beta <- sigmoid(beta) */
+    int chunk_size;          /* must be 64 */
+    /* state */
+    const float *initial_state; /* [N, H, K, V] or NULL (zeros) */
+    int output_final_state;
+    /* outputs */
+    void *o;                 /* [rows, H, V] in qkv_dtype */
+    float *final_state;      /* [N, H, K, V]; written when output_final_state != 0 */
+    /* resources */
+    void *workspace;
+    size_t workspace_bytes;
+    void *stream;            /* hipStream_t */
+} kda_chunk_args;
+
+/* Gradients for kda_chunk_bwd.  dq, dk, dv are in qkv_dtype; the others fp32.
+ * dg and dbeta are taken with respect to the tensors AS PASSED: the raw gate
+ * input in SAFE / SOFTPLUS mode, the logit when use_beta_sigmoid is set. */
+typedef struct {
+    const void *dO;              /* [rows, H, V], required */
+    const float *d_final_state;  /* [N, H, K, V] or NULL (= 0) */
+    void *dq, *dk, *dv;          /* required */
+    float *dg;                   /* [rows, H, K], required */
+    float *dbeta;                /* [rows, H], required */
+    float *d_initial_state;      /* [N, H, K, V] or NULL (not written) */
+    float *dA_log;               /* [H] or NULL; SAFE / SOFTPLUS only */
+    float *ddt_bias;             /* [H*K] or NULL; SAFE / SOFTPLUS only */
+} kda_chunk_grads;
+
+/* Chunked forward (chunk size 64): writes o and, if requested, final_state.
+ * Computes exactly the recurrence above, in chunkwise-parallel form
+ * (api.py chunk_kda; the chunk form's use of I + tril(A_kk * beta) is named in
+ * its l2-norm warning).  K = V in {32, 64, 128} for KDA_BF16 q/k/v and
+ * {32, 64} for KDA_F32 (the fp32 operand tiles of K = 128 exceed the 160 KiB
+ * of LDS a workgroup can hold); anything else is KDA_ERR_UNSUPPORTED.
+ * An empty sequence writes final_state = initial_state. */
+kda_status kda_chunk_fwd(const kda_chunk_args *a);
+size_t kda_chunk_fwd_workspace(const kda_chunk_args *a);
+
+/* Chunked backward: gradients of <o, dO> + <final_state, d_final_state>.
+ * Uses the same args as the forward (o and final_state are not read). */
+kda_status kda_chunk_bwd(const kda_chunk_args *a, const kda_chunk_grads *gr);
+size_t kda_chunk_bwd_workspace(const kda_chunk_args *a);
+
+/* One decode token per sequence ("atlas_core/kimi_k3/kda.rs" page,
+ * kda_decode_token = conv_update followed by kda_recurrent_step):
+ *   for each of the 3*H*D channels c of x = [q | k | v]:
+ *       window[c] shifts left one slot (slot 0 leaves), x[c] enters slot W-1,
+ *       y[c] = SiLU(sum_j conv_w[c, j] * window[c, j])   (no bias)
+ *   then per head the recurrence step above on (q, k, v) = y, writing
+ *   o [N, H*D] (fp32) and updating state in place. */
+typedef struct {
+    int N, H, D, W;          /* D = head dim (K = V = D) in {32, 64, 128}; 1 <= W <= 8 */
+    kda_dtype x_dtype;       /* KDA_F32 or KDA_BF16 */
+    const void *x_qkv;       /* [N, 3*H*D] pre-conv inputs, [q | k | v] */
+    const float *conv_w;     /* [3*H*D, W], slot 0 oldest */
+    float *conv_state;       /* [N, 3*H*D, W] in/out, oldest -> newest */
+    const float *g;          /* [N, H*D] log-decay or raw gate input (gate_mode) */
+    const float *beta;       /* [N, H] */
+    const float *A_log;      /* [H] (SAFE / SOFTPLUS) */
+    const float *dt_bias;    /* [H*D] or NULL */
+    float lower_bound;       /* NaN = none; required for SAFE */
+    int gate_mode;
+    int use_qk_l2norm;       /* kda.rs always normalises; 1 is the usual setting */
+    int use_beta_sigmoid;    /* kda.rs passes a logit; 1 is the usual setting */
+    float scale;             /* <= 0 or NaN means D^-1/2 */
+    float *state;            /* [N, H, D, D] in/out, key index major */
+    float *o;                /* [N, H*D] fp32 */
+    void *stream;            /* hipStream_t */
+} kda_step_args;
+
+kda_status kda_recurrent_step(const kda_step_args *a);
+
+/* Static description of a status code.  Thread-safe. */
+const char *kda_status_string(kda_status s);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

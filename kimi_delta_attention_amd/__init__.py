@@ -1,0 +1,227 @@
+"""MI355X-native Kimi Delta Attention: Python binding over the C ABI of libkda.so.
+
+This module only marshals torch tensors (device memory and the current HIP
+stream) into the C structs of include/kda.h; every step of the computation
+runs in the library's HIP kernels.  There is no CPU or eager fallback.
+
+    o, final_state = chunk_kda(q, k, v, g, beta, ...)        # forward
+    grads = chunk_kda_bwd(q, k, v, g, beta, dO, ...)          # backward
+    o = recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, ...)  # decode
+
+The keyword set follows the chunk_kda boundary of the "K3/kda/ops/api.py"
+page without its backend switch; ``cu_seqlens`` adds packed sequences.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import KDA_GATE_LOGDECAY, KDA_GATE_SAFE, KDA_GATE_SOFTPLUS  # noqa: F401
+
+__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_step", "chunk_fwd_workspace_bytes",
+           "chunk_bwd_workspace_bytes", "KDA_GATE_LOGDECAY", "KDA_GATE_SAFE", "KDA_GATE_SOFTPLUS"]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype=None, device=None):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _gate_mode(use_gate_in_kernel, safe_gate, gate_mode):
+    if gate_mode is not None:
+        return int(gate_mode)
+    if not use_gate_in_kernel:
+        return KDA_GATE_LOGDECAY
+    return KDA_GATE_SAFE if safe_gate else KDA_GATE_SOFTPLUS
+
+
+def _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, output_final_state,
+                use_qk_l2norm_in_kernel, gate_mode, use_beta_sigmoid_in_kernel, lower_bound,
+                chunk_size, cu_seqlens):
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B, T, H, K] and v [B, T, H, V]")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("q, k, v must be float32 or bfloat16")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, q.dtype, dev)
+    _need(g, "g", torch.float32, dev)
+    _need(beta, "beta", torch.float32, dev)
+    if tuple(g.shape) != (B, T, H, K) or tuple(beta.shape) != (B, T, H):
+        raise ValueError("g must be [B, T, H, K] and beta [B, T, H]")
+    _need(A_log, "A_log", torch.float32, dev)
+    _need(dt_bias, "dt_bias", torch.float32, dev)
+    if A_log is not None and A_log.numel() != H:
+        raise ValueError("A_log must have H elements")
+    if dt_bias is not None and dt_bias.numel() != H * K:
+        raise ValueError("dt_bias must have H*K elements")
+    N = B
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+        N = cu_seqlens.numel() - 1
+    _need(initial_state, "initial_state", torch.float32, dev)
+    if initial_state is not None and tuple(initial_state.shape) != (N, H, K, V):
+        raise ValueError(f"initial_state must be [{N}, {H}, {K}, {V}]")
+    a = _lib.ChunkArgs()
+    a.B, a.T, a.H, a.K, a.V = B, T, H, K, V
+    a.cu_seqlens = _ptr(cu_seqlens)
+    a.N = N if cu_seqlens is not None else 0
+    a.qkv_dtype = _lib.KDA_BF16 if q.dtype == torch.bfloat16 else _lib.KDA_F32
+    a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    a.A_log, a.dt_bias = _ptr(A_log), _ptr(dt_bias)
+    a.scale = float("nan") if scale is None else float(scale)
+    a.lower_bound = float("nan") if lower_bound is None else float(lower_bound)
+    a.gate_mode = gate_mode
+    a.use_qk_l2norm = int(bool(use_qk_l2norm_in_kernel))
+    a.use_beta_sigmoid = int(bool(use_beta_sigmoid_in_kernel))
+    a.chunk_size = int(chunk_size)
+    a.initial_state = _ptr(initial_state)
+    a.output_final_state = int(bool(output_final_state))
+    a.stream = _stream()
+    return a, (B, T, H, K, V, N, dev)
+
+
+def _workspace(nbytes, dev, workspace):
+    if nbytes == 0:
+        return None
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes or not workspace.is_cuda:
+            raise ValueError(f"workspace must hold {nbytes} bytes")
+        return workspace
+    return torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+
+def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
+              output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
+              use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
+              cu_seqlens=None, gate_mode=None, workspace=None, out=None):
+    """Chunked KDA forward (kda_chunk_fwd).  Returns (o, final_state or None)."""
+    gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
+    a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
+                                             output_final_state, use_qk_l2norm_in_kernel, gm,
+                                             use_beta_sigmoid_in_kernel, lower_bound, chunk_size, cu_seqlens)
+    lib = _lib.load()
+    o = out if out is not None else torch.empty(B, T, H, V, dtype=q.dtype, device=dev)
+    _need(o, "out", q.dtype, dev)
+    fs = torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    a.o, a.final_state = _ptr(o), _ptr(fs)
+    ws = _workspace(lib.kda_chunk_fwd_workspace(ctypes.byref(a)), dev, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(lib.kda_chunk_fwd(ctypes.byref(a)), "kda_chunk_fwd")
+    return o, fs
+
+
+def chunk_fwd_workspace_bytes(q, k, v, g, beta, **kw) -> int:
+    gm = _gate_mode(kw.pop("use_gate_in_kernel", False), kw.pop("safe_gate", False), kw.pop("gate_mode", None))
+    a, _ = _chunk_args(q, k, v, g, beta, kw.get("A_log"), kw.get("dt_bias"), kw.get("scale"),
+                       kw.get("initial_state"), kw.get("output_final_state", False),
+                       kw.get("use_qk_l2norm_in_kernel", False), gm, kw.get("use_beta_sigmoid_in_kernel", False),
+                       kw.get("lower_bound"), kw.get("chunk_size", 64), kw.get("cu_seqlens"))
+    return int(_lib.load().kda_chunk_fwd_workspace(ctypes.byref(a)))
+
+
+def chunk_kda_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bias=None, scale=None,
+                  initial_state=None, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
+                  use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
+                  cu_seqlens=None, gate_mode=None, need_d_initial_state=True, workspace=None):
+    """Chunked KDA backward (kda_chunk_bwd): gradients of <o, dO> + <final_state,
+    d_final_state> w.r.t. q, k, v, g and beta as passed, the initial state and,
+    for in-kernel gates, A_log and dt_bias.  Returns a dict."""
+    gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
+    a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, False,
+                                             use_qk_l2norm_in_kernel, gm, use_beta_sigmoid_in_kernel,
+                                             lower_bound, chunk_size, cu_seqlens)
+    _need(dO, "dO", q.dtype, dev)
+    _need(d_final_state, "d_final_state", torch.float32, dev)
+    lib = _lib.load()
+    out = {
+        "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+        "dg": torch.empty(B, T, H, K, dtype=torch.float32, device=dev),
+        "dbeta": torch.empty(B, T, H, dtype=torch.float32, device=dev),
+        "dh0": torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if need_d_initial_state else None,
+        "dA_log": None, "ddt_bias": None,
+    }
+    if gm != KDA_GATE_LOGDECAY:
+        out["dA_log"] = torch.empty(H, dtype=torch.float32, device=dev)
+        out["ddt_bias"] = torch.empty(H * K, dtype=torch.float32, device=dev)
+    gr = _lib.ChunkGrads()
+    gr.dO, gr.d_final_state = _ptr(dO), _ptr(d_final_state)
+    gr.dq, gr.dk, gr.dv = _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"])
+    gr.dg, gr.dbeta, gr.d_initial_state = _ptr(out["dg"]), _ptr(out["dbeta"]), _ptr(out["dh0"])
+    gr.dA_log, gr.ddt_bias = _ptr(out["dA_log"]), _ptr(out["ddt_bias"])
+    ws = _workspace(lib.kda_chunk_bwd_workspace(ctypes.byref(a)), dev, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _lib.check(lib.kda_chunk_bwd(ctypes.byref(a), ctypes.byref(gr)), "kda_chunk_bwd")
+    return out
+
+
+def recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, *, A_log=None, dt_bias=None, lower_bound=None,
+                   use_gate_in_kernel=False, safe_gate=False, gate_mode=None, use_qk_l2norm=True,
+                   use_beta_sigmoid=True, scale=None, out=None):
+    """One decode token per sequence with the short-conv update
+    (kda_recurrent_step).  conv_state and state are updated in place.
+    Returns o [N, H*D] fp32."""
+    if state.dim() != 4 or state.shape[2] != state.shape[3]:
+        raise ValueError("state must be [N, H, D, D]")
+    N, H, D, _ = state.shape
+    if conv_w.dim() != 2 or conv_w.shape[0] != 3 * H * D:
+        raise ValueError("conv_w must be [3*H*D, W]")
+    W = conv_w.shape[1]
+    if tuple(x_qkv.shape) != (N, 3 * H * D) or tuple(conv_state.shape) != (N, 3 * H * D, W):
+        raise ValueError("x_qkv must be [N, 3*H*D] and conv_state [N, 3*H*D, W]")
+    if tuple(g.shape) != (N, H * D) or tuple(beta.shape) != (N, H):
+        raise ValueError("g must be [N, H*D] and beta [N, H]")
+    dev = state.device
+    if x_qkv.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x_qkv must be float32 or bfloat16")
+    _need(x_qkv, "x_qkv", None, dev)
+    for name, t in (("conv_w", conv_w), ("conv_state", conv_state), ("g", g), ("beta", beta), ("state", state),
+                    ("A_log", A_log), ("dt_bias", dt_bias)):
+        _need(t, name, torch.float32, dev)
+    o = out if out is not None else torch.empty(N, H * D, dtype=torch.float32, device=dev)
+    _need(o, "out", torch.float32, dev)
+    a = _lib.StepArgs()
+    a.N, a.H, a.D, a.W = N, H, D, W
+    a.x_dtype = _lib.KDA_BF16 if x_qkv.dtype == torch.bfloat16 else _lib.KDA_F32
+    a.x_qkv, a.conv_w, a.conv_state = _ptr(x_qkv), _ptr(conv_w), _ptr(conv_state)
+    a.g, a.beta, a.A_log, a.dt_bias = _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias)
+    a.lower_bound = float("nan") if lower_bound is None else float(lower_bound)
+    a.gate_mode = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
+    a.use_qk_l2norm, a.use_beta_sigmoid = int(bool(use_qk_l2norm)), int(bool(use_beta_sigmoid))
+    a.scale = float("nan") if scale is None else float(scale)
+    a.state, a.o = _ptr(state), _ptr(o)
+    a.stream = _stream()
+    _lib.check(_lib.load().kda_recurrent_step(ctypes.byref(a)), "kda_recurrent_step")
+    return o
+
+
+def chunk_bwd_workspace_bytes(q, k, v, g, beta, **kw) -> int:
+    gm = _gate_mode(kw.pop("use_gate_in_kernel", False), kw.pop("safe_gate", False), kw.pop("gate_mode", None))
+    a, _ = _chunk_args(q, k, v, g, beta, kw.get("A_log"), kw.get("dt_bias"), kw.get("scale"),
+                       kw.get("initial_state"), False, kw.get("use_qk_l2norm_in_kernel", False), gm,
+                       kw.get("use_beta_sigmoid_in_kernel", False), kw.get("lower_bound"),
+                       kw.get("chunk_size", 64), kw.get("cu_seqlens"))
+    return int(_lib.load().kda_chunk_bwd_workspace(ctypes.byref(a)))
+

@@ -1,0 +1,160 @@
+// kda_api.cpp -- the C ABI declared in include/kda.h: host-side validation
+// (nothing is launched on any error) and dispatch to the kernels.
+#include <cmath>
+#include <cstdint>
+
+#include "kda.h"
+#include "kda_launch.hpp"
+
+namespace {
+
+constexpr int kVersion = 1 * 10000 + 0 * 100 + 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
+
+// Shared validation of the chunk arguments; fills the internal launch params.
+kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p) {
+    if (!a) return KDA_ERR_INVALID_ARG;
+    if (a->B <= 0 || a->T < 0 || a->H <= 0 || a->K <= 0 || a->V <= 0) return KDA_ERR_INVALID_ARG;
+    if (a->qkv_dtype != KDA_F32 && a->qkv_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (a->chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if (!supported_dim(a->K) || a->K != a->V) return KDA_ERR_UNSUPPORTED;
+    if (a->qkv_dtype == KDA_F32 && a->K > 64) return KDA_ERR_UNSUPPORTED;  // LDS budget
+    if (a->gate_mode < KDA_GATE_LOGDECAY || a->gate_mode > KDA_GATE_SOFTPLUS) return KDA_ERR_INVALID_ARG;
+    if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
+    if (a->use_beta_sigmoid != 0 && a->use_beta_sigmoid != 1) return KDA_ERR_INVALID_ARG;
+    int N = a->B;
+    if (a->cu_seqlens) {
+        if (a->B != 1 || a->N <= 0) return KDA_ERR_INVALID_ARG;
+        N = a->N;
+    }
+    if (a->gate_mode != KDA_GATE_LOGDECAY && !a->A_log) return KDA_ERR_MISSING_PARAM;
+    if (a->gate_mode == KDA_GATE_SAFE && std::isnan(a->lower_bound)) return KDA_ERR_MISSING_PARAM;
+    const int64_t rows = static_cast<int64_t>(a->B) * a->T;
+    if (rows > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)) return KDA_ERR_INVALID_ARG;
+    if (a->output_final_state && !a->final_state) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {a->q, a->k, a->v, a->g, a->o, a->initial_state, a->final_state};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    // element indices are formed in 64-bit; chunk counts and grid sizes in 32-bit
+    if (rows * a->H > (int64_t(1) << 40)) return KDA_ERR_UNSUPPORTED;
+
+    p.B = a->B; p.T = a->T; p.H = a->H; p.K = a->K; p.V = a->V;
+    p.N = N;
+    p.cu_seqlens = a->cu_seqlens;
+    p.bf16 = a->qkv_dtype == KDA_BF16;
+    p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
+    p.A_log = a->A_log;
+    p.dt_bias = a->dt_bias;
+    p.scale = (std::isnan(a->scale) || a->scale <= 0.f) ? 1.0f / std::sqrt(static_cast<float>(a->K)) : a->scale;
+    p.lower_bound = a->lower_bound;
+    p.gate_mode = a->gate_mode;
+    p.use_qk_l2norm = a->use_qk_l2norm;
+    p.use_beta_sigmoid = a->use_beta_sigmoid;
+    p.bounded = false;
+    p.h0 = a->initial_state;
+    p.o = a->o;
+    p.ht = a->output_final_state ? a->final_state : nullptr;
+    const int64_t nc_dense = (static_cast<int64_t>(a->T) + 63) / 64;
+    const int64_t bound = a->cu_seqlens ? nc_dense + N : nc_dense * N;
+    if (bound * a->H > INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
+    p.max_chunks = static_cast<int>(nc_dense);
+    p.total_chunks_bound = static_cast<int>(bound);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KDA_ERR_MISSING_PARAM: return "missing gate parameter (A_log, or lower_bound for the safe gate)";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int kda_version(void) { return kVersion; }
+
+size_t kda_chunk_fwd_workspace(const kda_chunk_args* a) {
+    kda::ChunkParams p{};
+    if (check_chunk(a, p) != KDA_OK) return 0;
+    return kda::chunk_fwd_workspace(p);
+}
+
+kda_status kda_chunk_fwd(const kda_chunk_args* a) {
+    kda::ChunkParams p{};
+    kda_status st = check_chunk(a, p);
+    if (st != KDA_OK) return st;
+    const size_t need = kda::chunk_fwd_workspace(p);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (a->workspace && !aligned16(a->workspace)) return KDA_ERR_WORKSPACE;
+    hipError_t e = kda::launch_chunk_fwd(p, a->workspace, static_cast<hipStream_t>(a->stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_chunk_bwd_workspace(const kda_chunk_args* a) {
+    kda::ChunkParams p{};
+    if (check_chunk(a, p) != KDA_OK) return 0;
+    return kda::chunk_bwd_workspace(p);
+}
+
+kda_status kda_chunk_bwd(const kda_chunk_args* a, const kda_chunk_grads* gr) {
+    kda::ChunkParams p{};
+    kda_status st = check_chunk(a, p);
+    if (st != KDA_OK) return st;
+    if (!gr) return KDA_ERR_INVALID_ARG;
+    const int64_t rows = static_cast<int64_t>(a->B) * a->T;
+    if (rows > 0 && (!gr->dO || !gr->dq || !gr->dk || !gr->dv || !gr->dg || !gr->dbeta))
+        return KDA_ERR_INVALID_ARG;
+    const void* gptrs[] = {gr->dO, gr->d_final_state, gr->dq, gr->dk, gr->dv, gr->dg, gr->d_initial_state};
+    for (const void* ptr : gptrs)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    if (a->gate_mode == KDA_GATE_LOGDECAY && (gr->dA_log || gr->ddt_bias)) return KDA_ERR_INVALID_ARG;
+    const size_t need = kda::chunk_bwd_workspace(p);
+    if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (a->workspace && !aligned16(a->workspace)) return KDA_ERR_WORKSPACE;
+    kda::ChunkGrads g{};
+    g.dO = gr->dO; g.dht = gr->d_final_state;
+    g.dq = gr->dq; g.dk = gr->dk; g.dv = gr->dv; g.dg = gr->dg; g.dbeta = gr->dbeta;
+    g.dh0 = gr->d_initial_state; g.dA_log = gr->dA_log; g.ddt_bias = gr->ddt_bias;
+    hipError_t e = kda::launch_chunk_bwd(p, g, a->workspace, static_cast<hipStream_t>(a->stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_recurrent_step(const kda_step_args* a) {
+    if (!a) return KDA_ERR_INVALID_ARG;
+    if (a->N < 0 || a->H <= 0 || a->D <= 0 || a->W < 1 || a->W > 8) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(a->D)) return KDA_ERR_UNSUPPORTED;
+    if (a->x_dtype != KDA_F32 && a->x_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (a->gate_mode < KDA_GATE_LOGDECAY || a->gate_mode > KDA_GATE_SOFTPLUS) return KDA_ERR_INVALID_ARG;
+    if (a->gate_mode != KDA_GATE_LOGDECAY && !a->A_log) return KDA_ERR_MISSING_PARAM;
+    if (a->gate_mode == KDA_GATE_SAFE && std::isnan(a->lower_bound)) return KDA_ERR_MISSING_PARAM;
+    if (a->N == 0) return KDA_OK;
+    if (!a->x_qkv || !a->conv_w || !a->conv_state || !a->g || !a->beta || !a->state || !a->o)
+        return KDA_ERR_INVALID_ARG;
+    const void* sptrs[] = {a->conv_w, a->conv_state, a->state};
+    for (const void* ptr : sptrs)
+        if (!aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(a->N) > 65535) return KDA_ERR_UNSUPPORTED;  // grid y
+    kda::DecodeParams p{};
+    p.N = a->N; p.H = a->H; p.D = a->D; p.W = a->W;
+    p.x_bf16 = a->x_dtype == KDA_BF16;
+    p.x = a->x_qkv; p.conv_w = a->conv_w; p.conv_state = a->conv_state;
+    p.g = a->g; p.beta = a->beta; p.A_log = a->A_log; p.dt_bias = a->dt_bias;
+    p.lower_bound = a->lower_bound; p.gate_mode = a->gate_mode;
+    p.use_qk_l2norm = a->use_qk_l2norm; p.use_beta_sigmoid = a->use_beta_sigmoid;
+    p.scale = (std::isnan(a->scale) || a->scale <= 0.f) ? 1.0f / std::sqrt(static_cast<float>(a->D)) : a->scale;
+    p.state = a->state; p.o = a->o;
+    hipError_t e = kda::launch_decode(p, static_cast<hipStream_t>(a->stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

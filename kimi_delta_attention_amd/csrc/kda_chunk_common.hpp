@@ -1,0 +1,158 @@
+// kda_chunk_common.hpp -- pieces shared by the chunked forward and backward
+// kernels: chunk geometry, MFMA tile helpers and the workspace layout.
+//
+// Chunk size is fixed at 64 tokens; inside a chunk rows are grouped in four
+// 16-row sub-blocks (the MFMA tile height).
+#pragma once
+
+#include "kda_device.hpp"
+#include "kda_launch.hpp"
+
+#include <type_traits>
+
+namespace kda {
+
+constexpr int kChunk = 64;
+constexpr int kSub = 16;
+constexpr int kThreads = 256;
+// Diagonal 16-row sub-blocks whose accumulated decay span stays under this
+// bound are factorised through the row before the block (factors up to
+// e^kSpanLimit, finite in fp32); wider spans are formed pairwise.
+constexpr float kSpanLimit = 85.0f;
+
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- MFMA tiles
+// C[16x16] += A[16 x KS] * B[KS x 16] with both operands stored k-contiguous
+// in LDS: A as [m][k], B transposed as [n][k].  Lane l supplies row l%16 and
+// the k-slice (l/16)*KPL .. +KPL; the accumulator holds column l%16, rows
+// 4*(l/16) .. +3.
+template <bool BF> struct Mma;
+
+template <> struct Mma<true> {        // bf16 inputs, fp32 accumulate
+    using ET = uint16_t;              // LDS / workspace element (bf16 bits)
+    static constexpr int KS = 32;
+    static constexpr int KPL = 8;
+    static constexpr int PAD = 8;     // row padding (elements) against bank conflicts
+    using Frag = bf16x8;
+    __device__ __forceinline__ static Frag load(const ET* base, int ld, int r0, int k0, int lane) {
+        return *reinterpret_cast<const Frag*>(base + (r0 + (lane & 15)) * ld + k0 + (lane >> 4) * 8);
+    }
+    __device__ __forceinline__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // Fragment times 8 per-k factors (fp32), rounded back to bf16.
+    __device__ __forceinline__ static Frag scale(Frag f, const float* s) {
+        u16x8 u = __builtin_bit_cast(u16x8, f);
+        u16x8 r;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) r[j] = f32_to_bf16_bits(bf16_bits_to_f32(u[j]) * s[j]);
+        return __builtin_bit_cast(Frag, r);
+    }
+    __device__ __forceinline__ static ET from_f32(float x) { return f32_to_bf16_bits(x); }
+    __device__ __forceinline__ static float to_f32(ET x) { return bf16_bits_to_f32(x); }
+};
+
+template <> struct Mma<false> {       // fp32 inputs, fp32 accumulate
+    using ET = float;
+    static constexpr int KS = 4;
+    static constexpr int KPL = 1;
+    static constexpr int PAD = 4;     // keeps rows 16-byte aligned and conflict-free
+    using Frag = float;
+    __device__ __forceinline__ static Frag load(const ET* base, int ld, int r0, int k0, int lane) {
+        return base[(r0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+    }
+    __device__ __forceinline__ static f32x4 mma(Frag a, Frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ __forceinline__ static Frag scale(Frag f, const float* s) { return f * s[0]; }
+    __device__ __forceinline__ static ET from_f32(float x) { return x; }
+    __device__ __forceinline__ static float to_f32(ET x) { return x; }
+};
+
+// ---------------------------------------------------------------- geometry
+// Sequence bounds: dense input (cu == nullptr) or packed offsets.  Offsets are
+// clamped into [0, T_total] so malformed device data cannot move an access
+// outside the tensors.
+__device__ __forceinline__ void seq_bounds(const ChunkParams& p, int n, int64_t& start, int& len) {
+    if (p.cu_seqlens) {
+        const int64_t total = static_cast<int64_t>(p.T);
+        int64_t a = p.cu_seqlens[n], b = p.cu_seqlens[n + 1];
+        a = a < 0 ? 0 : (a > total ? total : a);
+        b = b < a ? a : (b > total ? total : b);
+        start = a;
+        len = static_cast<int>(b - a);
+    } else {
+        start = static_cast<int64_t>(n) * p.T;
+        len = p.T;
+    }
+}
+
+__device__ __forceinline__ int n_chunks(int len) { return (len + kChunk - 1) / kChunk; }
+
+// Workspace layout of the per-chunk operands produced by the prep kernel, per
+// (chunk, head) slot, all [row][col] with the column fastest:
+//   QE  [64][K]  scale * q^ * exp(G)            (ET)
+//   KE  [64][K]  k^ * exp(G)                    (ET)
+//   KD  [64][K]  k^ * exp(G_last - G)           (ET)
+//   TB  [64][64] (I + A)^-1 * diag(beta)        (ET)
+//   MS  [64][64] scale * tril(q^ k^T decayed)   (ET)
+//   GC  [K]      exp(G_last)                    (fp32)
+// G is the inclusive cumulative log-decay inside the chunk.
+template <int K, bool BF>
+struct PrepLayout {
+    using ET = typename Mma<BF>::ET;
+    static constexpr size_t kQE = 0;
+    static constexpr size_t kKE = kQE + sizeof(ET) * kChunk * K;
+    static constexpr size_t kKD = kKE + sizeof(ET) * kChunk * K;
+    static constexpr size_t kTB = kKD + sizeof(ET) * kChunk * K;
+    static constexpr size_t kMS = kTB + sizeof(ET) * kChunk * kChunk;
+    static constexpr size_t kGC = kMS + sizeof(ET) * kChunk * kChunk;
+    static constexpr size_t kBytes = ((kGC + sizeof(float) * K) + 255) / 256 * 256;
+};
+
+// Chunk slot of chunk j of sequence n (slots are numbered over all sequences).
+__device__ __forceinline__ int64_t chunk_slot(const ChunkParams& p, const int32_t* chunk_off, int n,
+                                              int j) {
+    const int64_t base = p.cu_seqlens ? chunk_off[n] : static_cast<int64_t>(n) * n_chunks(p.T);
+    return base + j;
+}
+
+// Inverse of chunk_slot for the parallel kernels: slot c -> (n, j); returns
+// false when c is past the last chunk.
+__device__ __forceinline__ bool slot_to_chunk(const ChunkParams& p, const int32_t* chunk_off, int c,
+                                              int& n, int& j) {
+    if (!p.cu_seqlens) {
+        const int nc = n_chunks(p.T);
+        if (nc == 0) return false;
+        n = c / nc;
+        j = c % nc;
+        return n < p.N;
+    }
+    if (c >= chunk_off[p.N]) return false;
+    int lo = 0, hi = p.N - 1;  // last n with chunk_off[n] <= c
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    n = lo;
+    j = c - chunk_off[lo];
+    return true;
+}
+
+// Column-block grid remap: all V-column blocks of one (sequence, head) chain
+// get block ids with the same residue mod 8, i.e. land on the same XCD and
+// share its L2 for the chain's per-chunk operands.
+__device__ __forceinline__ bool chain_of_block(int bid, int n_chains, int nvb, int& chain, int& vb) {
+    const int grp = bid / (8 * nvb);
+    const int rem = bid % (8 * nvb);
+    vb = rem / 8;
+    chain = grp * 8 + rem % 8;
+    return chain < n_chains;
+}
+
+__host__ __device__ constexpr int chain_grid(int n_chains, int nvb) {
+    return ((n_chains + 7) / 8) * 8 * nvb;
+}
+
+}  // namespace kda

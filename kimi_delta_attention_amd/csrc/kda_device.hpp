@@ -1,0 +1,67 @@
+// kda_device.hpp -- device-side helpers shared by the KDA kernels (gfx950).
+//
+// Wavefront size is 64 on CDNA4; every helper below assumes it.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kWave = 64;
+constexpr float kL2Eps = 1e-6f;  // q/k normalisation epsilon of the in-kernel L2 norm
+
+enum GateMode : int { GATE_LOGDECAY = 0, GATE_SAFE = 1, GATE_SOFTPLUS = 2 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 <-> fp32.  Widening is exact; narrowing rounds to nearest even.
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) {           // inf / nan: keep, quiet nans
+        return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    __device__ __forceinline__ static float load(const float* p, int64_t i) { return p[i]; }
+    __device__ __forceinline__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
+    __device__ __forceinline__ static float load(const uint16_t* p, int64_t i) {
+        return bf16_bits_to_f32(p[i]);
+    }
+    __device__ __forceinline__ static void store(uint16_t* p, int64_t i, float v) {
+        p[i] = f32_to_bf16_bits(v);
+    }
+};
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// log(1 + e^x) without overflow: max(x, 0) + log1p(e^-|x|).
+__device__ __forceinline__ float softplusf_(float x) {
+    return fmaxf(x, 0.0f) + log1pf(__expf(-fabsf(x)));
+}
+
+// Per-channel log-decay from the raw gate input (see kda_gate_mode in kda.h).
+__device__ __forceinline__ float gate_eff(int mode, float x, float rate, float bias, float lb) {
+    if (mode == GATE_LOGDECAY) return x;
+    float z = x + bias;
+    if (mode == GATE_SAFE) return lb * sigmoidf_(rate * z);
+    return -rate * softplusf_(z);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+}  // namespace kda

@@ -1,0 +1,77 @@
+// kda_launch.hpp -- internal launch interface between the C ABI (kda_api.cpp)
+// and the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeParams {
+    int N, H, D, W;
+    bool x_bf16;
+    const void* x;
+    const float* conv_w;
+    float* conv_state;
+    const float* g;
+    const float* beta;
+    const float* A_log;
+    const float* dt_bias;
+    float lower_bound;
+    int gate_mode;
+    int use_qk_l2norm;
+    int use_beta_sigmoid;
+    float scale;
+    float* state;
+    float* o;
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
+
+// Chunked path.  Sizes are validated by the caller.
+struct ChunkParams {
+    int B, T, H, K, V;
+    int N;                     // number of sequences
+    const int32_t* cu_seqlens; // device [N+1] or nullptr (dense)
+    bool bf16;                 // q, k, v, o, dO, dq, dk, dv in bf16 (else fp32)
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const float* A_log;
+    const float* dt_bias;
+    float scale;
+    float lower_bound;         // NaN when absent
+    int gate_mode;
+    int use_qk_l2norm;
+    int use_beta_sigmoid;
+    bool bounded;              // every log-decay is >= lower_bound with 16*|lb| <= 80
+    const float* h0;           // [N,H,K,V] or nullptr
+    void* o;
+    float* ht;                 // [N,H,K,V] or nullptr
+    int max_chunks;            // upper bound of chunks per sequence
+    int total_chunks_bound;    // upper bound of sum over sequences of chunks
+};
+
+struct ChunkGrads {
+    const void* dO;
+    const float* dht;          // [N,H,K,V] or nullptr
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dg;
+    float* dbeta;
+    float* dh0;                // or nullptr
+    float* dA_log;             // or nullptr
+    float* ddt_bias;           // or nullptr
+};
+
+size_t chunk_fwd_workspace(const ChunkParams& p);
+hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st);
+
+size_t chunk_bwd_workspace(const ChunkParams& p);
+hipError_t launch_chunk_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st);
+
+}  // namespace kda

@@ -1,0 +1,115 @@
+"""GPU parity of kda_recurrent_step against the CPU oracle's decode step."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kimi_delta_attention_amd as kda
+from kimi_delta_attention_amd import inputs
+from parity import check, dev, TOL_F32
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_steps(init, steps, N, H, D, x_dtype, **kw):
+    cw = dev(init["conv_w"])
+    cs = dev(init["conv_state"]).clone()
+    st = dev(init["state"]).clone()
+    outs = []
+    for s in steps:
+        o = kda.recurrent_step(dev(s["x"].to(x_dtype)), cw, cs, dev(s["g"]), dev(s["beta"]), st, **kw)
+        outs.append(o.clone())
+    torch.cuda.synchronize()
+    return outs, cs, st
+
+
+def _oracle_steps(init, steps, x_dtype, **kw):
+    cs = init["conv_state"]
+    st = init["state"]
+    outs = []
+    for s in steps:
+        o, cs, st = oracle.decode_step(s["x"].to(x_dtype), init["conv_w"], cs, s["g"], s["beta"], st, **kw)
+        outs.append(o)
+    return outs, cs, st
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("x_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("W", [4, 3])
+def test_decode_small(D, x_dtype, W):
+    N, H, T = 3, 2, 5
+    init = inputs.decode_init(N, H, D, W, seed=11 + D + W)
+    steps = [inputs.decode_step_inputs(N, H, D, seed=5, step=t) for t in range(T)]
+    print(f"decode N={N} H={H} D={D} W={W} x={x_dtype}", flush=True)
+    go, gcs, gst = _gpu_steps(init, steps, N, H, D, x_dtype)
+    oo, ocs, ost = _oracle_steps(init, steps, x_dtype)
+    for t in range(T):
+        check(f"o[{t}]", go[t], oo[t], TOL_F32)
+    check("state", gst, ost, TOL_F32)
+    check("conv_state", gcs, ocs, TOL_F32)
+
+
+@pytest.mark.parametrize("mode", [kda.KDA_GATE_SAFE, kda.KDA_GATE_SOFTPLUS])
+def test_decode_gate_modes_and_flags(mode):
+    N, H, D, W = 2, 3, 64, 4
+    init = inputs.decode_init(N, H, D, W, seed=3)
+    steps = [inputs.decode_step_inputs(N, H, D, seed=9, step=t) for t in range(3)]
+    gen = torch.Generator().manual_seed(4)
+    A_log = torch.rand(H, generator=gen) * np.log(16.0)
+    dt = torch.randn(H * D, generator=gen) * 0.1
+    lb = -5.0 if mode == kda.KDA_GATE_SAFE else None
+    for st_ in steps:  # raw gate inputs for the in-kernel gate
+        st_["g"] = torch.randn(N, H * D, generator=gen)
+    kw_gpu = dict(gate_mode=mode, A_log=dev(A_log), dt_bias=dev(dt), lower_bound=lb, scale=0.3)
+    kw_or = dict(gate_mode=mode, A_log=A_log, dt_bias=dt, lower_bound=lb, scale=0.3)
+    go, gcs, gst = _gpu_steps(init, steps, N, H, D, torch.float32, **kw_gpu)
+    oo, ocs, ost = _oracle_steps(init, steps, torch.float32, **kw_or)
+    for t in range(3):
+        check(f"o[{t}]", go[t], oo[t], TOL_F32)
+    check("state", gst, ost, TOL_F32)
+    # beta as a value and no normalisation
+    go, _, gst = _gpu_steps(init, steps[:1], N, H, D, torch.float32, use_beta_sigmoid=False,
+                            use_qk_l2norm=False, **kw_gpu)
+    oo, _, ost = _oracle_steps(init, steps[:1], torch.float32, use_beta_sigmoid=False,
+                               use_qk_l2norm=False, **kw_or)
+    check("o/noflags", go[0], oo[0], TOL_F32)
+    check("state/noflags", gst, ost, TOL_F32)
+
+
+def test_decode_production_geometry_sampled():
+    """64 sequences x 96 heads x d128, 256 consecutive steps in place; sampled
+    (sequence, head) units are compared with the oracle after every 32 steps.
+    Units are independent, so the oracle runs on the sampled units alone."""
+    shp = inputs.DECODE_SHAPE
+    N, H, D, W = shp["N"], shp["H"], shp["D"], shp["W"]
+    seed = inputs.SEEDS["decode"]
+    init = inputs.decode_init(N, H, D, W, seed=seed)
+    units = [(0, 0), (5, 17), (33, 95), (63, 48), (17, 3), (48, 64)]
+    HD = H * D
+    # per-unit oracle state
+    def chan(h):
+        return np.concatenate([np.arange(p * HD + h * D, p * HD + h * D + D) for p in range(3)])
+    ost = {u: (init["conv_state"][u[0]][chan(u[1])].double().numpy()[None],
+               init["state"][u[0], u[1]].double().numpy()[None, None]) for u in units}
+    cw = dev(init["conv_w"])
+    cs = dev(init["conv_state"])
+    st = dev(init["state"])
+    print("decode production geometry: 256 steps", flush=True)
+    for t in range(256):
+        s = inputs.decode_step_inputs(N, H, D, seed=seed, step=t)
+        o = kda.recurrent_step(dev(s["x"]), cw, cs, dev(s["g"]), dev(s["beta"]), st)
+        for u in units:
+            n, h = u
+            c = chan(h)
+            oo, ocs, ostt = oracle.decode_step(s["x"][n:n + 1, c], init["conv_w"][c], ost[u][0],
+                                               s["g"][n:n + 1, h * D:(h + 1) * D], s["beta"][n:n + 1, h:h + 1],
+                                               ost[u][1], threads=1)
+            ost[u] = (ocs, ostt)
+            if (t + 1) % 32 == 0:
+                check(f"o step {t} unit {u}", o[n, h * D:(h + 1) * D], oo[0], TOL_F32)
+        if (t + 1) % 32 == 0:
+            for u in units:
+                n, h = u
+                check(f"state step {t} unit {u}", st[n, h], ost[u][1][0, 0], TOL_F32)
+                check(f"conv step {t} unit {u}", cs[n][chan(h)], ost[u][0][0], TOL_F32)
+            print(f"  step {t + 1} ok", flush=True)
