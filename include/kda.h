@@ -135,10 +135,33 @@ typedef struct {
 kda_status kda_chunk_fwd(const kda_chunk_args *a);
 size_t kda_chunk_fwd_workspace(const kda_chunk_args *a);
 
+/* Stage-split forward, for profilers that time each kernel with stream
+ * events.  Calling stage 0 then stage 1 with the same arguments (and the
+ * same workspace) on one stream is identical to kda_chunk_fwd:
+ *   stage 0  per-chunk preparation (fully parallel over chunk x head);
+ *   stage 1  sequential state pass and output (parallel over sequence x head
+ *            x value-column block).
+ * Other stage numbers return KDA_ERR_INVALID_ARG. */
+kda_status kda_chunk_fwd_stage(const kda_chunk_args *a, int stage);
+
 /* Chunked backward: gradients of <o, dO> + <final_state, d_final_state>.
  * Uses the same args as the forward (o and final_state are not read). */
 kda_status kda_chunk_bwd(const kda_chunk_args *a, const kda_chunk_grads *gr);
 size_t kda_chunk_bwd_workspace(const kda_chunk_args *a);
+
+/* Stage-split backward, for per-kernel timing (see kda_chunk_fwd_stage).
+ * Stages 0 .. kda_chunk_bwd_stages()-1 called in order with the same
+ * arguments and workspace equal one kda_chunk_bwd call:
+ *   0  per-chunk preparation (as the forward's, plus (I + A)^-1 and the
+ *      un-scaled k-k scores);
+ *   1  forward state pass, storing every chunk's entry state;
+ *   2  reverse state pass, storing every chunk's exit-state gradient and
+ *      writing d_initial_state;
+ *   3  per chunk: dv and the value-summed operand gradients;
+ *   4  per chunk: dq, dk, dg, dbeta, and the reduction of dA_log / ddt_bias.
+ * Other stage numbers return KDA_ERR_INVALID_ARG. */
+kda_status kda_chunk_bwd_stage(const kda_chunk_args *a, const kda_chunk_grads *gr, int stage);
+int kda_chunk_bwd_stages(void);
 
 /* One decode token per sequence ("atlas_core/kimi_k3/kda.rs" page,
  * kda_decode_token = conv_update followed by kda_recurrent_step):

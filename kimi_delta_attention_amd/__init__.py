@@ -225,3 +225,69 @@ def chunk_bwd_workspace_bytes(q, k, v, g, beta, **kw) -> int:
                        kw.get("chunk_size", 64), kw.get("cu_seqlens"))
     return int(_lib.load().kda_chunk_bwd_workspace(ctypes.byref(a)))
 
+
+
+class ChunkOp:
+    """A prepared chunk_kda call: the C argument structs, outputs and workspace
+    are built once, so repeated calls (benchmarks, training loops) pay no
+    Python marshalling.  ``forward(stage)`` / ``backward(stage)`` run the whole
+    operator (stage None) or one stage of it (for per-kernel timing)."""
+
+    def __init__(self, q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
+                 output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
+                 use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
+                 cu_seqlens=None, gate_mode=None, dO=None, d_final_state=None, need_d_initial_state=True):
+        gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
+        self._keep = [q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dO, d_final_state]
+        a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
+                                                 output_final_state, use_qk_l2norm_in_kernel, gm,
+                                                 use_beta_sigmoid_in_kernel, lower_bound, chunk_size, cu_seqlens)
+        lib = _lib.load()
+        self.lib = lib
+        self.o = torch.empty(B, T, H, V, dtype=q.dtype, device=dev)
+        self.final_state = torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+        a.o, a.final_state = _ptr(self.o), _ptr(self.final_state)
+        nb = lib.kda_chunk_fwd_workspace(ctypes.byref(a))
+        self.grads = None
+        if dO is not None:
+            _need(dO, "dO", q.dtype, dev)
+            _need(d_final_state, "d_final_state", torch.float32, dev)
+            nb = max(nb, lib.kda_chunk_bwd_workspace(ctypes.byref(a)))
+            self.grads = {
+                "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+                "dg": torch.empty(B, T, H, K, dtype=torch.float32, device=dev),
+                "dbeta": torch.empty(B, T, H, dtype=torch.float32, device=dev),
+                "dh0": torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if need_d_initial_state else None,
+                "dA_log": torch.empty(H, dtype=torch.float32, device=dev) if gm != KDA_GATE_LOGDECAY else None,
+                "ddt_bias": torch.empty(H * K, dtype=torch.float32, device=dev) if gm != KDA_GATE_LOGDECAY else None,
+            }
+            gr = _lib.ChunkGrads()
+            gr.dO, gr.d_final_state = _ptr(dO), _ptr(d_final_state)
+            for name, f in (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dg", "dg"), ("dbeta", "dbeta"),
+                            ("dh0", "d_initial_state"), ("dA_log", "dA_log"), ("ddt_bias", "ddt_bias")):
+                setattr(gr, f, _ptr(self.grads[name]))
+            self.gr = gr
+        self.workspace = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        a.workspace = _ptr(self.workspace)
+        a.workspace_bytes = self.workspace.numel()
+        self.args = a
+
+    def set_stream(self, stream):
+        self.args.stream = ctypes.c_void_p(stream.cuda_stream)
+
+    def forward(self, stage=None):
+        if stage is None:
+            _lib.check(self.lib.kda_chunk_fwd(ctypes.byref(self.args)), "kda_chunk_fwd")
+        else:
+            _lib.check(self.lib.kda_chunk_fwd_stage(ctypes.byref(self.args), int(stage)), "kda_chunk_fwd_stage")
+        return self.o, self.final_state
+
+    def backward(self, stage=None):
+        if self.grads is None:
+            raise ValueError("ChunkOp was built without dO")
+        if stage is None:
+            _lib.check(self.lib.kda_chunk_bwd(ctypes.byref(self.args), ctypes.byref(self.gr)), "kda_chunk_bwd")
+        else:
+            _lib.check(self.lib.kda_chunk_bwd_stage(ctypes.byref(self.args), ctypes.byref(self.gr), int(stage)),
+                       "kda_chunk_bwd_stage")
+        return self.grads

@@ -60,8 +60,9 @@ class StepArgs(ctypes.Structure):
 
 
 # Every symbol include/kda.h declares.
-EXPORTS = ["kda_chunk_fwd", "kda_chunk_fwd_workspace", "kda_chunk_bwd", "kda_chunk_bwd_workspace",
-           "kda_recurrent_step", "kda_status_string", "kda_version"]
+EXPORTS = ["kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace", "kda_chunk_bwd",
+           "kda_chunk_bwd_stage", "kda_chunk_bwd_stages", "kda_chunk_bwd_workspace", "kda_recurrent_step",
+           "kda_status_string", "kda_version"]
 
 _lib = None
 
@@ -78,10 +79,16 @@ def load(path: str = LIB_PATH):
     CA = ctypes.POINTER(ChunkArgs)
     lib.kda_chunk_fwd.argtypes = [CA]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_stage.argtypes = [CA, ctypes.c_int]
+    lib.kda_chunk_fwd_stage.restype = ctypes.c_int
     lib.kda_chunk_fwd_workspace.argtypes = [CA]
     lib.kda_chunk_fwd_workspace.restype = ctypes.c_size_t
     lib.kda_chunk_bwd.argtypes = [CA, ctypes.POINTER(ChunkGrads)]
     lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd_stage.argtypes = [CA, ctypes.POINTER(ChunkGrads), ctypes.c_int]
+    lib.kda_chunk_bwd_stage.restype = ctypes.c_int
+    lib.kda_chunk_bwd_stages.argtypes = []
+    lib.kda_chunk_bwd_stages.restype = ctypes.c_int
     lib.kda_chunk_bwd_workspace.argtypes = [CA]
     lib.kda_chunk_bwd_workspace.restype = ctypes.c_size_t
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(StepArgs)]

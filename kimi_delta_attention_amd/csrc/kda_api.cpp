@@ -15,7 +15,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
 
 // Shared validation of the chunk arguments; fills the internal launch params.
-kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p) {
+kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forward) {
     if (!a) return KDA_ERR_INVALID_ARG;
     if (a->B <= 0 || a->T < 0 || a->H <= 0 || a->K <= 0 || a->V <= 0) return KDA_ERR_INVALID_ARG;
     if (a->qkv_dtype != KDA_F32 && a->qkv_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
@@ -33,8 +33,9 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p) {
     if (a->gate_mode != KDA_GATE_LOGDECAY && !a->A_log) return KDA_ERR_MISSING_PARAM;
     if (a->gate_mode == KDA_GATE_SAFE && std::isnan(a->lower_bound)) return KDA_ERR_MISSING_PARAM;
     const int64_t rows = static_cast<int64_t>(a->B) * a->T;
-    if (rows > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)) return KDA_ERR_INVALID_ARG;
-    if (a->output_final_state && !a->final_state) return KDA_ERR_INVALID_ARG;
+    if (rows > 0 && (!a->q || !a->k || !a->v || !a->g || !a->beta)) return KDA_ERR_INVALID_ARG;
+    if (forward && rows > 0 && !a->o) return KDA_ERR_INVALID_ARG;
+    if (forward && a->output_final_state && !a->final_state) return KDA_ERR_INVALID_ARG;
     const void* ptrs[] = {a->q, a->k, a->v, a->g, a->o, a->initial_state, a->final_state};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
@@ -55,8 +56,8 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p) {
     p.use_beta_sigmoid = a->use_beta_sigmoid;
     p.bounded = false;
     p.h0 = a->initial_state;
-    p.o = a->o;
-    p.ht = a->output_final_state ? a->final_state : nullptr;
+    p.o = forward ? a->o : nullptr;
+    p.ht = (forward && a->output_final_state) ? a->final_state : nullptr;
     const int64_t nc_dense = (static_cast<int64_t>(a->T) + 63) / 64;
     const int64_t bound = a->cu_seqlens ? nc_dense + N : nc_dense * N;
     if (bound * a->H > INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
@@ -85,30 +86,37 @@ int kda_version(void) { return kVersion; }
 
 size_t kda_chunk_fwd_workspace(const kda_chunk_args* a) {
     kda::ChunkParams p{};
-    if (check_chunk(a, p) != KDA_OK) return 0;
+    if (check_chunk(a, p, true) != KDA_OK) return 0;
     return kda::chunk_fwd_workspace(p);
 }
 
-kda_status kda_chunk_fwd(const kda_chunk_args* a) {
+static kda_status chunk_fwd_impl(const kda_chunk_args* a, int stage) {
     kda::ChunkParams p{};
-    kda_status st = check_chunk(a, p);
+    kda_status st = check_chunk(a, p, true);
     if (st != KDA_OK) return st;
     const size_t need = kda::chunk_fwd_workspace(p);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     if (a->workspace && !aligned16(a->workspace)) return KDA_ERR_WORKSPACE;
-    hipError_t e = kda::launch_chunk_fwd(p, a->workspace, static_cast<hipStream_t>(a->stream));
+    hipError_t e = kda::launch_chunk_fwd(p, a->workspace, static_cast<hipStream_t>(a->stream), stage);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_fwd(const kda_chunk_args* a) { return chunk_fwd_impl(a, -1); }
+
+kda_status kda_chunk_fwd_stage(const kda_chunk_args* a, int stage) {
+    if (stage < 0 || stage > 1) return KDA_ERR_INVALID_ARG;
+    return chunk_fwd_impl(a, stage);
 }
 
 size_t kda_chunk_bwd_workspace(const kda_chunk_args* a) {
     kda::ChunkParams p{};
-    if (check_chunk(a, p) != KDA_OK) return 0;
+    if (check_chunk(a, p, false) != KDA_OK) return 0;
     return kda::chunk_bwd_workspace(p);
 }
 
-kda_status kda_chunk_bwd(const kda_chunk_args* a, const kda_chunk_grads* gr) {
+static kda_status chunk_bwd_impl(const kda_chunk_args* a, const kda_chunk_grads* gr, int stage) {
     kda::ChunkParams p{};
-    kda_status st = check_chunk(a, p);
+    kda_status st = check_chunk(a, p, false);
     if (st != KDA_OK) return st;
     if (!gr) return KDA_ERR_INVALID_ARG;
     const int64_t rows = static_cast<int64_t>(a->B) * a->T;
@@ -125,9 +133,18 @@ kda_status kda_chunk_bwd(const kda_chunk_args* a, const kda_chunk_grads* gr) {
     g.dO = gr->dO; g.dht = gr->d_final_state;
     g.dq = gr->dq; g.dk = gr->dk; g.dv = gr->dv; g.dg = gr->dg; g.dbeta = gr->dbeta;
     g.dh0 = gr->d_initial_state; g.dA_log = gr->dA_log; g.ddt_bias = gr->ddt_bias;
-    hipError_t e = kda::launch_chunk_bwd(p, g, a->workspace, static_cast<hipStream_t>(a->stream));
+    hipError_t e = kda::launch_chunk_bwd(p, g, a->workspace, static_cast<hipStream_t>(a->stream), stage);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
+
+kda_status kda_chunk_bwd(const kda_chunk_args* a, const kda_chunk_grads* gr) { return chunk_bwd_impl(a, gr, -1); }
+
+kda_status kda_chunk_bwd_stage(const kda_chunk_args* a, const kda_chunk_grads* gr, int stage) {
+    if (stage < 0 || stage >= kda::kBwdStages) return KDA_ERR_INVALID_ARG;
+    return chunk_bwd_impl(a, gr, stage);
+}
+
+int kda_chunk_bwd_stages(void) { return kda::kBwdStages; }
 
 kda_status kda_recurrent_step(const kda_step_args* a) {
     if (!a) return KDA_ERR_INVALID_ARG;

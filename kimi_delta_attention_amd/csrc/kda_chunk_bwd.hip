@@ -1,12 +1,813 @@
-// kda_chunk_bwd.hip -- chunked KDA backward (not built yet in this revision).
-#include "kda_chunk_common.hpp"
+// kda_chunk_bwd.hip -- chunked KDA backward on gfx950.
+//
+// The pages give no backward; this is the adjoint of the chunk form in
+// kda_chunk_kernels.hpp, written per chunk with QE = scale q^ e^G,
+// KE = k^ e^G, KD = k^ e^(G_last - G), TB = T diag(beta), MS = scale M,
+// gam = e^G_last and, for the entry state S and the exit-state gradient dS':
+//   Y  = v - KE S            D  = TB Y
+//   O  = QE S + MS D         S' = gam * S + KD^T D
+// which gives (all products column-local in V except where summed over V)
+//   dD  = KD dS' + MS^T dO            dY = TB^T dD            dv = dY
+//   dS  = gam * dS' + QE^T dO - KE^T dY                        (reverse pass)
+//   dQE = dO S^T   dKE = -dY S^T   dKD = D dS'^T   dMS = dO D^T   dTB = dD Y^T
+//   dgam = rowsum(dS' * S)
+// then, through the prologue of the chunk,
+//   dT = dTB diag(beta), dbeta_j += sum_i dTB_ij T_ij
+//   dA = -T^T dT T^T (strictly lower), dbeta_i += sum_j dA_ij Ak_ij, dAk = diag(beta) dA
+//   score rule for X_ij = sum_c x_ic k_jc e^(G_ic - G_jc) with gradient dX:
+//     dx_i += sum_j dX_ij k_j e^(G_i - G_j),  dk_j += sum_i dX_ij x_i e^(G_i - G_j),
+//     dG_i += x_i * (first sum),  dG_j -= k_j * (second sum)
+//   (x = q^ for M, x = k^ for Ak), the element-wise terms of QE, KE, KD, gam,
+//   the reverse cumulative sum of dG inside the chunk, and the chain rule of
+//   the gate, the beta sigmoid and the L2 norm.
+//
+// Kernels, in launch order (stage numbers of kda_chunk_bwd_stage):
+//   0 prep       the forward's prep kernel, also writing T and Ak;
+//   1 fstate     the forward state pass, storing every chunk's entry state;
+//   2 bstate     the reverse state pass, storing every chunk's exit-state
+//                gradient (sequential over chunks, parallel over sequence x
+//                head x V-column block), writing d(initial state);
+//   3 vlocal     per (chunk, head): dv and the V-summed operand gradients;
+//   4 klocal     per (chunk, head): dq, dk, dg, dbeta (and the gate-parameter
+//                shares), plus the reduction of d(A_log), d(dt_bias).
+// The score rule is formed pairwise (every exponent <= 0), so it is exact for
+// any gate without the sub-block factorisation.
+#include "kda_chunk_kernels.hpp"
 
 namespace kda {
 
-size_t chunk_bwd_workspace(const ChunkParams&) { return 0; }
+// Accumulator tile (16 x 16) store helpers.  Lane l holds column l % 16 and
+// rows 4 (l / 16) .. +3 of the tile at (r0, c0).
+template <class MM>
+__device__ __forceinline__ void tile_store(typename MM::ET* dst, int ld, int r0, int c0, f32x4 v, int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(r0 + 4 * (lane >> 4) + r) * ld + c0 + (lane & 15)] = MM::from_f32(v[r]);
+}
+template <class MM>
+__device__ __forceinline__ void tile_store_t(typename MM::ET* dst, int ld, int r0, int c0, f32x4 v, int lane) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(c0 + (lane & 15)) * ld + r0 + 4 * (lane >> 4) + r] = MM::from_f32(v[r]);
+}
+template <class MM>
+__device__ __forceinline__ f32x4 gemm(const typename MM::ET* A, int lda, int m0, const typename MM::ET* Bt, int ldb,
+                                      int n0, int k0, int k1, f32x4 acc, int lane) {
+    for (int k = k0; k < k1; k += MM::KS)
+        acc = MM::mma(MM::load(A, lda, m0, k, lane), MM::load(Bt, ldb, n0, k, lane), acc);
+    return acc;
+}
 
-hipError_t launch_chunk_bwd(const ChunkParams&, const ChunkGrads&, void*, hipStream_t) {
-    return hipErrorNotSupported;
+// ------------------------------------------------------------------ reverse state pass
+template <int K, int V, int BV, bool BF>
+__global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p, ChunkGrads gr,
+                                                                   const int32_t* chunk_off, uint8_t* ws,
+                                                                   int64_t slot_bytes) {
+    using MM = Mma<BF>;
+    using ET = typename MM::ET;
+    using IT = typename std::conditional<BF, uint16_t, float>::type;
+    using L = PrepLayout<K, BF>;
+    using X = BwdExtra<K, BF>;
+    constexpr int LDK = K + MM::PAD;
+    constexpr int LDC = kChunk + MM::PAD;
+    constexpr int NCT = BV / 16;
+    constexpr int NST = (K / 16) * NCT;
+    constexpr int SPW = (NST + 3) / 4;
+    constexpr int NVB = V / BV;
+
+    __shared__ __attribute__((aligned(16))) ET QEt[K][LDC];   // QE^T: A of QE^T dO
+    __shared__ __attribute__((aligned(16))) ET KEt[K][LDC];   // KE^T: A of KE^T dY
+    __shared__ __attribute__((aligned(16))) ET KDn[kChunk][LDK];  // A of KD dS'
+    __shared__ __attribute__((aligned(16))) ET MSt[kChunk][LDC];  // MS^T: A of MS^T dO
+    __shared__ __attribute__((aligned(16))) ET TBt[kChunk][LDC];  // TB^T: A of TB^T dD
+    __shared__ __attribute__((aligned(16))) ET dSt[BV][LDK];      // dS'^T: B of KD dS'
+    __shared__ __attribute__((aligned(16))) ET dOt[BV][LDC];
+    __shared__ __attribute__((aligned(16))) ET dDt[BV][LDC];
+    __shared__ __attribute__((aligned(16))) ET dYt[BV][LDC];
+    __shared__ float gC[K];
+
+    int chain, vb;
+    if (!chain_of_block(blockIdx.x, p.N * p.H, NVB, chain, vb)) return;
+    const int H = p.H;
+    const int n = chain / H, h = chain % H;
+    int64_t start;
+    int len;
+    seq_bounds(p, n, start, len);
+    const int nc = n_chunks(len);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int v0 = vb * BV;
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
+
+    f32x4 dS[SPW];
+#pragma unroll
+    for (int m = 0; m < SPW; ++m) {
+        const int tt = w + 4 * m;
+        const int rt = tt / NCT, ct = tt % NCT;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = 0.f;
+            if (tt < NST && gr.dht) v = gr.dht[sbase + (16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)];
+            dS[m][r] = v;
+        }
+    }
+    const IT* dOg = static_cast<const IT*>(gr.dO);
+    for (int jc = nc - 1; jc >= 0; --jc) {
+        uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
+        copy_in_t<ET, kChunk, K>(&QEt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kQE), t);
+        copy_in_t<ET, kChunk, K>(&KEt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kKE), t);
+        copy_in<ET, kChunk, K>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
+        copy_in_t<ET, kChunk, kChunk>(&MSt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
+        copy_in_t<ET, kChunk, kChunk>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
+        for (int c = t; c < K; c += kThreads) gC[c] = reinterpret_cast<const float*>(base + L::kGC)[c];
+        ET* gDS = reinterpret_cast<ET*>(base + X::kDS);
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int tt = w + 4 * m;
+            if (tt < NST) {
+                const int rt = tt / NCT, ct = tt % NCT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = 16 * rt + 4 * (lane >> 4) + r, col = 16 * ct + (lane & 15);
+                    const ET e = MM::from_f32(dS[m][r]);
+                    gDS[key * V + v0 + col] = e;
+                    dSt[col][key] = e;
+                }
+            }
+        }
+        const int rbase = jc * kChunk;
+        for (int e = t; e < kChunk * BV; e += kThreads) {
+            const int i = e / BV, c = e % BV;
+            float v = 0.f;
+            if (rbase + i < len) v = Elem<IT>::load(dOg, ((start + rbase + i) * H + h) * V + v0 + c);
+            dOt[c][i] = MM::from_f32(v);
+        }
+        __syncthreads();
+
+        // dD = KD dS' + MS^T dO   (rows 16w..; MS^T is upper triangular: k >= 16w)
+        const int klo = (16 * w / MM::KS) * MM::KS;
+        f32x4 dd[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = gemm<MM>(&KDn[0][0], LDK, 16 * w, &dSt[0][0], LDK, 16 * ct, 0, K, acc, lane);
+            acc = gemm<MM>(&MSt[0][0], LDC, 16 * w, &dOt[0][0], LDC, 16 * ct, klo, kChunk, acc, lane);
+            dd[ct] = acc;
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) tile_store_t<MM>(&dDt[0][0], LDC, 16 * w, 16 * ct, dd[ct], lane);
+        __syncthreads();
+
+        // dY = TB^T dD
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = gemm<MM>(&TBt[0][0], LDC, 16 * w, &dDt[0][0], LDC, 16 * ct, klo, kChunk, acc, lane);
+            tile_store_t<MM>(&dYt[0][0], LDC, 16 * w, 16 * ct, acc, lane);
+        }
+        __syncthreads();
+
+        // dS = gam * dS' + QE^T dO - KE^T dY
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int tt = w + 4 * m;
+            if (tt < NST) {
+                const int rt = tt / NCT, ct = tt % NCT;
+                f32x4 neg = {0.f, 0.f, 0.f, 0.f};
+                neg = gemm<MM>(&KEt[0][0], LDC, 16 * rt, &dYt[0][0], LDC, 16 * ct, 0, kChunk, neg, lane);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dS[m][r] = dS[m][r] * gC[16 * rt + 4 * (lane >> 4) + r] - neg[r];
+                dS[m] = gemm<MM>(&QEt[0][0], LDC, 16 * rt, &dOt[0][0], LDC, 16 * ct, 0, kChunk, dS[m], lane);
+            }
+        }
+        __syncthreads();
+    }
+    if (gr.dh0) {
+#pragma unroll
+        for (int m = 0; m < SPW; ++m) {
+            const int tt = w + 4 * m;
+            if (tt < NST) {
+                const int rt = tt / NCT, ct = tt % NCT;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    gr.dh0[sbase + (16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = dS[m][r];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ V-local gradients
+template <int K, int V, int BV, bool BF>
+__global__ __launch_bounds__(kThreads) void chunk_bwd_vlocal_kernel(ChunkParams p, ChunkGrads gr,
+                                                                    const int32_t* chunk_off, uint8_t* ws,
+                                                                    int64_t slot_bytes) {
+    using MM = Mma<BF>;
+    using ET = typename MM::ET;
+    using IT = typename std::conditional<BF, uint16_t, float>::type;
+    using L = PrepLayout<K, BF>;
+    using X = BwdExtra<K, BF>;
+    constexpr int LDK = K + MM::PAD;
+    constexpr int LDC = kChunk + MM::PAD;
+    constexpr int LDB = BV + MM::PAD;
+    constexpr int NCT = BV / 16;   // column tiles of a [64][BV] block
+    constexpr int NKT = K / 16;    // column tiles of a [64][K] product
+    static_assert(BV % MM::KS == 0, "products contract over the V block: it must hold whole MFMA k-steps");
+
+    __shared__ __attribute__((aligned(16))) ET KEn[kChunk][LDK];
+    __shared__ __attribute__((aligned(16))) ET KDn[kChunk][LDK];
+    __shared__ __attribute__((aligned(16))) ET TBn[kChunk][LDC];
+    __shared__ __attribute__((aligned(16))) ET TBt[kChunk][LDC];
+    __shared__ __attribute__((aligned(16))) ET MSt[kChunk][LDC];
+    __shared__ __attribute__((aligned(16))) ET St[BV][LDK];
+    __shared__ __attribute__((aligned(16))) ET dSt[BV][LDK];
+    __shared__ __attribute__((aligned(16))) ET Sn[K][LDB];
+    __shared__ __attribute__((aligned(16))) ET dSn[K][LDB];
+    __shared__ __attribute__((aligned(16))) ET dOn[kChunk][LDB];
+    __shared__ __attribute__((aligned(16))) ET Yn[kChunk][LDB];
+    __shared__ __attribute__((aligned(16))) ET Dn[kChunk][LDB];
+    __shared__ __attribute__((aligned(16))) ET dDn[kChunk][LDB];
+    __shared__ __attribute__((aligned(16))) ET dYn[kChunk][LDB];
+    __shared__ __attribute__((aligned(16))) ET dOt[BV][LDC];
+    __shared__ __attribute__((aligned(16))) ET Yt[BV][LDC];
+    __shared__ __attribute__((aligned(16))) ET dDt[BV][LDC];
+
+    const int H = p.H;
+    const int slot = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    int n, j;
+    if (!slot_to_chunk(p, chunk_off, slot, n, j)) return;
+    int64_t start;
+    int len;
+    seq_bounds(p, n, start, len);
+    const int rows = min(kChunk, len - j * kChunk);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
+    const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
+
+    copy_in<ET, kChunk, K>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKE), t);
+    copy_in<ET, kChunk, K>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
+    copy_in<ET, kChunk, kChunk>(&TBn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
+    copy_in_t<ET, kChunk, kChunk>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
+    copy_in_t<ET, kChunk, kChunk>(&MSt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
+
+    f32x4 aQE[NKT], aKE[NKT], aKD[NKT], aMS[4], aTB[4];
+#pragma unroll
+    for (int c = 0; c < NKT; ++c) aQE[c] = aKE[c] = aKD[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) aMS[c] = aTB[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dgam = 0.f;
+
+    const ET* gS = reinterpret_cast<const ET*>(base + X::kS);
+    const ET* gDS = reinterpret_cast<const ET*>(base + X::kDS);
+    const IT* dOg = static_cast<const IT*>(gr.dO);
+    const IT* vg = static_cast<const IT*>(p.v);
+    IT* dvg = static_cast<IT*>(gr.dv);
+    const int klo = (16 * w / MM::KS) * MM::KS;
+
+    for (int vb = 0; vb < V / BV; ++vb) {
+        const int v0 = vb * BV;
+        for (int e = t; e < K * BV; e += kThreads) {
+            const int key = e / BV, c = e % BV;
+            const ET s = gS[key * V + v0 + c], d = gDS[key * V + v0 + c];
+            Sn[key][c] = s;
+            St[c][key] = s;
+            dSn[key][c] = d;
+            dSt[c][key] = d;
+        }
+        for (int e = t; e < kChunk * BV; e += kThreads) {
+            const int i = e / BV, c = e % BV;
+            float v = 0.f;
+            if (i < rows) v = Elem<IT>::load(dOg, ((rbase + i) * H + h) * V + v0 + c);
+            dOn[i][c] = MM::from_f32(v);
+            dOt[c][i] = MM::from_f32(v);
+        }
+        __syncthreads();
+
+        // Y = v - KE S and dD = KD dS' + MS^T dO, rows 16w..
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 pp = {0.f, 0.f, 0.f, 0.f};
+            pp = gemm<MM>(&KEn[0][0], LDK, 16 * w, &St[0][0], LDK, 16 * ct, 0, K, pp, lane);
+            f32x4 y;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * (lane >> 4) + r;
+                float vv = 0.f;
+                if (i < rows) vv = Elem<IT>::load(vg, ((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15));
+                y[r] = vv - pp[r];
+            }
+            tile_store<MM>(&Yn[0][0], LDB, 16 * w, 16 * ct, y, lane);
+            tile_store_t<MM>(&Yt[0][0], LDC, 16 * w, 16 * ct, y, lane);
+            f32x4 dd = {0.f, 0.f, 0.f, 0.f};
+            dd = gemm<MM>(&KDn[0][0], LDK, 16 * w, &dSt[0][0], LDK, 16 * ct, 0, K, dd, lane);
+            dd = gemm<MM>(&MSt[0][0], LDC, 16 * w, &dOt[0][0], LDC, 16 * ct, klo, kChunk, dd, lane);
+            tile_store<MM>(&dDn[0][0], LDB, 16 * w, 16 * ct, dd, lane);
+            tile_store_t<MM>(&dDt[0][0], LDC, 16 * w, 16 * ct, dd, lane);
+        }
+        __syncthreads();
+
+        // D = TB Y; dY = TB^T dD; dv = dY
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = gemm<MM>(&TBn[0][0], LDC, 16 * w, &Yt[0][0], LDC, 16 * ct, 0, 16 * (w + 1), d, lane);
+            tile_store<MM>(&Dn[0][0], LDB, 16 * w, 16 * ct, d, lane);
+            f32x4 dy = {0.f, 0.f, 0.f, 0.f};
+            dy = gemm<MM>(&TBt[0][0], LDC, 16 * w, &dDt[0][0], LDC, 16 * ct, klo, kChunk, dy, lane);
+            tile_store<MM>(&dYn[0][0], LDB, 16 * w, 16 * ct, dy, lane);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * (lane >> 4) + r;
+                if (i < rows) Elem<IT>::store(dvg, ((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15), dy[r]);
+            }
+        }
+        __syncthreads();
+
+        // V-summed products over this column block
+#pragma unroll
+        for (int c = 0; c < NKT; ++c) {
+            aQE[c] = gemm<MM>(&dOn[0][0], LDB, 16 * w, &Sn[0][0], LDB, 16 * c, 0, BV, aQE[c], lane);
+            aKE[c] = gemm<MM>(&dYn[0][0], LDB, 16 * w, &Sn[0][0], LDB, 16 * c, 0, BV, aKE[c], lane);
+            aKD[c] = gemm<MM>(&Dn[0][0], LDB, 16 * w, &dSn[0][0], LDB, 16 * c, 0, BV, aKD[c], lane);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            aMS[c] = gemm<MM>(&dOn[0][0], LDB, 16 * w, &Dn[0][0], LDB, 16 * c, 0, BV, aMS[c], lane);
+            aTB[c] = gemm<MM>(&dDn[0][0], LDB, 16 * w, &Yn[0][0], LDB, 16 * c, 0, BV, aTB[c], lane);
+        }
+        for (int key = t; key < K; key += kThreads)
+#pragma unroll 4
+            for (int c = 0; c < BV; ++c) dgam += MM::to_f32(Sn[key][c]) * MM::to_f32(dSn[key][c]);
+        __syncthreads();
+    }
+
+    ET* gQE = reinterpret_cast<ET*>(base + X::kDQE);
+    ET* gKE = reinterpret_cast<ET*>(base + X::kDKE);
+    ET* gKD = reinterpret_cast<ET*>(base + X::kDKD);
+    ET* gMS = reinterpret_cast<ET*>(base + X::kDMS);
+    ET* gTB = reinterpret_cast<ET*>(base + X::kDTB);
+#pragma unroll
+    for (int c = 0; c < NKT; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * (lane >> 4) + r, col = 16 * c + (lane & 15);
+            gQE[i * K + col] = MM::from_f32(aQE[c][r]);
+            gKE[i * K + col] = MM::from_f32(-aKE[c][r]);
+            gKD[i * K + col] = MM::from_f32(aKD[c][r]);
+        }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * w + 4 * (lane >> 4) + r, col = 16 * c + (lane & 15);
+            gMS[i * kChunk + col] = MM::from_f32(aMS[c][r]);
+            gTB[i * kChunk + col] = MM::from_f32(aTB[c][r]);
+        }
+    for (int key = t; key < K; key += kThreads) reinterpret_cast<float*>(base + X::kDGAM)[key] = dgam;
+}
+
+// ------------------------------------------------------------------ K-local gradients
+template <int K, bool BF>
+struct KlocSmem {
+    using ET = typename Mma<BF>::ET;
+    static constexpr int LDE = K + Mma<BF>::PAD;
+    static constexpr int LDC = kChunk + Mma<BF>::PAD;
+    ET qh[kChunk][LDE];             // normalised q
+    ET kh[kChunk][LDE];             // normalised k
+    float G[kChunk][K + 1];         // inclusive cumulative log-decay
+    union alignas(16) {
+        struct {
+            ET Tn[kChunk][LDC];     // T
+            ET Tt[kChunk][LDC];     // T^T
+            ET dTt[kChunk][LDC];    // (dTB diag(beta))^T
+            ET Zn[kChunk][LDC];     // T^T dT
+        } mm;
+        struct {
+            float dM[kChunk][kChunk + 1];  // gradient of the decayed q-k scores
+            float dA[kChunk][kChunk + 1];  // gradient of the decayed k-k scores
+        } sc;
+    } u;
+    float beta[kChunk], rq[kChunk], rk[kChunk];
+    float dbc[4][kChunk];           // partial sums of dbeta (column part)
+    float dbr[kChunk];              // dbeta (row part)
+    float red[kThreads / K][K];     // per-part channel partials
+    float dots[2][2][kChunk];       // row dot products (q, k) per 64-channel half
+    float gpa[kThreads / 64];
+};
+
+template <int K, bool BF>
+__global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_kernel(ChunkParams p, ChunkGrads gr,
+                                                                    const int32_t* chunk_off, uint8_t* ws,
+                                                                    int64_t slot_bytes) {
+    using MM = Mma<BF>;
+    using ET = typename MM::ET;
+    using IT = typename std::conditional<BF, uint16_t, float>::type;
+    using X = BwdExtra<K, BF>;
+    using SM = KlocSmem<K, BF>;
+    constexpr int LDC = SM::LDC;
+    constexpr int CPT = K / 4;
+    constexpr int NP = kThreads / K;   // row parts in the channel-parallel phases
+    constexpr int RPP = kChunk / NP;   // rows per part
+    __shared__ __attribute__((aligned(16))) SM s;
+
+    const int H = p.H;
+    const int slot = blockIdx.x / H;
+    const int h = blockIdx.x % H;
+    int n, j;
+    if (!slot_to_chunk(p, chunk_off, slot, n, j)) return;
+    int64_t start;
+    int len;
+    seq_bounds(p, n, start, len);
+    const int rows = min(kChunk, len - j * kChunk);
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
+    const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
+    const float rate = (p.gate_mode == GATE_LOGDECAY) ? 0.f : __expf(p.A_log[h]);
+
+    // ---- 0. prologue again (row-wise), then the cumulative sum (channel-wise)
+    {
+        const int i = t >> 2, c0 = (t & 3) * CPT;
+        const bool valid = i < rows;
+        float qv[CPT], kv[CPT], gv[CPT];
+        if (valid) {
+            const int64_t off = ((rbase + i) * H + h) * K + c0;
+            load_row<CPT>(static_cast<const IT*>(p.q) + off, qv);
+            load_row<CPT>(static_cast<const IT*>(p.k) + off, kv);
+            load_row<CPT>(p.g + off, gv);
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) qv[c] = kv[c] = gv[c] = 0.f;
+        }
+        float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            ssq += qv[c] * qv[c];
+            ssk += kv[c] * kv[c];
+        }
+        ssq += __shfl_xor(ssq, 1, 64);
+        ssq += __shfl_xor(ssq, 2, 64);
+        ssk += __shfl_xor(ssk, 1, 64);
+        ssk += __shfl_xor(ssk, 2, 64);
+        float rq = 1.f, rk = 1.f;
+        if (p.use_qk_l2norm) {
+            rq = rsqrtf(ssq + kL2Eps);
+            rk = rsqrtf(ssk + kL2Eps);
+        }
+        if (!valid) rq = rk = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            s.qh[i][c0 + c] = MM::from_f32(qv[c] * rq);
+            s.kh[i][c0 + c] = MM::from_f32(kv[c] * rk);
+            float g = 0.f;
+            if (valid) {
+                const float bias = p.dt_bias ? p.dt_bias[h * K + c0 + c] : 0.f;
+                g = gate_eff(p.gate_mode, gv[c], rate, bias, p.lower_bound);
+            }
+            s.G[i][c0 + c] = g;
+        }
+        if ((t & 3) == 0) {
+            s.rq[i] = rq;
+            s.rk[i] = rk;
+            float b = 0.f;
+            if (valid) {
+                b = p.beta[(rbase + i) * H + h];
+                if (p.use_beta_sigmoid) b = sigmoidf_(b);
+            }
+            s.beta[i] = b;
+        }
+    }
+    __syncthreads();
+    const int c = t % K;      // channel of this thread in the channel-parallel phases
+    const int hh = t / K;     // row part
+    const int r0 = hh * RPP;
+    {
+        float acc = 0.f;
+        for (int r = r0; r < r0 + RPP; ++r) {
+            acc += s.G[r][c];
+            s.G[r][c] = acc;
+        }
+        __syncthreads();
+        float off = 0.f;
+        for (int q = 0; q < hh; ++q) off += s.G[(q + 1) * RPP - 1][c];
+        __syncthreads();
+        if (hh > 0)
+            for (int r = r0; r < r0 + RPP; ++r) s.G[r][c] += off;
+    }
+    __syncthreads();
+
+    // ---- 1. element-wise terms of QE, KE, KD (channel-parallel, rows r0..r0+RPP)
+    const float Glast = s.G[kChunk - 1][c];
+    float dqh[RPP], dkh[RPP], dG[RPP];
+    float gcp = 0.f;
+    {
+        const ET* gQE = reinterpret_cast<const ET*>(base + X::kDQE);
+        const ET* gKE = reinterpret_cast<const ET*>(base + X::kDKE);
+        const ET* gKD = reinterpret_cast<const ET*>(base + X::kDKD);
+#pragma unroll
+        for (int a = 0; a < RPP; ++a) {
+            const int r = r0 + a;
+            const float E = __expf(s.G[r][c]);
+            const float Ed = __expf(Glast - s.G[r][c]);
+            const float q_ = MM::to_f32(s.qh[r][c]), k_ = MM::to_f32(s.kh[r][c]);
+            const float dqe = MM::to_f32(gQE[r * K + c]);
+            const float dke = MM::to_f32(gKE[r * K + c]);
+            const float dkd = MM::to_f32(gKD[r * K + c]);
+            const float QE = p.scale * q_ * E, KE = k_ * E, KD = k_ * Ed;
+            dqh[a] = p.scale * dqe * E;
+            dkh[a] = dke * E + dkd * Ed;
+            dG[a] = dqe * QE + dke * KE - dkd * KD;
+            gcp += dkd * KD;
+        }
+    }
+
+    // ---- 2. dA = -T^T (dTB diag(beta)) T^T and the beta terms of TB and A
+    {
+        const ET* gT = reinterpret_cast<const ET*>(base + X::kT);
+        const ET* gTB = reinterpret_cast<const ET*>(base + X::kDTB);
+        float part = 0.f;  // column j = t % 64
+        for (int e = t; e < kChunk * kChunk; e += kThreads) {
+            const int a = e / kChunk, b = e % kChunk;
+            const ET tv = gT[e];
+            s.u.mm.Tn[a][b] = tv;
+            s.u.mm.Tt[b][a] = tv;
+            const float dtb = (b <= a) ? MM::to_f32(gTB[e]) : 0.f;
+            part += dtb * MM::to_f32(tv);
+            s.u.mm.dTt[b][a] = MM::from_f32(dtb * s.beta[b]);
+        }
+        s.dbc[t >> 6][t & 63] = part;
+    }
+    __syncthreads();
+    {
+        f32x4 z[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            z[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            z[ct] = gemm<MM>(&s.u.mm.Tt[0][0], LDC, 16 * w, &s.u.mm.dTt[0][0], LDC, 16 * ct, 0, kChunk, z[ct], lane);
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) tile_store<MM>(&s.u.mm.Zn[0][0], LDC, 16 * w, 16 * ct, z[ct], lane);
+    }
+    __syncthreads();
+    f32x4 da[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+        da[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        da[ct] = gemm<MM>(&s.u.mm.Zn[0][0], LDC, 16 * w, &s.u.mm.Tn[0][0], LDC, 16 * ct, 0, kChunk, da[ct], lane);
+    }
+    __syncthreads();  // the score buffers below overlay T, Z
+    {
+        const ET* gAK = reinterpret_cast<const ET*>(base + X::kAK);
+        const ET* gMS = reinterpret_cast<const ET*>(base + X::kDMS);
+        float rowp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * w + 4 * (lane >> 4) + r, jj = 16 * ct + (lane & 15);
+                const float dAv = (jj < i) ? -da[ct][r] : 0.f;
+                rowp[r] += dAv * MM::to_f32(gAK[i * kChunk + jj]);
+                s.u.sc.dA[i][jj] = dAv * s.beta[i];
+            }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float v = rowp[r];
+            v += __shfl_xor(v, 1, 64);
+            v += __shfl_xor(v, 2, 64);
+            v += __shfl_xor(v, 4, 64);
+            v += __shfl_xor(v, 8, 64);
+            if ((lane & 15) == 0) s.dbr[16 * w + 4 * (lane >> 4) + r] = v;
+        }
+        for (int e = t; e < kChunk * kChunk; e += kThreads) {
+            const int a = e / kChunk, b = e % kChunk;
+            s.u.sc.dM[a][b] = (b <= a) ? p.scale * MM::to_f32(gMS[e]) : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. score rule, pairwise, for the q-k (dM) and k-k (dA) scores
+#pragma unroll
+    for (int a = 0; a < RPP; ++a) {
+        const int i = r0 + a;
+        const float Gi = s.G[i][c];
+        float pq = 0.f, pk = 0.f;
+        for (int jj = 0; jj <= i; ++jj) {
+            const float e = __expf(Gi - s.G[jj][c]);
+            const float kj = MM::to_f32(s.kh[jj][c]) * e;
+            pq += s.u.sc.dM[i][jj] * kj;
+            pk += s.u.sc.dA[i][jj] * kj;  // zero on the diagonal
+        }
+        float rq = 0.f, rk = 0.f;
+        for (int ii = i; ii < kChunk; ++ii) {
+            const float e = __expf(s.G[ii][c] - Gi);
+            rq += s.u.sc.dM[ii][i] * MM::to_f32(s.qh[ii][c]) * e;
+            rk += s.u.sc.dA[ii][i] * MM::to_f32(s.kh[ii][c]) * e;
+        }
+        const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
+        dqh[a] += pq;
+        dkh[a] += pk + rq + rk;
+        dG[a] += q_ * pq + k_ * pk - k_ * (rq + rk);
+    }
+
+    // ---- 4. d(G_last), reverse cumulative sum, gate chain rule
+    s.red[hh][c] = gcp;
+    __syncthreads();
+    if (hh == NP - 1) {
+        float tot = 0.f;
+#pragma unroll
+        for (int q = 0; q < NP; ++q) tot += s.red[q][c];
+        const float dgam = reinterpret_cast<const float*>(base + X::kDGAM)[c];
+        dG[RPP - 1] += tot + dgam * __expf(Glast);
+    }
+    __syncthreads();
+    {
+        float acc = 0.f;
+#pragma unroll
+        for (int a = RPP - 1; a >= 0; --a) {
+            acc += dG[a];
+            dG[a] = acc;
+        }
+        s.red[hh][c] = acc;
+    }
+    __syncthreads();
+    {
+        float off = 0.f;
+        for (int q = hh + 1; q < NP; ++q) off += s.red[q][c];
+        float ddt = 0.f, dal = 0.f;
+        const float bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias[h * K + c] : 0.f;
+#pragma unroll
+        for (int a = 0; a < RPP; ++a) {
+            const int i = r0 + a;
+            const float dge = dG[a] + off;  // gradient of this row's log-decay
+            if (i < rows) {
+                const int64_t gi = ((rbase + i) * H + h) * K + c;
+                float dx = dge;
+                if (p.gate_mode != GATE_LOGDECAY) {
+                    const float z = p.g[gi] + bias;
+                    if (p.gate_mode == GATE_SAFE) {
+                        const float sg = sigmoidf_(rate * z);
+                        const float base_ = p.lower_bound * sg * (1.f - sg);
+                        dx = dge * base_ * rate;
+                        dal += dge * base_ * rate * z;
+                    } else {
+                        dx = -dge * rate * sigmoidf_(z);
+                        dal += -dge * rate * softplusf_(z);
+                    }
+                    ddt += dx;
+                }
+                gr.dg[gi] = dx;
+            }
+        }
+        if (p.gate_mode != GATE_LOGDECAY) {
+            __syncthreads();
+            s.red[hh][c] = ddt;
+            dal = wave_sum(dal);
+            if (lane == 0) s.gpa[w] = dal;
+            __syncthreads();
+            float* gp = reinterpret_cast<float*>(base + X::kGP);
+            if (hh == 0) {
+                float tot = 0.f;
+#pragma unroll
+                for (int q = 0; q < NP; ++q) tot += s.red[q][c];
+                gp[c] = tot;
+            }
+            if (t == 0) {
+                float tot = 0.f;
+                for (int q = 0; q < kThreads / 64; ++q) tot += s.gpa[q];
+                gp[K] = tot;
+            }
+        }
+    }
+
+    // ---- 5. L2-norm and sigmoid chain rules, stores
+    {
+        // row dot products q^.dq^ and k^.dk^ over the K channels
+        float dq_[RPP], dk_[RPP];
+#pragma unroll
+        for (int a = 0; a < RPP; ++a) {
+            dq_[a] = MM::to_f32(s.qh[r0 + a][c]) * dqh[a];
+            dk_[a] = MM::to_f32(s.kh[r0 + a][c]) * dkh[a];
+            constexpr int span = K < 64 ? K : 64;
+#pragma unroll
+            for (int o = 1; o < span; o <<= 1) {
+                dq_[a] += __shfl_xor(dq_[a], o, 64);
+                dk_[a] += __shfl_xor(dk_[a], o, 64);
+            }
+        }
+        if (K > 64) {
+            if ((c & 63) == 0) {
+#pragma unroll
+                for (int a = 0; a < RPP; ++a) {
+                    s.dots[0][c >> 6][r0 + a] = dq_[a];
+                    s.dots[1][c >> 6][r0 + a] = dk_[a];
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int a = 0; a < RPP; ++a) {
+                dq_[a] = s.dots[0][0][r0 + a] + s.dots[0][1][r0 + a];
+                dk_[a] = s.dots[1][0][r0 + a] + s.dots[1][1][r0 + a];
+            }
+        }
+        IT* dqg = static_cast<IT*>(gr.dq);
+        IT* dkg = static_cast<IT*>(gr.dk);
+#pragma unroll
+        for (int a = 0; a < RPP; ++a) {
+            const int i = r0 + a;
+            if (i >= rows) continue;
+            const int64_t gi = ((rbase + i) * H + h) * K + c;
+            float oq = dqh[a], ok = dkh[a];
+            if (p.use_qk_l2norm) {
+                oq = s.rq[i] * (dqh[a] - MM::to_f32(s.qh[i][c]) * dq_[a]);
+                ok = s.rk[i] * (dkh[a] - MM::to_f32(s.kh[i][c]) * dk_[a]);
+            }
+            Elem<IT>::store(dqg, gi, oq);
+            Elem<IT>::store(dkg, gi, ok);
+        }
+        if (t < kChunk && t < rows) {
+            const float db = s.dbc[0][t] + s.dbc[1][t] + s.dbc[2][t] + s.dbc[3][t] + s.dbr[t];
+            const float b = s.beta[t];
+            gr.dbeta[(rbase + t) * H + h] = p.use_beta_sigmoid ? db * b * (1.f - b) : db;
+        }
+    }
+}
+
+// d(A_log) and d(dt_bias): deterministic sums of the per-chunk shares.
+template <int K>
+__global__ void gate_param_reduce_kernel(ChunkParams p, ChunkGrads gr, const int32_t* chunk_off, const uint8_t* ws,
+                                         int64_t slot_bytes, size_t gp_off) {
+    const int h = blockIdx.x;
+    const int H = p.H;
+    const int nslots = p.cu_seqlens ? chunk_off[p.N] : p.N * n_chunks(p.T);
+    for (int c = threadIdx.x; c <= K; c += blockDim.x) {
+        float acc = 0.f;
+        for (int sl = 0; sl < nslots; ++sl)
+            acc += reinterpret_cast<const float*>(ws + (static_cast<int64_t>(sl) * H + h) * slot_bytes + gp_off)[c];
+        if (c < K) {
+            if (gr.ddt_bias) gr.ddt_bias[h * K + c] = acc;
+        } else if (gr.dA_log) {
+            gr.dA_log[h] = acc;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host side
+template <int K, bool BF>
+static size_t bwd_bytes(const ChunkParams& p) {
+    return chunk_off_bytes(p) + static_cast<size_t>(p.total_chunks_bound) * p.H * BwdExtra<K, BF>::kBytes;
+}
+
+size_t chunk_bwd_workspace(const ChunkParams& p) {
+    switch (p.K) {
+        case 32: return p.bf16 ? bwd_bytes<32, true>(p) : bwd_bytes<32, false>(p);
+        case 64: return p.bf16 ? bwd_bytes<64, true>(p) : bwd_bytes<64, false>(p);
+        case 128: return p.bf16 ? bwd_bytes<128, true>(p) : 0;
+        default: return 0;
+    }
+}
+
+template <int K, int BV, bool BF>
+static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st, int stage) {
+    constexpr int V = K;
+    using X = BwdExtra<K, BF>;
+    uint8_t* w8 = static_cast<uint8_t*>(ws);
+    int32_t* chunk_off = reinterpret_cast<int32_t*>(w8);
+    uint8_t* slots = w8 + chunk_off_bytes(p);
+    const int64_t sb = static_cast<int64_t>(X::kBytes);
+    const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
+    const int cgrid = chain_grid(p.N * p.H, V / BV);
+    auto want = [stage](int s) { return stage < 0 || stage == s; };
+    if (want(0)) {
+        if (p.cu_seqlens)
+            hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
+        if (nblk > 0)
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+                               st, p, chunk_off, slots, sb);
+    }
+    if (want(1) && cgrid > 0)
+        hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kThreads), 0, st,
+                           p, chunk_off, slots, sb);
+    if (want(2) && cgrid > 0)
+        hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,
+                           chunk_off, slots, sb);
+    if (want(3) && nblk > 0)
+        hipLaunchKernelGGL((chunk_bwd_vlocal_kernel<K, V, BV, BF>), dim3(static_cast<unsigned>(nblk)),
+                           dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb);
+    if (want(4)) {
+        if (nblk > 0)
+            hipLaunchKernelGGL((chunk_bwd_klocal_kernel<K, BF>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
+                               0, st, p, gr, chunk_off, slots, sb);
+        if (p.gate_mode != GATE_LOGDECAY && (gr.dA_log || gr.ddt_bias))
+            hipLaunchKernelGGL((gate_param_reduce_kernel<K>), dim3(p.H), dim3(256), 0, st, p, gr, chunk_off, slots, sb,
+                               X::kGP);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st, int stage) {
+    if (p.K != p.V) return hipErrorInvalidValue;
+    switch (p.K) {
+        case 32: return p.bf16 ? run_bwd<32, 32, true>(p, gr, ws, st, stage) : run_bwd<32, 16, false>(p, gr, ws, st, stage);
+        case 64: return p.bf16 ? run_bwd<64, 32, true>(p, gr, ws, st, stage) : run_bwd<64, 16, false>(p, gr, ws, st, stage);
+        case 128: return p.bf16 ? run_bwd<128, 32, true>(p, gr, ws, st, stage) : hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace kda

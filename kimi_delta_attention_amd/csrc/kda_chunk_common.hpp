@@ -111,6 +111,39 @@ struct PrepLayout {
     static constexpr size_t kBytes = ((kGC + sizeof(float) * K) + 255) / 256 * 256;
 };
 
+// Backward-only additions to a slot, placed after the PrepLayout operands:
+//   T    [64][64] (I + A)^-1                      (ET)
+//   AK   [64][64] strict_tril(k^ k^T decayed)      (ET)
+//   S    [K][V]   state entering the chunk         (ET)
+//   DS   [K][V]   gradient of the state leaving it (ET)
+//   DQE, DKE, DKD [64][K]  gradients of the QE, KE, KD operands, summed over V (ET)
+//   DMS, DTB      [64][64] gradients of MS and TB, summed over V (ET)
+//   DGAM [K]      gradient of exp(G_last) (fp32)
+//   GP   [K + 1]  this chunk's share of d(dt_bias) and d(A_log) (fp32)
+template <int K, bool BF>
+struct BwdExtra {
+    using ET = typename Mma<BF>::ET;
+    static constexpr int V = K;
+    static constexpr size_t kT = PrepLayout<K, BF>::kBytes;
+    static constexpr size_t kAK = kT + sizeof(ET) * kChunk * kChunk;
+    static constexpr size_t kS = kAK + sizeof(ET) * kChunk * kChunk;
+    static constexpr size_t kDS = kS + sizeof(ET) * K * V;
+    static constexpr size_t kDQE = kDS + sizeof(ET) * K * V;
+    static constexpr size_t kDKE = kDQE + sizeof(ET) * kChunk * K;
+    static constexpr size_t kDKD = kDKE + sizeof(ET) * kChunk * K;
+    static constexpr size_t kDMS = kDKD + sizeof(ET) * kChunk * K;
+    static constexpr size_t kDTB = kDMS + sizeof(ET) * kChunk * kChunk;
+    static constexpr size_t kDGAM = kDTB + sizeof(ET) * kChunk * kChunk;
+    static constexpr size_t kGP = kDGAM + sizeof(float) * K;
+    static constexpr size_t kBytes = ((kGP + sizeof(float) * (K + 1)) + 255) / 256 * 256;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+__host__ inline size_t chunk_off_bytes(const ChunkParams& p) {
+    return align256(sizeof(int32_t) * (static_cast<size_t>(p.N) + 1));
+}
+
 // Chunk slot of chunk j of sequence n (slots are numbered over all sequences).
 __device__ __forceinline__ int64_t chunk_slot(const ChunkParams& p, const int32_t* chunk_off, int n,
                                               int j) {

@@ -1,608 +1,13 @@
-// kda_chunk_fwd.hip -- chunkwise-parallel KDA forward on gfx950.
-//
-// The chunk form computes exactly the token recurrence of the
-// "atlas_core/kimi_k3/kda.rs" page (module doc "Recurrence"): per chunk of 64
-// rows, with G the inclusive cumulative log-decay inside the chunk,
-//   A  = diag(beta) * strict_tril(sum_c k_i k_j exp(G_i - G_j))
-//   M  = tril(sum_c q_i k_j exp(G_i - G_j))            (diagonal included)
-//   T  = (I + A)^-1                                     (the inverse named in the
-//                                                        "K3/kda/ops/api.py" page's
-//                                                        l2-norm warning)
-//   D  = T diag(beta) (v - (k exp(G)) S)
-//   O  = scale * ((q exp(G)) S + M D)
-//   S' = diag(exp(G_last)) S + (k exp(G_last - G))^T D
-// The in-kernel prologue (q/k L2 norm, beta sigmoid, gate transform) follows
-// the order of api.py chunk_kda; the gate fused with its cumulative sum is the
-// in-kernel gate path of the "KDA <=> FLA Parity in Primus" page (section
-// "What changed and why", table A).
-//
-// Two kernels:
-//   prep   one workgroup per (chunk, head), fully parallel: prologue, cumsum,
-//          the exponentials, A and M on MFMA, the blocked triangular inverse;
-//          writes the chunk's operands (PrepLayout) to the workspace.
-//   state  one workgroup per (sequence, head, V-column block), sequential over
-//          the sequence's chunks: four small MFMA products per chunk with the
-//          fp32 state held in MFMA accumulators.  Every term is local to a
-//          value column, so column blocks of one head are independent.
-//
-// Overflow-safe decay: exponents are always taken against a reference row so
-// that no factor exceeds 1, except on the diagonal 16x16 sub-blocks, where the
-// reference is the row before the block and the opposite factor is at most
-// exp(span of the block).  A block whose span exceeds kSpanLimit for any
-// channel (possible only with unbounded gates) is formed pairwise instead.
-#include "kda_chunk_common.hpp"
+// kda_chunk_fwd.hip -- chunkwise-parallel KDA forward on gfx950: the
+// launch sequence of the prep and state kernels (kda_chunk_kernels.hpp).
+#include "kda_chunk_kernels.hpp"
 
 namespace kda {
 
-// ------------------------------------------------------------------ plan
-// chunk_off[n] = number of chunks in sequences 0..n-1 (packed input only).
-__global__ void plan_chunks_kernel(const int32_t* cu, int N, int T, int32_t* chunk_off) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    int acc = 0;
-    for (int n = 0; n < N; ++n) {
-        chunk_off[n] = acc;
-        int a = cu[n], b = cu[n + 1];
-        a = a < 0 ? 0 : (a > T ? T : a);
-        b = b < a ? a : (b > T ? T : b);
-        acc += n_chunks(b - a);
-    }
-    chunk_off[N] = acc;
-}
-
-// Vector load of CPT consecutive elements into fp32 registers.
-template <int CPT>
-__device__ __forceinline__ void load_row(const uint16_t* src, float* dst) {
-    static_assert(CPT % 8 == 0, "bf16 rows are loaded 8 at a time");
-#pragma unroll
-    for (int v = 0; v < CPT / 8; ++v) {
-        const u16x8 u = *reinterpret_cast<const u16x8*>(src + 8 * v);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dst[8 * v + e] = bf16_bits_to_f32(u[e]);
-    }
-}
-template <int CPT>
-__device__ __forceinline__ void load_row(const float* src, float* dst) {
-    static_assert(CPT % 4 == 0, "fp32 rows are loaded 4 at a time");
-#pragma unroll
-    for (int v = 0; v < CPT / 4; ++v) {
-        const f32x4 u = *reinterpret_cast<const f32x4*>(src + 4 * v);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[4 * v + e] = u[e];
-    }
-}
-template <int CPT>
-__device__ __forceinline__ void store_row(uint16_t* dst, const float* src) {
-#pragma unroll
-    for (int v = 0; v < CPT / 8; ++v) {
-        u16x8 u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = f32_to_bf16_bits(src[8 * v + e]);
-        *reinterpret_cast<u16x8*>(dst + 8 * v) = u;
-    }
-}
-template <int CPT>
-__device__ __forceinline__ void store_row(float* dst, const float* src) {
-#pragma unroll
-    for (int v = 0; v < CPT / 4; ++v) {
-        f32x4 u = {src[4 * v], src[4 * v + 1], src[4 * v + 2], src[4 * v + 3]};
-        *reinterpret_cast<f32x4*>(dst + 4 * v) = u;
-    }
-}
-
-// ------------------------------------------------------------------ prep
-template <int K, bool BF>
-struct PrepSmem {
-    using ET = typename Mma<BF>::ET;
-    static constexpr int LDE = K + Mma<BF>::PAD;
-    float G[kChunk][K + 1];
-    union alignas(16) {
-        struct {
-            ET qL[kChunk][LDE];   // q^ exp(G_i - G_ref(I))
-            ET kL[kChunk][LDE];   // k^ exp(G_i - G_ref(I))
-            ET kbe[kChunk][LDE];  // k^ exp(G_end(J) - G_j)
-        } op;
-        float T[kChunk][kChunk + 1];
-    } u;
-    float A[kChunk][kChunk + 1];
-    float M[kChunk][kChunk + 1];
-    float P[4][K];     // exp(G_end(I) - G_ref(I)): decay across sub-block I
-    float invP[4][K];  // 1 / P (finite where the block is factorised)
-    float Er[4][K];    // exp(G_ref(I))
-    float Ec[4][K];    // exp(G_last - G_end(I))
-    float F20[K];      // P_1:      sub-block pair (2, 0)
-    float F30[K];      // P_1 P_2:  pair (3, 0)
-    float F31[K];      // P_2:      pair (3, 1)
-    float gC[K];
-    float rq[kChunk], rk[kChunk], beta[kChunk];
-    float X[3][kSub][kSub + 1];
-    int unsafe[4];
-};
-
-template <int K, bool BF>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, const int32_t* chunk_off,
-                                                              uint8_t* ws) {
-    using MM = Mma<BF>;
-    using ET = typename MM::ET;
-    using IT = typename std::conditional<BF, uint16_t, float>::type;  // q/k/v element
-    using L = PrepLayout<K, BF>;
-    constexpr int CPT = K / 4;  // channels per thread in row-wise phases
-    constexpr int LDE = PrepSmem<K, BF>::LDE;
-    __shared__ __attribute__((aligned(16))) PrepSmem<K, BF> s;
-
-    const int H = p.H;
-    const int slot = blockIdx.x / H;
-    const int h = blockIdx.x % H;
-    int n, j;
-    if (!slot_to_chunk(p, chunk_off, slot, n, j)) return;
-    int64_t start;
-    int len;
-    seq_bounds(p, n, start, len);
-    const int rows = min(kChunk, len - j * kChunk);  // >= 1 by construction
-
-    const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int w = t >> 6;
-    uint8_t* out = ws + (static_cast<int64_t>(slot) * H + h) * L::kBytes;
-    ET* gQE = reinterpret_cast<ET*>(out + L::kQE);
-    ET* gKE = reinterpret_cast<ET*>(out + L::kKE);
-    ET* gKD = reinterpret_cast<ET*>(out + L::kKD);
-    ET* gTB = reinterpret_cast<ET*>(out + L::kTB);
-    ET* gMS = reinterpret_cast<ET*>(out + L::kMS);
-    float* gGC = reinterpret_cast<float*>(out + L::kGC);
-
-    // ---- 1. prologue, row-wise: thread -> (row i, quarter pq of the channels)
-    const int i = t >> 2;
-    const int pq = t & 3;
-    const int c0 = pq * CPT;
-    const bool valid = i < rows;
-    const int64_t grow = start + static_cast<int64_t>(j) * kChunk + i;
-    float qh[CPT], kh[CPT], gv[CPT];
-    if (valid) {
-        const int64_t off = (grow * H + h) * K + c0;
-        load_row<CPT>(static_cast<const IT*>(p.q) + off, qh);
-        load_row<CPT>(static_cast<const IT*>(p.k) + off, kh);
-        load_row<CPT>(p.g + off, gv);
-    } else {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) qh[c] = kh[c] = gv[c] = 0.0f;
-    }
-    float ssq = 0.f, ssk = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        ssq += qh[c] * qh[c];
-        ssk += kh[c] * kh[c];
-    }
-    ssq += __shfl_xor(ssq, 1, 64);
-    ssq += __shfl_xor(ssq, 2, 64);
-    ssk += __shfl_xor(ssk, 1, 64);
-    ssk += __shfl_xor(ssk, 2, 64);
-    float rq = 1.f, rk = 1.f;
-    if (p.use_qk_l2norm) {
-        rq = rsqrtf(ssq + kL2Eps);
-        rk = rsqrtf(ssk + kL2Eps);
-    }
-    if (!valid) rq = rk = 0.f;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-        qh[c] *= rq;
-        kh[c] *= rk;
-    }
-    if (valid && p.gate_mode != GATE_LOGDECAY) {
-        const float rate = __expf(p.A_log[h]);
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const float bias = p.dt_bias ? p.dt_bias[h * K + c0 + c] : 0.f;
-            gv[c] = gate_eff(p.gate_mode, gv[c], rate, bias, p.lower_bound);
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) s.G[i][c0 + c] = gv[c];
-    if (pq == 0) {
-        s.rq[i] = rq;
-        s.rk[i] = rk;
-        float b = 0.f;
-        if (valid) {
-            b = p.beta[grow * H + h];
-            if (p.use_beta_sigmoid) b = sigmoidf_(b);
-        }
-        s.beta[i] = b;
-    }
-    if (t < 4) s.unsafe[t] = 0;
-    for (int e = t; e < kChunk * (kChunk + 1); e += kThreads) {
-        (&s.A[0][0])[e] = 0.f;
-        (&s.M[0][0])[e] = 0.f;
-    }
-    __syncthreads();
-
-    // ---- 2. inclusive cumulative sum over the 64 rows, per channel
-    {
-        constexpr int SEGS = kThreads / K;      // row segments per channel
-        constexpr int SEGLEN = kChunk / SEGS;
-        const int c = t % K;
-        const int sg = t / K;
-        float acc = 0.f;
-        for (int r = sg * SEGLEN; r < (sg + 1) * SEGLEN; ++r) {
-            acc += s.G[r][c];
-            s.G[r][c] = acc;
-        }
-        __syncthreads();
-        float off = 0.f;
-        for (int q = 0; q < sg; ++q) off += s.G[(q + 1) * SEGLEN - 1][c];
-        __syncthreads();
-        if (sg > 0)
-            for (int r = sg * SEGLEN; r < (sg + 1) * SEGLEN; ++r) s.G[r][c] += off;
-    }
-    __syncthreads();
-
-    // ---- 3. per-channel sub-block factors
-    for (int c = t; c < K; c += kThreads) {
-        float Gref[4], Gend[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            Gref[I] = I == 0 ? 0.f : s.G[kSub * I - 1][c];
-            Gend[I] = s.G[kSub * I + kSub - 1][c];
-        }
-        const float Glast = Gend[3];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const float span = Gref[I] - Gend[I];  // >= 0 for decays
-            s.P[I][c] = __expf(-span);
-            s.invP[I][c] = __expf(span);
-            s.Er[I][c] = __expf(Gref[I]);
-            s.Ec[I][c] = __expf(Glast - Gend[I]);
-            if (!(span <= kSpanLimit)) s.unsafe[I] = 1;  // also catches NaN
-        }
-        s.F20[c] = s.P[1][c];
-        s.F31[c] = s.P[2][c];
-        s.F30[c] = s.P[1][c] * s.P[2][c];
-        s.gC[c] = __expf(Glast);
-    }
-    __syncthreads();
-
-    // ---- 4. factored operands (LDS) and the chunk's outputs QE, KE, KD (workspace)
-    {
-        const int I = i / kSub;
-        float a_[CPT], e_[CPT], o_[CPT];
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const float Gi = s.G[i][c0 + c];
-            const float Gr = I == 0 ? 0.f : s.G[kSub * I - 1][c0 + c];
-            const float Ge = s.G[kSub * I + kSub - 1][c0 + c];
-            a_[c] = __expf(Gi - Gr);
-            e_[c] = __expf(Ge - Gi);
-        }
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            s.u.op.qL[i][c0 + c] = MM::from_f32(qh[c] * a_[c]);
-            s.u.op.kL[i][c0 + c] = MM::from_f32(kh[c] * a_[c]);
-            s.u.op.kbe[i][c0 + c] = MM::from_f32(kh[c] * e_[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) o_[c] = p.scale * qh[c] * a_[c] * s.Er[I][c0 + c];
-        store_row<CPT>(gQE + i * K + c0, o_);
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * a_[c] * s.Er[I][c0 + c];
-        store_row<CPT>(gKE + i * K + c0, o_);
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * e_[c] * s.Ec[I][c0 + c];
-        store_row<CPT>(gKD + i * K + c0, o_);
-    }
-    __syncthreads();
-
-    // ---- 5. A and M sub-block tiles on MFMA (job = (matrix, I, J<=I)); 20 jobs
-    for (int job = w; job < 20; job += 4) {
-        const bool isM = job >= 10;
-        int tj = isM ? job - 10 : job;
-        int I = 0;
-        while (tj > I) { tj -= I + 1; ++I; }
-        const int J = tj;
-        if (J == I && s.unsafe[I]) continue;  // formed pairwise below
-        const float* fac = nullptr;
-        if (J == I) fac = s.invP[I];
-        else if (I == 2 && J == 0) fac = s.F20;
-        else if (I == 3 && J == 0) fac = s.F30;
-        else if (I == 3 && J == 1) fac = s.F31;
-        const ET* Lop = isM ? &s.u.op.qL[0][0] : &s.u.op.kL[0][0];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-        for (int k0 = 0; k0 < K; k0 += MM::KS) {
-            auto a = MM::load(Lop, LDE, kSub * I, k0, lane);
-            auto b = MM::load(&s.u.op.kbe[0][0], LDE, kSub * J, k0, lane);
-            if (fac) b = MM::scale(b, fac + k0 + (lane >> 4) * MM::KPL);
-            acc = MM::mma(a, b, acc);
-        }
-        const int col = kSub * J + (lane & 15);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = kSub * I + 4 * (lane >> 4) + r;
-            float v = acc[r];
-            if (isM) {
-                if (J == I && col > row) v = 0.f;
-                s.M[row][col] = v;
-            } else {
-                if (J == I && col >= row) v = 0.f;
-                s.A[row][col] = v * s.beta[row];
-            }
-        }
-    }
-    // pairwise diagonal sub-blocks whose decay span is too wide to factorise
-    for (int I = 0; I < 4; ++I) {
-        if (!s.unsafe[I]) continue;
-        const IT* qg = static_cast<const IT*>(p.q);
-        const IT* kg = static_cast<const IT*>(p.k);
-        for (int pr = t; pr < kSub * (kSub + 1) / 2; pr += kThreads) {
-            int a = 0, b = pr;
-            while (b > a) { b -= a + 1; ++a; }
-            const int ri = kSub * I + a, rj = kSub * I + b;
-            if (ri >= rows) continue;  // padding rows stay zero
-            const int64_t oi = ((start + static_cast<int64_t>(j) * kChunk + ri) * H + h) * K;
-            const int64_t oj = ((start + static_cast<int64_t>(j) * kChunk + rj) * H + h) * K;
-            float sa = 0.f, sm = 0.f;
-            for (int c = 0; c < K; ++c) {
-                const float e = __expf(s.G[ri][c] - s.G[rj][c]);
-                const float kj = Elem<IT>::load(kg, oj + c) * s.rk[rj];
-                sa += Elem<IT>::load(kg, oi + c) * s.rk[ri] * kj * e;
-                sm += Elem<IT>::load(qg, oi + c) * s.rq[ri] * kj * e;
-            }
-            s.M[ri][rj] = sm;
-            s.A[ri][rj] = (rj < ri) ? sa * s.beta[ri] : 0.f;
-        }
-    }
-    __syncthreads();
-
-    // ---- 6. T = (I + A)^-1: diagonal sub-blocks by forward substitution ...
-    for (int e = t; e < kChunk * (kChunk + 1); e += kThreads) (&s.u.T[0][0])[e] = 0.f;
-    __syncthreads();
-    if (lane < kSub) {
-        const int I = w;
-        const int jc = lane;
-        float x[kSub];
-#pragma unroll
-        for (int m = 0; m < kSub; ++m) x[m] = (m == jc) ? 1.f : 0.f;
-#pragma unroll
-        for (int r = 1; r < kSub; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < r; ++m) acc += s.A[kSub * I + r][kSub * I + m] * x[m];
-            if (r > jc) x[r] = -acc;
-        }
-#pragma unroll
-        for (int r = 0; r < kSub; ++r) s.u.T[kSub * I + r][kSub * I + jc] = x[r];
-    }
-    __syncthreads();
-    // ... then the off-diagonal sub-blocks by distance: T_IJ = -T_II sum_L A_IL T_LJ
-    for (int d = 1; d < 4; ++d) {
-        const int nb = 4 - d;
-        for (int e = t; e < nb * kSub * kSub; e += kThreads) {
-            const int bi = e / (kSub * kSub);
-            const int a = (e / kSub) % kSub, b = e % kSub;
-            const int I = d + bi, J = bi;
-            float acc = 0.f;
-            for (int Lb = J; Lb < I; ++Lb)
-#pragma unroll
-                for (int m = 0; m < kSub; ++m)
-                    acc += s.A[kSub * I + a][kSub * Lb + m] * s.u.T[kSub * Lb + m][kSub * J + b];
-            s.X[bi][a][b] = acc;
-        }
-        __syncthreads();
-        for (int e = t; e < nb * kSub * kSub; e += kThreads) {
-            const int bi = e / (kSub * kSub);
-            const int a = (e / kSub) % kSub, b = e % kSub;
-            const int I = d + bi, J = bi;
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < kSub; ++m) acc += s.u.T[kSub * I + a][kSub * I + m] * s.X[bi][m][b];
-            s.u.T[kSub * I + a][kSub * J + b] = -acc;
-        }
-        __syncthreads();
-    }
-
-    // ---- 7. T diag(beta) and scale * M to the workspace
-    for (int e = t; e < kChunk * kChunk; e += kThreads) {
-        const int a = e / kChunk, b = e % kChunk;
-        gTB[e] = MM::from_f32(s.u.T[a][b] * s.beta[b]);
-        gMS[e] = MM::from_f32(p.scale * s.M[a][b]);
-    }
-    for (int c = t; c < K; c += kThreads) gGC[c] = s.gC[c];
-}
-
-// ------------------------------------------------------------------ state
-// Copy a [R][C] global matrix into LDS rows of leading dimension ld.
-template <typename ET, int R, int C>
-__device__ __forceinline__ void copy_in(ET* dst, int ld, const ET* src, int t) {
-    constexpr int VE = 16 / sizeof(ET);  // elements per 16-byte vector
-    constexpr int NV = R * C / VE;
-    for (int e = t; e < NV; e += kThreads) {
-        const int r = (e * VE) / C, c = (e * VE) % C;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * C + c);
-        *reinterpret_cast<f32x4*>(dst + r * ld + c) = v;
-    }
-}
-// Same, transposed: dst[c][r] = src[r][c].
-template <typename ET, int R, int C>
-__device__ __forceinline__ void copy_in_t(ET* dst, int ld, const ET* src, int t) {
-    constexpr int VE = 16 / sizeof(ET);
-    constexpr int NV = R * C / VE;
-    for (int e = t; e < NV; e += kThreads) {
-        const int r = (e * VE) / C, c = (e * VE) % C;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * C + c);
-        const ET* ve = reinterpret_cast<const ET*>(&v);
-#pragma unroll
-        for (int x = 0; x < VE; ++x) dst[(c + x) * ld + r] = ve[x];
-    }
-}
-
-template <int K, int V, int BV, bool BF>
-__global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p, const int32_t* chunk_off,
-                                                                   const uint8_t* ws) {
-    using MM = Mma<BF>;
-    using ET = typename MM::ET;
-    using IT = typename std::conditional<BF, uint16_t, float>::type;
-    using L = PrepLayout<K, BF>;
-    constexpr int LDK = K + MM::PAD;
-    constexpr int LDC = kChunk + MM::PAD;
-    constexpr int NCT = BV / 16;
-    constexpr int NST = (K / 16) * NCT;
-    constexpr int SPW = (NST + 3) / 4;
-    constexpr int NVB = V / BV;
-
-    __shared__ __attribute__((aligned(16))) ET QK[2 * kChunk][LDK];
-    __shared__ __attribute__((aligned(16))) ET KDt[K][LDC];
-    __shared__ __attribute__((aligned(16))) ET TB[kChunk][LDC];
-    __shared__ __attribute__((aligned(16))) ET MS[kChunk][LDC];
-    __shared__ __attribute__((aligned(16))) ET St[BV][LDK];
-    __shared__ __attribute__((aligned(16))) ET Yt[BV][LDC];
-    __shared__ __attribute__((aligned(16))) ET Dt[BV][LDC];
-    __shared__ float gC[K];
-
-    int chain, vb;
-    if (!chain_of_block(blockIdx.x, p.N * p.H, NVB, chain, vb)) return;
-    const int H = p.H;
-    const int n = chain / H, h = chain % H;
-    int64_t start;
-    int len;
-    seq_bounds(p, n, start, len);
-    const int nc = n_chunks(len);
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int v0 = vb * BV;
-
-    // fp32 state tiles owned by this wave: tile m -> (row tile, col tile)
-    f32x4 S[SPW];
-    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
-#pragma unroll
-    for (int m = 0; m < SPW; ++m) {
-        const int tt = w + 4 * m;
-        const int rt = tt / NCT, ct = tt % NCT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float v = 0.f;
-            if (tt < NST && p.h0) v = p.h0[sbase + (16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)];
-            S[m][r] = v;
-        }
-    }
-
-    const IT* vg = static_cast<const IT*>(p.v);
-    IT* og = static_cast<IT*>(p.o);
-    for (int jc = 0; jc < nc; ++jc) {
-        const uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * L::kBytes;
-        copy_in<ET, kChunk, K>(&QK[0][0], LDK, reinterpret_cast<const ET*>(base + L::kQE), t);
-        copy_in<ET, kChunk, K>(&QK[kChunk][0], LDK, reinterpret_cast<const ET*>(base + L::kKE), t);
-        copy_in_t<ET, kChunk, K>(&KDt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kKD), t);
-        copy_in<ET, kChunk, kChunk>(&TB[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-        copy_in<ET, kChunk, kChunk>(&MS[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
-        for (int c = t; c < K; c += kThreads) gC[c] = reinterpret_cast<const float*>(base + L::kGC)[c];
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int tt = w + 4 * m;
-            if (tt < NST) {
-                const int rt = tt / NCT, ct = tt % NCT;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    St[16 * ct + (lane & 15)][16 * rt + 4 * (lane >> 4) + r] = MM::from_f32(S[m][r]);
-            }
-        }
-        __syncthreads();
-
-        // (q exp(G)) S and (k exp(G)) S for this wave's 16 rows
-        f32x4 oq[NCT], pp[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) oq[ct] = pp[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-        for (int k0 = 0; k0 < K; k0 += MM::KS) {
-            const auto aq = MM::load(&QK[0][0], LDK, 16 * w, k0, lane);
-            const auto ak = MM::load(&QK[0][0], LDK, kChunk + 16 * w, k0, lane);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const auto b = MM::load(&St[0][0], LDK, 16 * ct, k0, lane);
-                oq[ct] = MM::mma(aq, b, oq[ct]);
-                pp[ct] = MM::mma(ak, b, pp[ct]);
-            }
-        }
-        // Y = v - (k exp(G)) S
-        const int rbase = jc * kChunk;
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * w + 4 * (lane >> 4) + r;
-                const int col = 16 * ct + (lane & 15);
-                float vv = 0.f;
-                if (rbase + row < len) vv = Elem<IT>::load(vg, ((start + rbase + row) * H + h) * V + v0 + col);
-                Yt[col][row] = MM::from_f32(vv - pp[ct][r]);
-            }
-        __syncthreads();
-
-        // D = T diag(beta) Y   (T lower triangular: k < 16 (w + 1))
-        f32x4 dd[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) dd[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < 16 * (w + 1); k0 += MM::KS) {
-            const auto a = MM::load(&TB[0][0], LDC, 16 * w, k0, lane);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) dd[ct] = MM::mma(a, MM::load(&Yt[0][0], LDC, 16 * ct, k0, lane), dd[ct]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Dt[16 * ct + (lane & 15)][16 * w + 4 * (lane >> 4) + r] = MM::from_f32(dd[ct][r]);
-        __syncthreads();
-
-        // O = scale (q exp(G)) S + scale M D
-        for (int k0 = 0; k0 < 16 * (w + 1); k0 += MM::KS) {
-            const auto a = MM::load(&MS[0][0], LDC, 16 * w, k0, lane);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) oq[ct] = MM::mma(a, MM::load(&Dt[0][0], LDC, 16 * ct, k0, lane), oq[ct]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * w + 4 * (lane >> 4) + r;
-                if (rbase + row < len)
-                    Elem<IT>::store(og, ((start + rbase + row) * H + h) * V + v0 + 16 * ct + (lane & 15), oq[ct][r]);
-            }
-
-        // S' = diag(exp(G_last)) S + (k exp(G_last - G))^T D
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int tt = w + 4 * m;
-            if (tt < NST) {
-                const int rt = tt / NCT, ct = tt % NCT;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) S[m][r] *= gC[16 * rt + 4 * (lane >> 4) + r];
-#pragma unroll
-                for (int k0 = 0; k0 < kChunk; k0 += MM::KS)
-                    S[m] = MM::mma(MM::load(&KDt[0][0], LDC, 16 * rt, k0, lane),
-                                   MM::load(&Dt[0][0], LDC, 16 * ct, k0, lane), S[m]);
-            }
-        }
-        __syncthreads();
-    }
-
-    if (p.ht) {
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int tt = w + 4 * m;
-            if (tt < NST) {
-                const int rt = tt / NCT, ct = tt % NCT;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    p.ht[sbase + (16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = S[m][r];
-            }
-        }
-    }
-}
-
 // ------------------------------------------------------------------ host side
-static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
-
 template <int K, bool BF>
 static size_t prep_bytes(const ChunkParams& p) {
     return static_cast<size_t>(p.total_chunks_bound) * p.H * PrepLayout<K, BF>::kBytes;
-}
-
-static size_t chunk_off_bytes(const ChunkParams& p) {
-    return align256(sizeof(int32_t) * (static_cast<size_t>(p.N) + 1));
 }
 
 size_t chunk_fwd_workspace(const ChunkParams& p) {
@@ -617,29 +22,35 @@ size_t chunk_fwd_workspace(const ChunkParams& p) {
 }
 
 template <int K, int V, int BV, bool BF>
-static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st) {
+static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage) {
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     int32_t* chunk_off = reinterpret_cast<int32_t*>(w8);
     uint8_t* prep = w8 + chunk_off_bytes(p);
-    if (p.cu_seqlens)
-        hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
-    const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
-    if (nblk > 0)
-        hipLaunchKernelGGL((chunk_prep_kernel<K, BF>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0, st,
-                           p, chunk_off, prep);
-    const int grid = chain_grid(p.N * p.H, V / BV);
-    if (grid > 0)
-        hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF>), dim3(grid), dim3(kThreads), 0, st, p,
-                           chunk_off, prep);
+    if (stage < 0 || stage == 0) {
+        if (p.cu_seqlens)
+            hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
+        const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
+        if (nblk > 0)
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, false>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
+                               0, st, p, chunk_off, prep, static_cast<int64_t>(PrepLayout<K, BF>::kBytes));
+    }
+    if (stage < 0 || stage == 1) {
+        const int grid = chain_grid(p.N * p.H, V / BV);
+        if (grid > 0)
+            hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, false, true>), dim3(grid), dim3(kThreads), 0,
+                               st, p, chunk_off, prep, static_cast<int64_t>(PrepLayout<K, BF>::kBytes));
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st) {
+hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage) {
     if (p.K != p.V) return hipErrorInvalidValue;
     switch (p.K) {
-        case 32: return p.bf16 ? run_fwd<32, 32, 16, true>(p, ws, st) : run_fwd<32, 32, 16, false>(p, ws, st);
-        case 64: return p.bf16 ? run_fwd<64, 64, 32, true>(p, ws, st) : run_fwd<64, 64, 32, false>(p, ws, st);
-        case 128: return p.bf16 ? run_fwd<128, 128, 32, true>(p, ws, st) : hipErrorInvalidValue;
+        case 32:
+            return p.bf16 ? run_fwd<32, 32, 16, true>(p, ws, st, stage) : run_fwd<32, 32, 16, false>(p, ws, st, stage);
+        case 64:
+            return p.bf16 ? run_fwd<64, 64, 32, true>(p, ws, st, stage) : run_fwd<64, 64, 32, false>(p, ws, st, stage);
+        case 128: return p.bf16 ? run_fwd<128, 128, 32, true>(p, ws, st, stage) : hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

@@ -69,9 +69,13 @@ struct ChunkGrads {
 };
 
 size_t chunk_fwd_workspace(const ChunkParams& p);
-hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st);
+// stage < 0 runs every stage; 0 = prep, 1 = state pass.
+hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage = -1);
 
 size_t chunk_bwd_workspace(const ChunkParams& p);
-hipError_t launch_chunk_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st);
+// stage < 0 runs every stage; 0 prep, 1 state pass (stores states), 2 reverse
+// state pass, 3 V-local gradients, 4 K-local gradients.
+constexpr int kBwdStages = 5;
+hipError_t launch_chunk_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st, int stage = -1);
 
 }  // namespace kda

@@ -1,0 +1,144 @@
+"""GPU parity of kda_chunk_bwd against the oracle's hand-derived backward
+(itself pinned by central finite differences in test_oracle.py)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import kimi_delta_attention_amd as kda
+from kimi_delta_attention_amd import inputs
+from parity import check, dev, tol_for
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["dq", "dk", "dv", "dg", "dbeta", "dh0"]
+
+
+def _gpu_bwd(w, **over):
+    kw = dict(A_log=dev(w["A_log"]), dt_bias=dev(w["dt_bias"]), scale=w["scale"],
+              initial_state=dev(w["initial_state"]), use_qk_l2norm_in_kernel=w["use_qk_l2norm"],
+              gate_mode=w["gate_mode"], use_beta_sigmoid_in_kernel=w["use_beta_sigmoid"],
+              lower_bound=w["lower_bound"], cu_seqlens=dev(w["cu_seqlens"]),
+              d_final_state=dev(w.get("d_final_state")))
+    kw.update(over)
+    out = kda.chunk_kda_bwd(dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["g"]), dev(w["beta"]), dev(w["dO"]), **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_bwd(w):
+    return oracle.chunk_bwd(w["q"], w["k"], w["v"], w["g"], w["beta"], w["dO"], d_final_state=w.get("d_final_state"),
+                            A_log=w["A_log"], dt_bias=w["dt_bias"], scale=w["scale"], initial_state=w["initial_state"],
+                            use_qk_l2norm=w["use_qk_l2norm"], gate_mode=w["gate_mode"],
+                            use_beta_sigmoid=w["use_beta_sigmoid"], lower_bound=w["lower_bound"],
+                            cu_seqlens=w["cu_seqlens"])
+
+
+def _compare(w, tag, names=NAMES):
+    tol = tol_for(w["q"].dtype)
+    print(f"{tag}: q{tuple(w['q'].shape)} {w['q'].dtype} gate={w['gate_mode']}", flush=True)
+    g = _gpu_bwd(w)
+    o = _oracle_bwd(w)
+    for name in names:
+        check(f"{tag} {name}", g[name], o[name], tol)
+    if w["gate_mode"] != inputs.GATE_LOGDECAY:
+        check(f"{tag} dA_log", g["dA_log"], o["dA_log"], tol)
+        check(f"{tag} ddt_bias", g["ddt_bias"], o["ddt_bias"], tol)
+
+
+@pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 130])
+@pytest.mark.parametrize("dtype,K", [(torch.float32, 32), (torch.float32, 64), (torch.bfloat16, 32),
+                                     (torch.bfloat16, 64), (torch.bfloat16, 128)])
+def test_bwd_boundary_lengths(T, dtype, K):
+    w = inputs.chunk_inputs(2, T, 2, K, K, seed=300 + T + K, dtype=dtype, h0_std=0.1, with_grad_out=True,
+                            dfinal_std=0.1)
+    _compare(w, f"T={T} K={K}")
+
+
+@pytest.mark.parametrize("mode", [inputs.GATE_SAFE, inputs.GATE_SOFTPLUS])
+@pytest.mark.parametrize("dtype,K", [(torch.float32, 32), (torch.bfloat16, 128)])
+def test_bwd_in_kernel_gates(mode, dtype, K):
+    w = inputs.chunk_inputs(2, 150, 2, K, K, seed=17 + mode, dtype=dtype, gate_mode=mode, beta_logits=True,
+                            h0_std=0.1, with_grad_out=True, dfinal_std=0.1)
+    _compare(w, f"gate {mode}")
+
+
+def test_bwd_small_fp32_workload():
+    """B1 T128 H2 K=V=32 fp32 with an upstream dO and final-state cotangent."""
+    w = inputs.chunk_inputs(1, 128, 2, 32, 32, seed=inputs.SEEDS["fwd_small"], with_grad_out=True, dfinal_std=0.1)
+    _compare(w, "small")
+
+
+def test_bwd_twin_fp32_unbounded_gate():
+    """B4 T2048 H8 K=V=32 fp32, unbounded in-kernel gate, beta logits."""
+    w = inputs.chunk_inputs(4, 2048, 8, 32, 32, seed=inputs.SEEDS["fwd_twin"], gate_mode=inputs.GATE_SOFTPLUS,
+                            beta_logits=True, h0_std=0.1, with_grad_out=True, dfinal_std=0.1)
+    _compare(w, "twin")
+
+
+def test_bwd_varlen_empty_and_tiny():
+    cu = [0, 0, 1, 66, 66, 130, 200]
+    w = inputs.chunk_inputs(1, 200, 2, 64, 64, seed=23, dtype=torch.bfloat16, cu_seqlens=cu, h0_std=0.2,
+                            with_grad_out=True, dfinal_std=0.1)
+    _compare(w, "varlen")
+
+
+def _slice_units(w, units):
+    """Inputs restricted to the (batch row, head) units listed; units are
+    independent, so the oracle's result on the slice is exact for them."""
+    out = {}
+    bs = [b for b, _ in units]
+    hs = [h for _, h in units]
+    for key in ("q", "k", "v", "g", "dO"):
+        out[key] = torch.stack([w[key][b, :, h] for b, h in units], 0).unsqueeze(2)
+    out["beta"] = torch.stack([w["beta"][b, :, h] for b, h in units], 0).unsqueeze(2)
+    out["initial_state"] = torch.stack([w["initial_state"][b, h] for b, h in units], 0).unsqueeze(1)
+    out["d_final_state"] = None
+    for key in ("scale", "use_qk_l2norm", "gate_mode", "use_beta_sigmoid", "lower_bound"):
+        out[key] = w[key]
+    out["A_log"] = out["dt_bias"] = None
+    out["cu_seqlens"] = None
+    return out, bs, hs
+
+
+def test_bwd_train_geometry_sampled_units():
+    """B8 T4096 H16 K=V=128 bf16 with dO ~ N(0,1): the whole batch runs on the
+    GPU; the oracle checks 4 sampled (sequence, head) units."""
+    w = inputs.workload("train")
+    print("train geometry", flush=True)
+    g = _gpu_bwd(w)
+    units = [(0, 0), (3, 7), (5, 12), (7, 15)]
+    sub, bs, hs = _slice_units(w, units)
+    o = _oracle_bwd(sub)
+    for name in ["dq", "dk", "dv", "dg"]:
+        got = torch.stack([g[name][b, :, h] for b, h in units], 0).unsqueeze(2)
+        check(f"train {name}", got, o[name], 2e-2)
+    got = torch.stack([g["dbeta"][b, :, h] for b, h in units], 0).unsqueeze(2)
+    check("train dbeta", got, o["dbeta"], 2e-2)
+    got = torch.stack([g["dh0"][b, h] for b, h in units], 0).unsqueeze(1)
+    check("train dh0", got, o["dh0"], 2e-2)
+
+
+def test_bwd_hybrid_varlen_sampled_heads():
+    """Packed 1024/2048/1024/4096, H16 K=V=128 bf16, dO ~ N(0,1): 3 heads checked."""
+    w = inputs.chunk_inputs(1, 8192, 16, 128, 128, seed=inputs.SEEDS["fwd_hybrid"], dtype=torch.bfloat16,
+                            cu_seqlens=[0, 1024, 3072, 4096, 8192], with_grad_out=True)
+    g = _gpu_bwd(w)
+    heads = [1, 8, 14]
+    sub = dict(w)
+    for key in ("q", "k", "v", "g", "dO"):
+        sub[key] = w[key][:, :, heads]
+    sub["beta"] = w["beta"][:, :, heads]
+    sub["initial_state"] = w["initial_state"][:, heads]
+    o = _oracle_bwd(sub)
+    for name in ["dq", "dk", "dv", "dg", "dbeta"]:
+        check(f"hybrid {name}", g[name][:, :, heads], o[name], 2e-2)
+    check("hybrid dh0", g["dh0"][:, heads], o["dh0"], 2e-2)
+
+
+def test_bwd_deterministic():
+    w = inputs.chunk_inputs(2, 200, 2, 128, 128, seed=9, dtype=torch.bfloat16, with_grad_out=True)
+    a = _gpu_bwd(w)
+    b = _gpu_bwd(w)
+    for name in NAMES:
+        assert torch.equal(a[name], b[name]), name
