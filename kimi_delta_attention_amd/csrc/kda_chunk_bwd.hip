@@ -8,7 +8,8 @@
 //   O  = QE S + MS D         S' = gam * S + KD^T D
 // which gives (all products column-local in V except where summed over V)
 //   dD  = KD dS' + MS^T dO            dY = TB^T dD            dv = dY
-//   dS  = gam * dS' + QE^T dO - KE^T dY                        (reverse pass)
+//   dS  = gam * dS' + QE^T dO - KE^T dY = gam * dS' + QE^T dO - W^T dD
+//                                        (reverse pass; W = TB KE from the prep)
 //   dQE = dO S^T   dKE = -dY S^T   dKD = D dS'^T   dMS = dO D^T   dTB = dD Y^T
 //   dgam = rowsum(dS' * S)
 // then, through the prologue of the chunk,
@@ -57,6 +58,9 @@ __device__ __forceinline__ f32x4 gemm(const typename MM::ET* A, int lda, int m0,
 }
 
 // ------------------------------------------------------------------ reverse state pass
+// Per chunk in reverse, with dS' the gradient of the state leaving the chunk:
+//   dD = KD dS' + MS^T dO,   dS = GC * dS' + QE^T dO - W^T dD
+// (W^T dD = (k exp(G))^T TB^T dD).  dS' is stored in the chunk's slot.
 template <int K, int V, int BV, bool BF>
 __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p, ChunkGrads gr,
                                                                    const int32_t* chunk_off, uint8_t* ws,
@@ -73,16 +77,14 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     constexpr int SPW = (NST + 3) / 4;
     constexpr int NVB = V / BV;
 
-    __shared__ __attribute__((aligned(16))) ET QEt[K][LDC];   // QE^T: A of QE^T dO
-    __shared__ __attribute__((aligned(16))) ET KEt[K][LDC];   // KE^T: A of KE^T dY
+    __shared__ __attribute__((aligned(16))) ET QEt[K][LDC];       // QE^T: A of QE^T dO
+    __shared__ __attribute__((aligned(16))) ET Wt[K][LDC];        // W^T:  A of W^T dD
     __shared__ __attribute__((aligned(16))) ET KDn[kChunk][LDK];  // A of KD dS'
     __shared__ __attribute__((aligned(16))) ET MSt[kChunk][LDC];  // MS^T: A of MS^T dO
-    __shared__ __attribute__((aligned(16))) ET TBt[kChunk][LDC];  // TB^T: A of TB^T dD
     __shared__ __attribute__((aligned(16))) ET dSt[BV][LDK];      // dS'^T: B of KD dS'
     __shared__ __attribute__((aligned(16))) ET dOt[BV][LDC];
     __shared__ __attribute__((aligned(16))) ET dDt[BV][LDC];
-    __shared__ __attribute__((aligned(16))) ET dYt[BV][LDC];
-    __shared__ float gC[K];
+    __shared__ __attribute__((aligned(16))) float gC[K];
 
     int chain, vb;
     if (!chain_of_block(blockIdx.x, p.N * p.H, NVB, chain, vb)) return;
@@ -96,6 +98,23 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     const int v0 = vb * BV;
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
 
+    Seg<ET, kChunk, K, true> sQE, sW;
+    Seg<ET, kChunk, K, false> sKD;
+    Seg<ET, kChunk, kChunk, true> sMS;
+    Seg<ET, kChunk, BV, true> sdO;
+    Seg<float, 1, K, false> sGC;
+    const ET* dOg = static_cast<const ET*>(gr.dO);
+    auto prefetch = [&](int jc) {
+        const uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
+        sQE.load(reinterpret_cast<const ET*>(base + L::kQE), K, t);
+        sW.load(reinterpret_cast<const ET*>(base + L::kW), K, t);
+        sKD.load(reinterpret_cast<const ET*>(base + L::kKD), K, t);
+        sMS.load(reinterpret_cast<const ET*>(base + L::kMS), kChunk, t);
+        sGC.load(reinterpret_cast<const float*>(base + L::kGC), K, t);
+        sdO.load(dOg + ((start + static_cast<int64_t>(jc) * kChunk) * H + h) * V + v0,
+                 static_cast<int64_t>(H) * V, t, min(kChunk, len - jc * kChunk));
+    };
+
     f32x4 dS[SPW];
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
@@ -108,15 +127,16 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
             dS[m][r] = v;
         }
     }
-    const IT* dOg = static_cast<const IT*>(gr.dO);
+    if (nc > 0) prefetch(nc - 1);
+    const int klo = (16 * w / MM::KS) * MM::KS;
     for (int jc = nc - 1; jc >= 0; --jc) {
+        sQE.store(&QEt[0][0], LDC, t);
+        sW.store(&Wt[0][0], LDC, t);
+        sKD.store(&KDn[0][0], LDK, t);
+        sMS.store(&MSt[0][0], LDC, t);
+        sGC.store(&gC[0], K, t);
+        sdO.store(&dOt[0][0], LDC, t);
         uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
-        copy_in_t<ET, kChunk, K>(&QEt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kQE), t);
-        copy_in_t<ET, kChunk, K>(&KEt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kKE), t);
-        copy_in<ET, kChunk, K>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
-        copy_in_t<ET, kChunk, kChunk>(&MSt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
-        copy_in_t<ET, kChunk, kChunk>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-        for (int c = t; c < K; c += kThreads) gC[c] = reinterpret_cast<const float*>(base + L::kGC)[c];
         ET* gDS = reinterpret_cast<ET*>(base + X::kDS);
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
@@ -132,46 +152,27 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
                 }
             }
         }
-        const int rbase = jc * kChunk;
-        for (int e = t; e < kChunk * BV; e += kThreads) {
-            const int i = e / BV, c = e % BV;
-            float v = 0.f;
-            if (rbase + i < len) v = Elem<IT>::load(dOg, ((start + rbase + i) * H + h) * V + v0 + c);
-            dOt[c][i] = MM::from_f32(v);
-        }
         __syncthreads();
+        if (jc > 0) prefetch(jc - 1);
 
         // dD = KD dS' + MS^T dO   (rows 16w..; MS^T is upper triangular: k >= 16w)
-        const int klo = (16 * w / MM::KS) * MM::KS;
-        f32x4 dd[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = gemm<MM>(&KDn[0][0], LDK, 16 * w, &dSt[0][0], LDK, 16 * ct, 0, K, acc, lane);
             acc = gemm<MM>(&MSt[0][0], LDC, 16 * w, &dOt[0][0], LDC, 16 * ct, klo, kChunk, acc, lane);
-            dd[ct] = acc;
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) tile_store_t<MM>(&dDt[0][0], LDC, 16 * w, 16 * ct, dd[ct], lane);
-        __syncthreads();
-
-        // dY = TB^T dD
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = gemm<MM>(&TBt[0][0], LDC, 16 * w, &dDt[0][0], LDC, 16 * ct, klo, kChunk, acc, lane);
-            tile_store_t<MM>(&dYt[0][0], LDC, 16 * w, 16 * ct, acc, lane);
+            tile_store_t<MM>(&dDt[0][0], LDC, 16 * w, 16 * ct, acc, lane);
         }
         __syncthreads();
 
-        // dS = gam * dS' + QE^T dO - KE^T dY
+        // dS = GC * dS' + QE^T dO - W^T dD
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
             const int tt = w + 4 * m;
             if (tt < NST) {
                 const int rt = tt / NCT, ct = tt % NCT;
                 f32x4 neg = {0.f, 0.f, 0.f, 0.f};
-                neg = gemm<MM>(&KEt[0][0], LDC, 16 * rt, &dYt[0][0], LDC, 16 * ct, 0, kChunk, neg, lane);
+                neg = gemm<MM>(&Wt[0][0], LDC, 16 * rt, &dDt[0][0], LDC, 16 * ct, 0, kChunk, neg, lane);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dS[m][r] = dS[m][r] * gC[16 * rt + 4 * (lane >> 4) + r] - neg[r];
                 dS[m] = gemm<MM>(&QEt[0][0], LDC, 16 * rt, &dOt[0][0], LDC, 16 * ct, 0, kChunk, dS[m], lane);
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_vlocal_kernel(ChunkParams 
     uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
     const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
 
-    copy_in<ET, kChunk, K>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKE), t);
+    copy_in<ET, kChunk, K>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + X::kKE), t);
     copy_in<ET, kChunk, K>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
     copy_in<ET, kChunk, kChunk>(&TBn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
     copy_in_t<ET, kChunk, kChunk>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);

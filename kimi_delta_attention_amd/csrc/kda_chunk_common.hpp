@@ -92,26 +92,31 @@ __device__ __forceinline__ int n_chunks(int len) { return (len + kChunk - 1) / k
 
 // Workspace layout of the per-chunk operands produced by the prep kernel, per
 // (chunk, head) slot, all [row][col] with the column fastest:
-//   QE  [64][K]  scale * q^ * exp(G)            (ET)
-//   KE  [64][K]  k^ * exp(G)                    (ET)
-//   KD  [64][K]  k^ * exp(G_last - G)           (ET)
-//   TB  [64][64] (I + A)^-1 * diag(beta)        (ET)
-//   MS  [64][64] scale * tril(q^ k^T decayed)   (ET)
-//   GC  [K]      exp(G_last)                    (fp32)
-// G is the inclusive cumulative log-decay inside the chunk.
+//   QE  [64][K]  scale * q^ * exp(G)                     (ET)
+//   W   [64][K]  T diag(beta) (k^ * exp(G))              (ET)
+//   KD  [64][K]  k^ * exp(G_last - G)                    (ET)
+//   U   [64][V]  T diag(beta) v                          (ET)
+//   TB  [64][64] T diag(beta), T = (I + A)^-1            (ET)
+//   MS  [64][64] scale * tril(q^ k^T decayed)            (ET)
+//   GC  [K]      exp(G_last)                             (fp32)
+// G is the inclusive cumulative log-decay inside the chunk.  With S the state
+// entering the chunk, D = U - W S, O = QE S + MS D and S' = GC * S + KD^T D.
 template <int K, bool BF>
 struct PrepLayout {
     using ET = typename Mma<BF>::ET;
+    static constexpr int V = K;
     static constexpr size_t kQE = 0;
-    static constexpr size_t kKE = kQE + sizeof(ET) * kChunk * K;
-    static constexpr size_t kKD = kKE + sizeof(ET) * kChunk * K;
-    static constexpr size_t kTB = kKD + sizeof(ET) * kChunk * K;
+    static constexpr size_t kW = kQE + sizeof(ET) * kChunk * K;
+    static constexpr size_t kKD = kW + sizeof(ET) * kChunk * K;
+    static constexpr size_t kU = kKD + sizeof(ET) * kChunk * K;
+    static constexpr size_t kTB = kU + sizeof(ET) * kChunk * V;
     static constexpr size_t kMS = kTB + sizeof(ET) * kChunk * kChunk;
     static constexpr size_t kGC = kMS + sizeof(ET) * kChunk * kChunk;
     static constexpr size_t kBytes = ((kGC + sizeof(float) * K) + 255) / 256 * 256;
 };
 
 // Backward-only additions to a slot, placed after the PrepLayout operands:
+//   KE   [64][K]  k^ * exp(G)                     (ET)
 //   T    [64][64] (I + A)^-1                      (ET)
 //   AK   [64][64] strict_tril(k^ k^T decayed)      (ET)
 //   S    [K][V]   state entering the chunk         (ET)
@@ -124,7 +129,8 @@ template <int K, bool BF>
 struct BwdExtra {
     using ET = typename Mma<BF>::ET;
     static constexpr int V = K;
-    static constexpr size_t kT = PrepLayout<K, BF>::kBytes;
+    static constexpr size_t kKE = PrepLayout<K, BF>::kBytes;
+    static constexpr size_t kT = kKE + sizeof(ET) * kChunk * K;
     static constexpr size_t kAK = kT + sizeof(ET) * kChunk * kChunk;
     static constexpr size_t kS = kAK + sizeof(ET) * kChunk * kChunk;
     static constexpr size_t kDS = kS + sizeof(ET) * K * V;

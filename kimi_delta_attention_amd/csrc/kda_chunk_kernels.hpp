@@ -104,6 +104,11 @@ struct PrepSmem {
             ET kbe[kChunk][LDE];  // k^ exp(G_end(J) - G_j)
         } op;
         float T[kChunk][kChunk + 1];
+        struct {
+            ET TB[kChunk][kChunk + Mma<BF>::PAD];  // T diag(beta): A operand of W and U
+            ET KEt[K][kChunk + Mma<BF>::PAD];      // (k^ exp(G))^T
+            ET Vt[K][kChunk + Mma<BF>::PAD];       // v^T (V = K)
+        } wu;
     } u;
     float A[kChunk][kChunk + 1];
     float M[kChunk][kChunk + 1];
@@ -149,7 +154,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     const int w = t >> 6;
     uint8_t* out = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
     ET* gQE = reinterpret_cast<ET*>(out + L::kQE);
-    ET* gKE = reinterpret_cast<ET*>(out + L::kKE);
     ET* gKD = reinterpret_cast<ET*>(out + L::kKD);
     ET* gTB = reinterpret_cast<ET*>(out + L::kTB);
     ET* gMS = reinterpret_cast<ET*>(out + L::kMS);
@@ -265,7 +269,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     }
     __syncthreads();
 
-    // ---- 4. factored operands (LDS) and the chunk's outputs QE, KE, KD (workspace)
+    // ---- 4. factored operands (LDS) and the chunk's outputs QE, KD (workspace);
+    //         k^ exp(G) stays in registers for W
+    float ke_[CPT];
     {
         const int I = i / kSub;
         float a_[CPT], e_[CPT], o_[CPT];
@@ -287,8 +293,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
         for (int c = 0; c < CPT; ++c) o_[c] = p.scale * qh[c] * a_[c] * s.Er[I][c0 + c];
         store_row<CPT>(gQE + i * K + c0, o_);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * a_[c] * s.Er[I][c0 + c];
-        store_row<CPT>(gKE + i * K + c0, o_);
+        for (int c = 0; c < CPT; ++c) ke_[c] = kh[c] * a_[c] * s.Er[I][c0 + c];
+        if (BWD) store_row<CPT>(reinterpret_cast<ET*>(out + BwdExtra<K, BF>::kKE) + i * K + c0, ke_);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * e_[c] * s.Ec[I][c0 + c];
         store_row<CPT>(gKD + i * K + c0, o_);
@@ -406,9 +412,14 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     }
 
     // ---- 7. T diag(beta) and scale * M to the workspace
-    for (int e = t; e < kChunk * kChunk; e += kThreads) {
+    constexpr int TPT = kChunk * kChunk / kThreads;
+    float tbr[TPT];
+#pragma unroll
+    for (int m = 0; m < TPT; ++m) {
+        const int e = t + m * kThreads;
         const int a = e / kChunk, b = e % kChunk;
-        gTB[e] = MM::from_f32(s.u.T[a][b] * s.beta[b]);
+        tbr[m] = s.u.T[a][b] * s.beta[b];
+        gTB[e] = MM::from_f32(tbr[m]);
         gMS[e] = MM::from_f32(p.scale * s.M[a][b]);
     }
     for (int c = t; c < K; c += kThreads) gGC[c] = s.gC[c];
@@ -419,6 +430,47 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
             const int a = e / kChunk, b = e % kChunk;
             gT[e] = MM::from_f32(s.u.T[a][b]);
             gAK[e] = MM::from_f32(s.Ak[a][b]);
+        }
+    }
+    __syncthreads();
+
+    // ---- 8. the WY pair W = T diag(beta) (k^ exp(G)), U = T diag(beta) v on MFMA
+    {
+        constexpr int LDC = kChunk + MM::PAD;
+#pragma unroll
+        for (int m = 0; m < TPT; ++m) {
+            const int e = t + m * kThreads;
+            s.u.wu.TB[e / kChunk][e % kChunk] = MM::from_f32(tbr[m]);
+        }
+        float vv[CPT];
+        if (valid) {
+            load_row<CPT>(static_cast<const IT*>(p.v) + (grow * H + h) * K + c0, vv);
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) vv[c] = 0.f;
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+            s.u.wu.KEt[c0 + c][i] = MM::from_f32(ke_[c]);
+            s.u.wu.Vt[c0 + c][i] = MM::from_f32(vv[c]);
+        }
+        __syncthreads();
+        ET* gW = reinterpret_cast<ET*>(out + L::kW);
+        ET* gU = reinterpret_cast<ET*>(out + L::kU);
+#pragma unroll 2
+        for (int ct = 0; ct < K / 16; ++ct) {
+            f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+            for (int k0 = 0; k0 < 16 * (w + 1); k0 += MM::KS) {
+                const auto a = MM::load(&s.u.wu.TB[0][0], LDC, 16 * w, k0, lane);
+                aw = MM::mma(a, MM::load(&s.u.wu.KEt[0][0], LDC, 16 * ct, k0, lane), aw);
+                au = MM::mma(a, MM::load(&s.u.wu.Vt[0][0], LDC, 16 * ct, k0, lane), au);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * w + 4 * (lane >> 4) + r, col = 16 * ct + (lane & 15);
+                gW[row * K + col] = MM::from_f32(aw[r]);
+                gU[row * K + col] = MM::from_f32(au[r]);
+            }
         }
     }
 }
@@ -435,13 +487,15 @@ __device__ __forceinline__ void copy_in(ET* dst, int ld, const ET* src, int t) {
         *reinterpret_cast<f32x4*>(dst + r * ld + c) = v;
     }
 }
-// Same, transposed: dst[c][r] = src[r][c].
+// Same, transposed: dst[c][r] = src[r][c].  Consecutive threads take
+// consecutive rows, so the scattered LDS stores of a wavefront land on
+// consecutive addresses.
 template <typename ET, int R, int C>
 __device__ __forceinline__ void copy_in_t(ET* dst, int ld, const ET* src, int t) {
     constexpr int VE = 16 / sizeof(ET);
     constexpr int NV = R * C / VE;
     for (int e = t; e < NV; e += kThreads) {
-        const int r = (e * VE) / C, c = (e * VE) % C;
+        const int r = e % R, c = (e / R) * VE;
         const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * C + c);
         const ET* ve = reinterpret_cast<const ET*>(&v);
 #pragma unroll
@@ -449,8 +503,63 @@ __device__ __forceinline__ void copy_in_t(ET* dst, int ld, const ET* src, int t)
     }
 }
 
+// A [R][C] block (row stride `stride` elements in global memory) moved
+// global -> registers -> LDS in 16-byte vectors, so that the load of the next
+// chunk's block can be issued before the current chunk's work and consumed
+// after it.  TRANS stores the block transposed (dst[c][r]); rows at or past
+// `rows` load as zero.
+template <typename ET, int R, int C, bool TRANS>
+struct Seg {
+    static constexpr int VE = 16 / sizeof(ET);
+    static constexpr int NV = R * C / VE;
+    static constexpr int PER = (NV + kThreads - 1) / kThreads;
+    f32x4 r[PER];
+    __device__ __forceinline__ static void at(int e, int& row, int& col) {
+        if (TRANS) {
+            row = e % R;
+            col = (e / R) * VE;
+        } else {
+            row = (e * VE) / C;
+            col = (e * VE) % C;
+        }
+    }
+    __device__ __forceinline__ void load(const ET* src, int64_t stride, int t, int rows = R) {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = t + m * kThreads;
+            if (NV % kThreads == 0 || e < NV) {
+                int row, col;
+                at(e, row, col);
+                if (row < rows) r[m] = *reinterpret_cast<const f32x4*>(src + row * stride + col);
+                else r[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+    }
+    __device__ __forceinline__ void store(ET* dst, int ld, int t) const {
+#pragma unroll
+        for (int m = 0; m < PER; ++m) {
+            const int e = t + m * kThreads;
+            if (NV % kThreads == 0 || e < NV) {
+                int row, col;
+                at(e, row, col);
+                if (TRANS) {
+                    const ET* ve = reinterpret_cast<const ET*>(&r[m]);
+#pragma unroll
+                    for (int x = 0; x < VE; ++x) dst[(col + x) * ld + row] = ve[x];
+                } else {
+                    *reinterpret_cast<f32x4*>(dst + row * ld + col) = r[m];
+                }
+            }
+        }
+    }
+};
+
+// Forward state pass.  Per chunk, with the chunk's operands from its slot and
+// the fp32 state S (K x BV columns of this workgroup) in MFMA accumulators:
+//   WS = W S, D = U - WS, O = QE S + MS D, S = GC * S + KD^T D.
 // STORE writes each chunk's entry state (BwdExtra::kS, element type ET) for
-// the backward; WRITE_O computes and stores the output.
+// the backward; WRITE_O computes and stores the output.  The next chunk's
+// operands are prefetched into registers while the current chunk computes.
 template <int K, int V, int BV, bool BF, bool STORE, bool WRITE_O>
 __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p, const int32_t* chunk_off,
                                                                    uint8_t* ws, int64_t slot_bytes) {
@@ -460,20 +569,20 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
     using L = PrepLayout<K, BF>;
     constexpr int LDK = K + MM::PAD;
     constexpr int LDC = kChunk + MM::PAD;
+    constexpr int LDB = BV + MM::PAD;
     constexpr int NCT = BV / 16;
-    (void)sizeof(L);
     constexpr int NST = (K / 16) * NCT;
     constexpr int SPW = (NST + 3) / 4;
     constexpr int NVB = V / BV;
+    constexpr int QR = WRITE_O ? kChunk : 0;  // rows of QE ahead of W in QW
 
-    __shared__ __attribute__((aligned(16))) ET QK[2 * kChunk][LDK];
+    __shared__ __attribute__((aligned(16))) ET QW[QR + kChunk][LDK];   // [QE;] W
     __shared__ __attribute__((aligned(16))) ET KDt[K][LDC];
-    __shared__ __attribute__((aligned(16))) ET TB[kChunk][LDC];
-    __shared__ __attribute__((aligned(16))) ET MS[kChunk][LDC];
+    __shared__ __attribute__((aligned(16))) ET MS[WRITE_O ? kChunk : 1][LDC];
     __shared__ __attribute__((aligned(16))) ET St[BV][LDK];
-    __shared__ __attribute__((aligned(16))) ET Yt[BV][LDC];
+    __shared__ __attribute__((aligned(16))) ET Un[kChunk][LDB];
     __shared__ __attribute__((aligned(16))) ET Dt[BV][LDC];
-    __shared__ float gC[K];
+    __shared__ __attribute__((aligned(16))) float gC[K];
 
     int chain, vb;
     if (!chain_of_block(blockIdx.x, p.N * p.H, NVB, chain, vb)) return;
@@ -485,6 +594,21 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
     const int nc = n_chunks(len);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int v0 = vb * BV;
+
+    Seg<ET, kChunk, K, false> sQE, sW;
+    Seg<ET, kChunk, K, true> sKD;
+    Seg<ET, kChunk, kChunk, false> sMS;
+    Seg<ET, kChunk, BV, false> sU;
+    Seg<float, 1, K, false> sGC;
+    auto prefetch = [&](int jc) {
+        const uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
+        if (WRITE_O) sQE.load(reinterpret_cast<const ET*>(base + L::kQE), K, t);
+        sW.load(reinterpret_cast<const ET*>(base + L::kW), K, t);
+        sKD.load(reinterpret_cast<const ET*>(base + L::kKD), K, t);
+        if (WRITE_O) sMS.load(reinterpret_cast<const ET*>(base + L::kMS), kChunk, t);
+        sU.load(reinterpret_cast<const ET*>(base + L::kU) + v0, V, t);
+        sGC.load(reinterpret_cast<const float*>(base + L::kGC), K, t);
+    };
 
     // fp32 state tiles owned by this wave: tile m -> (row tile, col tile)
     f32x4 S[SPW];
@@ -501,11 +625,17 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
         }
     }
 
-    const IT* vg = static_cast<const IT*>(p.v);
     IT* og = static_cast<IT*>(p.o);
+    if (nc > 0) prefetch(0);
     for (int jc = 0; jc < nc; ++jc) {
-        uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
+        if (WRITE_O) sQE.store(&QW[0][0], LDK, t);
+        sW.store(&QW[QR][0], LDK, t);
+        sKD.store(&KDt[0][0], LDC, t);
+        if (WRITE_O) sMS.store(&MS[0][0], LDC, t);
+        sU.store(&Un[0][0], LDB, t);
+        sGC.store(&gC[0], K, t);
         if (STORE) {
+            uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
             ET* gS = reinterpret_cast<ET*>(base + BwdExtra<K, BF>::kS);
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
@@ -518,12 +648,6 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
                 }
             }
         }
-        copy_in<ET, kChunk, K>(&QK[0][0], LDK, reinterpret_cast<const ET*>(base + L::kQE), t);
-        copy_in<ET, kChunk, K>(&QK[kChunk][0], LDK, reinterpret_cast<const ET*>(base + L::kKE), t);
-        copy_in_t<ET, kChunk, K>(&KDt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kKD), t);
-        copy_in<ET, kChunk, kChunk>(&TB[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-        copy_in<ET, kChunk, kChunk>(&MS[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
-        for (int c = t; c < K; c += kThreads) gC[c] = reinterpret_cast<const float*>(base + L::kGC)[c];
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
             const int tt = w + 4 * m;
@@ -535,49 +659,33 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
             }
         }
         __syncthreads();
+        if (jc + 1 < nc) prefetch(jc + 1);
 
-        // (q exp(G)) S and (k exp(G)) S for this wave's 16 rows
-        f32x4 oq[NCT], pp[NCT];
+        // WS and (scale q exp(G)) S for this wave's 16 rows
+        f32x4 oq[NCT], ws_[NCT];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) oq[ct] = pp[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ct = 0; ct < NCT; ++ct) oq[ct] = ws_[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
         for (int k0 = 0; k0 < K; k0 += MM::KS) {
-            const auto aq = MM::load(&QK[0][0], LDK, 16 * w, k0, lane);
-            const auto ak = MM::load(&QK[0][0], LDK, kChunk + 16 * w, k0, lane);
+            const auto aw = MM::load(&QW[0][0], LDK, QR + 16 * w, k0, lane);
+            typename MM::Frag aq{};
+            if (WRITE_O) aq = MM::load(&QW[0][0], LDK, 16 * w, k0, lane);
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 const auto b = MM::load(&St[0][0], LDK, 16 * ct, k0, lane);
-                oq[ct] = MM::mma(aq, b, oq[ct]);
-                pp[ct] = MM::mma(ak, b, pp[ct]);
+                ws_[ct] = MM::mma(aw, b, ws_[ct]);
+                if (WRITE_O) oq[ct] = MM::mma(aq, b, oq[ct]);
             }
         }
-        // Y = v - (k exp(G)) S
-        const int rbase = jc * kChunk;
+        // D = U - W S
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * w + 4 * (lane >> 4) + r;
                 const int col = 16 * ct + (lane & 15);
-                float vv = 0.f;
-                if (rbase + row < len) vv = Elem<IT>::load(vg, ((start + rbase + row) * H + h) * V + v0 + col);
-                Yt[col][row] = MM::from_f32(vv - pp[ct][r]);
+                Dt[col][row] = MM::from_f32(MM::to_f32(Un[row][col]) - ws_[ct][r]);
             }
-        __syncthreads();
-
-        // D = T diag(beta) Y   (T lower triangular: k < 16 (w + 1))
-        f32x4 dd[NCT];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) dd[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < 16 * (w + 1); k0 += MM::KS) {
-            const auto a = MM::load(&TB[0][0], LDC, 16 * w, k0, lane);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) dd[ct] = MM::mma(a, MM::load(&Yt[0][0], LDC, 16 * ct, k0, lane), dd[ct]);
-        }
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Dt[16 * ct + (lane & 15)][16 * w + 4 * (lane >> 4) + r] = MM::from_f32(dd[ct][r]);
         __syncthreads();
 
         // O = scale (q exp(G)) S + scale M D
@@ -588,6 +696,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
                 for (int ct = 0; ct < NCT; ++ct)
                     oq[ct] = MM::mma(a, MM::load(&Dt[0][0], LDC, 16 * ct, k0, lane), oq[ct]);
             }
+            const int rbase = jc * kChunk;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
