@@ -729,6 +729,558 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_kernel(ChunkParams 
     }
 }
 
+// ------------------------------------------------------------------ K-local gradients, MFMA form
+// The same gradients as chunk_bwd_klocal_kernel, for bf16 operands, with the
+// score rule on MFMA.  With I the 16-row sub-block of row i, a_i =
+// e^(G_i - G_ref(I)) and b_j = e^(G_end(J) - G_j), e^(G_i - G_j) factors as
+// a_i * f(J, I) * b_j where f is 1 for adjacent sub-blocks, the decay across
+// the sub-blocks in between for J < I - 1, and e^(G_ref(I) - G_end(I)) on the
+// diagonal (only where that span is small enough to stay finite; otherwise the
+// diagonal sub-block is formed pairwise from G).  Thus
+//   P_x = a * sum_J f (dX_IJ (k b)_J),  R = b * sum_I f (dM_IJ^T (q a)_I + dA_IJ^T (k a)_I),
+// exact fp32 16 x 16 x 16 products (four fp32 MFMA steps each).
+// Each wave takes whole 16-column tiles of dq^, dk^ and dG over all 64 rows
+// (a runtime loop when K > 64), so the reverse cumulative sum and the
+// d(G_last) term stay inside the wave and each tile's operands are built in
+// the wave's own LDS buffer.  With more than one tile per wave, the
+// pre-normalisation dq^, dk^ of finished tiles wait in the slot's entry-state
+// region (consumed by the V-local kernel) until the row dot products of the
+// L2-norm rule are complete.  Workgroups loop over (chunk, head) slots.
+template <int K>
+struct KlocMfmaSmem {
+    using ET = uint16_t;
+    static constexpr int LDE = K + 8;
+    static constexpr int LDC = kChunk + 8;
+    static constexpr int LDF = kChunk + 4;  // fp32 rows of a tile's score-rule B operand
+    ET qh[kChunk][LDE];             // normalised q
+    ET kh[kChunk][LDE];             // normalised k
+    float G[kChunk][K + 1];         // inclusive cumulative log-decay
+    union alignas(16) {
+        struct {
+            ET Tn[kChunk][LDC];
+            ET Tt[kChunk][LDC];
+            ET dTt[kChunk][LDC];
+            ET Zn[kChunk][LDC];
+        } mm;
+        struct {
+            float dM[kChunk][kChunk + 1];  // scale * dMS (lower incl. diagonal)
+            float dA[kChunk][kChunk + 1];  // diag(beta) dA (strictly lower)
+        } sc;
+    } x;
+    float op[4][16][LDF];           // per wave: (k b)^T, (q a)^T or (k a)^T of its tile
+    float P[4][K], invP[4][K];
+    float F20[K], F30[K], F31[K];
+    float beta[kChunk], rq[kChunk], rk[kChunk];
+    float dbc[4][kChunk];
+    float dbr[kChunk];
+    float dots[2][K / 16][kChunk];  // per-tile row dot products (q^.dq^, k^.dk^)
+    float ddt[K];
+    float gpa[4];
+    int unsafe[4];
+};
+
+// Per-lane factor f(J, I) between the sub-block J of the k-side row and the
+// sub-block I of the x-side row (see above); 0 where the product must vanish.
+template <int K>
+__device__ __forceinline__ float sub_factor(const KlocMfmaSmem<K>& s, int J, int I, int c) {
+    if (J > I) return 0.f;
+    if (J == I) return s.unsafe[I] ? 0.f : s.invP[I][c];
+    if (J == I - 1) return 1.f;
+    if (I == 2) return s.F20[c];          // J = 0
+    return J == 0 ? s.F30[c] : s.F31[c];  // I = 3
+}
+
+// fp32 16 x 16 x 16 product for the score rule, as four 16 x 16 x 4 fp32 MFMA
+// steps: acc = A[m0 .. m0+15][k0 .. k0+15] * Bt[n0 .. n0+15][k0 .. k0+15]^T.
+// One call spans exactly one 16-row sub-block of k, so the per-sub-block
+// factor is applied to the returned tile.  TRANS_A reads A transposed.
+template <bool TRANS_A>
+__device__ __forceinline__ f32x4 mma16_f32(const float* A, int lda, int m0, const float* Bt, int ldb, int n0,
+                                           int k0, int lane) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int m = m0 + (lane & 15), n = n0 + (lane & 15);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int k = k0 + 4 * st + (lane >> 4);
+        const float a = TRANS_A ? A[k * lda + m] : A[m * lda + k];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bt[n * ldb + k], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+template <int K>
+__global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkParams p, ChunkGrads gr,
+                                                                         const int32_t* chunk_off, uint8_t* ws,
+                                                                         int64_t slot_bytes, int nblk) {
+    using MM = Mma<true>;
+    using ET = uint16_t;
+    using X = BwdExtra<K, true>;
+    using SM = KlocMfmaSmem<K>;
+    constexpr int LDC = SM::LDC;
+    constexpr int LDF = SM::LDF;
+    constexpr int CPT = K / 4;
+    constexpr int NKT = K / 16;
+    constexpr bool PARK = NKT > 4;      // more than one tile per wave
+    static_assert(!PARK || 2 * kChunk * K * sizeof(float) <= 2 * K * K * sizeof(ET),
+                  "parked dq^/dk^ must fit the slot's state regions");
+    __shared__ __attribute__((aligned(16))) SM s;
+
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int lg = lane >> 4, lc = lane & 15;
+    const int H = p.H;
+
+    for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        const int slot = blk / H;
+        const int h = blk % H;
+        int n, j;
+        if (!slot_to_chunk(p, chunk_off, slot, n, j)) break;  // slots past the last chunk are all empty
+        int64_t start;
+        int len;
+        seq_bounds(p, n, start, len);
+        const int rows = min(kChunk, len - j * kChunk);
+        uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
+        const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
+        const float rate = (p.gate_mode == GATE_LOGDECAY) ? 0.f : __expf(p.A_log[h]);
+        __syncthreads();  // the previous slot is done with the shared buffers
+
+        // ---- 0. prologue (row-wise), cumulative sum, sub-block factors
+        {
+            const int i = t >> 2, c0 = (t & 3) * CPT;
+            const bool valid = i < rows;
+            float qv[CPT], kv[CPT], gv[CPT];
+            if (valid) {
+                const int64_t off = ((rbase + i) * H + h) * K + c0;
+                load_row<CPT>(static_cast<const uint16_t*>(p.q) + off, qv);
+                load_row<CPT>(static_cast<const uint16_t*>(p.k) + off, kv);
+                load_row<CPT>(p.g + off, gv);
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) qv[c] = kv[c] = gv[c] = 0.f;
+            }
+            float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+                ssq += qv[c] * qv[c];
+                ssk += kv[c] * kv[c];
+            }
+            ssq += __shfl_xor(ssq, 1, 64);
+            ssq += __shfl_xor(ssq, 2, 64);
+            ssk += __shfl_xor(ssk, 1, 64);
+            ssk += __shfl_xor(ssk, 2, 64);
+            float rq = 1.f, rk = 1.f;
+            if (p.use_qk_l2norm) {
+                rq = rsqrtf(ssq + kL2Eps);
+                rk = rsqrtf(ssk + kL2Eps);
+            }
+            if (!valid) rq = rk = 0.f;
+            const float* bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias + h * K + c0 : nullptr;
+#pragma unroll 8
+            for (int c = 0; c < CPT; ++c) {
+                s.qh[i][c0 + c] = MM::from_f32(qv[c] * rq);
+                s.kh[i][c0 + c] = MM::from_f32(kv[c] * rk);
+                s.G[i][c0 + c] = valid ? gate_eff(p.gate_mode, gv[c], rate, bias ? bias[c] : 0.f, p.lower_bound)
+                                       : 0.f;
+            }
+            if ((t & 3) == 0) {
+                s.rq[i] = rq;
+                s.rk[i] = rk;
+                float b = 0.f;
+                if (valid) {
+                    b = p.beta[(rbase + i) * H + h];
+                    if (p.use_beta_sigmoid) b = sigmoidf_(b);
+                }
+                s.beta[i] = b;
+            }
+            if (t < 4) s.unsafe[t] = 0;
+        }
+        __syncthreads();
+        {
+            constexpr int SEGS = kThreads / K;
+            constexpr int SEGLEN = kChunk / SEGS;
+            const int c = t % K, sg = t / K;
+            float acc = 0.f;
+            for (int r = sg * SEGLEN; r < (sg + 1) * SEGLEN; ++r) {
+                acc += s.G[r][c];
+                s.G[r][c] = acc;
+            }
+            __syncthreads();
+            float off = 0.f;
+            for (int q = 0; q < sg; ++q) off += s.G[(q + 1) * SEGLEN - 1][c];
+            __syncthreads();
+            if (sg > 0)
+                for (int r = sg * SEGLEN; r < (sg + 1) * SEGLEN; ++r) s.G[r][c] += off;
+        }
+        __syncthreads();
+        for (int c = t; c < K; c += kThreads) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const float Gref = I == 0 ? 0.f : s.G[kSub * I - 1][c];
+                const float span = Gref - s.G[kSub * I + kSub - 1][c];
+                s.P[I][c] = __expf(-span);
+                s.invP[I][c] = __expf(span);
+                if (!(span <= kSpanLimit)) s.unsafe[I] = 1;
+            }
+            s.F20[c] = s.P[1][c];
+            s.F31[c] = s.P[2][c];
+            s.F30[c] = s.P[1][c] * s.P[2][c];
+        }
+
+        // ---- 1. dA = -T^T (dTB diag(beta)) T^T and the beta terms of TB and A
+        {
+            const ET* gT = reinterpret_cast<const ET*>(base + X::kT);
+            const ET* gTB = reinterpret_cast<const ET*>(base + X::kDTB);
+            float part = 0.f;  // column t % 64
+            for (int e = t; e < kChunk * kChunk; e += kThreads) {
+                const int a = e / kChunk, b = e % kChunk;
+                const ET tv = gT[e];
+                s.x.mm.Tn[a][b] = tv;
+                s.x.mm.Tt[b][a] = tv;
+                const float dtb = (b <= a) ? MM::to_f32(gTB[e]) : 0.f;
+                part += dtb * MM::to_f32(tv);
+                s.x.mm.dTt[b][a] = MM::from_f32(dtb * s.beta[b]);
+            }
+            s.dbc[w][t & 63] = part;
+        }
+        __syncthreads();
+        {
+            f32x4 z[4];
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                z[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+                z[ct] = gemm<MM>(&s.x.mm.Tt[0][0], LDC, 16 * w, &s.x.mm.dTt[0][0], LDC, 16 * ct, 0, kChunk, z[ct],
+                                 lane);
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) tile_store<MM>(&s.x.mm.Zn[0][0], LDC, 16 * w, 16 * ct, z[ct], lane);
+        }
+        __syncthreads();
+        f32x4 da[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            da[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            da[ct] = gemm<MM>(&s.x.mm.Zn[0][0], LDC, 16 * w, &s.x.mm.Tn[0][0], LDC, 16 * ct, 0, kChunk, da[ct], lane);
+        }
+        __syncthreads();  // the score gradients below overlay T and Z
+        {
+            const ET* gAK = reinterpret_cast<const ET*>(base + X::kAK);
+            const ET* gMS = reinterpret_cast<const ET*>(base + X::kDMS);
+            float rowp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * w + 4 * lg + r, jj = 16 * ct + lc;
+                    const float dAv = (jj < i) ? -da[ct][r] : 0.f;
+                    rowp[r] += dAv * MM::to_f32(gAK[i * kChunk + jj]);
+                    s.x.sc.dA[i][jj] = dAv * s.beta[i];
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = rowp[r];
+                v += __shfl_xor(v, 1, 64);
+                v += __shfl_xor(v, 2, 64);
+                v += __shfl_xor(v, 4, 64);
+                v += __shfl_xor(v, 8, 64);
+                if (lc == 0) s.dbr[16 * w + 4 * lg + r] = v;
+            }
+            for (int e = t; e < kChunk * kChunk; e += kThreads) {
+                const int a = e / kChunk, b = e % kChunk;
+                s.x.sc.dM[a][b] = (b <= a) ? p.scale * MM::to_f32(gMS[e]) : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ---- 2. per column tile: score rule, element-wise terms, reverse cumsum, gate rule
+        const ET* gQE = reinterpret_cast<const ET*>(base + X::kDQE);
+        const ET* gKE = reinterpret_cast<const ET*>(base + X::kDKE);
+        const ET* gKD = reinterpret_cast<const ET*>(base + X::kDKD);
+        const float* dgam = reinterpret_cast<const float*>(base + X::kDGAM);
+        float* park_q = reinterpret_cast<float*>(base + X::kS);   // [64][K] fp32 over S and DS
+        float* park_k = park_q + kChunk * K;
+        const bool any_unsafe = s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3];
+        float (*opw)[LDF] = s.op[w];
+        float dal = 0.f;
+        f32x4 dq[4], dk[4];
+#pragma unroll 1
+        for (int ct = w; ct < NKT; ct += 4) {
+            const int c = 16 * ct + lc;     // this lane's channel
+            f32x4 dG[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) dq[I] = dk[I] = dG[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            // P terms with (k b)^T of this tile, b_j = e^(G_end(J) - G_j)
+            for (int e = lane; e < 16 * kChunk; e += 64) {
+                const int jr = e % kChunk, cc = 16 * ct + e / kChunk;
+                const float Ge = s.G[kSub * (jr / kSub) + kSub - 1][cc];
+                opw[e / kChunk][jr] = MM::to_f32(s.kh[jr][cc]) * __expf(Ge - s.G[jr][cc]);
+            }
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+                for (int J = 0; J <= I; ++J) {
+                    if (J == I && s.unsafe[I]) continue;  // formed pairwise below
+                    const float f = sub_factor(s, J, I, c);
+                    const f32x4 aq = mma16_f32<false>(&s.x.sc.dM[0][0], kChunk + 1, kSub * I, &opw[0][0], LDF, 0,
+                                                      kSub * J, lane);
+                    const f32x4 ak = mma16_f32<false>(&s.x.sc.dA[0][0], kChunk + 1, kSub * I, &opw[0][0], LDF, 0,
+                                                      kSub * J, lane);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pq[r] += f * aq[r];
+                        pk[r] += f * ak[r];
+                    }
+                }
+                const float Gr = I == 0 ? 0.f : s.G[kSub * I - 1][c];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    const float a = __expf(s.G[i][c] - Gr);
+                    const float Pq = a * pq[r], Pk = a * pk[r];
+                    dq[I][r] += Pq;
+                    dk[I][r] += Pk;
+                    dG[I][r] += MM::to_f32(s.qh[i][c]) * Pq + MM::to_f32(s.kh[i][c]) * Pk;
+                }
+            }
+
+            // R terms: (q a)^T against dM, then (k a)^T against dA, a_i = e^(G_i - G_ref(I))
+            f32x4 rr[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) rr[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int pass = 0; pass < 2; ++pass) {
+                for (int e = lane; e < 16 * kChunk; e += 64) {
+                    const int ir = e % kChunk, cc = 16 * ct + e / kChunk;
+                    const float Gr = ir < kSub ? 0.f : s.G[kSub * (ir / kSub) - 1][cc];
+                    const float x_ = MM::to_f32(pass == 0 ? s.qh[ir][cc] : s.kh[ir][cc]);
+                    opw[e / kChunk][ir] = x_ * __expf(s.G[ir][cc] - Gr);
+                }
+                const float* dX = pass == 0 ? &s.x.sc.dM[0][0] : &s.x.sc.dA[0][0];
+#pragma unroll
+                for (int J = 0; J < 4; ++J) {
+#pragma unroll 1
+                    for (int I = J; I < 4; ++I) {
+                        if (I == J && s.unsafe[J]) continue;
+                        const float f = sub_factor(s, J, I, c);
+                        const f32x4 acc =
+                            mma16_f32<true>(dX, kChunk + 1, kSub * J, &opw[0][0], LDF, 0, kSub * I, lane);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rr[J][r] += f * acc[r];
+                    }
+                }
+            }
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const float Ge = s.G[kSub * J + kSub - 1][c];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * J + 4 * lg + r;
+                    const float R = __expf(Ge - s.G[i][c]) * rr[J][r];
+                    dk[J][r] += R;
+                    dG[J][r] -= MM::to_f32(s.kh[i][c]) * R;
+                }
+            }
+
+            // diagonal sub-blocks too wide to factorise: pairwise from G
+            if (any_unsafe) {
+#pragma unroll 1
+                for (int I = 0; I < 4; ++I) {
+                    if (!s.unsafe[I]) continue;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int x = 4 * lg + r, i = kSub * I + x;
+                        const float Gi = s.G[i][c];
+                        float Pq = 0.f, Pk = 0.f, R = 0.f;
+#pragma unroll 1
+                        for (int y = 0; y < kSub; ++y) {
+                            const int jr = kSub * I + y;
+                            const float Gj = s.G[jr][c];
+                            if (y <= x) {
+                                const float e = __expf(Gi - Gj) * MM::to_f32(s.kh[jr][c]);
+                                Pq += s.x.sc.dM[i][jr] * e;
+                                Pk += s.x.sc.dA[i][jr] * e;
+                            }
+                            if (y >= x) {
+                                const float e = __expf(Gj - Gi);
+                                R += (s.x.sc.dM[jr][i] * MM::to_f32(s.qh[jr][c]) +
+                                      s.x.sc.dA[jr][i] * MM::to_f32(s.kh[jr][c])) * e;
+                            }
+                        }
+                        const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
+                        // I is a runtime index here: update through a small switch-free select
+#pragma unroll
+                        for (int II = 0; II < 4; ++II)
+                            if (II == I) {
+                                dq[II][r] += Pq;
+                                dk[II][r] += Pk + R;
+                                dG[II][r] += q_ * Pq + k_ * Pk - k_ * R;
+                            }
+                    }
+                }
+            }
+
+            // element-wise terms of QE, KE, KD and d(G_last)
+            const float Glast = s.G[kChunk - 1][c];
+            float colp = 0.f;
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    const float Gi = s.G[i][c];
+                    const float E = __expf(Gi), Ed = __expf(Glast - Gi);
+                    const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
+                    const float dqe = MM::to_f32(gQE[i * K + c]);
+                    const float dke = MM::to_f32(gKE[i * K + c]);
+                    const float dkd = MM::to_f32(gKD[i * K + c]);
+                    const float KD = k_ * Ed;
+                    dq[I][r] += p.scale * dqe * E;
+                    dk[I][r] += dke * E + dkd * Ed;
+                    dG[I][r] += dqe * p.scale * q_ * E + dke * k_ * E - dkd * KD;
+                    colp += dkd * KD;
+                }
+            colp += __shfl_xor(colp, 16, 64);
+            colp += __shfl_xor(colp, 32, 64);
+            if (lg == 3) dG[3][3] += colp + dgam[c] * __expf(Glast);
+
+            // reverse cumulative sum over the 64 rows of this column
+            float carry = 0.f;
+#pragma unroll
+            for (int I = 3; I >= 0; --I) {
+                dG[I][2] += dG[I][3];
+                dG[I][1] += dG[I][2];
+                dG[I][0] += dG[I][1];
+                const float own = dG[I][0];
+                const float up1 = __shfl(own, (lane + 16) & 63, 64);
+                const float up2 = __shfl(own, (lane + 32) & 63, 64);
+                const float up3 = __shfl(own, (lane + 48) & 63, 64);
+                float add = carry;
+                if (lg < 3) add += up1;
+                if (lg < 2) add += up2;
+                if (lg < 1) add += up3;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dG[I][r] += add;
+                carry = __shfl(dG[I][0], lc, 64);  // suffix sum from row 16 I
+            }
+
+            // gate chain rule
+            const float bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias[h * K + c] : 0.f;
+            float ddt = 0.f;
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    if (i < rows) {
+                        const int64_t gi = ((rbase + i) * H + h) * K + c;
+                        const float dge = dG[I][r];
+                        float dx = dge;
+                        if (p.gate_mode != GATE_LOGDECAY) {
+                            const float z = p.g[gi] + bias;
+                            if (p.gate_mode == GATE_SAFE) {
+                                const float sg = sigmoidf_(rate * z);
+                                const float b_ = p.lower_bound * sg * (1.f - sg);
+                                dx = dge * b_ * rate;
+                                dal += dge * b_ * rate * z;
+                            } else {
+                                dx = -dge * rate * sigmoidf_(z);
+                                dal += -dge * rate * softplusf_(z);
+                            }
+                            ddt += dx;
+                        }
+                        gr.dg[gi] = dx;
+                    }
+                }
+            ddt += __shfl_xor(ddt, 16, 64);
+            ddt += __shfl_xor(ddt, 32, 64);
+            if (lg == 0) s.ddt[c] = ddt;
+
+            // row dot products of the L2-norm rule; park this tile if more follow
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    float vq = MM::to_f32(s.qh[i][c]) * dq[I][r];
+                    float vk = MM::to_f32(s.kh[i][c]) * dk[I][r];
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) {
+                        vq += __shfl_xor(vq, o, 64);
+                        vk += __shfl_xor(vk, o, 64);
+                    }
+                    if (lc == 0) {
+                        s.dots[0][ct][i] = vq;
+                        s.dots[1][ct][i] = vk;
+                    }
+                    if (PARK) {
+                        park_q[i * K + c] = dq[I][r];
+                        park_k[i * K + c] = dk[I][r];
+                    }
+                }
+        }
+
+        // ---- 3. L2-norm and sigmoid chain rules, gate shares, stores
+        __syncthreads();  // dots, ddt and the parked tiles are complete
+        uint16_t* dqg = static_cast<uint16_t*>(gr.dq);
+        uint16_t* dkg = static_cast<uint16_t*>(gr.dk);
+        if (PARK) {
+            for (int e = t; e < rows * K; e += kThreads) {
+                const int i = e / K, c = e % K;
+                float dotq = 0.f, dotk = 0.f;
+#pragma unroll
+                for (int q = 0; q < NKT; ++q) {
+                    dotq += s.dots[0][q][i];
+                    dotk += s.dots[1][q][i];
+                }
+                float oq = park_q[e], ok = park_k[e];
+                if (p.use_qk_l2norm) {
+                    oq = s.rq[i] * (oq - MM::to_f32(s.qh[i][c]) * dotq);
+                    ok = s.rk[i] * (ok - MM::to_f32(s.kh[i][c]) * dotk);
+                }
+                const int64_t gi = ((rbase + i) * H + h) * K + c;
+                dqg[gi] = f32_to_bf16_bits(oq);
+                dkg[gi] = f32_to_bf16_bits(ok);
+            }
+        } else if (w < NKT) {
+            const int c = 16 * w + lc;
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    if (i >= rows) continue;
+                    float dotq = 0.f, dotk = 0.f;
+#pragma unroll
+                    for (int q = 0; q < NKT; ++q) {
+                        dotq += s.dots[0][q][i];
+                        dotk += s.dots[1][q][i];
+                    }
+                    float oq = dq[I][r], ok = dk[I][r];
+                    if (p.use_qk_l2norm) {
+                        oq = s.rq[i] * (oq - MM::to_f32(s.qh[i][c]) * dotq);
+                        ok = s.rk[i] * (ok - MM::to_f32(s.kh[i][c]) * dotk);
+                    }
+                    const int64_t gi = ((rbase + i) * H + h) * K + c;
+                    dqg[gi] = f32_to_bf16_bits(oq);
+                    dkg[gi] = f32_to_bf16_bits(ok);
+                }
+        }
+        if (t < kChunk && t < rows) {
+            const float db = s.dbc[0][t] + s.dbc[1][t] + s.dbc[2][t] + s.dbc[3][t] + s.dbr[t];
+            const float b = s.beta[t];
+            gr.dbeta[(rbase + t) * H + h] = p.use_beta_sigmoid ? db * b * (1.f - b) : db;
+        }
+        if (p.gate_mode != GATE_LOGDECAY) {
+            dal = wave_sum(dal);
+            if (lane == 0) s.gpa[w] = dal;
+            __syncthreads();
+            float* gp = reinterpret_cast<float*>(base + X::kGP);
+            for (int cc = t; cc < K; cc += kThreads) gp[cc] = s.ddt[cc];
+            if (t == 0) gp[K] = s.gpa[0] + s.gpa[1] + s.gpa[2] + s.gpa[3];
+        }
+    }
+}
+
 // d(A_log) and d(dt_bias): deterministic sums of the per-chunk shares.
 template <int K>
 __global__ void gate_param_reduce_kernel(ChunkParams p, ChunkGrads gr, const int32_t* chunk_off, const uint8_t* ws,
@@ -791,9 +1343,15 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
         hipLaunchKernelGGL((chunk_bwd_vlocal_kernel<K, V, BV, BF>), dim3(static_cast<unsigned>(nblk)),
                            dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb);
     if (want(4)) {
-        if (nblk > 0)
-            hipLaunchKernelGGL((chunk_bwd_klocal_kernel<K, BF>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
-                               0, st, p, gr, chunk_off, slots, sb);
+        if (nblk > 0) {
+            if constexpr (BF)
+                hipLaunchKernelGGL((chunk_bwd_klocal_mfma_kernel<K>),
+                                   dim3(static_cast<unsigned>(nblk < kPersistentGrid ? nblk : kPersistentGrid)),
+                                   dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb, static_cast<int>(nblk));
+            else
+                hipLaunchKernelGGL((chunk_bwd_klocal_kernel<K, BF>), dim3(static_cast<unsigned>(nblk)),
+                                   dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb);
+        }
         if (p.gate_mode != GATE_LOGDECAY && (gr.dA_log || gr.ddt_bias))
             hipLaunchKernelGGL((gate_param_reduce_kernel<K>), dim3(p.H), dim3(256), 0, st, p, gr, chunk_off, slots, sb,
                                X::kGP);

@@ -15,6 +15,9 @@ namespace kda {
 constexpr int kChunk = 64;
 constexpr int kSub = 16;
 constexpr int kThreads = 256;
+// Grid of the kernels that loop over (chunk, head) slots: one workgroup per
+// compute unit of an MI355X (their LDS use allows one per CU).
+constexpr int kPersistentGrid = 256;
 // Diagonal 16-row sub-blocks whose accumulated decay span stays under this
 // bound are factorised through the row before the block (factors up to
 // e^kSpanLimit, finite in fp32); wider spans are formed pairwise.

@@ -21,6 +21,7 @@ def check(name, got, want, tol):
     assert np.isfinite(got).all(), f"{name}: non-finite values in the GPU result"
     scale = max(float(np.abs(want).max()) if want.size else 0.0, 1e-6)
     md = float(np.abs(got - want).max()) if want.size else 0.0
+    print(f"  {name}: rel {md / scale:.3e} (tol {tol:.0e})", flush=True)
     assert md <= tol * scale, f"{name}: maxdiff {md:.3e} scale {scale:.3e} rel {md / scale:.3e} tol {tol:.1e}"
     return md / scale
 
