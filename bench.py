@@ -36,32 +36,75 @@ def _log(msg):
 
 
 # ---------------------------------------------------------------- algorithmic work
-def chunk_fwd_bytes(tokens, H, K, V, elt, n_seq):
-    """q, k, v and o in the input dtype, g fp32, beta fp32, final state fp32."""
-    return tokens * H * (2 * K * elt + V * elt + K * 4 + 4 + V * elt) + n_seq * H * K * V * 4
+# Per (chunk, head) slot of C = 64 rows: the HBM bytes each kernel must move in
+# this design (every operand read once, every result written once; the
+# per-chunk operands that one kernel hands to the next live in the workspace
+# in bf16) and the flops of its MFMA-shaped products (triangular products at
+# their triangular size).  elt is the byte size of q, k, v, o, dO and their
+# gradients; intermediates are bf16.  Per-sequence terms (initial and final
+# states) are added by stage_work().
+C = 64
 
 
-def chunk_bwd_bytes(tokens, H, K, V, elt, n_seq):
-    """Reads q, k, v, g, beta, dO; writes dq, dk, dv, dg, dbeta and d(initial state)."""
-    reads = tokens * H * (2 * K * elt + V * elt + K * 4 + 4 + V * elt)
-    writes = tokens * H * (2 * K * elt + V * elt + K * 4 + 4) + n_seq * H * K * V * 4
-    return reads + writes
+def _slot_terms(K, V, elt):
+    e = 2
+    tri = (C + 1) / 2
+    qkv_in = C * (2 * K + V) * elt + 4 * C * K + 4 * C          # q, k, v, g, beta
+    prep_out = e * (3 * C * K + C * V + 2 * C * C) + 4 * K      # QE, W, KD, U, TB, MS, GC
+    prep_f = C * (2 * tri * K * 2 + 2 * tri * V) + C ** 3 / 3   # A, M, W, U; the solve
+    return {
+        "fwd.prep": (qkv_in + prep_out, prep_f),
+        "fwd.state": (e * (3 * C * K + C * V + C * C) + 4 * K + C * V * elt, C * 6 * K * V + C * 2 * tri * V),
+        "bwd.0": (qkv_in + prep_out + e * (C * K + 2 * C * C), prep_f),
+        "bwd.1": (e * (2 * C * K + C * V) + 4 * K + e * K * V, C * 4 * K * V),
+        "bwd.2": (e * (3 * C * K + C * C) + 4 * K + C * V * elt + e * K * V, C * (6 * K * V + 2 * tri * V)),
+        "bwd.3": (e * (2 * C * K + 2 * C * C + 2 * K * V) + C * V * elt + C * V * elt
+                  + e * (3 * C * K + 2 * C * C) + 4 * K,
+                  C * (6 * K * V + 3 * 2 * tri * V)),
+        "bwd.4": (C * 2 * K * elt + 4 * C * K + 4 * C + e * (4 * C * C + 3 * C * K) + 4 * K
+                  + C * 2 * K * elt + 4 * C * K + 4 * C + 4 * (K + 1),
+                  4 * C ** 3 + C * 4 * 2 * tri * K),
+    }
+
+
+def stage_work(slots, n_seq, H, K, V, elt, with_h0=False):
+    """{stage: (bytes, flops)} for one launch over `slots` (chunk, head) slots."""
+    out = {k: (b * slots, f * slots) for k, (b, f) in _slot_terms(K, V, elt).items()}
+    st = n_seq * H * K * V * 4
+    b, f = out["fwd.state"]
+    out["fwd.state"] = (b + st * (2 if with_h0 else 1), f)
+    b, f = out["bwd.2"]
+    out["bwd.2"] = (b + st * 2, f)  # d(final state) in, d(initial state) out
+    return out
+
+
+def stage_roofline(name, work, ms):
+    """Roofline entry of one kernel: the bound is the one its algorithmic work hits first."""
+    nbytes, flops = work
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        ach = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": name, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                "kernel_ms": ms}
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": name, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "kernel_ms": ms}
+
+
+# Whole-path figures per token-head at d = 128 (operator inputs and outputs
+# only): forward 1,540 B and 141,013 flops; forward + backward 4,364 B and
+# about 423 k flops (three times the forward, recomputation not counted).
+PATH_FWD = (1540, 141013)
+PATH_FWDBWD = (4364, 423039)
 
 
 def decode_bytes(N, H, D, W, x_elt):
     """State and conv state read + written once; x, g, beta, conv_w read; o written."""
     return (2 * N * H * D * D * 4 + 2 * N * 3 * H * D * W * 4 + N * 3 * H * D * x_elt + N * H * D * 4
             + N * H * 4 + 3 * H * D * W * 4 + N * H * D * 4)
-
-
-# Flops per token-head of the chunk form at C = 64 (triangular products at
-# their triangular size): the three 2*d^2 state products and the intra-chunk
-# part (A, M, the two products with T and the solve).
-def chunk_flops_per_token_head(d, C=64):
-    state = 3 * 2 * d * d
-    tri = (C + 1) / 2
-    intra = 2 * tri * d * 2 + 2 * tri * d * 2 + C * C / 3
-    return state, intra
 
 
 # ---------------------------------------------------------------- workloads
@@ -78,14 +121,6 @@ def chunk_op(d, with_bwd):
                        output_final_state=True, use_qk_l2norm_in_kernel=True, gate_mode=d["gate_mode"],
                        use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"], lower_bound=d["lower_bound"],
                        cu_seqlens=d["cu_seqlens"], dO=d["dO"] if with_bwd else None)
-
-
-def _bwd_probe():
-    # The backward entry point exists in every build; a build without the
-    # backward kernels reports it through its stage count.
-    from kimi_delta_attention_amd import _lib
-    lib = _lib.load()
-    return hasattr(lib, "kda_chunk_bwd_stage")
 
 
 def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages):
@@ -179,6 +214,78 @@ def cpu_baseline(host):
             "sample": f"whole packed batch (T{T_H} H{H_H} d{D_H}, 4 sequences), fwd+bwd in fp64, {dt:.1f} s"}
 
 
+def csrc_digest():
+    """SHA-256 over the kernel sources, to tell whether stored counter readings still apply."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kimi_delta_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(stage):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summary, or None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_T8192_H16_D128.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ":" in ln and not ln.startswith((" ", "#", "|")):
+                k, v = ln.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("csrc_sha256") != csrc_digest():
+        return None
+    v = kv.get(f"hbm_bytes_per_launch[{stage}]")
+    return float(v) if v else None
+
+
+def copy_probe(mib, device):
+    """A plain device copy of known size, so that a counter run can calibrate FETCH_SIZE / WRITE_SIZE."""
+    n = mib * (1 << 20) // 4
+    src = torch.empty(n, dtype=torch.float32, device=device).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    _log(f"copy probe: {mib} MiB read + {mib} MiB written per launch")
+    del src, dst
+
+
+def run_train(steps, warmup, device):
+    """Forward + backward on the dense training shape B8 x T4096, H16, K=V=128 (bf16 q/k/v/dO, fp32
+    g/beta/state), with an explicit zero initial state so that d(initial state) is produced."""
+    from kimi_delta_attention_amd import inputs
+    import kimi_delta_attention_amd as kda
+    w = inputs.workload("train")
+    d = {k: (v.to(device) if hasattr(v, "to") else v) for k, v in w.items()}
+    B, T, H, K = d["q"].shape
+    h0 = torch.zeros(B, H, K, K, dtype=torch.float32, device=device)
+    op = kda.ChunkOp(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"], initial_state=h0,
+                     output_final_state=True, use_qk_l2norm_in_kernel=True, gate_mode=d["gate_mode"],
+                     use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"], lower_bound=d["lower_bound"], dO=d["dO"])
+    sec, per_stage = time_chunk([op], steps, warmup, True, _lib_stages())
+    tokens = B * T
+    fwd_ms = per_stage["fwd.prep"] + per_stage["fwd.state"]
+    pb, pf = PATH_FWDBWD
+    th = tokens * H
+    return {"workload": f"chunk_kda fwd+bwd, dense B{B} x T{T}, H{H}, K=V={K}, bf16 q/k/v/dO, fp32 g/beta/state, "
+                        "zero initial state passed", "tokens_per_s": tokens / sec, "ms_per_step": sec * 1e3,
+            "fwd_tokens_per_s": tokens / (fwd_ms * 1e-3), "stages_ms": per_stage,
+            "path_hbm_frac": pb * th / sec / 1e9 / PEAK_HBM_GBS,
+            "path_mfma_frac": pf * th / sec / 1e12 / PEAK_BF16_TFLOPS}
+
+
+def _lib_stages():
+    from kimi_delta_attention_amd import _lib
+    return _lib.load().kda_chunk_bwd_stages()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -186,6 +293,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip the dense B8 x T4096 training shape")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA operator needs no cross-GPU exchange and this build "
@@ -195,36 +305,32 @@ def main():
     torch.cuda.set_device(device)
     from kimi_delta_attention_amd import _lib
     _lib.load()
+    if args.copy_probe_mib > 0:
+        copy_probe(args.copy_probe_mib, device)
 
-    with_bwd = _bwd_probe()
-    n_bwd = 0
-    if with_bwd:
-        n_bwd = _lib.load().kda_chunk_bwd_stages()
-    _log(f"building inputs (bwd={'yes' if with_bwd else 'no'})")
+    n_bwd = _lib_stages()
+    _log("building inputs")
     host0, d0 = make_hybrid(1003, device)
     _, d1 = make_hybrid(2003, device)
-    ops = [chunk_op(d0, with_bwd), chunk_op(d1, with_bwd)]
-    _log("timing chunk path")
-    sec, per_stage = time_chunk(ops, args.steps, args.warmup, with_bwd, n_bwd)
+    ops = [chunk_op(d0, True), chunk_op(d1, True)]
+    _log("timing chunk path (packed T8192)")
+    sec, per_stage = time_chunk(ops, args.steps, args.warmup, True, n_bwd)
     tokens = T_H
     n_seq = len(HYBRID_CU) - 1
     fwd_ms = per_stage["fwd.prep"] + per_stage["fwd.state"]
-
+    slots = sum((HYBRID_CU[i + 1] - HYBRID_CU[i] + C - 1) // C for i in range(n_seq)) * H_H
+    work = stage_work(slots, n_seq, H_H, D_H, D_H, 2)
     # dominant kernel: the stage with the largest mean duration
     dom = max(per_stage, key=per_stage.get)
-    st_f, in_f = chunk_flops_per_token_head(D_H)
+    roof = stage_roofline(dom, work[dom], per_stage[dom])
+    tr = stored_traffic(dom)
+    roof["traffic"] = tr
     th = tokens * H_H
-    flops_of = {"fwd.prep": in_f * th, "fwd.state": st_f * th}
-    roof = None
-    if dom in flops_of:
-        ach = flops_of[dom] / (per_stage[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": ach / PEAK_BF16_TFLOPS, "traffic": None, "algorithmic_flops": flops_of[dom],
-                "kernel_ms": per_stage[dom]}
-    fb = chunk_fwd_bytes(tokens, H_H, D_H, D_H, 2, n_seq)
+    pb, pf = PATH_FWDBWD
+    fb, ff = PATH_FWD
     line = {
         "metric": "chunk_kda fwd+bwd tokens/s (H16,D128,T8192) + decode seq/s; % MFMA/HBM peak",
-        "value": tokens / sec if with_bwd else None,
+        "value": tokens / sec,
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": sec * 1e3,
@@ -233,13 +339,22 @@ def main():
         "config": {"workload": "chunk_kda fwd+bwd, packed 1024/2048/1024/4096 (T8192), H16, K=V=128, "
                                "bf16 q/k/v, fp32 g/beta/state, l2norm in kernel, log-decay gate",
                    "global_batch": n_seq, "seq_len": tokens, "parallelism": "none (1 GPU)"},
-        "stages_ms": per_stage,
-        "fwd_tokens_per_s": tokens / (fwd_ms * 1e-3),
-        "fwd_hbm_frac": fb / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
         "roofline": roof,
+        "stages_ms": per_stage,
+        "stage_roofline": {k: {kk: v[kk] for kk in ("bound", "achieved", "unit", "frac")}
+                           for k, v in ((n, stage_roofline(n, work[n], per_stage[n])) for n in per_stage)},
+        "path_roofline": {"fwd+bwd_hbm_frac": pb * th / sec / 1e9 / PEAK_HBM_GBS,
+                          "fwd+bwd_mfma_frac": pf * th / sec / 1e12 / PEAK_BF16_TFLOPS,
+                          "fwd_tokens_per_s": tokens / (fwd_ms * 1e-3),
+                          "fwd_hbm_frac": fb * th / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "fwd_mfma_frac": ff * th / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
     }
     del ops, d0, d1
     torch.cuda.empty_cache()
+    if not args.no_train:
+        _log("timing chunk path (dense B8 x T4096)")
+        line["train"] = run_train(max(args.steps // 2, 3), min(args.warmup, 3), device)
+        torch.cuda.empty_cache()
     if not args.no_decode:
         _log("timing decode")
         line["decode"] = run_decode(max(args.steps, 10), args.warmup, device)
