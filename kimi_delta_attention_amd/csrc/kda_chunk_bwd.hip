@@ -751,10 +751,12 @@ struct KlocMfmaSmem {
     using ET = uint16_t;
     static constexpr int LDE = K + 8;
     static constexpr int LDC = kChunk + 8;
+    static constexpr int LDG = K + 4;       // G rows: 16-byte aligned, column reads conflict-free
+    static constexpr int LDD = kChunk + 4;  // fp32 score-gradient rows, 16-byte aligned
     static constexpr int LDF = kChunk + 4;  // fp32 rows of a tile's score-rule B operand
     ET qh[kChunk][LDE];             // normalised q
     ET kh[kChunk][LDE];             // normalised k
-    float G[kChunk][K + 1];         // inclusive cumulative log-decay
+    float G[kChunk][LDG];           // inclusive cumulative log-decay
     union alignas(16) {
         struct {
             ET Tn[kChunk][LDC];
@@ -763,11 +765,12 @@ struct KlocMfmaSmem {
             ET Zn[kChunk][LDC];
         } mm;
         struct {
-            float dM[kChunk][kChunk + 1];  // scale * dMS (lower incl. diagonal)
-            float dA[kChunk][kChunk + 1];  // diag(beta) dA (strictly lower)
+            float dM[kChunk][LDD];  // scale * dMS (lower incl. diagonal)
+            float dA[kChunk][LDD];  // diag(beta) dA (strictly lower)
         } sc;
     } x;
     float op[4][16][LDF];           // per wave: (k b)^T, (q a)^T or (k a)^T of its tile
+    ET ew[4][3][kChunk][16];        // per wave: the tile's dQE, dKE, dKD
     float P[4][K], invP[4][K];
     float F20[K], F30[K], F31[K];
     float beta[kChunk], rq[kChunk], rk[kChunk];
@@ -779,32 +782,33 @@ struct KlocMfmaSmem {
     int unsafe[4];
 };
 
-// Per-lane factor f(J, I) between the sub-block J of the k-side row and the
-// sub-block I of the x-side row (see above); 0 where the product must vanish.
-template <int K>
-__device__ __forceinline__ float sub_factor(const KlocMfmaSmem<K>& s, int J, int I, int c) {
-    if (J > I) return 0.f;
-    if (J == I) return s.unsafe[I] ? 0.f : s.invP[I][c];
-    if (J == I - 1) return 1.f;
-    if (I == 2) return s.F20[c];          // J = 0
-    return J == 0 ? s.F30[c] : s.F31[c];  // I = 3
-}
-
 // fp32 16 x 16 x 16 product for the score rule, as four 16 x 16 x 4 fp32 MFMA
 // steps: acc = A[m0 .. m0+15][k0 .. k0+15] * Bt[n0 .. n0+15][k0 .. k0+15]^T.
-// One call spans exactly one 16-row sub-block of k, so the per-sub-block
-// factor is applied to the returned tile.  TRANS_A reads A transposed.
+// The contraction order is permuted so that lane group q supplies the four
+// consecutive indices k0 + 4q .. k0 + 4q + 3 (one per step): each lane reads
+// its B quad, and its A quad unless TRANS_A, as one 16-byte LDS load.  One
+// call spans exactly one 16-row sub-block of the contraction, so the
+// per-sub-block factor is applied to the returned tile.  TRANS_A reads A
+// transposed (A[k][m]).  Row strides must be multiples of 4 floats.
 template <bool TRANS_A>
 __device__ __forceinline__ f32x4 mma16_f32(const float* A, int lda, int m0, const float* Bt, int ldb, int n0,
                                            int k0, int lane) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int m = m0 + (lane & 15), n = n0 + (lane & 15);
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int k = k0 + 4 * st + (lane >> 4);
-        const float a = TRANS_A ? A[k * lda + m] : A[m * lda + k];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bt[n * ldb + k], acc, 0, 0, 0);
+    const int m = m0 + (lane & 15), n = n0 + (lane & 15), kq = k0 + 4 * (lane >> 4);
+    const float4 b4 = *reinterpret_cast<const float4*>(Bt + n * ldb + kq);
+    float4 a4;
+    if (TRANS_A) {
+        a4.x = A[(kq + 0) * lda + m];
+        a4.y = A[(kq + 1) * lda + m];
+        a4.z = A[(kq + 2) * lda + m];
+        a4.w = A[(kq + 3) * lda + m];
+    } else {
+        a4 = *reinterpret_cast<const float4*>(A + m * lda + kq);
     }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, b4.x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, b4.y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, b4.z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, b4.w, acc, 0, 0, 0);
     return acc;
 }
 
@@ -820,9 +824,9 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
     constexpr int LDF = SM::LDF;
     constexpr int CPT = K / 4;
     constexpr int NKT = K / 16;
-    constexpr bool PARK = NKT > 4;      // more than one tile per wave
-    static_assert(!PARK || 2 * kChunk * K * sizeof(float) <= 2 * K * K * sizeof(ET),
-                  "parked dq^/dk^ must fit the slot's state regions");
+    constexpr bool TWO = NKT == 8;      // each wave owns tiles w and w + 4
+    static_assert(NKT <= 8, "at most two column tiles per wave");
+    static_assert(!TWO || 4 * 32 * 64 * sizeof(float) <= K * K * sizeof(ET), "parked tile must fit the state region");
     __shared__ __attribute__((aligned(16))) SM s;
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -848,8 +852,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             const int i = t >> 2, c0 = (t & 3) * CPT;
             const bool valid = i < rows;
             float qv[CPT], kv[CPT], gv[CPT];
+            float braw = 0.f;
             if (valid) {
                 const int64_t off = ((rbase + i) * H + h) * K + c0;
+                braw = p.beta[(rbase + i) * H + h];
                 load_row<CPT>(static_cast<const uint16_t*>(p.q) + off, qv);
                 load_row<CPT>(static_cast<const uint16_t*>(p.k) + off, kv);
                 load_row<CPT>(p.g + off, gv);
@@ -884,11 +890,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             if ((t & 3) == 0) {
                 s.rq[i] = rq;
                 s.rk[i] = rk;
-                float b = 0.f;
-                if (valid) {
-                    b = p.beta[(rbase + i) * H + h];
-                    if (p.use_beta_sigmoid) b = sigmoidf_(b);
-                }
+                float b = braw;
+                if (valid && p.use_beta_sigmoid) b = sigmoidf_(b);
                 s.beta[i] = b;
             }
             if (t < 4) s.unsafe[t] = 0;
@@ -926,17 +929,35 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         }
 
         // ---- 1. dA = -T^T (dTB diag(beta)) T^T and the beta terms of TB and A
+        // Every global operand of this phase is requested before any is used.
+        // Thread t owns column t % 64 of rows t / 64 + 4 e of T, dTB and dMS,
+        // and row 16 w + 4 lg + r, column 16 ct + lc of AK (the dA layout).
+        ET tv[16], tbv[16], msv[16], akv[16];
         {
             const ET* gT = reinterpret_cast<const ET*>(base + X::kT);
             const ET* gTB = reinterpret_cast<const ET*>(base + X::kDTB);
+            const ET* gMS = reinterpret_cast<const ET*>(base + X::kDMS);
+            const ET* gAK = reinterpret_cast<const ET*>(base + X::kAK);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                tv[e] = gT[t + kThreads * e];
+                tbv[e] = gTB[t + kThreads * e];
+                msv[e] = gMS[t + kThreads * e];
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) akv[4 * ct + r] = gAK[(16 * w + 4 * lg + r) * kChunk + 16 * ct + lc];
+        }
+        {
             float part = 0.f;  // column t % 64
-            for (int e = t; e < kChunk * kChunk; e += kThreads) {
-                const int a = e / kChunk, b = e % kChunk;
-                const ET tv = gT[e];
-                s.x.mm.Tn[a][b] = tv;
-                s.x.mm.Tt[b][a] = tv;
-                const float dtb = (b <= a) ? MM::to_f32(gTB[e]) : 0.f;
-                part += dtb * MM::to_f32(tv);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int a = (t >> 6) + 4 * e, b = t & 63;
+                s.x.mm.Tn[a][b] = tv[e];
+                s.x.mm.Tt[b][a] = tv[e];
+                const float dtb = (b <= a) ? MM::to_f32(tbv[e]) : 0.f;
+                part += dtb * MM::to_f32(tv[e]);
                 s.x.mm.dTt[b][a] = MM::from_f32(dtb * s.beta[b]);
             }
             s.dbc[w][t & 63] = part;
@@ -962,8 +983,6 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         }
         __syncthreads();  // the score gradients below overlay T and Z
         {
-            const ET* gAK = reinterpret_cast<const ET*>(base + X::kAK);
-            const ET* gMS = reinterpret_cast<const ET*>(base + X::kDMS);
             float rowp[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct)
@@ -971,7 +990,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * w + 4 * lg + r, jj = 16 * ct + lc;
                     const float dAv = (jj < i) ? -da[ct][r] : 0.f;
-                    rowp[r] += dAv * MM::to_f32(gAK[i * kChunk + jj]);
+                    rowp[r] += dAv * MM::to_f32(akv[4 * ct + r]);
                     s.x.sc.dA[i][jj] = dAv * s.beta[i];
                 }
 #pragma unroll
@@ -983,9 +1002,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 v += __shfl_xor(v, 8, 64);
                 if (lc == 0) s.dbr[16 * w + 4 * lg + r] = v;
             }
-            for (int e = t; e < kChunk * kChunk; e += kThreads) {
-                const int a = e / kChunk, b = e % kChunk;
-                s.x.sc.dM[a][b] = (b <= a) ? p.scale * MM::to_f32(gMS[e]) : 0.f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int a = (t >> 6) + 4 * e, b = t & 63;
+                s.x.sc.dM[a][b] = (b <= a) ? p.scale * MM::to_f32(msv[e]) : 0.f;
             }
         }
         __syncthreads();
@@ -995,35 +1015,71 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         const ET* gKE = reinterpret_cast<const ET*>(base + X::kDKE);
         const ET* gKD = reinterpret_cast<const ET*>(base + X::kDKD);
         const float* dgam = reinterpret_cast<const float*>(base + X::kDGAM);
-        float* park_q = reinterpret_cast<float*>(base + X::kS);   // [64][K] fp32 over S and DS
-        float* park_k = park_q + kChunk * K;
         const bool any_unsafe = s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3];
         float (*opw)[LDF] = s.op[w];
+        ET (*eww)[kChunk][16] = s.ew[w];
         float dal = 0.f;
         f32x4 dq[4], dk[4];
+        f32x4 sq[4], sk[4];  // the first tile's dq^, dk^ when the wave owns two
+        float* park = reinterpret_cast<float*>(base + X::kS) + w * 32 * 64 + lane;
 #pragma unroll 1
         for (int ct = w; ct < NKT; ct += 4) {
             const int c = 16 * ct + lc;     // this lane's channel
+            // The tile's dQE, dKE, dKD (64 rows x 32 bytes each) are requested
+            // now and staged in LDS after the P terms: vector v = lane + 64 hf
+            // holds row v / 2, columns 8 (v % 2) .. +7.
+            uint4 ewv[6];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int v = lane + 64 * hf;
+                const int off = (v >> 1) * K + 16 * ct + 8 * (v & 1);
+                ewv[hf] = *reinterpret_cast<const uint4*>(gQE + off);
+                ewv[2 + hf] = *reinterpret_cast<const uint4*>(gKE + off);
+                ewv[4 + hf] = *reinterpret_cast<const uint4*>(gKD + off);
+            }
+            // sub-block factors f(J, I) of this lane's column
+            float invp[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) invp[I] = s.unsafe[I] ? 0.f : s.invP[I][c];
+            const float f20 = s.F20[c], f30 = s.F30[c], f31 = s.F31[c];
+            auto fac = [&](int J, int I) -> float {
+                if (J == I) return invp[I];
+                if (J == I - 1) return 1.f;
+                if (I == 2) return f20;
+                return J == 0 ? f30 : f31;
+            };
+            float Gc[16];  // G of this lane's rows 16 I + 4 lg + r
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Gc[4 * I + r] = s.G[kSub * I + 4 * lg + r][c];
             f32x4 dG[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) dq[I] = dk[I] = dG[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            // P terms with (k b)^T of this tile, b_j = e^(G_end(J) - G_j)
-            for (int e = lane; e < 16 * kChunk; e += 64) {
-                const int jr = e % kChunk, cc = 16 * ct + e / kChunk;
-                const float Ge = s.G[kSub * (jr / kSub) + kSub - 1][cc];
-                opw[e / kChunk][jr] = MM::to_f32(s.kh[jr][cc]) * __expf(Ge - s.G[jr][cc]);
+            // (k b)^T of this tile, b_j = e^(G_end(J) - G_j): lane builds row j = lane
+            {
+                const int jr = lane, je = kSub * (jr / kSub) + kSub - 1;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 g4 = *reinterpret_cast<const float4*>(&s.G[jr][16 * ct + 4 * q]);
+                    const float4 e4 = *reinterpret_cast<const float4*>(&s.G[je][16 * ct + 4 * q]);
+                    opw[4 * q + 0][jr] = MM::to_f32(s.kh[jr][16 * ct + 4 * q + 0]) * __expf(e4.x - g4.x);
+                    opw[4 * q + 1][jr] = MM::to_f32(s.kh[jr][16 * ct + 4 * q + 1]) * __expf(e4.y - g4.y);
+                    opw[4 * q + 2][jr] = MM::to_f32(s.kh[jr][16 * ct + 4 * q + 2]) * __expf(e4.z - g4.z);
+                    opw[4 * q + 3][jr] = MM::to_f32(s.kh[jr][16 * ct + 4 * q + 3]) * __expf(e4.w - g4.w);
+                }
             }
+            // P terms: P_x[I] = a_I * sum_J f(J, I) dX_IJ (k b)_J
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
+#pragma unroll
                 for (int J = 0; J <= I; ++J) {
-                    if (J == I && s.unsafe[I]) continue;  // formed pairwise below
-                    const float f = sub_factor(s, J, I, c);
-                    const f32x4 aq = mma16_f32<false>(&s.x.sc.dM[0][0], kChunk + 1, kSub * I, &opw[0][0], LDF, 0,
+                    const float f = fac(J, I);
+                    const f32x4 aq = mma16_f32<false>(&s.x.sc.dM[0][0], SM::LDD, kSub * I, &opw[0][0], LDF, 0,
                                                       kSub * J, lane);
-                    const f32x4 ak = mma16_f32<false>(&s.x.sc.dA[0][0], kChunk + 1, kSub * I, &opw[0][0], LDF, 0,
+                    const f32x4 ak = mma16_f32<false>(&s.x.sc.dA[0][0], SM::LDD, kSub * I, &opw[0][0], LDF, 0,
                                                       kSub * J, lane);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -1035,12 +1091,20 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
-                    const float a = __expf(s.G[i][c] - Gr);
-                    const float Pq = a * pq[r], Pk = a * pk[r];
+                    const float a_ = __expf(Gc[4 * I + r] - Gr);
+                    const float Pq = a_ * pq[r], Pk = a_ * pk[r];
                     dq[I][r] += Pq;
                     dk[I][r] += Pk;
                     dG[I][r] += MM::to_f32(s.qh[i][c]) * Pq + MM::to_f32(s.kh[i][c]) * Pk;
                 }
+            }
+            // stage the element-wise operands (requested at the tile start)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int v = lane + 64 * hf;
+#pragma unroll
+                for (int a3 = 0; a3 < 3; ++a3)
+                    *reinterpret_cast<uint4*>(&eww[a3][v >> 1][8 * (v & 1)]) = ewv[2 * a3 + hf];
             }
 
             // R terms: (q a)^T against dM, then (k a)^T against dA, a_i = e^(G_i - G_ref(I))
@@ -1049,21 +1113,28 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             for (int J = 0; J < 4; ++J) rr[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
             for (int pass = 0; pass < 2; ++pass) {
-                for (int e = lane; e < 16 * kChunk; e += 64) {
-                    const int ir = e % kChunk, cc = 16 * ct + e / kChunk;
-                    const float Gr = ir < kSub ? 0.f : s.G[kSub * (ir / kSub) - 1][cc];
-                    const float x_ = MM::to_f32(pass == 0 ? s.qh[ir][cc] : s.kh[ir][cc]);
-                    opw[e / kChunk][ir] = x_ * __expf(s.G[ir][cc] - Gr);
+                {
+                    const int ir = lane, I = ir / kSub;
+                    const ET* xr = pass == 0 ? &s.qh[ir][16 * ct] : &s.kh[ir][16 * ct];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 g4 = *reinterpret_cast<const float4*>(&s.G[ir][16 * ct + 4 * q]);
+                        float4 r4 = {0.f, 0.f, 0.f, 0.f};
+                        if (I > 0) r4 = *reinterpret_cast<const float4*>(&s.G[kSub * I - 1][16 * ct + 4 * q]);
+                        opw[4 * q + 0][ir] = MM::to_f32(xr[4 * q + 0]) * __expf(g4.x - r4.x);
+                        opw[4 * q + 1][ir] = MM::to_f32(xr[4 * q + 1]) * __expf(g4.y - r4.y);
+                        opw[4 * q + 2][ir] = MM::to_f32(xr[4 * q + 2]) * __expf(g4.z - r4.z);
+                        opw[4 * q + 3][ir] = MM::to_f32(xr[4 * q + 3]) * __expf(g4.w - r4.w);
+                    }
                 }
                 const float* dX = pass == 0 ? &s.x.sc.dM[0][0] : &s.x.sc.dA[0][0];
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
-#pragma unroll 1
+#pragma unroll
                     for (int I = J; I < 4; ++I) {
-                        if (I == J && s.unsafe[J]) continue;
-                        const float f = sub_factor(s, J, I, c);
+                        const float f = fac(J, I);
                         const f32x4 acc =
-                            mma16_f32<true>(dX, kChunk + 1, kSub * J, &opw[0][0], LDF, 0, kSub * I, lane);
+                            mma16_f32<true>(dX, SM::LDD, kSub * J, &opw[0][0], LDF, 0, kSub * I, lane);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) rr[J][r] += f * acc[r];
                     }
@@ -1075,7 +1146,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * J + 4 * lg + r;
-                    const float R = __expf(Ge - s.G[i][c]) * rr[J][r];
+                    const float R = __expf(Ge - Gc[4 * J + r]) * rr[J][r];
                     dk[J][r] += R;
                     dG[J][r] -= MM::to_f32(s.kh[i][c]) * R;
                 }
@@ -1107,7 +1178,6 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                             }
                         }
                         const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
-                        // I is a runtime index here: update through a small switch-free select
 #pragma unroll
                         for (int II = 0; II < 4; ++II)
                             if (II == I) {
@@ -1127,12 +1197,12 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
-                    const float Gi = s.G[i][c];
+                    const float Gi = Gc[4 * I + r];
                     const float E = __expf(Gi), Ed = __expf(Glast - Gi);
                     const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
-                    const float dqe = MM::to_f32(gQE[i * K + c]);
-                    const float dke = MM::to_f32(gKE[i * K + c]);
-                    const float dkd = MM::to_f32(gKD[i * K + c]);
+                    const float dqe = MM::to_f32(eww[0][i][lc]);
+                    const float dke = MM::to_f32(eww[1][i][lc]);
+                    const float dkd = MM::to_f32(eww[2][i][lc]);
                     const float KD = k_ * Ed;
                     dq[I][r] += p.scale * dqe * E;
                     dk[I][r] += dke * E + dkd * Ed;
@@ -1195,7 +1265,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             ddt += __shfl_xor(ddt, 32, 64);
             if (lg == 0) s.ddt[c] = ddt;
 
-            // row dot products of the L2-norm rule; park this tile if more follow
+            // row dot products of the L2-norm rule
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
@@ -1212,58 +1282,68 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         s.dots[0][ct][i] = vq;
                         s.dots[1][ct][i] = vk;
                     }
-                    if (PARK) {
-                        park_q[i * K + c] = dq[I][r];
-                        park_k[i * K + c] = dk[I][r];
-                    }
                 }
-        }
-
-        // ---- 3. L2-norm and sigmoid chain rules, gate shares, stores
-        __syncthreads();  // dots, ddt and the parked tiles are complete
-        uint16_t* dqg = static_cast<uint16_t*>(gr.dq);
-        uint16_t* dkg = static_cast<uint16_t*>(gr.dk);
-        if (PARK) {
-            for (int e = t; e < rows * K; e += kThreads) {
-                const int i = e / K, c = e % K;
-                float dotq = 0.f, dotk = 0.f;
+            if (TWO && ct == w) {
+                // the first tile waits for the row dot products in this lane's
+                // own 32-float strip of the slot's entry-state region (read by
+                // the V-local kernel, free now), coalesced across the wave
 #pragma unroll
-                for (int q = 0; q < NKT; ++q) {
-                    dotq += s.dots[0][q][i];
-                    dotk += s.dots[1][q][i];
-                }
-                float oq = park_q[e], ok = park_k[e];
-                if (p.use_qk_l2norm) {
-                    oq = s.rq[i] * (oq - MM::to_f32(s.qh[i][c]) * dotq);
-                    ok = s.rk[i] * (ok - MM::to_f32(s.kh[i][c]) * dotk);
-                }
-                const int64_t gi = ((rbase + i) * H + h) * K + c;
-                dqg[gi] = f32_to_bf16_bits(oq);
-                dkg[gi] = f32_to_bf16_bits(ok);
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        park[(4 * I + r) * 64] = dq[I][r];
+                        park[(16 + 4 * I + r) * 64] = dk[I][r];
+                    }
             }
-        } else if (w < NKT) {
-            const int c = 16 * w + lc;
+        }
+        if (TWO) {
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int i = kSub * I + 4 * lg + r;
-                    if (i >= rows) continue;
-                    float dotq = 0.f, dotk = 0.f;
-#pragma unroll
-                    for (int q = 0; q < NKT; ++q) {
-                        dotq += s.dots[0][q][i];
-                        dotk += s.dots[1][q][i];
-                    }
-                    float oq = dq[I][r], ok = dk[I][r];
-                    if (p.use_qk_l2norm) {
-                        oq = s.rq[i] * (oq - MM::to_f32(s.qh[i][c]) * dotq);
-                        ok = s.rk[i] * (ok - MM::to_f32(s.kh[i][c]) * dotk);
-                    }
-                    const int64_t gi = ((rbase + i) * H + h) * K + c;
-                    dqg[gi] = f32_to_bf16_bits(oq);
-                    dkg[gi] = f32_to_bf16_bits(ok);
+                    sq[I][r] = park[(4 * I + r) * 64];
+                    sk[I][r] = park[(16 + 4 * I + r) * 64];
                 }
+        }
+
+        // ---- 3. L2-norm and sigmoid chain rules, gate shares, stores
+        __syncthreads();  // dots and ddt are complete
+        if (t < 2 * kChunk) {  // row totals of the dot products, kept in tile slot 0
+            const int i = t & (kChunk - 1), which = t / kChunk;
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < NKT; ++q) acc += s.dots[which][q][i];
+            s.dots[which][0][i] = acc;
+        }
+        __syncthreads();
+        {
+            uint16_t* dqg = static_cast<uint16_t*>(gr.dq);
+            uint16_t* dkg = static_cast<uint16_t*>(gr.dk);
+            auto store_tile = [&](int ct, const f32x4* tq, const f32x4* tk) {
+                const int c = 16 * ct + lc;
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = kSub * I + 4 * lg + r;
+                        if (i >= rows) continue;
+                        const float dotq = s.dots[0][0][i], dotk = s.dots[1][0][i];
+                        float oq = tq[I][r], ok = tk[I][r];
+                        if (p.use_qk_l2norm) {
+                            oq = s.rq[i] * (oq - MM::to_f32(s.qh[i][c]) * dotq);
+                            ok = s.rk[i] * (ok - MM::to_f32(s.kh[i][c]) * dotk);
+                        }
+                        const int64_t gi = ((rbase + i) * H + h) * K + c;
+                        dqg[gi] = f32_to_bf16_bits(oq);
+                        dkg[gi] = f32_to_bf16_bits(ok);
+                    }
+            };
+            if (TWO) {
+                store_tile(w, sq, sk);
+                store_tile(w + 4, dq, dk);
+            } else if (w < NKT) {
+                store_tile(w, dq, dk);
+            }
         }
         if (t < kChunk && t < rows) {
             const float db = s.dbc[0][t] + s.dbc[1][t] + s.dbc[2][t] + s.dbc[3][t] + s.dbr[t];
