@@ -1410,7 +1410,7 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
         if (p.cu_seqlens)
             hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
         if (nblk > 0)
-            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0,
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true>), dim3(static_cast<unsigned>(nblk)), dim3(prep_threads(K)), 0,
                                st, p, chunk_off, slots, sb);
     }
     if (want(1) && cgrid > 0)

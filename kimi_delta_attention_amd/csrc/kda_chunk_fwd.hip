@@ -31,7 +31,7 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
             hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
         const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
         if (nblk > 0)
-            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, false>), dim3(static_cast<unsigned>(nblk)), dim3(kThreads),
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, false>), dim3(static_cast<unsigned>(nblk)), dim3(prep_threads(K)),
                                0, st, p, chunk_off, prep, static_cast<int64_t>(PrepLayout<K, BF>::kBytes));
     }
     if (stage < 0 || stage == 1) {

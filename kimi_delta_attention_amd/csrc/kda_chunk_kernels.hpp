@@ -92,6 +92,11 @@ __device__ __forceinline__ void store_row(float* dst, const float* src) {
 }
 
 // ------------------------------------------------------------------ prep
+// Threads of a prep workgroup: its LDS allows one workgroup per CU, so wide
+// channels take 8 waves (two per SIMD) to overlap the latency of one wave's
+// LDS and memory chains with another's work.
+__host__ __device__ constexpr int prep_threads(int K) { return K >= 64 ? 512 : 256; }
+
 template <int K, bool BF, bool BWD>
 struct PrepSmem {
     using ET = typename Mma<BF>::ET;
@@ -129,13 +134,17 @@ struct PrepSmem {
 // BWD additionally writes T = (I + A)^-1 and the un-scaled strictly lower
 // k-k score matrix (BwdExtra layout) for the backward kernels.
 template <int K, bool BF, bool BWD>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, const int32_t* chunk_off,
+__global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams p, const int32_t* chunk_off,
                                                               uint8_t* ws, int64_t slot_bytes) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;  // q/k/v element
     using L = PrepLayout<K, BF>;
-    constexpr int CPT = K / 4;  // channels per thread in row-wise phases
+    constexpr int NT = prep_threads(K);
+    constexpr int NW = NT / 64;     // waves
+    constexpr int TPR = NT / kChunk;  // threads per row in row-wise phases
+    constexpr int CPT = K / TPR;      // channels per thread in row-wise phases
+    static_assert(CPT % 8 == 0, "row segments are whole 16-byte vectors");
     constexpr int LDE = PrepSmem<K, BF, BWD>::LDE;
     __shared__ __attribute__((aligned(16))) PrepSmem<K, BF, BWD> s;
 
@@ -160,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     float* gGC = reinterpret_cast<float*>(out + L::kGC);
 
     // ---- 1. prologue, row-wise: thread -> (row i, quarter pq of the channels)
-    const int i = t >> 2;
-    const int pq = t & 3;
+    const int i = t / TPR;
+    const int pq = t % TPR;
     const int c0 = pq * CPT;
     const bool valid = i < rows;
     const int64_t grow = start + static_cast<int64_t>(j) * kChunk + i;
@@ -181,10 +190,11 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
         ssq += qh[c] * qh[c];
         ssk += kh[c] * kh[c];
     }
-    ssq += __shfl_xor(ssq, 1, 64);
-    ssq += __shfl_xor(ssq, 2, 64);
-    ssk += __shfl_xor(ssk, 1, 64);
-    ssk += __shfl_xor(ssk, 2, 64);
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) {
+        ssq += __shfl_xor(ssq, o, 64);
+        ssk += __shfl_xor(ssk, o, 64);
+    }
     float rq = 1.f, rk = 1.f;
     if (p.use_qk_l2norm) {
         rq = rsqrtf(ssq + kL2Eps);
@@ -217,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
         s.beta[i] = b;
     }
     if (t < 4) s.unsafe[t] = 0;
-    for (int e = t; e < kChunk * (kChunk + 1); e += kThreads) {
+    for (int e = t; e < kChunk * (kChunk + 1); e += NT) {
         (&s.A[0][0])[e] = 0.f;
         (&s.M[0][0])[e] = 0.f;
         if (BWD) (&s.Ak[0][0])[e] = 0.f;
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
 
     // ---- 2. inclusive cumulative sum over the 64 rows, per channel
     {
-        constexpr int SEGS = kThreads / K;      // row segments per channel
+        constexpr int SEGS = NT / K;      // row segments per channel
         constexpr int SEGLEN = kChunk / SEGS;
         const int c = t % K;
         const int sg = t / K;
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     __syncthreads();
 
     // ---- 3. per-channel sub-block factors
-    for (int c = t; c < K; c += kThreads) {
+    for (int c = t; c < K; c += NT) {
         float Gref[4], Gend[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -302,7 +312,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     __syncthreads();
 
     // ---- 5. A and M sub-block tiles on MFMA (job = (matrix, I, J<=I)); 20 jobs
-    for (int job = w; job < 20; job += 4) {
+    for (int job = w; job < 20; job += NW) {
         const bool isM = job >= 10;
         int tj = isM ? job - 10 : job;
         int I = 0;
@@ -343,7 +353,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
         if (!s.unsafe[I]) continue;
         const IT* qg = static_cast<const IT*>(p.q);
         const IT* kg = static_cast<const IT*>(p.k);
-        for (int pr = t; pr < kSub * (kSub + 1) / 2; pr += kThreads) {
+        for (int pr = t; pr < kSub * (kSub + 1) / 2; pr += NT) {
             int a = 0, b = pr;
             while (b > a) { b -= a + 1; ++a; }
             const int ri = kSub * I + a, rj = kSub * I + b;
@@ -365,9 +375,9 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     __syncthreads();
 
     // ---- 6. T = (I + A)^-1: diagonal sub-blocks by forward substitution ...
-    for (int e = t; e < kChunk * (kChunk + 1); e += kThreads) (&s.u.T[0][0])[e] = 0.f;
+    for (int e = t; e < kChunk * (kChunk + 1); e += NT) (&s.u.T[0][0])[e] = 0.f;
     __syncthreads();
-    if (lane < kSub) {
+    if (w < 4 && lane < kSub) {
         const int I = w;
         const int jc = lane;
         float x[kSub];
@@ -387,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     // ... then the off-diagonal sub-blocks by distance: T_IJ = -T_II sum_L A_IL T_LJ
     for (int d = 1; d < 4; ++d) {
         const int nb = 4 - d;
-        for (int e = t; e < nb * kSub * kSub; e += kThreads) {
+        for (int e = t; e < nb * kSub * kSub; e += NT) {
             const int bi = e / (kSub * kSub);
             const int a = (e / kSub) % kSub, b = e % kSub;
             const int I = d + bi, J = bi;
@@ -399,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
             s.X[bi][a][b] = acc;
         }
         __syncthreads();
-        for (int e = t; e < nb * kSub * kSub; e += kThreads) {
+        for (int e = t; e < nb * kSub * kSub; e += NT) {
             const int bi = e / (kSub * kSub);
             const int a = (e / kSub) % kSub, b = e % kSub;
             const int I = d + bi, J = bi;
@@ -412,21 +422,21 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
     }
 
     // ---- 7. T diag(beta) and scale * M to the workspace
-    constexpr int TPT = kChunk * kChunk / kThreads;
+    constexpr int TPT = kChunk * kChunk / NT;
     float tbr[TPT];
 #pragma unroll
     for (int m = 0; m < TPT; ++m) {
-        const int e = t + m * kThreads;
+        const int e = t + m * NT;
         const int a = e / kChunk, b = e % kChunk;
         tbr[m] = s.u.T[a][b] * s.beta[b];
         gTB[e] = MM::from_f32(tbr[m]);
         gMS[e] = MM::from_f32(p.scale * s.M[a][b]);
     }
-    for (int c = t; c < K; c += kThreads) gGC[c] = s.gC[c];
+    for (int c = t; c < K; c += NT) gGC[c] = s.gC[c];
     if (BWD) {
         ET* gT = reinterpret_cast<ET*>(out + BwdExtra<K, BF>::kT);
         ET* gAK = reinterpret_cast<ET*>(out + BwdExtra<K, BF>::kAK);
-        for (int e = t; e < kChunk * kChunk; e += kThreads) {
+        for (int e = t; e < kChunk * kChunk; e += NT) {
             const int a = e / kChunk, b = e % kChunk;
             gT[e] = MM::from_f32(s.u.T[a][b]);
             gAK[e] = MM::from_f32(s.Ak[a][b]);
@@ -439,7 +449,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
         constexpr int LDC = kChunk + MM::PAD;
 #pragma unroll
         for (int m = 0; m < TPT; ++m) {
-            const int e = t + m * kThreads;
+            const int e = t + m * NT;
             s.u.wu.TB[e / kChunk][e % kChunk] = MM::from_f32(tbr[m]);
         }
         float vv[CPT];
@@ -457,17 +467,19 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(ChunkParams p, con
         __syncthreads();
         ET* gW = reinterpret_cast<ET*>(out + L::kW);
         ET* gU = reinterpret_cast<ET*>(out + L::kU);
+        // wave w: row tile w % 4, every (NW / 4)-th column tile from w / 4
+        const int rt = w & 3;
 #pragma unroll 2
-        for (int ct = 0; ct < K / 16; ++ct) {
+        for (int ct = w >> 2; ct < K / 16; ct += NW / 4) {
             f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
-            for (int k0 = 0; k0 < 16 * (w + 1); k0 += MM::KS) {
-                const auto a = MM::load(&s.u.wu.TB[0][0], LDC, 16 * w, k0, lane);
+            for (int k0 = 0; k0 < 16 * (rt + 1); k0 += MM::KS) {
+                const auto a = MM::load(&s.u.wu.TB[0][0], LDC, 16 * rt, k0, lane);
                 aw = MM::mma(a, MM::load(&s.u.wu.KEt[0][0], LDC, 16 * ct, k0, lane), aw);
                 au = MM::mma(a, MM::load(&s.u.wu.Vt[0][0], LDC, 16 * ct, k0, lane), au);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = 16 * w + 4 * (lane >> 4) + r, col = 16 * ct + (lane & 15);
+                const int row = 16 * rt + 4 * (lane >> 4) + r, col = 16 * ct + (lane & 15);
                 gW[row * K + col] = MM::from_f32(aw[r]);
                 gU[row * K + col] = MM::from_f32(au[r]);
             }
