@@ -195,21 +195,42 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
 }
 
 // ------------------------------------------------------------------ V-local gradients
+// Threads of a V-local workgroup (its LDS allows one per CU): the bf16
+// variant takes 8 waves, two per 16-row tile splitting the column tiles, so
+// that one wave's LDS and memory chains overlap another's products.
+__host__ __device__ constexpr int vlocal_threads(bool bf) { return bf ? 512 : 256; }
+
+// Per V-column block of BV columns: Y = v - KE S, dD = KD dS' + MS^T dO,
+// D = TB Y, dY = TB^T dD (= dv), and the V-summed products dQE, dKE, dKD,
+// dMS, dTB, dgam accumulate over the blocks.  The next block's S, dS', dO and
+// v are requested before the current block's products.
 template <int K, int V, int BV, bool BF>
-__global__ __launch_bounds__(kThreads) void chunk_bwd_vlocal_kernel(ChunkParams p, ChunkGrads gr,
-                                                                    const int32_t* chunk_off, uint8_t* ws,
-                                                                    int64_t slot_bytes) {
+__global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(ChunkParams p, ChunkGrads gr,
+                                                                              const int32_t* chunk_off,
+                                                                              uint8_t* ws, int64_t slot_bytes) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
     using L = PrepLayout<K, BF>;
     using X = BwdExtra<K, BF>;
+    constexpr int NT = vlocal_threads(BF);
+    constexpr int WPR = NT / 256;  // waves per 16-row tile
     constexpr int LDK = K + MM::PAD;
     constexpr int LDC = kChunk + MM::PAD;
     constexpr int LDB = BV + MM::PAD;
     constexpr int NCT = BV / 16;   // column tiles of a [64][BV] block
     constexpr int NKT = K / 16;    // column tiles of a [64][K] product
+    constexpr int VE = 16 / sizeof(ET);          // elements per 16-byte vector
+    constexpr int VPR = BV / VE;                 // vectors per block row
+    constexpr int NVS = K * VPR;                 // vectors of an S (or dS') block
+    constexpr int NVO = kChunk * VPR;            // vectors of a dO block
+    constexpr int PS = (NVS + NT - 1) / NT;
+    constexpr int PO = (NVO + NT - 1) / NT;
+    constexpr int TW = (NCT + WPR - 1) / WPR;    // column tiles per wave in a block
+    constexpr int AW = NKT / WPR;                // [64][K] accumulator tiles per wave
+    constexpr int CW = 4 / WPR;                  // [64][64] accumulator tiles per wave
     static_assert(BV % MM::KS == 0, "products contract over the V block: it must hold whole MFMA k-steps");
+    static_assert(BV % VE == 0 && NKT % WPR == 0, "block shapes");
 
     __shared__ __attribute__((aligned(16))) ET KEn[kChunk][LDK];
     __shared__ __attribute__((aligned(16))) ET KDn[kChunk][LDK];
@@ -239,83 +260,142 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_vlocal_kernel(ChunkParams 
     seq_bounds(p, n, start, len);
     const int rows = min(kChunk, len - j * kChunk);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const int rt = w & 3, hv = w >> 2;  // 16-row tile and column-tile phase of this wave
     uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
     const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
-
-    copy_in<ET, kChunk, K>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + X::kKE), t);
-    copy_in<ET, kChunk, K>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
-    copy_in<ET, kChunk, kChunk>(&TBn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-    copy_in_t<ET, kChunk, kChunk>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-    copy_in_t<ET, kChunk, kChunk>(&MSt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
-
-    f32x4 aQE[NKT], aKE[NKT], aKD[NKT], aMS[4], aTB[4];
-#pragma unroll
-    for (int c = 0; c < NKT; ++c) aQE[c] = aKE[c] = aKD[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) aMS[c] = aTB[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dgam = 0.f;
 
     const ET* gS = reinterpret_cast<const ET*>(base + X::kS);
     const ET* gDS = reinterpret_cast<const ET*>(base + X::kDS);
     const IT* dOg = static_cast<const IT*>(gr.dO);
     const IT* vg = static_cast<const IT*>(p.v);
     IT* dvg = static_cast<IT*>(gr.dv);
-    const int klo = (16 * w / MM::KS) * MM::KS;
+
+    // next block's operands in registers: S and dS' rows key, dO rows i (16-byte
+    // vectors), and v in the accumulator layout of this wave's tiles
+    f32x4 rS[PS], rD[PS], rO[PO];
+    float rv[TW][4];
+    auto fetch = [&](int vb) {
+        const int v0 = vb * BV;
+#pragma unroll
+        for (int m = 0; m < PS; ++m) {
+            const int e = t + m * NT;
+            if (NVS % NT == 0 || e < NVS) {
+                const int key = e / VPR, c = (e % VPR) * VE;
+                rS[m] = *reinterpret_cast<const f32x4*>(gS + key * V + v0 + c);
+                rD[m] = *reinterpret_cast<const f32x4*>(gDS + key * V + v0 + c);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < PO; ++m) {
+            const int e = t + m * NT;
+            if (NVO % NT == 0 || e < NVO) {
+                const int i = e / VPR, c = (e % VPR) * VE;
+                rO[m] = i < rows ? *reinterpret_cast<const f32x4*>(dOg + ((rbase + i) * H + h) * V + v0 + c)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < TW; ++m) {
+            const int ct = hv + WPR * m;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * rt + 4 * (lane >> 4) + r;
+                rv[m][r] = (ct < NCT && i < rows)
+                               ? Elem<IT>::load(vg, ((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15))
+                               : 0.f;
+            }
+        }
+    };
+    auto stage = [&]() {
+#pragma unroll
+        for (int m = 0; m < PS; ++m) {
+            const int e = t + m * NT;
+            if (NVS % NT == 0 || e < NVS) {
+                const int key = e / VPR, c = (e % VPR) * VE;
+                *reinterpret_cast<f32x4*>(&Sn[key][c]) = rS[m];
+                *reinterpret_cast<f32x4*>(&dSn[key][c]) = rD[m];
+                const ET* se = reinterpret_cast<const ET*>(&rS[m]);
+                const ET* de = reinterpret_cast<const ET*>(&rD[m]);
+#pragma unroll
+                for (int x = 0; x < VE; ++x) {
+                    St[c + x][key] = se[x];
+                    dSt[c + x][key] = de[x];
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < PO; ++m) {
+            const int e = t + m * NT;
+            if (NVO % NT == 0 || e < NVO) {
+                const int i = e / VPR, c = (e % VPR) * VE;
+                *reinterpret_cast<f32x4*>(&dOn[i][c]) = rO[m];
+                const ET* oe = reinterpret_cast<const ET*>(&rO[m]);
+#pragma unroll
+                for (int x = 0; x < VE; ++x) dOt[c + x][i] = oe[x];
+            }
+        }
+    };
+
+    fetch(0);
+    copy_in<ET, kChunk, K, NT>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + X::kKE), t);
+    copy_in<ET, kChunk, K, NT>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
+    copy_in<ET, kChunk, kChunk, NT>(&TBn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
+    copy_in_t<ET, kChunk, kChunk, NT>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
+    copy_in_t<ET, kChunk, kChunk, NT>(&MSt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
+
+    f32x4 aQE[AW], aKE[AW], aKD[AW], aMS[CW], aTB[CW];
+#pragma unroll
+    for (int c = 0; c < AW; ++c) aQE[c] = aKE[c] = aKD[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < CW; ++c) aMS[c] = aTB[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float dgam = 0.f;
+    const int klo = (16 * rt / MM::KS) * MM::KS;
 
     for (int vb = 0; vb < V / BV; ++vb) {
         const int v0 = vb * BV;
-        for (int e = t; e < K * BV; e += kThreads) {
-            const int key = e / BV, c = e % BV;
-            const ET s = gS[key * V + v0 + c], d = gDS[key * V + v0 + c];
-            Sn[key][c] = s;
-            St[c][key] = s;
-            dSn[key][c] = d;
-            dSt[c][key] = d;
-        }
-        for (int e = t; e < kChunk * BV; e += kThreads) {
-            const int i = e / BV, c = e % BV;
-            float v = 0.f;
-            if (i < rows) v = Elem<IT>::load(dOg, ((rbase + i) * H + h) * V + v0 + c);
-            dOn[i][c] = MM::from_f32(v);
-            dOt[c][i] = MM::from_f32(v);
-        }
+        stage();
+        float vcur[TW][4];
+#pragma unroll
+        for (int m = 0; m < TW; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) vcur[m][r] = rv[m][r];
+        if (vb + 1 < V / BV) fetch(vb + 1);
         __syncthreads();
 
-        // Y = v - KE S and dD = KD dS' + MS^T dO, rows 16w..
+        // Y = v - KE S and dD = KD dS' + MS^T dO on this wave's tiles
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
+        for (int m = 0; m < TW; ++m) {
+            const int ct = hv + WPR * m;
+            if (ct >= NCT) continue;
             f32x4 pp = {0.f, 0.f, 0.f, 0.f};
-            pp = gemm<MM>(&KEn[0][0], LDK, 16 * w, &St[0][0], LDK, 16 * ct, 0, K, pp, lane);
+            pp = gemm<MM>(&KEn[0][0], LDK, 16 * rt, &St[0][0], LDK, 16 * ct, 0, K, pp, lane);
             f32x4 y;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * (lane >> 4) + r;
-                float vv = 0.f;
-                if (i < rows) vv = Elem<IT>::load(vg, ((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15));
-                y[r] = vv - pp[r];
-            }
-            tile_store<MM>(&Yn[0][0], LDB, 16 * w, 16 * ct, y, lane);
-            tile_store_t<MM>(&Yt[0][0], LDC, 16 * w, 16 * ct, y, lane);
+            for (int r = 0; r < 4; ++r) y[r] = vcur[m][r] - pp[r];
+            tile_store<MM>(&Yn[0][0], LDB, 16 * rt, 16 * ct, y, lane);
+            tile_store_t<MM>(&Yt[0][0], LDC, 16 * rt, 16 * ct, y, lane);
             f32x4 dd = {0.f, 0.f, 0.f, 0.f};
-            dd = gemm<MM>(&KDn[0][0], LDK, 16 * w, &dSt[0][0], LDK, 16 * ct, 0, K, dd, lane);
-            dd = gemm<MM>(&MSt[0][0], LDC, 16 * w, &dOt[0][0], LDC, 16 * ct, klo, kChunk, dd, lane);
-            tile_store<MM>(&dDn[0][0], LDB, 16 * w, 16 * ct, dd, lane);
-            tile_store_t<MM>(&dDt[0][0], LDC, 16 * w, 16 * ct, dd, lane);
+            dd = gemm<MM>(&KDn[0][0], LDK, 16 * rt, &dSt[0][0], LDK, 16 * ct, 0, K, dd, lane);
+            dd = gemm<MM>(&MSt[0][0], LDC, 16 * rt, &dOt[0][0], LDC, 16 * ct, klo, kChunk, dd, lane);
+            tile_store<MM>(&dDn[0][0], LDB, 16 * rt, 16 * ct, dd, lane);
+            tile_store_t<MM>(&dDt[0][0], LDC, 16 * rt, 16 * ct, dd, lane);
         }
         __syncthreads();
 
         // D = TB Y; dY = TB^T dD; dv = dY
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
+        for (int m = 0; m < TW; ++m) {
+            const int ct = hv + WPR * m;
+            if (ct >= NCT) continue;
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            d = gemm<MM>(&TBn[0][0], LDC, 16 * w, &Yt[0][0], LDC, 16 * ct, 0, 16 * (w + 1), d, lane);
-            tile_store<MM>(&Dn[0][0], LDB, 16 * w, 16 * ct, d, lane);
+            d = gemm<MM>(&TBn[0][0], LDC, 16 * rt, &Yt[0][0], LDC, 16 * ct, 0, 16 * (rt + 1), d, lane);
+            tile_store<MM>(&Dn[0][0], LDB, 16 * rt, 16 * ct, d, lane);
             f32x4 dy = {0.f, 0.f, 0.f, 0.f};
-            dy = gemm<MM>(&TBt[0][0], LDC, 16 * w, &dDt[0][0], LDC, 16 * ct, klo, kChunk, dy, lane);
-            tile_store<MM>(&dYn[0][0], LDB, 16 * w, 16 * ct, dy, lane);
+            dy = gemm<MM>(&TBt[0][0], LDC, 16 * rt, &dDt[0][0], LDC, 16 * ct, klo, kChunk, dy, lane);
+            tile_store<MM>(&dYn[0][0], LDB, 16 * rt, 16 * ct, dy, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * w + 4 * (lane >> 4) + r;
+                const int i = 16 * rt + 4 * (lane >> 4) + r;
                 if (i < rows) Elem<IT>::store(dvg, ((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15), dy[r]);
             }
         }
@@ -323,17 +403,19 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_vlocal_kernel(ChunkParams 
 
         // V-summed products over this column block
 #pragma unroll
-        for (int c = 0; c < NKT; ++c) {
-            aQE[c] = gemm<MM>(&dOn[0][0], LDB, 16 * w, &Sn[0][0], LDB, 16 * c, 0, BV, aQE[c], lane);
-            aKE[c] = gemm<MM>(&dYn[0][0], LDB, 16 * w, &Sn[0][0], LDB, 16 * c, 0, BV, aKE[c], lane);
-            aKD[c] = gemm<MM>(&Dn[0][0], LDB, 16 * w, &dSn[0][0], LDB, 16 * c, 0, BV, aKD[c], lane);
+        for (int m = 0; m < AW; ++m) {
+            const int c = hv + WPR * m;
+            aQE[m] = gemm<MM>(&dOn[0][0], LDB, 16 * rt, &Sn[0][0], LDB, 16 * c, 0, BV, aQE[m], lane);
+            aKE[m] = gemm<MM>(&dYn[0][0], LDB, 16 * rt, &Sn[0][0], LDB, 16 * c, 0, BV, aKE[m], lane);
+            aKD[m] = gemm<MM>(&Dn[0][0], LDB, 16 * rt, &dSn[0][0], LDB, 16 * c, 0, BV, aKD[m], lane);
         }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            aMS[c] = gemm<MM>(&dOn[0][0], LDB, 16 * w, &Dn[0][0], LDB, 16 * c, 0, BV, aMS[c], lane);
-            aTB[c] = gemm<MM>(&dDn[0][0], LDB, 16 * w, &Yn[0][0], LDB, 16 * c, 0, BV, aTB[c], lane);
+        for (int m = 0; m < CW; ++m) {
+            const int c = hv + WPR * m;
+            aMS[m] = gemm<MM>(&dOn[0][0], LDB, 16 * rt, &Dn[0][0], LDB, 16 * c, 0, BV, aMS[m], lane);
+            aTB[m] = gemm<MM>(&dDn[0][0], LDB, 16 * rt, &Yn[0][0], LDB, 16 * c, 0, BV, aTB[m], lane);
         }
-        for (int key = t; key < K; key += kThreads)
+        for (int key = t; key < K; key += NT)
 #pragma unroll 4
             for (int c = 0; c < BV; ++c) dgam += MM::to_f32(Sn[key][c]) * MM::to_f32(dSn[key][c]);
         __syncthreads();
@@ -345,23 +427,23 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_vlocal_kernel(ChunkParams 
     ET* gMS = reinterpret_cast<ET*>(base + X::kDMS);
     ET* gTB = reinterpret_cast<ET*>(base + X::kDTB);
 #pragma unroll
-    for (int c = 0; c < NKT; ++c)
+    for (int m = 0; m < AW; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * (lane >> 4) + r, col = 16 * c + (lane & 15);
-            gQE[i * K + col] = MM::from_f32(aQE[c][r]);
-            gKE[i * K + col] = MM::from_f32(-aKE[c][r]);
-            gKD[i * K + col] = MM::from_f32(aKD[c][r]);
+            const int i = 16 * rt + 4 * (lane >> 4) + r, col = 16 * (hv + WPR * m) + (lane & 15);
+            gQE[i * K + col] = MM::from_f32(aQE[m][r]);
+            gKE[i * K + col] = MM::from_f32(-aKE[m][r]);
+            gKD[i * K + col] = MM::from_f32(aKD[m][r]);
         }
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int m = 0; m < CW; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 16 * w + 4 * (lane >> 4) + r, col = 16 * c + (lane & 15);
-            gMS[i * kChunk + col] = MM::from_f32(aMS[c][r]);
-            gTB[i * kChunk + col] = MM::from_f32(aTB[c][r]);
+            const int i = 16 * rt + 4 * (lane >> 4) + r, col = 16 * (hv + WPR * m) + (lane & 15);
+            gMS[i * kChunk + col] = MM::from_f32(aMS[m][r]);
+            gTB[i * kChunk + col] = MM::from_f32(aTB[m][r]);
         }
-    for (int key = t; key < K; key += kThreads) reinterpret_cast<float*>(base + X::kDGAM)[key] = dgam;
+    for (int key = t; key < K; key += NT) reinterpret_cast<float*>(base + X::kDGAM)[key] = dgam;
 }
 
 // ------------------------------------------------------------------ K-local gradients
@@ -1421,7 +1503,7 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                            chunk_off, slots, sb);
     if (want(3) && nblk > 0)
         hipLaunchKernelGGL((chunk_bwd_vlocal_kernel<K, V, BV, BF>), dim3(static_cast<unsigned>(nblk)),
-                           dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb);
+                           dim3(vlocal_threads(BF)), 0, st, p, gr, chunk_off, slots, sb);
     if (want(4)) {
         if (nblk > 0) {
             if constexpr (BF)

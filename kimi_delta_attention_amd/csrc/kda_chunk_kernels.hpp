@@ -488,12 +488,16 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
 }
 
 // ------------------------------------------------------------------ state
-// Copy a [R][C] global matrix into LDS rows of leading dimension ld.
-template <typename ET, int R, int C>
+// Copy a [R][C] global matrix into LDS rows of leading dimension ld, with NT
+// threads; every load is issued before the first store.
+template <typename ET, int R, int C, int NT = kThreads>
 __device__ __forceinline__ void copy_in(ET* dst, int ld, const ET* src, int t) {
     constexpr int VE = 16 / sizeof(ET);  // elements per 16-byte vector
     constexpr int NV = R * C / VE;
-    for (int e = t; e < NV; e += kThreads) {
+#pragma unroll
+    for (int m = 0; m < (NV + NT - 1) / NT; ++m) {
+        const int e = t + m * NT;
+        if (NV % NT != 0 && e >= NV) break;
         const int r = (e * VE) / C, c = (e * VE) % C;
         const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * C + c);
         *reinterpret_cast<f32x4*>(dst + r * ld + c) = v;
@@ -502,11 +506,14 @@ __device__ __forceinline__ void copy_in(ET* dst, int ld, const ET* src, int t) {
 // Same, transposed: dst[c][r] = src[r][c].  Consecutive threads take
 // consecutive rows, so the scattered LDS stores of a wavefront land on
 // consecutive addresses.
-template <typename ET, int R, int C>
+template <typename ET, int R, int C, int NT = kThreads>
 __device__ __forceinline__ void copy_in_t(ET* dst, int ld, const ET* src, int t) {
     constexpr int VE = 16 / sizeof(ET);
     constexpr int NV = R * C / VE;
-    for (int e = t; e < NV; e += kThreads) {
+#pragma unroll
+    for (int m = 0; m < (NV + NT - 1) / NT; ++m) {
+        const int e = t + m * NT;
+        if (NV % NT != 0 && e >= NV) break;
         const int r = e % R, c = (e / R) * VE;
         const f32x4 v = *reinterpret_cast<const f32x4*>(src + r * C + c);
         const ET* ve = reinterpret_cast<const ET*>(&v);
