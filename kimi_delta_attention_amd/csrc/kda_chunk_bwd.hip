@@ -906,9 +906,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
     constexpr int LDF = SM::LDF;
     constexpr int CPT = K / 4;
     constexpr int NKT = K / 16;
-    constexpr bool TWO = NKT == 8;      // each wave owns tiles w and w + 4
     static_assert(NKT <= 8, "at most two column tiles per wave");
-    static_assert(!TWO || 4 * 32 * 64 * sizeof(float) <= K * K * sizeof(ET), "parked tile must fit the state region");
+    constexpr bool PARK = NKT > 4;      // each wave owns tiles w and w + 4
+    static_assert(!PARK || NKT * 32 * 64 * sizeof(float) <= X::kDQE - X::kS,
+                  "parked tiles must fit the state regions");
     __shared__ __attribute__((aligned(16))) SM s;
 
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -961,14 +962,27 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 rk = rsqrtf(ssk + kL2Eps);
             }
             if (!valid) rq = rk = 0.f;
-            const float* bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias + h * K + c0 : nullptr;
-#pragma unroll 8
-            for (int c = 0; c < CPT; ++c) {
-                s.qh[i][c0 + c] = MM::from_f32(qv[c] * rq);
-                s.kh[i][c0 + c] = MM::from_f32(kv[c] * rk);
-                s.G[i][c0 + c] = valid ? gate_eff(p.gate_mode, gv[c], rate, bias ? bias[c] : 0.f, p.lower_bound)
-                                       : 0.f;
+            if (p.gate_mode != GATE_LOGDECAY) {
+                const float* bias = p.dt_bias ? p.dt_bias + h * K + c0 : nullptr;
+#pragma unroll 4
+                for (int c = 0; c < CPT; ++c)
+                    gv[c] = valid ? gate_eff(p.gate_mode, gv[c], rate, bias ? bias[c] : 0.f, p.lower_bound) : 0.f;
             }
+#pragma unroll
+            for (int v = 0; v < CPT / 8; ++v) {
+                u16x8 uq, uk;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uq[e] = MM::from_f32(qv[8 * v + e] * rq);
+                    uk[e] = MM::from_f32(kv[8 * v + e] * rk);
+                }
+                *reinterpret_cast<u16x8*>(&s.qh[i][c0 + 8 * v]) = uq;
+                *reinterpret_cast<u16x8*>(&s.kh[i][c0 + 8 * v]) = uk;
+            }
+#pragma unroll
+            for (int v = 0; v < CPT / 4; ++v)
+                *reinterpret_cast<f32x4*>(&s.G[i][c0 + 4 * v]) =
+                    f32x4{gv[4 * v], gv[4 * v + 1], gv[4 * v + 2], gv[4 * v + 3]};
             if ((t & 3) == 0) {
                 s.rq[i] = rq;
                 s.rk[i] = rk;
@@ -1102,8 +1116,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         ET (*eww)[kChunk][16] = s.ew[w];
         float dal = 0.f;
         f32x4 dq[4], dk[4];
-        f32x4 sq[4], sk[4];  // the first tile's dq^, dk^ when the wave owns two
-        float* park = reinterpret_cast<float*>(base + X::kS) + w * 32 * 64 + lane;
+        // per wave and tile, 32 floats per lane (dq^ then dk^), lane-minor
+        float* park = reinterpret_cast<float*>(base + X::kS) + w * 2 * 32 * 64 + lane;
 #pragma unroll 1
         for (int ct = w; ct < NKT; ct += 4) {
             const int c = 16 * ct + lc;     // this lane's channel
@@ -1365,27 +1379,20 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         s.dots[1][ct][i] = vk;
                     }
                 }
-            if (TWO && ct == w) {
-                // the first tile waits for the row dot products in this lane's
-                // own 32-float strip of the slot's entry-state region (read by
-                // the V-local kernel, free now), coalesced across the wave
+            // with two tiles per wave, the tile's dq^, dk^ wait for the row
+            // dot products in this lane's own strip of the slot's state
+            // regions (read by the V-local kernel, free now), coalesced across
+            // the wave; a single tile stays in registers
+            if (PARK) {
+                float* pk = park + ((ct - w) / 4) * 32 * 64;
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        park[(4 * I + r) * 64] = dq[I][r];
-                        park[(16 + 4 * I + r) * 64] = dk[I][r];
+                        pk[(4 * I + r) * 64] = dq[I][r];
+                        pk[(16 + 4 * I + r) * 64] = dk[I][r];
                     }
             }
-        }
-        if (TWO) {
-#pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    sq[I][r] = park[(4 * I + r) * 64];
-                    sk[I][r] = park[(16 + 4 * I + r) * 64];
-                }
         }
 
         // ---- 3. L2-norm and sigmoid chain rules, gate shares, stores
@@ -1420,11 +1427,21 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         dkg[gi] = f32_to_bf16_bits(ok);
                     }
             };
-            if (TWO) {
-                store_tile(w, sq, sk);
-                store_tile(w + 4, dq, dk);
-            } else if (w < NKT) {
-                store_tile(w, dq, dk);
+            if (!PARK) {
+                if (w < NKT) store_tile(w, dq, dk);
+            } else
+#pragma unroll 1
+            for (int ct = w; ct < NKT; ct += 4) {
+                const float* pk = park + ((ct - w) / 4) * 32 * 64;
+                f32x4 tq[4], tk[4];
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        tq[I][r] = pk[(4 * I + r) * 64];
+                        tk[I][r] = pk[(16 + 4 * I + r) * 64];
+                    }
+                store_tile(ct, tq, tk);
             }
         }
         if (t < kChunk && t < rows) {

@@ -101,7 +101,7 @@ template <int K, bool BF, bool BWD>
 struct PrepSmem {
     using ET = typename Mma<BF>::ET;
     static constexpr int LDE = K + Mma<BF>::PAD;
-    float G[kChunk][K + 1];
+    float G[kChunk][K + 4];  // 16-byte aligned rows
     union alignas(16) {
         struct {
             ET qL[kChunk][LDE];   // q^ exp(G_i - G_ref(I))
@@ -214,8 +214,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             gv[c] = gate_eff(p.gate_mode, gv[c], rate, bias, p.lower_bound);
         }
     }
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) s.G[i][c0 + c] = gv[c];
+    store_row<CPT>(&s.G[i][c0], gv);
     if (pq == 0) {
         s.rq[i] = rq;
         s.rk[i] = rk;
@@ -294,11 +293,14 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             e_[c] = __expf(Ge - Gi);
         }
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            s.u.op.qL[i][c0 + c] = MM::from_f32(qh[c] * a_[c]);
-            s.u.op.kL[i][c0 + c] = MM::from_f32(kh[c] * a_[c]);
-            s.u.op.kbe[i][c0 + c] = MM::from_f32(kh[c] * e_[c]);
-        }
+        for (int c = 0; c < CPT; ++c) o_[c] = qh[c] * a_[c];
+        store_row<CPT>(&s.u.op.qL[i][c0], o_);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * a_[c];
+        store_row<CPT>(&s.u.op.kL[i][c0], o_);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * e_[c];
+        store_row<CPT>(&s.u.op.kbe[i][c0], o_);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) o_[c] = p.scale * qh[c] * a_[c] * s.Er[I][c0 + c];
         store_row<CPT>(gQE + i * K + c0, o_);
