@@ -37,26 +37,6 @@
 
 namespace kda {
 
-// Accumulator tile (16 x 16) store helpers.  Lane l holds column l % 16 and
-// rows 4 (l / 16) .. +3 of the tile at (r0, c0).
-template <class MM>
-__device__ __forceinline__ void tile_store(typename MM::ET* dst, int ld, int r0, int c0, f32x4 v, int lane) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(r0 + 4 * (lane >> 4) + r) * ld + c0 + (lane & 15)] = MM::from_f32(v[r]);
-}
-template <class MM>
-__device__ __forceinline__ void tile_store_t(typename MM::ET* dst, int ld, int r0, int c0, f32x4 v, int lane) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dst[(c0 + (lane & 15)) * ld + r0 + 4 * (lane >> 4) + r] = MM::from_f32(v[r]);
-}
-template <class MM>
-__device__ __forceinline__ f32x4 gemm(const typename MM::ET* A, int lda, int m0, const typename MM::ET* Bt, int ldb,
-                                      int n0, int k0, int k1, f32x4 acc, int lane) {
-    for (int k = k0; k < k1; k += MM::KS)
-        acc = MM::mma(MM::load(A, lda, m0, k, lane), MM::load(Bt, ldb, n0, k, lane), acc);
-    return acc;
-}
-
 // ------------------------------------------------------------------ reverse state pass
 // Per chunk in reverse, with dS' the gradient of the state leaving the chunk:
 //   dD = KD dS' + MS^T dO,   dS = GC * dS' + QE^T dO - W^T dD
@@ -1513,7 +1493,7 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                st, p, chunk_off, slots, sb);
     }
     if (want(1) && cgrid > 0)
-        hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kThreads), 0, st,
+        hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kStateThreads), 0, st,
                            p, chunk_off, slots, sb);
     if (want(2) && cgrid > 0)
         hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,

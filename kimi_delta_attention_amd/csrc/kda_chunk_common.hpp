@@ -24,6 +24,7 @@ constexpr int kPersistentGrid = 256;
 constexpr float kSpanLimit = 85.0f;
 
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------- MFMA tiles
 // C[16x16] += A[16 x KS] * B[KS x 16] with both operands stored k-contiguous
