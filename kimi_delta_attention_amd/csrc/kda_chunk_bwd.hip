@@ -1493,7 +1493,7 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                st, p, chunk_off, slots, sb);
     }
     if (want(1) && cgrid > 0)
-        hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kStateThreads), 0, st,
+        hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kThreads), 0, st,
                            p, chunk_off, slots, sb);
     if (want(2) && cgrid > 0)
         hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,

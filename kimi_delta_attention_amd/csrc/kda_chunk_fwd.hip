@@ -37,7 +37,7 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
     if (stage < 0 || stage == 1) {
         const int grid = chain_grid(p.N * p.H, V / BV);
         if (grid > 0)
-            hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, false, true>), dim3(grid), dim3(kStateThreads), 0,
+            hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, false, true>), dim3(grid), dim3(kThreads), 0,
                                st, p, chunk_off, prep, static_cast<int64_t>(PrepLayout<K, BF>::kBytes));
     }
     return hipGetLastError();

@@ -604,42 +604,36 @@ struct Seg {
     }
 };
 
-// Threads of a state-pass workgroup: 8 waves, a pair per 16-row tile of the
-// chunk splitting the column tiles of the V block.
-constexpr int kStateThreads = 512;
 
 // Forward state pass.  Per chunk, with the chunk's operands from its slot and
 // the fp32 state S (K x BV columns of this workgroup) in MFMA accumulators:
 //   WS = W S, D = U - WS, O = QE S + MS D, S = GC * S + KD^T D.
 // STORE writes each chunk's entry state (BwdExtra::kS, element type ET) for
-// the backward; WRITE_O writes the output rows.  The A operands W, QE and MS
-// and the per-lane U and GC values go from the workspace straight to
-// registers in MFMA fragment layout (each wave reads only its own rows), and
-// each is requested for the next chunk as soon as this chunk has used it;
-// KD^T, the state and D are shared through LDS.
+// the backward; WRITE_O computes and stores the output.  The next chunk's
+// operands are prefetched into registers while the current chunk computes.
 template <int K, int V, int BV, bool BF, bool STORE, bool WRITE_O>
-__global__ __launch_bounds__(kStateThreads) void chunk_state_fwd_kernel(ChunkParams p, const int32_t* chunk_off,
-                                                                        uint8_t* ws, int64_t slot_bytes) {
+__global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p, const int32_t* chunk_off,
+                                                                   uint8_t* ws, int64_t slot_bytes) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
-    using Frag = typename MM::Frag;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
     using L = PrepLayout<K, BF>;
-    constexpr int NT = kStateThreads;
-    constexpr int NW = NT / 64;
     constexpr int LDK = K + MM::PAD;
     constexpr int LDC = kChunk + MM::PAD;
+    constexpr int LDB = BV + MM::PAD;
     constexpr int NCT = BV / 16;
     constexpr int NST = (K / 16) * NCT;
-    constexpr int SPW = (NST + NW - 1) / NW;
+    constexpr int SPW = (NST + 3) / 4;
     constexpr int NVB = V / BV;
-    constexpr int NKS = K / MM::KS;       // k-steps of a K-long contraction
-    constexpr int NCS = kChunk / MM::KS;  // k-steps of a chunk-long contraction
-    static_assert(NCT <= 2, "two column tiles at most");
+    constexpr int QR = WRITE_O ? kChunk : 0;  // rows of QE ahead of W in QW
 
+    __shared__ __attribute__((aligned(16))) ET QW[QR + kChunk][LDK];   // [QE;] W
     __shared__ __attribute__((aligned(16))) ET KDt[K][LDC];
+    __shared__ __attribute__((aligned(16))) ET MS[WRITE_O ? kChunk : 1][LDC];
     __shared__ __attribute__((aligned(16))) ET St[BV][LDK];
+    __shared__ __attribute__((aligned(16))) ET Un[kChunk][LDB];
     __shared__ __attribute__((aligned(16))) ET Dt[BV][LDC];
+    __shared__ __attribute__((aligned(16))) float gC[K];
 
     int chain, vb;
     if (!chain_of_block(blockIdx.x, p.N * p.H, NVB, chain, vb)) return;
@@ -650,151 +644,130 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_fwd_kernel(ChunkPar
     seq_bounds(p, n, start, len);
     const int nc = n_chunks(len);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int lg = lane >> 4, lc = lane & 15;
     const int v0 = vb * BV;
-    const int rt = w & 3, ct = w >> 2;    // output tile of WS, D and O
-    const bool has_ct = NCT == 2 || ct < NCT;
-    const int ctl = ct < NCT ? ct : NCT - 1;  // column tile whose U this lane reads
     const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
-    auto slot_base = [&](int jc) { return ws + ((slot0 + jc) * H + h) * slot_bytes; };
 
-    // Operands of the next chunk, in registers.  Every request is issued
-    // unconditionally and in the same order each chunk (values are converted
-    // only where used), so that waiting for one group never waits for the
-    // groups requested after it.
-    Frag fW[NKS], fQ[WRITE_O ? NKS : 1], fM[NCS];
-    ET uv[4];
-    f32x4 gcv[SPW];
-    Seg<ET, kChunk, K, true, NT> sKD;
-    auto fetch_wq = [&](const uint8_t* base) {
-#pragma unroll
-        for (int k = 0; k < NKS; ++k) {
-            fW[k] = MM::load(reinterpret_cast<const ET*>(base + L::kW), K, 16 * rt, k * MM::KS, lane);
-            if (WRITE_O) fQ[k] = MM::load(reinterpret_cast<const ET*>(base + L::kQE), K, 16 * rt, k * MM::KS, lane);
-        }
-    };
-    auto fetch_u = [&](const uint8_t* base) {
-        const ET* gU = reinterpret_cast<const ET*>(base + L::kU);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) uv[r] = gU[(16 * rt + 4 * lg + r) * V + v0 + 16 * ctl + lc];
-    };
-    auto fetch_m = [&](const uint8_t* base) {
-        if (WRITE_O) {
-#pragma unroll
-            for (int k = 0; k < NCS; ++k)
-                fM[k] = MM::load(reinterpret_cast<const ET*>(base + L::kMS), kChunk, 16 * rt, k * MM::KS, lane);
-        }
-    };
-    auto fetch_s = [&](const uint8_t* base) {
-        const float* gGC = reinterpret_cast<const float*>(base + L::kGC);
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) {
-            const int tt = w + NW * m;
-            gcv[m] = *reinterpret_cast<const f32x4*>(gGC + 16 * ((tt < NST ? tt : 0) / NCT) + 4 * lg);
-        }
+    Seg<ET, kChunk, K, false> sQE, sW;
+    Seg<ET, kChunk, K, true> sKD;
+    Seg<ET, kChunk, kChunk, false> sMS;
+    Seg<ET, kChunk, BV, false> sU;
+    Seg<float, 1, K, false> sGC;
+    auto prefetch = [&](int jc) {
+        const uint8_t* base = ws + ((slot0 + jc) * H + h) * slot_bytes;
+        if (WRITE_O) sQE.load(reinterpret_cast<const ET*>(base + L::kQE), K, t);
+        sW.load(reinterpret_cast<const ET*>(base + L::kW), K, t);
         sKD.load(reinterpret_cast<const ET*>(base + L::kKD), K, t);
+        if (WRITE_O) sMS.load(reinterpret_cast<const ET*>(base + L::kMS), kChunk, t);
+        sU.load(reinterpret_cast<const ET*>(base + L::kU) + v0, V, t);
+        sGC.load(reinterpret_cast<const float*>(base + L::kGC), K, t);
     };
 
-    // fp32 state tiles owned by this wave: tile w + NW m -> (row tile, col tile)
+    // fp32 state tiles owned by this wave: tile m -> (row tile, col tile)
     f32x4 S[SPW];
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
-        const int tt = w + NW * m;
-        const int srt = tt / NCT, sct = tt % NCT;
+        const int tt = w + 4 * m;
+        const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[m][r] = (p.h0 && tt < NST) ? p.h0[sbase + (16 * srt + 4 * lg + r) * V + v0 + 16 * sct + lc] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+            float v = 0.f;
+            if (tt < NST && p.h0) v = p.h0[sbase + (16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)];
+            S[m][r] = v;
+        }
     }
-    // the entry state has arrived before the chunk operands are requested, so
-    // no wait in the chunk loop covers requests issued after these
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
     IT* og = static_cast<IT*>(p.o);
-    if (nc > 0) {
-        const uint8_t* b0 = slot_base(0);
-        fetch_s(b0);
-        fetch_wq(b0);
-        fetch_u(b0);
-        fetch_m(b0);
-    }
+    if (nc > 0) prefetch(0);
     for (int jc = 0; jc < nc; ++jc) {
-        // the last chunk requests its own operands again (unused)
-        const uint8_t* bnext = slot_base(jc + 1 < nc ? jc + 1 : jc);
-        // KD^T and the entry state (bf16) to LDS; GC of this chunk from registers
+        if (WRITE_O) sQE.store(&QW[0][0], LDK, t);
+        sW.store(&QW[QR][0], LDK, t);
         sKD.store(&KDt[0][0], LDC, t);
-        f32x4 gcc[SPW];
-#pragma unroll
-        for (int m = 0; m < SPW; ++m) gcc[m] = gcv[m];
+        if (WRITE_O) sMS.store(&MS[0][0], LDC, t);
+        sU.store(&Un[0][0], LDB, t);
+        sGC.store(&gC[0], K, t);
         if (STORE) {
-            ET* gS = reinterpret_cast<ET*>(slot_base(jc) + BwdExtra<K, BF>::kS);
+            uint8_t* base = ws + ((slot0 + jc) * H + h) * slot_bytes;
+            ET* gS = reinterpret_cast<ET*>(base + BwdExtra<K, BF>::kS);
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
-                const int tt = w + NW * m;
-                const int srt = tt / NCT, sct = tt % NCT;
-                if (tt < NST)
+                const int tt = w + 4 * m;
+                if (tt < NST) {
+                    const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    gS[(16 * srt + 4 * lg + r) * V + v0 + 16 * sct + lc] = MM::from_f32(S[m][r]);
+                    for (int r = 0; r < 4; ++r)
+                        gS[(16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = MM::from_f32(S[m][r]);
+                }
             }
         }
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int tt = w + NW * m;
+            const int tt = w + 4 * m;
             if (tt < NST) tile_store_t<MM>(&St[0][0], LDK, 16 * (tt / NCT), 16 * (tt % NCT), S[m], lane);
         }
-        fetch_s(bnext);
         __syncthreads();
+        if (jc + 1 < nc) prefetch(jc + 1);
 
-        // WS and (scale q exp(G)) S on this wave's tile
-        f32x4 ws_ = {0.f, 0.f, 0.f, 0.f}, oq = {0.f, 0.f, 0.f, 0.f};
-        if (has_ct) {
+        // WS and (scale q exp(G)) S for this wave's 16 rows
+        f32x4 oq[NCT], ws_[NCT];
 #pragma unroll
-            for (int k = 0; k < NKS; ++k) {
-                const auto b = MM::load(&St[0][0], LDK, 16 * ct, k * MM::KS, lane);
-                ws_ = MM::mma(fW[k], b, ws_);
-                if (WRITE_O) oq = MM::mma(fQ[k], b, oq);
+        for (int ct = 0; ct < NCT; ++ct) oq[ct] = ws_[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int k0 = 0; k0 < K; k0 += MM::KS) {
+            const auto aw = MM::load(&QW[0][0], LDK, QR + 16 * w, k0, lane);
+            typename MM::Frag aq{};
+            if (WRITE_O) aq = MM::load(&QW[0][0], LDK, 16 * w, k0, lane);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const auto b = MM::load(&St[0][0], LDK, 16 * ct, k0, lane);
+                ws_[ct] = MM::mma(aw, b, ws_[ct]);
+                if (WRITE_O) oq[ct] = MM::mma(aq, b, oq[ct]);
             }
         }
-        fetch_wq(bnext);
         // D = U - W S
-        if (has_ct) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
             f32x4 d;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) d[r] = MM::to_f32(uv[r]) - ws_[r];
-            tile_store_t<MM>(&Dt[0][0], LDC, 16 * rt, 16 * ct, d, lane);
+            for (int r = 0; r < 4; ++r)
+                d[r] = MM::to_f32(Un[16 * w + 4 * (lane >> 4) + r][16 * ct + (lane & 15)]) - ws_[ct][r];
+            tile_store_t<MM>(&Dt[0][0], LDC, 16 * w, 16 * ct, d, lane);
         }
-        fetch_u(bnext);
         __syncthreads();
 
         // O = scale (q exp(G)) S + scale M D
-        if (WRITE_O && has_ct) {
+        if (WRITE_O) {
+            for (int k0 = 0; k0 < 16 * (w + 1); k0 += MM::KS) {
+                const auto a = MM::load(&MS[0][0], LDC, 16 * w, k0, lane);
 #pragma unroll
-            for (int k = 0; k < NCS; ++k)
-                if (k * MM::KS < 16 * (rt + 1))
-                    oq = MM::mma(fM[k], MM::load(&Dt[0][0], LDC, 16 * ct, k * MM::KS, lane), oq);
-            const int rb = jc * kChunk;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = 16 * rt + 4 * lg + r;
-                if (rb + row < len)
-                    Elem<IT>::store(og, ((start + rb + row) * H + h) * V + v0 + 16 * ct + lc, oq[r]);
+                for (int ct = 0; ct < NCT; ++ct)
+                    oq[ct] = MM::mma(a, MM::load(&Dt[0][0], LDC, 16 * ct, k0, lane), oq[ct]);
             }
+            const int rbase = jc * kChunk;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * w + 4 * (lane >> 4) + r;
+                    if (rbase + row < len)
+                        Elem<IT>::store(og, ((start + rbase + row) * H + h) * V + v0 + 16 * ct + (lane & 15),
+                                        oq[ct][r]);
+                }
         }
-        fetch_m(bnext);
 
         // S' = diag(exp(G_last)) S + (k exp(G_last - G))^T D
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int tt = w + NW * m;
-            const int srt = tt / NCT, sct = tt % NCT;
-            if (tt >= NST) continue;
+            const int tt = w + 4 * m;
+            if (tt < NST) {
+                const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[m][r] *= gcc[m][r];
+                for (int r = 0; r < 4; ++r) S[m][r] *= gC[16 * rt + 4 * (lane >> 4) + r];
 #pragma unroll
-            for (int k = 0; k < NCS; ++k)
-                S[m] = MM::mma(MM::load(&KDt[0][0], LDC, 16 * srt, k * MM::KS, lane),
-                               MM::load(&Dt[0][0], LDC, 16 * sct, k * MM::KS, lane), S[m]);
+                for (int k0 = 0; k0 < kChunk; k0 += MM::KS)
+                    S[m] = MM::mma(MM::load(&KDt[0][0], LDC, 16 * rt, k0, lane),
+                                   MM::load(&Dt[0][0], LDC, 16 * ct, k0, lane), S[m]);
+            }
         }
         __syncthreads();
     }
@@ -802,11 +775,13 @@ __global__ __launch_bounds__(kStateThreads) void chunk_state_fwd_kernel(ChunkPar
     if (p.ht) {
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int tt = w + NW * m;
-            const int srt = tt / NCT, sct = tt % NCT;
-            if (tt < NST)
+            const int tt = w + 4 * m;
+            if (tt < NST) {
+                const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p.ht[sbase + (16 * srt + 4 * lg + r) * V + v0 + 16 * sct + lc] = S[m][r];
+                for (int r = 0; r < 4; ++r)
+                    p.ht[sbase + (16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = S[m][r];
+            }
         }
     }
 }
