@@ -67,10 +67,17 @@ def _slot_terms(K, V, elt):
     }
 
 
-def stage_work(slots, n_seq, H, K, V, elt, with_h0=False):
-    """{stage: (bytes, flops)} for one launch over `slots` (chunk, head) slots."""
-    out = {k: (b * slots, f * slots) for k, (b, f) in _slot_terms(K, V, elt).items()}
+def stage_work(slots, n_seq, H, K, V, elt, with_h0=False, keep=True):
+    """{stage: (bytes, flops)} for one launch over `slots` (chunk, head) slots.
+    With keep the forward's prep writes the backward's operands too (as bwd.0)
+    and its state pass also stores each chunk's entry state (as bwd.1)."""
+    terms = _slot_terms(K, V, elt)
+    out = {k: (b * slots, f * slots) for k, (b, f) in terms.items()}
     st = n_seq * H * K * V * 4
+    if keep:
+        out["fwd.prep"] = out["bwd.0"]
+        b, f = out["fwd.state"]
+        out["fwd.state"] = (b + 2 * K * V * slots, f)
     b, f = out["fwd.state"]
     out["fwd.state"] = (b + st * (2 if with_h0 else 1), f)
     b, f = out["bwd.2"]
@@ -115,17 +122,23 @@ def make_hybrid(seed, device):
     return w, {k: (v.to(device) if hasattr(v, "to") else v) for k, v in w.items()}
 
 
-def chunk_op(d, with_bwd):
+def chunk_op(d, with_bwd, keep=True):
     import kimi_delta_attention_amd as kda
     return kda.ChunkOp(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"], initial_state=None,
                        output_final_state=True, use_qk_l2norm_in_kernel=True, gate_mode=d["gate_mode"],
                        use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"], lower_bound=d["lower_bound"],
-                       cu_seqlens=d["cu_seqlens"], dO=d["dO"] if with_bwd else None)
+                       cu_seqlens=d["cu_seqlens"], dO=d["dO"] if with_bwd else None,
+                       keep_for_backward=with_bwd and keep)
 
 
-def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages):
+def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages, keep=True):
+    """Mean seconds per fwd(+bwd) step and mean ms per stage.  With keep the
+    forward saves what the backward's stages 0 and 1 would recompute, and those
+    stages (which then launch nothing) are not called."""
     stream = torch.cuda.current_stream()
-    names = ["fwd.prep", "fwd.state"] + ([f"bwd.{i}" for i in range(n_bwd_stages)] if with_bwd else [])
+    first = 2 if keep else 0
+    bwd_stages = list(range(first, n_bwd_stages)) if with_bwd else []
+    names = ["fwd.prep", "fwd.state"] + [f"bwd.{i}" for i in bwd_stages]
 
     def one(op, evs):
         k = 0
@@ -134,7 +147,7 @@ def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages):
             op.forward(stage=st)
             k += 1
         if with_bwd:
-            for st in range(n_bwd_stages):
+            for st in bwd_stages:
                 evs[k].record(stream)
                 op.backward(stage=st)
                 k += 1
@@ -268,14 +281,16 @@ def run_train(steps, warmup, device):
     h0 = torch.zeros(B, H, K, K, dtype=torch.float32, device=device)
     op = kda.ChunkOp(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=d["scale"], initial_state=h0,
                      output_final_state=True, use_qk_l2norm_in_kernel=True, gate_mode=d["gate_mode"],
-                     use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"], lower_bound=d["lower_bound"], dO=d["dO"])
+                     use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"], lower_bound=d["lower_bound"], dO=d["dO"],
+                     keep_for_backward=True)
     sec, per_stage = time_chunk([op], steps, warmup, True, _lib_stages())
     tokens = B * T
     fwd_ms = per_stage["fwd.prep"] + per_stage["fwd.state"]
     pb, pf = PATH_FWDBWD
     th = tokens * H
     return {"workload": f"chunk_kda fwd+bwd, dense B{B} x T{T}, H{H}, K=V={K}, bf16 q/k/v/dO, fp32 g/beta/state, "
-                        "zero initial state passed", "tokens_per_s": tokens / sec, "ms_per_step": sec * 1e3,
+                        "zero initial state passed, forward saves for backward",
+            "tokens_per_s": tokens / sec, "ms_per_step": sec * 1e3,
             "fwd_tokens_per_s": tokens / (fwd_ms * 1e-3), "stages_ms": per_stage,
             "path_hbm_frac": pb * th / sec / 1e9 / PEAK_HBM_GBS,
             "path_mfma_frac": pf * th / sec / 1e12 / PEAK_BF16_TFLOPS}
@@ -315,9 +330,15 @@ def main():
     ops = [chunk_op(d0, True), chunk_op(d1, True)]
     _log("timing chunk path (packed T8192)")
     sec, per_stage = time_chunk(ops, args.steps, args.warmup, True, n_bwd)
+    del ops
+    torch.cuda.empty_cache()
+    _log("timing chunk path (packed T8192), backward recomputing the forward's operands")
+    ops = [chunk_op(d0, True, keep=False), chunk_op(d1, True, keep=False)]
+    sec_r, per_stage_r = time_chunk(ops, args.steps, args.warmup, True, n_bwd, keep=False)
     tokens = T_H
     n_seq = len(HYBRID_CU) - 1
-    fwd_ms = per_stage["fwd.prep"] + per_stage["fwd.state"]
+    # the inference forward (nothing saved) is the recomputing run's forward
+    fwd_ms = per_stage_r["fwd.prep"] + per_stage_r["fwd.state"]
     slots = sum((HYBRID_CU[i + 1] - HYBRID_CU[i] + C - 1) // C for i in range(n_seq)) * H_H
     work = stage_work(slots, n_seq, H_H, D_H, D_H, 2)
     # dominant kernel: the stage with the largest mean duration
@@ -337,7 +358,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "chunk_kda fwd+bwd, packed 1024/2048/1024/4096 (T8192), H16, K=V=128, "
-                               "bf16 q/k/v, fp32 g/beta/state, l2norm in kernel, log-decay gate",
+                               "bf16 q/k/v, fp32 g/beta/state, l2norm in kernel, log-decay gate, "
+                               "forward saves for backward",
                    "global_batch": n_seq, "seq_len": tokens, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "stages_ms": per_stage,
@@ -348,6 +370,7 @@ def main():
                           "fwd_tokens_per_s": tokens / (fwd_ms * 1e-3),
                           "fwd_hbm_frac": fb * th / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                           "fwd_mfma_frac": ff * th / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "recompute": {"tokens_per_s": tokens / sec_r, "ms_per_step": sec_r * 1e3, "stages_ms": per_stage_r},
     }
     del ops, d0, d1
     torch.cuda.empty_cache()

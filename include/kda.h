@@ -109,6 +109,17 @@ typedef struct {
     void *workspace;
     size_t workspace_bytes;
     void *stream;            /* hipStream_t */
+    /* Save-for-backward (0 or 1).  0: the forward keeps only its own per-chunk
+     * operands in the workspace (kda_chunk_fwd_workspace bytes) and a later
+     * kda_chunk_bwd recomputes them and every chunk's entry state.  1: the
+     * forward also writes what the backward's stages 0 and 1 would compute (the
+     * backward's per-chunk operands and each chunk's entry state) into a
+     * workspace of kda_chunk_bwd_workspace bytes (kda_chunk_fwd_workspace then
+     * returns that size), and a backward called with the flag set and the same
+     * workspace reads them instead, its stages 0 and 1 doing nothing.  Between
+     * the two calls the caller keeps the workspace and every input unchanged;
+     * the library cannot check this. */
+    int keep_for_backward;
 } kda_chunk_args;
 
 /* Gradients for kda_chunk_bwd.  dq, dk, dv are in qkv_dtype; the others fp32.

@@ -114,12 +114,19 @@ def _workspace(nbytes, dev, workspace):
 def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
               output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
               use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
-              cu_seqlens=None, gate_mode=None, workspace=None, out=None):
-    """Chunked KDA forward (kda_chunk_fwd).  Returns (o, final_state or None)."""
+              cu_seqlens=None, gate_mode=None, workspace=None, out=None, keep_for_backward=False):
+    """Chunked KDA forward (kda_chunk_fwd).  Returns (o, final_state or None).
+
+    keep_for_backward=True also stores in ``workspace`` what the backward would
+    recompute; pass the same workspace, unchanged inputs and
+    keep_for_backward=True to chunk_kda_bwd to reuse it."""
     gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
     a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
                                              output_final_state, use_qk_l2norm_in_kernel, gm,
                                              use_beta_sigmoid_in_kernel, lower_bound, chunk_size, cu_seqlens)
+    if keep_for_backward and workspace is None:
+        raise ValueError("keep_for_backward needs a caller-owned workspace (chunk_bwd_workspace_bytes)")
+    a.keep_for_backward = int(bool(keep_for_backward))
     lib = _lib.load()
     o = out if out is not None else torch.empty(B, T, H, V, dtype=q.dtype, device=dev)
     _need(o, "out", q.dtype, dev)
@@ -144,14 +151,21 @@ def chunk_fwd_workspace_bytes(q, k, v, g, beta, **kw) -> int:
 def chunk_kda_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bias=None, scale=None,
                   initial_state=None, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
                   use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
-                  cu_seqlens=None, gate_mode=None, need_d_initial_state=True, workspace=None):
+                  cu_seqlens=None, gate_mode=None, need_d_initial_state=True, workspace=None,
+                  keep_for_backward=False):
     """Chunked KDA backward (kda_chunk_bwd): gradients of <o, dO> + <final_state,
     d_final_state> w.r.t. q, k, v, g and beta as passed, the initial state and,
-    for in-kernel gates, A_log and dt_bias.  Returns a dict."""
+    for in-kernel gates, A_log and dt_bias.  Returns a dict.
+
+    keep_for_backward=True reuses what a chunk_kda(..., keep_for_backward=True)
+    call stored in the same ``workspace``."""
     gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
     a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, False,
                                              use_qk_l2norm_in_kernel, gm, use_beta_sigmoid_in_kernel,
                                              lower_bound, chunk_size, cu_seqlens)
+    if keep_for_backward and workspace is None:
+        raise ValueError("keep_for_backward needs the workspace the forward wrote")
+    a.keep_for_backward = int(bool(keep_for_backward))
     _need(dO, "dO", q.dtype, dev)
     _need(d_final_state, "d_final_state", torch.float32, dev)
     lib = _lib.load()
@@ -231,17 +245,24 @@ class ChunkOp:
     """A prepared chunk_kda call: the C argument structs, outputs and workspace
     are built once, so repeated calls (benchmarks, training loops) pay no
     Python marshalling.  ``forward(stage)`` / ``backward(stage)`` run the whole
-    operator (stage None) or one stage of it (for per-kernel timing)."""
+    operator (stage None) or one stage of it (for per-kernel timing).  With
+    keep_for_backward=True (and dO given) the forward stores what the backward
+    would recompute and the backward reuses it: call forward before backward,
+    with the inputs unchanged in between."""
 
     def __init__(self, q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
                  output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
                  use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
-                 cu_seqlens=None, gate_mode=None, dO=None, d_final_state=None, need_d_initial_state=True):
+                 cu_seqlens=None, gate_mode=None, dO=None, d_final_state=None, need_d_initial_state=True,
+                 keep_for_backward=False):
         gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
         self._keep = [q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dO, d_final_state]
         a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
                                                  output_final_state, use_qk_l2norm_in_kernel, gm,
                                                  use_beta_sigmoid_in_kernel, lower_bound, chunk_size, cu_seqlens)
+        if keep_for_backward and dO is None:
+            raise ValueError("keep_for_backward needs dO")
+        a.keep_for_backward = int(bool(keep_for_backward))
         lib = _lib.load()
         self.lib = lib
         self.o = torch.empty(B, T, H, V, dtype=q.dtype, device=dev)

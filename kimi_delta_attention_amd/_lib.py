@@ -33,6 +33,7 @@ class ChunkArgs(ctypes.Structure):
         ("o", _vp), ("final_state", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("stream", _vp),
+        ("keep_for_backward", ctypes.c_int),
     ]
 
 

@@ -25,6 +25,7 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forwar
     if (a->gate_mode < KDA_GATE_LOGDECAY || a->gate_mode > KDA_GATE_SOFTPLUS) return KDA_ERR_INVALID_ARG;
     if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return KDA_ERR_INVALID_ARG;
     if (a->use_beta_sigmoid != 0 && a->use_beta_sigmoid != 1) return KDA_ERR_INVALID_ARG;
+    if (a->keep_for_backward != 0 && a->keep_for_backward != 1) return KDA_ERR_INVALID_ARG;
     int N = a->B;
     if (a->cu_seqlens) {
         if (a->B != 1 || a->N <= 0) return KDA_ERR_INVALID_ARG;
@@ -61,6 +62,7 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forwar
     const int64_t nc_dense = (static_cast<int64_t>(a->T) + 63) / 64;
     const int64_t bound = a->cu_seqlens ? nc_dense + N : nc_dense * N;
     if (bound * a->H > INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
+    p.keep = a->keep_for_backward != 0;
     p.max_chunks = static_cast<int>(nc_dense);
     p.total_chunks_bound = static_cast<int>(bound);
     return KDA_OK;
@@ -87,14 +89,14 @@ int kda_version(void) { return kVersion; }
 size_t kda_chunk_fwd_workspace(const kda_chunk_args* a) {
     kda::ChunkParams p{};
     if (check_chunk(a, p, true) != KDA_OK) return 0;
-    return kda::chunk_fwd_workspace(p);
+    return p.keep ? kda::chunk_bwd_workspace(p) : kda::chunk_fwd_workspace(p);
 }
 
 static kda_status chunk_fwd_impl(const kda_chunk_args* a, int stage) {
     kda::ChunkParams p{};
     kda_status st = check_chunk(a, p, true);
     if (st != KDA_OK) return st;
-    const size_t need = kda::chunk_fwd_workspace(p);
+    const size_t need = p.keep ? kda::chunk_bwd_workspace(p) : kda::chunk_fwd_workspace(p);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     if (a->workspace && !aligned16(a->workspace)) return KDA_ERR_WORKSPACE;
     hipError_t e = kda::launch_chunk_fwd(p, a->workspace, static_cast<hipStream_t>(a->stream), stage);

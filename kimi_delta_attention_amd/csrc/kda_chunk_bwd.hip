@@ -1484,7 +1484,8 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
     const int64_t sb = static_cast<int64_t>(X::kBytes);
     const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
     const int cgrid = chain_grid(p.N * p.H, V / BV);
-    auto want = [stage](int s) { return stage < 0 || stage == s; };
+    // with p.keep the forward has already done stages 0 and 1
+    auto want = [stage, &p](int s) { return (stage < 0 || stage == s) && !(p.keep && s < 2); };
     if (want(0)) {
         if (p.cu_seqlens)
             hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);

@@ -21,36 +21,45 @@ size_t chunk_fwd_workspace(const ChunkParams& p) {
     return chunk_off_bytes(p) + prep;
 }
 
-template <int K, int V, int BV, bool BF>
+// KEEP writes the backward's slot layout (BwdExtra): the prep also stores
+// KE, T and AK, and the state pass also stores every chunk's entry state, so
+// that the backward can skip its stages 0 and 1.
+template <int K, int V, int BV, bool BF, bool KEEP>
 static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage) {
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     int32_t* chunk_off = reinterpret_cast<int32_t*>(w8);
     uint8_t* prep = w8 + chunk_off_bytes(p);
+    const int64_t sb = static_cast<int64_t>(KEEP ? BwdExtra<K, BF>::kBytes : PrepLayout<K, BF>::kBytes);
     if (stage < 0 || stage == 0) {
         if (p.cu_seqlens)
             hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
         const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
         if (nblk > 0)
-            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, false>), dim3(static_cast<unsigned>(nblk)), dim3(prep_threads(K)),
-                               0, st, p, chunk_off, prep, static_cast<int64_t>(PrepLayout<K, BF>::kBytes));
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, KEEP>), dim3(static_cast<unsigned>(nblk)), dim3(prep_threads(K)),
+                               0, st, p, chunk_off, prep, sb);
     }
     if (stage < 0 || stage == 1) {
         const int grid = chain_grid(p.N * p.H, V / BV);
         if (grid > 0)
-            hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, false, true>), dim3(grid), dim3(kThreads), 0,
-                               st, p, chunk_off, prep, static_cast<int64_t>(PrepLayout<K, BF>::kBytes));
+            hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, KEEP, true>), dim3(grid), dim3(kThreads), 0,
+                               st, p, chunk_off, prep, sb);
     }
     return hipGetLastError();
+}
+
+template <int K, int V, int BV, bool BF>
+static hipError_t run_fwd_any(const ChunkParams& p, void* ws, hipStream_t st, int stage) {
+    return p.keep ? run_fwd<K, V, BV, BF, true>(p, ws, st, stage) : run_fwd<K, V, BV, BF, false>(p, ws, st, stage);
 }
 
 hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage) {
     if (p.K != p.V) return hipErrorInvalidValue;
     switch (p.K) {
         case 32:
-            return p.bf16 ? run_fwd<32, 32, 16, true>(p, ws, st, stage) : run_fwd<32, 32, 16, false>(p, ws, st, stage);
+            return p.bf16 ? run_fwd_any<32, 32, 16, true>(p, ws, st, stage) : run_fwd_any<32, 32, 16, false>(p, ws, st, stage);
         case 64:
-            return p.bf16 ? run_fwd<64, 64, 32, true>(p, ws, st, stage) : run_fwd<64, 64, 32, false>(p, ws, st, stage);
-        case 128: return p.bf16 ? run_fwd<128, 128, 32, true>(p, ws, st, stage) : hipErrorInvalidValue;
+            return p.bf16 ? run_fwd_any<64, 64, 32, true>(p, ws, st, stage) : run_fwd_any<64, 64, 32, false>(p, ws, st, stage);
+        case 128: return p.bf16 ? run_fwd_any<128, 128, 32, true>(p, ws, st, stage) : hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }

@@ -53,6 +53,7 @@ struct ChunkParams {
     float* ht;                 // [N,H,K,V] or nullptr
     int max_chunks;            // upper bound of chunks per sequence
     int total_chunks_bound;    // upper bound of sum over sequences of chunks
+    bool keep;                 // forward writes the backward's slot layout; backward reuses it
 };
 
 struct ChunkGrads {
@@ -68,13 +69,15 @@ struct ChunkGrads {
     float* ddt_bias;           // or nullptr
 };
 
-size_t chunk_fwd_workspace(const ChunkParams& p);
-// stage < 0 runs every stage; 0 = prep, 1 = state pass.
+size_t chunk_fwd_workspace(const ChunkParams& p);  // of the forward's own layout
+// stage < 0 runs every stage; 0 = prep, 1 = state pass.  With p.keep the
+// forward writes the backward's layout (chunk_bwd_workspace bytes).
 hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage = -1);
 
 size_t chunk_bwd_workspace(const ChunkParams& p);
 // stage < 0 runs every stage; 0 prep, 1 state pass (stores states), 2 reverse
-// state pass, 3 V-local gradients, 4 K-local gradients.
+// state pass, 3 V-local gradients, 4 K-local gradients.  With p.keep stages 0
+// and 1 were done by the forward and launch nothing.
 constexpr int kBwdStages = 5;
 hipError_t launch_chunk_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st, int stage = -1);
 

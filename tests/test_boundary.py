@@ -73,6 +73,7 @@ def _args(**over):
     (dict(gate_mode=_lib.KDA_GATE_SAFE, A_log=FAKE), _lib.KDA_ERR_MISSING_PARAM),
     (dict(output_final_state=1), _lib.KDA_ERR_INVALID_ARG),
     (dict(cu_seqlens=FAKE, B=2, N=2), _lib.KDA_ERR_INVALID_ARG),
+    (dict(keep_for_backward=2), _lib.KDA_ERR_INVALID_ARG),
     (dict(), _lib.KDA_ERR_WORKSPACE),                         # workspace required, none given
 ])
 def test_chunk_fwd_rejects_before_launch(lib, over, status):
@@ -89,6 +90,20 @@ def test_workspace_query_is_host_only(lib):
     assert lib.kda_chunk_fwd(ctypes.byref(a)) == _lib.KDA_ERR_WORKSPACE
     bad = _args(chunk_size=16)
     assert lib.kda_chunk_fwd_workspace(ctypes.byref(bad)) == 0
+
+
+def test_keep_for_backward_needs_the_backward_workspace(lib):
+    # the saving forward writes the backward's layout, so it asks for (and
+    # checks against) the backward's workspace size
+    a = _args()
+    need_fwd = lib.kda_chunk_fwd_workspace(ctypes.byref(a))
+    need_bwd = lib.kda_chunk_bwd_workspace(ctypes.byref(a))
+    assert need_bwd > need_fwd > 0
+    k = _args(keep_for_backward=1)
+    assert lib.kda_chunk_fwd_workspace(ctypes.byref(k)) == need_bwd
+    k.workspace = FAKE
+    k.workspace_bytes = need_fwd
+    assert lib.kda_chunk_fwd(ctypes.byref(k)) == _lib.KDA_ERR_WORKSPACE
 
 
 def test_chunk_bwd_rejects_before_launch(lib):

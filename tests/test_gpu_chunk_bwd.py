@@ -142,3 +142,41 @@ def test_bwd_deterministic():
     b = _gpu_bwd(w)
     for name in NAMES:
         assert torch.equal(a[name], b[name]), name
+
+
+@pytest.mark.parametrize("case", ["bf16_128_varlen_tail", "f32_32_softplus_h0", "bf16_64_safe_dfinal"])
+def test_bwd_reuses_saved_forward(case):
+    """A forward with keep_for_backward writes what the backward's first two
+    stages compute; the backward with the flag skips them.  Same kernels, same
+    inputs: o, the final state and every gradient are bit-identical to the
+    recomputing path, which the other tests check against the oracle."""
+    if case == "bf16_128_varlen_tail":
+        w = inputs.chunk_inputs(1, 300, 2, 128, 128, seed=71, dtype=torch.bfloat16, cu_seqlens=[0, 100, 300],
+                                with_grad_out=True, h0_std=0.1)
+    elif case == "f32_32_softplus_h0":
+        w = inputs.chunk_inputs(2, 130, 2, 32, 32, seed=72, gate_mode=inputs.GATE_SOFTPLUS, beta_logits=True,
+                                h0_std=0.1, with_grad_out=True, dfinal_std=0.1)
+    else:
+        w = inputs.chunk_inputs(2, 97, 2, 64, 64, seed=73, dtype=torch.bfloat16, gate_mode=inputs.GATE_SAFE,
+                                with_grad_out=True, dfinal_std=0.1)
+    print(f"saved-forward {case}", flush=True)
+    kw = dict(A_log=dev(w["A_log"]), dt_bias=dev(w["dt_bias"]), scale=w["scale"],
+              initial_state=dev(w["initial_state"]), use_qk_l2norm_in_kernel=True, gate_mode=w["gate_mode"],
+              use_beta_sigmoid_in_kernel=w["use_beta_sigmoid"], lower_bound=w["lower_bound"],
+              cu_seqlens=dev(w["cu_seqlens"]))
+    q, k, v, g, beta, dO = (dev(w[n]) for n in ("q", "k", "v", "g", "beta", "dO"))
+    nb = kda.chunk_bwd_workspace_bytes(q, k, v, g, beta, **kw)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    o0, s0 = kda.chunk_kda(q, k, v, g, beta, output_final_state=True, **kw)
+    ref = kda.chunk_kda_bwd(q, k, v, g, beta, dO, d_final_state=dev(w["d_final_state"]), **kw)
+    o1, s1 = kda.chunk_kda(q, k, v, g, beta, output_final_state=True, workspace=ws, keep_for_backward=True, **kw)
+    got = kda.chunk_kda_bwd(q, k, v, g, beta, dO, d_final_state=dev(w["d_final_state"]), workspace=ws,
+                            keep_for_backward=True, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(s0, s1)
+    for name in NAMES + (["dA_log", "ddt_bias"] if w["gate_mode"] != inputs.GATE_LOGDECAY else []):
+        assert torch.equal(ref[name], got[name]), name
+    if case == "bf16_128_varlen_tail":
+        o = _oracle_bwd(w)
+        for name in NAMES:
+            check(f"saved {name}", got[name], o[name], tol_for(w["q"].dtype))
