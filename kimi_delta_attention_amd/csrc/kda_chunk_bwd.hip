@@ -1440,6 +1440,599 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
     }
 }
 
+// ------------------------------------------------------------------ K-local gradients, 8 waves (K = 128)
+// The computation of chunk_bwd_klocal_mfma_kernel with one 16-column tile per
+// wave: 8 waves, two per SIMD, so that one wave's LDS and memory latency
+// overlaps another's work.  In the score-rule products (contraction order
+// permuted as in mma16_f32) each lane's four B values per step lie in its own
+// rows and column of the tile, so the B operands (k b), (q a), (k a) are
+// formed in registers; only the fp32 score gradients dM and dA are shared
+// through LDS.  The tile's dQE, dKE, dKD are requested at the start of the
+// slot and staged one array at a time through a 2 KB buffer per wave.
+struct KlocW8Smem {
+    using ET = uint16_t;
+    static constexpr int K = 128;
+    static constexpr int LDE = K + 8;
+    static constexpr int LDC = kChunk + 8;
+    static constexpr int LDG = K + 4;
+    static constexpr int LDD = kChunk + 4;
+    ET qh[kChunk][LDE];
+    ET kh[kChunk][LDE];
+    float G[kChunk][LDG];
+    union alignas(16) {
+        struct {
+            ET Tn[kChunk][LDC];
+            ET Tt[kChunk][LDC];
+            ET dTt[kChunk][LDC];
+            ET Zn[kChunk][LDC];
+        } mm;
+        struct {
+            float dM[kChunk][LDD];  // scale * dMS (lower incl. diagonal)
+            float dA[kChunk][LDD];  // diag(beta) dA (strictly lower)
+        } sc;
+    } x;
+    ET ew[8][kChunk][16];
+    float invP[4][K];
+    float F20[K], F30[K], F31[K];
+    float beta[kChunk], rq[kChunk], rk[kChunk];
+    float dbc[8][kChunk];
+    float dbr[2][kChunk];
+    float dots[2][8][kChunk];
+    float ddt[K];
+    float gpa[8];
+    int unsafe[4];
+};
+
+// fp32 16 x 16 x 16 product with the lane's four B values given (step st
+// uses b[st], the B element at contraction index k0 + 4 (lane / 16) + st);
+// TRANS_A reads A[k][m] instead of A[m][k].
+template <bool TRANS_A>
+__device__ __forceinline__ f32x4 mma16_f32_rb(const float* A, int lda, int m0, const float* b, int k0, int lane) {
+    const int m = m0 + (lane & 15), kq = k0 + 4 * (lane >> 4);
+    float4 a4;
+    if (TRANS_A) {
+        a4.x = A[(kq + 0) * lda + m];
+        a4.y = A[(kq + 1) * lda + m];
+        a4.z = A[(kq + 2) * lda + m];
+        a4.w = A[(kq + 3) * lda + m];
+    } else {
+        a4 = *reinterpret_cast<const float4*>(A + m * lda + kq);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, b[3], acc, 0, 0, 0);
+    return acc;
+}
+
+constexpr int kKlocW8Threads = 512;
+
+__global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(ChunkParams p, ChunkGrads gr,
+                                                                            const int32_t* chunk_off, uint8_t* ws,
+                                                                            int64_t slot_bytes, int nblk) {
+    using MM = Mma<true>;
+    using ET = uint16_t;
+    constexpr int K = 128;
+    using X = BwdExtra<K, true>;
+    using SM = KlocW8Smem;
+    constexpr int NT = kKlocW8Threads;
+    constexpr int NW = NT / 64;
+    constexpr int LDC = SM::LDC;
+    constexpr int LDD = SM::LDD;
+    constexpr int TPR = NT / kChunk;  // threads per row in the prologue
+    constexpr int CPT = K / TPR;
+    static_assert(NW * 16 == K, "one 16-column tile per wave");
+    __shared__ __attribute__((aligned(16))) SM s;
+
+    const int H = p.H;
+
+    for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        // The thread index passes through an empty asm each slot, so the
+        // per-lane LDS addresses derived from it are recomputed per slot
+        // rather than hoisted out of the loop (where they would be spilled).
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        const int lane = t & 63, w = t >> 6;
+        const int lg = lane >> 4, lc = lane & 15;
+        const int c = 16 * w + lc;  // this lane's channel in the tile phase
+        const int slot = blk / H;
+        const int h = blk % H;
+        int n, j;
+        if (!slot_to_chunk(p, chunk_off, slot, n, j)) break;  // slots past the last chunk are all empty
+        int64_t start;
+        int len;
+        seq_bounds(p, n, start, len);
+        const int rows = min(kChunk, len - j * kChunk);
+        uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
+        const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
+        const float rate = (p.gate_mode == GATE_LOGDECAY) ? 0.f : __expf(p.A_log[h]);
+        __syncthreads();  // the previous slot is done with the shared buffers
+
+        // ---- 0. prologue (row-wise), cumulative sum, sub-block factors
+        {
+            const int i = t / TPR, c0 = (t % TPR) * CPT;
+            const bool valid = i < rows;
+            float qv[CPT], kv[CPT], gv[CPT];
+            float braw = 0.f;
+            if (valid) {
+                const int64_t off = ((rbase + i) * H + h) * K + c0;
+                braw = p.beta[(rbase + i) * H + h];
+                load_row<CPT>(static_cast<const uint16_t*>(p.q) + off, qv);
+                load_row<CPT>(static_cast<const uint16_t*>(p.k) + off, kv);
+                load_row<CPT>(p.g + off, gv);
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) qv[cc] = kv[cc] = gv[cc] = 0.f;
+            }
+            float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < CPT; ++cc) {
+                ssq += qv[cc] * qv[cc];
+                ssk += kv[cc] * kv[cc];
+            }
+#pragma unroll
+            for (int o = 1; o < TPR; o <<= 1) {
+                ssq += __shfl_xor(ssq, o, 64);
+                ssk += __shfl_xor(ssk, o, 64);
+            }
+            float rq = 1.f, rk = 1.f;
+            if (p.use_qk_l2norm) {
+                rq = rsqrtf(ssq + kL2Eps);
+                rk = rsqrtf(ssk + kL2Eps);
+            }
+            if (!valid) rq = rk = 0.f;
+            if (p.gate_mode != GATE_LOGDECAY) {
+                const float* bias = p.dt_bias ? p.dt_bias + h * K + c0 : nullptr;
+#pragma unroll 4
+                for (int cc = 0; cc < CPT; ++cc)
+                    gv[cc] = valid ? gate_eff(p.gate_mode, gv[cc], rate, bias ? bias[cc] : 0.f, p.lower_bound) : 0.f;
+            }
+#pragma unroll
+            for (int v = 0; v < CPT / 8; ++v) {
+                u16x8 uq, uk;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uq[e] = MM::from_f32(qv[8 * v + e] * rq);
+                    uk[e] = MM::from_f32(kv[8 * v + e] * rk);
+                }
+                *reinterpret_cast<u16x8*>(&s.qh[i][c0 + 8 * v]) = uq;
+                *reinterpret_cast<u16x8*>(&s.kh[i][c0 + 8 * v]) = uk;
+            }
+#pragma unroll
+            for (int v = 0; v < CPT / 4; ++v)
+                *reinterpret_cast<f32x4*>(&s.G[i][c0 + 4 * v]) =
+                    f32x4{gv[4 * v], gv[4 * v + 1], gv[4 * v + 2], gv[4 * v + 3]};
+            if (t % TPR == 0) {
+                s.rq[i] = rq;
+                s.rk[i] = rk;
+                s.beta[i] = (valid && p.use_beta_sigmoid) ? sigmoidf_(braw) : braw;
+            }
+            if (t < 4) s.unsafe[t] = 0;
+        }
+        __syncthreads();
+        {
+            constexpr int SEGS = NT / K;
+            constexpr int SEGLEN = kChunk / SEGS;
+            const int cc = t % K, sg = t / K;
+            float acc = 0.f;
+            for (int r = sg * SEGLEN; r < (sg + 1) * SEGLEN; ++r) {
+                acc += s.G[r][cc];
+                s.G[r][cc] = acc;
+            }
+            __syncthreads();
+            float off = 0.f;
+            for (int q = 0; q < sg; ++q) off += s.G[(q + 1) * SEGLEN - 1][cc];
+            __syncthreads();
+            if (sg > 0)
+                for (int r = sg * SEGLEN; r < (sg + 1) * SEGLEN; ++r) s.G[r][cc] += off;
+        }
+        __syncthreads();
+        if (t < K) {
+            float P[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const float Gref = I == 0 ? 0.f : s.G[kSub * I - 1][t];
+                const float span = Gref - s.G[kSub * I + kSub - 1][t];
+                P[I] = __expf(-span);
+                s.invP[I][t] = __expf(span);
+                if (!(span <= kSpanLimit)) s.unsafe[I] = 1;
+            }
+            s.F20[t] = P[1];
+            s.F31[t] = P[2];
+            s.F30[t] = P[1] * P[2];
+        }
+
+        // ---- 1. dA = -T^T (dTB diag(beta)) T^T and the beta terms of TB and A.
+        // Thread t owns column t % 64 of rows t / 64 + 8 e of T, dTB and dMS;
+        // wave w owns the dA tiles (w % 4, w / 4) and (w % 4, w / 4 + 2).
+        const int rt = w & 3, ch = w >> 2;
+        ET tv[8], tbv[8], msv[8], akv[8];
+        {
+            const ET* gT = reinterpret_cast<const ET*>(base + X::kT);
+            const ET* gTB = reinterpret_cast<const ET*>(base + X::kDTB);
+            const ET* gMS = reinterpret_cast<const ET*>(base + X::kDMS);
+            const ET* gAK = reinterpret_cast<const ET*>(base + X::kAK);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                tv[e] = gT[t + NT * e];
+                tbv[e] = gTB[t + NT * e];
+                msv[e] = gMS[t + NT * e];
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    akv[4 * m + r] = gAK[(16 * rt + 4 * lg + r) * kChunk + 16 * (ch + 2 * m) + lc];
+        }
+        {
+            float part = 0.f;  // column t % 64
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int a = (t >> 6) + 8 * e, b = t & 63;
+                s.x.mm.Tn[a][b] = tv[e];
+                s.x.mm.Tt[b][a] = tv[e];
+                const float dtb = (b <= a) ? MM::to_f32(tbv[e]) : 0.f;
+                part += dtb * MM::to_f32(tv[e]);
+                s.x.mm.dTt[b][a] = MM::from_f32(dtb * s.beta[b]);
+            }
+            s.dbc[w][t & 63] = part;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            z = gemm<MM>(&s.x.mm.Tt[0][0], LDC, 16 * rt, &s.x.mm.dTt[0][0], LDC, 16 * (ch + 2 * m), 0, kChunk, z, lane);
+            tile_store<MM>(&s.x.mm.Zn[0][0], LDC, 16 * rt, 16 * (ch + 2 * m), z, lane);
+        }
+        __syncthreads();
+        f32x4 da[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            da[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            da[m] = gemm<MM>(&s.x.mm.Zn[0][0], LDC, 16 * rt, &s.x.mm.Tn[0][0], LDC, 16 * (ch + 2 * m), 0, kChunk,
+                             da[m], lane);
+        }
+        __syncthreads();  // the score gradients below overlay T and Z
+        {
+            float rowp[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * rt + 4 * lg + r, jj = 16 * (ch + 2 * m) + lc;
+                    const float dAv = (jj < i) ? -da[m][r] : 0.f;
+                    rowp[r] += dAv * MM::to_f32(akv[4 * m + r]);
+                    s.x.sc.dA[i][jj] = dAv * s.beta[i];
+                }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = rowp[r];
+                v += __shfl_xor(v, 1, 64);
+                v += __shfl_xor(v, 2, 64);
+                v += __shfl_xor(v, 4, 64);
+                v += __shfl_xor(v, 8, 64);
+                if (lc == 0) s.dbr[ch][16 * rt + 4 * lg + r] = v;
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int a = (t >> 6) + 8 * e, b = t & 63;
+                s.x.sc.dM[a][b] = (b <= a) ? p.scale * MM::to_f32(msv[e]) : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ---- 2. this wave's column tile: score rule, element-wise terms, reverse cumsum, gate rule
+        // this wave's tile of dQE, dKE, dKD (64 rows x 32 bytes each), requested at
+        // the start of the tile phase: vector v = lane + 64 hf holds row v / 2, columns 8 (v % 2) .. +7
+        uint4 ewv[6];
+        {
+            const ET* gQE = reinterpret_cast<const ET*>(base + X::kDQE);
+            const ET* gKE = reinterpret_cast<const ET*>(base + X::kDKE);
+            const ET* gKD = reinterpret_cast<const ET*>(base + X::kDKD);
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int v = lane + 64 * hf;
+                const int off = (v >> 1) * K + 16 * w + 8 * (v & 1);
+                ewv[hf] = *reinterpret_cast<const uint4*>(gQE + off);
+                ewv[2 + hf] = *reinterpret_cast<const uint4*>(gKE + off);
+                ewv[4 + hf] = *reinterpret_cast<const uint4*>(gKD + off);
+            }
+        }
+
+        float dal = 0.f;
+        f32x4 dq[4], dk[4];
+        {
+            float Gc[16], qo[16], ko[16];  // the lane's rows 16 I + 4 lg + r of column c
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    Gc[4 * I + r] = s.G[i][c];
+                    qo[4 * I + r] = MM::to_f32(s.qh[i][c]);
+                    ko[4 * I + r] = MM::to_f32(s.kh[i][c]);
+                }
+            float Ge[4], Gr[4], invp[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                Ge[I] = s.G[kSub * I + kSub - 1][c];
+                Gr[I] = I == 0 ? 0.f : s.G[kSub * I - 1][c];
+                invp[I] = s.unsafe[I] ? 0.f : s.invP[I][c];
+            }
+            const float f20 = s.F20[c], f30 = s.F30[c], f31 = s.F31[c];
+            auto fac = [&](int J, int I) -> float {
+                if (J == I) return invp[I];
+                if (J == I - 1) return 1.f;
+                if (I == 2) return f20;
+                return J == 0 ? f30 : f31;
+            };
+            f32x4 dG[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) dq[I] = dk[I] = dG[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            // P terms: P_x[I] = a_I * sum_J f(J, I) dX_IJ (k b)_J,  b_j = e^(G_end(J) - G_j)
+            float bv[16];
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) bv[4 * J + r] = ko[4 * J + r] * __expf(Ge[J] - Gc[4 * J + r]);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int J = 0; J <= I; ++J) {
+                    const float f = fac(J, I);
+                    const f32x4 aq = mma16_f32_rb<false>(&s.x.sc.dM[0][0], LDD, kSub * I, &bv[4 * J], kSub * J, lane);
+                    const f32x4 ak = mma16_f32_rb<false>(&s.x.sc.dA[0][0], LDD, kSub * I, &bv[4 * J], kSub * J, lane);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        pq[r] += f * aq[r];
+                        pk[r] += f * ak[r];
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float a_ = __expf(Gc[4 * I + r] - Gr[I]);
+                    const float Pq = a_ * pq[r], Pk = a_ * pk[r];
+                    dq[I][r] += Pq;
+                    dk[I][r] += Pk;
+                    dG[I][r] += qo[4 * I + r] * Pq + ko[4 * I + r] * Pk;
+                }
+            }
+
+            // R terms: (q a) against dM, then (k a) against dA, a_i = e^(G_i - G_ref(I))
+            f32x4 rr[4];
+#pragma unroll
+            for (int J = 0; J < 4; ++J) rr[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        bv[4 * I + r] = (pass == 0 ? qo[4 * I + r] : ko[4 * I + r]) * __expf(Gc[4 * I + r] - Gr[I]);
+                const float* dX = pass == 0 ? &s.x.sc.dM[0][0] : &s.x.sc.dA[0][0];
+#pragma unroll
+                for (int J = 0; J < 4; ++J)
+#pragma unroll
+                    for (int I = J; I < 4; ++I) {
+                        const float f = fac(J, I);
+                        const f32x4 acc = mma16_f32_rb<true>(dX, LDD, kSub * J, &bv[4 * I], kSub * I, lane);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) rr[J][r] += f * acc[r];
+                    }
+            }
+#pragma unroll
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float R = __expf(Ge[J] - Gc[4 * J + r]) * rr[J][r];
+                    dk[J][r] += R;
+                    dG[J][r] -= ko[4 * J + r] * R;
+                }
+
+            // diagonal sub-blocks too wide to factorise: pairwise from G
+            if (s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3]) {
+#pragma unroll 1
+                for (int I = 0; I < 4; ++I) {
+                    if (!s.unsafe[I]) continue;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int xr = 4 * lg + r, i = kSub * I + xr;
+                        const float Gi = s.G[i][c];
+                        float Pq = 0.f, Pk = 0.f, R = 0.f;
+#pragma unroll 1
+                        for (int y = 0; y < kSub; ++y) {
+                            const int jr = kSub * I + y;
+                            const float Gj = s.G[jr][c];
+                            if (y <= xr) {
+                                const float e = __expf(Gi - Gj) * MM::to_f32(s.kh[jr][c]);
+                                Pq += s.x.sc.dM[i][jr] * e;
+                                Pk += s.x.sc.dA[i][jr] * e;
+                            }
+                            if (y >= xr) {
+                                const float e = __expf(Gj - Gi);
+                                R += (s.x.sc.dM[jr][i] * MM::to_f32(s.qh[jr][c]) +
+                                      s.x.sc.dA[jr][i] * MM::to_f32(s.kh[jr][c])) * e;
+                            }
+                        }
+                        const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
+#pragma unroll
+                        for (int II = 0; II < 4; ++II)
+                            if (II == I) {
+                                dq[II][r] += Pq;
+                                dk[II][r] += Pk + R;
+                                dG[II][r] += q_ * Pq + k_ * Pk - k_ * R;
+                            }
+                    }
+                }
+            }
+
+            // element-wise terms of QE, KE, KD and d(G_last); the operands pass
+            // through the wave's 2 KB buffer one array at a time
+            const float Glast = s.G[kChunk - 1][c];
+            float E[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) E[q] = __expf(Gc[q]);
+            ET (*eww)[16] = s.ew[w];
+            float colp = 0.f;
+#pragma unroll
+            for (int a3 = 0; a3 < 3; ++a3) {
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int v = lane + 64 * hf;
+                    *reinterpret_cast<uint4*>(&eww[v >> 1][8 * (v & 1)]) = ewv[2 * a3 + hf];
+                }
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int q = 4 * I + r;
+                        const float x_ = MM::to_f32(eww[kSub * I + 4 * lg + r][lc]);
+                        if (a3 == 0) {
+                            dq[I][r] += p.scale * x_ * E[q];
+                            dG[I][r] += x_ * p.scale * qo[q] * E[q];
+                        } else if (a3 == 1) {
+                            dk[I][r] += x_ * E[q];
+                            dG[I][r] += x_ * ko[q] * E[q];
+                        } else {
+                            const float Ed = __expf(Glast - Gc[q]);
+                            const float KD = ko[q] * Ed;
+                            dk[I][r] += x_ * Ed;
+                            dG[I][r] -= x_ * KD;
+                            colp += x_ * KD;
+                        }
+                    }
+            }
+            colp += __shfl_xor(colp, 16, 64);
+            colp += __shfl_xor(colp, 32, 64);
+            if (lg == 3)
+                dG[3][3] += colp + reinterpret_cast<const float*>(base + X::kDGAM)[c] * __expf(Glast);
+
+            // reverse cumulative sum over the 64 rows of this column
+            float carry = 0.f;
+#pragma unroll
+            for (int I = 3; I >= 0; --I) {
+                dG[I][2] += dG[I][3];
+                dG[I][1] += dG[I][2];
+                dG[I][0] += dG[I][1];
+                const float own = dG[I][0];
+                const float up1 = __shfl(own, (lane + 16) & 63, 64);
+                const float up2 = __shfl(own, (lane + 32) & 63, 64);
+                const float up3 = __shfl(own, (lane + 48) & 63, 64);
+                float add = carry;
+                if (lg < 3) add += up1;
+                if (lg < 2) add += up2;
+                if (lg < 1) add += up3;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dG[I][r] += add;
+                carry = __shfl(dG[I][0], lc, 64);  // suffix sum from row 16 I
+            }
+
+            // gate chain rule
+            const float bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias[h * K + c] : 0.f;
+            float ddt = 0.f;
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    if (i < rows) {
+                        const int64_t gi = ((rbase + i) * H + h) * K + c;
+                        const float dge = dG[I][r];
+                        float dx = dge;
+                        if (p.gate_mode != GATE_LOGDECAY) {
+                            const float z = p.g[gi] + bias;
+                            if (p.gate_mode == GATE_SAFE) {
+                                const float sg = sigmoidf_(rate * z);
+                                const float b_ = p.lower_bound * sg * (1.f - sg);
+                                dx = dge * b_ * rate;
+                                dal += dge * b_ * rate * z;
+                            } else {
+                                dx = -dge * rate * sigmoidf_(z);
+                                dal += -dge * rate * softplusf_(z);
+                            }
+                            ddt += dx;
+                        }
+                        gr.dg[gi] = dx;
+                    }
+                }
+            ddt += __shfl_xor(ddt, 16, 64);
+            ddt += __shfl_xor(ddt, 32, 64);
+            if (lg == 0) s.ddt[c] = ddt;
+
+            // row dot products of the L2-norm rule
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float vq = qo[4 * I + r] * dq[I][r];
+                    float vk = ko[4 * I + r] * dk[I][r];
+#pragma unroll
+                    for (int o = 1; o < 16; o <<= 1) {
+                        vq += __shfl_xor(vq, o, 64);
+                        vk += __shfl_xor(vk, o, 64);
+                    }
+                    if (lc == 0) {
+                        s.dots[0][w][kSub * I + 4 * lg + r] = vq;
+                        s.dots[1][w][kSub * I + 4 * lg + r] = vk;
+                    }
+                }
+        }
+
+        // ---- 3. L2-norm and sigmoid chain rules, gate shares, stores
+        __syncthreads();  // dots and ddt are complete
+        if (t < 2 * kChunk) {  // row totals of the dot products, kept in tile slot 0
+            const int i = t & (kChunk - 1), which = t / kChunk;
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < NW; ++q) acc += s.dots[which][q][i];
+            s.dots[which][0][i] = acc;
+        }
+        __syncthreads();
+        {
+            uint16_t* dqg = static_cast<uint16_t*>(gr.dq);
+            uint16_t* dkg = static_cast<uint16_t*>(gr.dk);
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = kSub * I + 4 * lg + r;
+                    if (i >= rows) continue;
+                    float oq = dq[I][r], ok = dk[I][r];
+                    if (p.use_qk_l2norm) {
+                        oq = s.rq[i] * (oq - MM::to_f32(s.qh[i][c]) * s.dots[0][0][i]);
+                        ok = s.rk[i] * (ok - MM::to_f32(s.kh[i][c]) * s.dots[1][0][i]);
+                    }
+                    const int64_t gi = ((rbase + i) * H + h) * K + c;
+                    dqg[gi] = f32_to_bf16_bits(oq);
+                    dkg[gi] = f32_to_bf16_bits(ok);
+                }
+        }
+        if (t < kChunk && t < rows) {
+            float db = s.dbr[0][t] + s.dbr[1][t];
+#pragma unroll
+            for (int q = 0; q < NW; ++q) db += s.dbc[q][t];
+            const float b = s.beta[t];
+            gr.dbeta[(rbase + t) * H + h] = p.use_beta_sigmoid ? db * b * (1.f - b) : db;
+        }
+        if (p.gate_mode != GATE_LOGDECAY) {
+            dal = wave_sum(dal);
+            if (lane == 0) s.gpa[w] = dal;
+            __syncthreads();
+            float* gp = reinterpret_cast<float*>(base + X::kGP);
+            for (int cc = t; cc < K; cc += NT) gp[cc] = s.ddt[cc];
+            if (t == 0) {
+                float a = 0.f;
+#pragma unroll
+                for (int q = 0; q < NW; ++q) a += s.gpa[q];
+                gp[K] = a;
+            }
+        }
+    }
+}
+
 // d(A_log) and d(dt_bias): deterministic sums of the per-chunk shares.
 template <int K>
 __global__ void gate_param_reduce_kernel(ChunkParams p, ChunkGrads gr, const int32_t* chunk_off, const uint8_t* ws,
@@ -1504,7 +2097,11 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                            dim3(vlocal_threads(BF)), 0, st, p, gr, chunk_off, slots, sb);
     if (want(4)) {
         if (nblk > 0) {
-            if constexpr (BF)
+            if constexpr (BF && K == 128)
+                hipLaunchKernelGGL(chunk_bwd_klocal_w8_kernel,
+                                   dim3(static_cast<unsigned>(nblk < kPersistentGrid ? nblk : kPersistentGrid)),
+                                   dim3(kKlocW8Threads), 0, st, p, gr, chunk_off, slots, sb, static_cast<int>(nblk));
+            else if constexpr (BF)
                 hipLaunchKernelGGL((chunk_bwd_klocal_mfma_kernel<K>),
                                    dim3(static_cast<unsigned>(nblk < kPersistentGrid ? nblk : kPersistentGrid)),
                                    dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb, static_cast<int>(nblk));
