@@ -7,8 +7,9 @@
 // then kda_recurrent_step (L2-normalised q and k, sigmoid of the beta logit,
 // key-axis decay, delta-rule write, read-out after the write).
 //
-// Mapping: one 256-thread workgroup per (sequence, head).  The D x D state
-// tile (64 KiB at D = 128) is held in registers: thread t owns column quad
+// Mapping: one workgroup per (sequence, head), 512 threads at D = 128 (256
+// below; measured faster than 256 or 1024 at the production geometry).  The
+// D x D state tile (64 KiB at D = 128) is held in registers: thread t owns column quad
 // t % (D/4) and rows rg, rg + RG, rg + 2 RG, ... with rg = t / (D/4), so each
 // load instruction of a wavefront covers whole 512-byte rows.  Every term of
 // the step is local to a value column, so the only cross-thread traffic is
@@ -22,9 +23,12 @@
 
 namespace kda {
 
+template <int D>
+constexpr int decode_threads() { return D >= 128 ? 512 : 256; }
+
 template <int D, typename XT>
-__global__ __launch_bounds__(256) void decode_step_kernel(DecodeParams p) {
-    constexpr int NT = 256;
+__global__ __launch_bounds__(decode_threads<D>()) void decode_step_kernel(DecodeParams p) {
+    constexpr int NT = decode_threads<D>();
     constexpr int CQ = D / 4;        // column quads
     constexpr int RG = NT / CQ;      // row groups
     constexpr int RPT = D / RG;      // rows per thread
@@ -166,9 +170,9 @@ template <int D>
 static hipError_t launch_decode_d(const DecodeParams& p, hipStream_t st) {
     dim3 grid(p.H, p.N);
     if (p.x_bf16)
-        hipLaunchKernelGGL((decode_step_kernel<D, uint16_t>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((decode_step_kernel<D, uint16_t>), grid, dim3(decode_threads<D>()), 0, st, p);
     else
-        hipLaunchKernelGGL((decode_step_kernel<D, float>), grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((decode_step_kernel<D, float>), grid, dim3(decode_threads<D>()), 0, st, p);
     return hipGetLastError();
 }
 
