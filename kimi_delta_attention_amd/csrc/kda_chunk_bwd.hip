@@ -2086,9 +2086,14 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
             hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true>), dim3(static_cast<unsigned>(nblk)), dim3(prep_threads(K)), 0,
                                st, p, chunk_off, slots, sb);
     }
-    if (want(1) && cgrid > 0)
-        hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kThreads), 0, st,
-                           p, chunk_off, slots, sb);
+    if (want(1) && cgrid > 0) {
+        if (cgrid <= kPersistentGrid)  // few chains: 8 waves per chain (see the forward)
+            hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false, 512>), dim3(cgrid), dim3(512), 0,
+                               st, p, chunk_off, slots, sb);
+        else
+            hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kThreads), 0,
+                               st, p, chunk_off, slots, sb);
+    }
     if (want(2) && cgrid > 0)
         hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,
                            chunk_off, slots, sb);

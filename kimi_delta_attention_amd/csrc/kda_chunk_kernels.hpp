@@ -611,9 +611,9 @@ struct Seg {
 // STORE writes each chunk's entry state (BwdExtra::kS, element type ET) for
 // the backward; WRITE_O computes and stores the output.  The next chunk's
 // operands are prefetched into registers while the current chunk computes.
-template <int K, int V, int BV, bool BF, bool STORE, bool WRITE_O>
-__global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p, const int32_t* chunk_off,
-                                                                   uint8_t* ws, int64_t slot_bytes) {
+template <int K, int V, int BV, bool BF, bool STORE, bool WRITE_O, int NT = kThreads>
+__global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, const int32_t* chunk_off,
+                                                             uint8_t* ws, int64_t slot_bytes) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
@@ -623,7 +623,10 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
     constexpr int LDB = BV + MM::PAD;
     constexpr int NCT = BV / 16;
     constexpr int NST = (K / 16) * NCT;
-    constexpr int SPW = (NST + 3) / 4;
+    constexpr int NW = NT / 64;
+    constexpr int SPW = (NST + NW - 1) / NW;
+    constexpr int CSTEP = NW / 4;                 // waves per 16-row tile of the chunk
+    constexpr int TW = (NCT + CSTEP - 1) / CSTEP;  // column tiles per wave
     constexpr int NVB = V / BV;
     constexpr int QR = WRITE_O ? kChunk : 0;  // rows of QE ahead of W in QW
 
@@ -644,14 +647,16 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
     seq_bounds(p, n, start, len);
     const int nc = n_chunks(len);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+    // 16-row tile and first column tile of this wave (4 waves: every column tile)
+    const int rw = NW > 4 ? (w & 3) : w, cw = NW > 4 ? (w >> 2) : 0;
     const int v0 = vb * BV;
     const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
 
-    Seg<ET, kChunk, K, false> sQE, sW;
-    Seg<ET, kChunk, K, true> sKD;
-    Seg<ET, kChunk, kChunk, false> sMS;
-    Seg<ET, kChunk, BV, false> sU;
-    Seg<float, 1, K, false> sGC;
+    Seg<ET, kChunk, K, false, NT> sQE, sW;
+    Seg<ET, kChunk, K, true, NT> sKD;
+    Seg<ET, kChunk, kChunk, false, NT> sMS;
+    Seg<ET, kChunk, BV, false, NT> sU;
+    Seg<float, 1, K, false, NT> sGC;
     auto prefetch = [&](int jc) {
         const uint8_t* base = ws + ((slot0 + jc) * H + h) * slot_bytes;
         if (WRITE_O) sQE.load(reinterpret_cast<const ET*>(base + L::kQE), K, t);
@@ -667,7 +672,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
 #pragma unroll
     for (int m = 0; m < SPW; ++m) {
-        const int tt = w + 4 * m;
+        const int tt = w + NW * m;
         const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -691,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
             ET* gS = reinterpret_cast<ET*>(base + BwdExtra<K, BF>::kS);
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
-                const int tt = w + 4 * m;
+                const int tt = w + NW * m;
                 if (tt < NST) {
                     const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
@@ -702,63 +707,74 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
         }
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int tt = w + 4 * m;
+            const int tt = w + NW * m;
             if (tt < NST) tile_store_t<MM>(&St[0][0], LDK, 16 * (tt / NCT), 16 * (tt % NCT), S[m], lane);
         }
         __syncthreads();
         if (jc + 1 < nc) prefetch(jc + 1);
 
-        // WS and (scale q exp(G)) S for this wave's 16 rows
-        f32x4 oq[NCT], ws_[NCT];
+        // WS and (scale q exp(G)) S for this wave's 16 rows and column tiles
+        f32x4 oq[TW], ws_[TW];
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) oq[ct] = ws_[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < TW; ++m) oq[m] = ws_[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
         for (int k0 = 0; k0 < K; k0 += MM::KS) {
-            const auto aw = MM::load(&QW[0][0], LDK, QR + 16 * w, k0, lane);
+            const auto aw = MM::load(&QW[0][0], LDK, QR + 16 * rw, k0, lane);
             typename MM::Frag aq{};
-            if (WRITE_O) aq = MM::load(&QW[0][0], LDK, 16 * w, k0, lane);
+            if (WRITE_O) aq = MM::load(&QW[0][0], LDK, 16 * rw, k0, lane);
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const auto b = MM::load(&St[0][0], LDK, 16 * ct, k0, lane);
-                ws_[ct] = MM::mma(aw, b, ws_[ct]);
-                if (WRITE_O) oq[ct] = MM::mma(aq, b, oq[ct]);
+            for (int m = 0; m < TW; ++m) {
+                const int ct = cw + CSTEP * m;
+                if (ct < NCT) {
+                    const auto b = MM::load(&St[0][0], LDK, 16 * ct, k0, lane);
+                    ws_[m] = MM::mma(aw, b, ws_[m]);
+                    if (WRITE_O) oq[m] = MM::mma(aq, b, oq[m]);
+                }
             }
         }
         // D = U - W S
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 d;
+        for (int m = 0; m < TW; ++m) {
+            const int ct = cw + CSTEP * m;
+            if (ct < NCT) {
+                f32x4 d;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                d[r] = MM::to_f32(Un[16 * w + 4 * (lane >> 4) + r][16 * ct + (lane & 15)]) - ws_[ct][r];
-            tile_store_t<MM>(&Dt[0][0], LDC, 16 * w, 16 * ct, d, lane);
+                for (int r = 0; r < 4; ++r)
+                    d[r] = MM::to_f32(Un[16 * rw + 4 * (lane >> 4) + r][16 * ct + (lane & 15)]) - ws_[m][r];
+                tile_store_t<MM>(&Dt[0][0], LDC, 16 * rw, 16 * ct, d, lane);
+            }
         }
         __syncthreads();
 
         // O = scale (q exp(G)) S + scale M D
         if (WRITE_O) {
-            for (int k0 = 0; k0 < 16 * (w + 1); k0 += MM::KS) {
-                const auto a = MM::load(&MS[0][0], LDC, 16 * w, k0, lane);
+            for (int k0 = 0; k0 < 16 * (rw + 1); k0 += MM::KS) {
+                const auto a = MM::load(&MS[0][0], LDC, 16 * rw, k0, lane);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct)
-                    oq[ct] = MM::mma(a, MM::load(&Dt[0][0], LDC, 16 * ct, k0, lane), oq[ct]);
+                for (int m = 0; m < TW; ++m) {
+                    const int ct = cw + CSTEP * m;
+                    if (ct < NCT) oq[m] = MM::mma(a, MM::load(&Dt[0][0], LDC, 16 * ct, k0, lane), oq[m]);
+                }
             }
             const int rbase = jc * kChunk;
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct)
+            for (int m = 0; m < TW; ++m) {
+                const int ct = cw + CSTEP * m;
+                if (ct < NCT)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = 16 * w + 4 * (lane >> 4) + r;
-                    if (rbase + row < len)
-                        Elem<IT>::store(og, ((start + rbase + row) * H + h) * V + v0 + 16 * ct + (lane & 15),
-                                        oq[ct][r]);
-                }
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * rw + 4 * (lane >> 4) + r;
+                        if (rbase + row < len)
+                            Elem<IT>::store(og, ((start + rbase + row) * H + h) * V + v0 + 16 * ct + (lane & 15),
+                                            oq[m][r]);
+                    }
+            }
         }
 
         // S' = diag(exp(G_last)) S + (k exp(G_last - G))^T D
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int tt = w + 4 * m;
+            const int tt = w + NW * m;
             if (tt < NST) {
                 const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
@@ -775,7 +791,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_fwd_kernel(ChunkParams p
     if (p.ht) {
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
-            const int tt = w + 4 * m;
+            const int tt = w + NW * m;
             if (tt < NST) {
                 const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
