@@ -77,6 +77,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int v0 = vb * BV;
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
+    const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
 
     Seg<ET, kChunk, K, true> sQE, sW;
     Seg<ET, kChunk, K, false> sKD;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     Seg<float, 1, K, false> sGC;
     const ET* dOg = static_cast<const ET*>(gr.dO);
     auto prefetch = [&](int jc) {
-        const uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
+        const uint8_t* base = ws + ((slot0 + jc) * H + h) * slot_bytes;
         sQE.load(reinterpret_cast<const ET*>(base + L::kQE), K, t);
         sW.load(reinterpret_cast<const ET*>(base + L::kW), K, t);
         sKD.load(reinterpret_cast<const ET*>(base + L::kKD), K, t);
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
         sMS.store(&MSt[0][0], LDC, t);
         sGC.store(&gC[0], K, t);
         sdO.store(&dOt[0][0], LDC, t);
-        uint8_t* base = ws + (chunk_slot(p, chunk_off, n, jc) * H + h) * slot_bytes;
+        uint8_t* base = ws + ((slot0 + jc) * H + h) * slot_bytes;
         ET* gDS = reinterpret_cast<ET*>(base + X::kDS);
 #pragma unroll
         for (int m = 0; m < SPW; ++m) {
@@ -124,12 +125,9 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
             if (tt < NST) {
                 const int rt = tt / NCT, ct = tt % NCT;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int key = 16 * rt + 4 * (lane >> 4) + r, col = 16 * ct + (lane & 15);
-                    const ET e = MM::from_f32(dS[m][r]);
-                    gDS[key * V + v0 + col] = e;
-                    dSt[col][key] = e;
-                }
+                for (int r = 0; r < 4; ++r)
+                    gDS[(16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = MM::from_f32(dS[m][r]);
+                tile_store_t<MM>(&dSt[0][0], LDK, 16 * rt, 16 * ct, dS[m], lane);
             }
         }
         __syncthreads();
