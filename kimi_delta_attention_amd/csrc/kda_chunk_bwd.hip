@@ -251,7 +251,7 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     // next block's operands in registers: S and dS' rows key, dO rows i (16-byte
     // vectors), and v in the accumulator layout of this wave's tiles
     f32x4 rS[PS], rD[PS], rO[PO];
-    float rv[TW][4];
+    IT rv[TW][4];  // raw: converted where used, so that the request is not waited on here
     auto fetch = [&](int vb) {
         const int v0 = vb * BV;
 #pragma unroll
@@ -278,9 +278,8 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * rt + 4 * (lane >> 4) + r;
-                rv[m][r] = (ct < NCT && i < rows)
-                               ? Elem<IT>::load(vg, ((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15))
-                               : 0.f;
+                rv[m][r] = (ct < NCT && i < rows) ? vg[((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15)]
+                                                  : IT(0);
             }
         }
     };
@@ -314,12 +313,12 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         }
     };
 
-    fetch(0);
     copy_in<ET, kChunk, K, NT>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + X::kKE), t);
     copy_in<ET, kChunk, K, NT>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
     copy_in<ET, kChunk, kChunk, NT>(&TBn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
     copy_in_t<ET, kChunk, kChunk, NT>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
     copy_in_t<ET, kChunk, kChunk, NT>(&MSt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
+    fetch(0);  // after the copies, whose stores would otherwise wait for it too
 
     f32x4 aQE[AW], aKE[AW], aKD[AW], aMS[CW], aTB[CW];
 #pragma unroll
@@ -336,7 +335,7 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
 #pragma unroll
         for (int m = 0; m < TW; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vcur[m][r] = rv[m][r];
+            for (int r = 0; r < 4; ++r) vcur[m][r] = Elem<IT>::load(&rv[m][r], 0);
         if (vb + 1 < V / BV) fetch(vb + 1);
         __syncthreads();
 
