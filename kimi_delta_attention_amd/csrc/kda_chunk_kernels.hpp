@@ -137,14 +137,14 @@ struct PrepSmem {
             ET kL[kChunk][LDE];   // k^ exp(G_i - G_ref(I))
             ET kbe[kChunk][LDE];  // k^ exp(G_end(J) - G_j)
         } op;
-        float T[kChunk][kChunk + 1];
+        float T[kChunk][kChunk + 4];  // 16-byte aligned rows (MFMA A operand)
         struct {
             ET TB[kChunk][kChunk + Mma<BF>::PAD];  // T diag(beta): A operand of W and U
             ET KEt[K][kChunk + Mma<BF>::PAD];      // (k^ exp(G))^T
             ET Vt[K][kChunk + Mma<BF>::PAD];       // v^T (V = K)
         } wu;
     } u;
-    float A[kChunk][kChunk + 1];
+    float A[kChunk][kChunk + 4];  // 16-byte aligned rows (MFMA A operand)
     float M[kChunk][kChunk + 1];
     float Ak[BWD ? kChunk : 1][kChunk + 1];  // un-scaled k-k scores (backward only)
     float P[4][K];     // exp(G_end(I) - G_ref(I)): decay across sub-block I
@@ -255,8 +255,8 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         s.beta[i] = b;
     }
     if (t < 4) s.unsafe[t] = 0;
+    for (int e = t; e < kChunk * (kChunk + 4); e += NT) (&s.A[0][0])[e] = 0.f;
     for (int e = t; e < kChunk * (kChunk + 1); e += NT) {
-        (&s.A[0][0])[e] = 0.f;
         (&s.M[0][0])[e] = 0.f;
         if (BWD) (&s.Ak[0][0])[e] = 0.f;
     }
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     __syncthreads();
 
     // ---- 6. T = (I + A)^-1: diagonal sub-blocks by forward substitution ...
-    for (int e = t; e < kChunk * (kChunk + 1); e += NT) (&s.u.T[0][0])[e] = 0.f;
+    for (int e = t; e < kChunk * (kChunk + 4); e += NT) (&s.u.T[0][0])[e] = 0.f;
     __syncthreads();
     if (w < 4 && lane < kSub) {
         const int I = w;
@@ -425,29 +425,32 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         for (int r = 0; r < kSub; ++r) s.u.T[kSub * I + r][kSub * I + jc] = x[r];
     }
     __syncthreads();
-    // ... then the off-diagonal sub-blocks by distance: T_IJ = -T_II sum_L A_IL T_LJ
+    // ... then the off-diagonal sub-blocks by distance d = I - J: T_IJ = -T_II
+    // sum_L A_IL T_LJ.  Wave w forms block (d + w, w) as two fp32 16 x 16 x 16
+    // MFMA products: lane (lc, lg) supplies A[lc][4 lg + st] and B[4 lg + st][lc]
+    // at step st, and holds rows 4 lg + r of column lc of the result.
     for (int d = 1; d < 4; ++d) {
-        const int nb = 4 - d;
-        for (int e = t; e < nb * kSub * kSub; e += NT) {
-            const int bi = e / (kSub * kSub);
-            const int a = (e / kSub) % kSub, b = e % kSub;
-            const int I = d + bi, J = bi;
-            float acc = 0.f;
-            for (int Lb = J; Lb < I; ++Lb)
+        if (w < 4 - d) {
+            const int J = w, I = d + w, lc = lane & 15, lg = lane >> 4;
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
+            for (int Lb = J; Lb < I; ++Lb) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&s.A[kSub * I + lc][kSub * Lb + 4 * lg]);
+                const float* tc = &s.u.T[kSub * Lb + 4 * lg][kSub * J + lc];
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, tc[0 * (kChunk + 4)], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, tc[1 * (kChunk + 4)], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, tc[2 * (kChunk + 4)], x, 0, 0, 0);
+                x = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, tc[3 * (kChunk + 4)], x, 0, 0, 0);
+            }
 #pragma unroll
-                for (int m = 0; m < kSub; ++m)
-                    acc += s.A[kSub * I + a][kSub * Lb + m] * s.u.T[kSub * Lb + m][kSub * J + b];
-            s.X[bi][a][b] = acc;
-        }
-        __syncthreads();
-        for (int e = t; e < nb * kSub * kSub; e += NT) {
-            const int bi = e / (kSub * kSub);
-            const int a = (e / kSub) % kSub, b = e % kSub;
-            const int I = d + bi, J = bi;
-            float acc = 0.f;
+            for (int r = 0; r < 4; ++r) s.X[w][4 * lg + r][lc] = x[r];  // read back by this wave only
+            const float4 t4 = *reinterpret_cast<const float4*>(&s.u.T[kSub * I + lc][kSub * I + 4 * lg]);
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.x, s.X[w][4 * lg + 0][lc], y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.y, s.X[w][4 * lg + 1][lc], y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.z, s.X[w][4 * lg + 2][lc], y, 0, 0, 0);
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(t4.w, s.X[w][4 * lg + 3][lc], y, 0, 0, 0);
 #pragma unroll
-            for (int m = 0; m < kSub; ++m) acc += s.u.T[kSub * I + a][kSub * I + m] * s.X[bi][m][b];
-            s.u.T[kSub * I + a][kSub * J + b] = -acc;
+            for (int r = 0; r < 4; ++r) s.u.T[kSub * I + 4 * lg + r][kSub * J + lc] = -y[r];
         }
         __syncthreads();
     }
