@@ -23,7 +23,10 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 arithmetic is disabled for all device code (see the comment in
 # kda_device.hpp); hipcc's host pass warns that it does not know the feature.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA accumulators are kept in ordinary VGPRs: the state passes scale and
+# round their accumulators every chunk, which the accumulation-register form
+# turns into copies between the two register files.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"]
 

@@ -2084,7 +2084,10 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                st, p, chunk_off, slots, sb);
     }
     if (want(1) && cgrid > 0) {
-        if (cgrid <= kPersistentGrid)  // few chains: 8 waves per chain (see the forward)
+        if constexpr (K == 128 && BF)
+            hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<true, false>), dim3(cgrid), dim3(256), 0, st, p, chunk_off,
+                               slots, sb);
+        else if (cgrid <= kPersistentGrid)  // few chains: 8 waves per chain (see the forward)
             hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false, 512>), dim3(cgrid), dim3(512), 0,
                                st, p, chunk_off, slots, sb);
         else

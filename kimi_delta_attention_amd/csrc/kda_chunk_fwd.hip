@@ -42,7 +42,11 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
         // few chains (no more workgroups than CUs): 8 waves per chain shorten
         // each chunk step; otherwise 4 waves let two chains share a CU
         const int grid = chain_grid(p.N * p.H, V / BV);
-        if (grid > 0 && grid <= kPersistentGrid)
+        if constexpr (K == 128 && BF) {
+            if (grid > 0)
+                hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<KEEP, true>), dim3(grid), dim3(256), 0, st, p, chunk_off,
+                                   prep, sb);
+        } else if (grid > 0 && grid <= kPersistentGrid)
             hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, KEEP, true, 512>), dim3(grid), dim3(512), 0,
                                st, p, chunk_off, prep, sb);
         else if (grid > 0)

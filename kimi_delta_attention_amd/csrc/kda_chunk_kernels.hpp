@@ -33,6 +33,7 @@
 #pragma once
 
 #include "kda_chunk_common.hpp"
+#include "kda_lds.hpp"
 
 namespace kda {
 
@@ -802,6 +803,247 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
                     p.ht[sbase + (16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = S[m][r];
             }
         }
+    }
+}
+
+// ------------------------------------------------------------------ state (producer/consumer)
+// Forward state pass for K = V = 128 in bf16, 32 value columns per workgroup,
+// 256 threads.  Waves 0-1 (consumers) each own a 16-column strip of the fp32
+// state over all 128 rows, in MFMA accumulators.  Every product of a chunk
+// step takes its B operand from registers: S itself, or D = U - W S formed
+// in registers.  Its A operand is one of the chunk's operand tiles in LDS, read
+// row-wise or transposed.  A consumer thus needs no other wave within a step.
+// Waves 2-3 (producers) do all global memory traffic: the next chunk's operand
+// tiles go straight into the other half of a double-buffered LDS area, and the
+// previous chunk's output rows and entry state go out from LDS staging.
+// There is one barrier per chunk.
+struct StatePcFwd {
+    static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oU = 57344, oGC = 61440;
+    static constexpr int kBuf = 61952;  // one chunk's operand tiles
+};
+
+template <bool STORE, bool WRITE_O>
+__global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, const int32_t* chunk_off,
+                                                                 uint8_t* ws, int64_t slot_bytes) {
+    using Z = StatePcFwd;
+    using L = PrepLayout<128, true>;
+    constexpr int K = 128, V = 128, BV = 32, NVB = V / BV;
+    // L2 warm-up: the chunk after next, 128-byte lines split over the chain's
+    // NVB workgroups, NWARM loads per producer lane
+    constexpr int NL_OP = WRITE_O ? 384 : 256;                       // [QE,] W, KD
+    constexpr int NL = NL_OP + (WRITE_O ? 64 : 0) + 128 + 4;         // + MS, U, GC
+    constexpr int NWARM = (NL + NVB * 128 - 1) / (NVB * 128);
+    // separate arrays, so that the compiler knows the staging and operand
+    // reads do not alias the warm-up copies
+    __shared__ __attribute__((aligned(1024))) uint8_t smb[2 * Z::kBuf];
+    __shared__ __attribute__((aligned(1024))) uint8_t sms[2 * 8192];  // S^T staging [32][128] per parity
+    __shared__ __attribute__((aligned(1024))) uint8_t smo[2 * 4096];  // O^T staging [32][64] per parity
+    __shared__ __attribute__((aligned(256))) uint8_t smj[256];
+
+    int chain, vb;
+    if (!chain_of_block(blockIdx.x, p.N * p.H, NVB, chain, vb)) return;
+    const int H = p.H;
+    const int n = chain / H, h = chain % H;
+    int64_t start;
+    int len;
+    seq_bounds(p, n, start, len);
+    const int nc = n_chunks(len);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lg = lane >> 4, m = lane & 15;
+    const int v0 = vb * BV;
+    const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
+    const bool prod = w >= 2;
+    const int pw = w - 2;
+    auto slot = [&](int jc) { return ws + ((slot0 + jc) * H + h) * slot_bytes; };
+
+    // ---- producer: chunk jc's operand tiles into buffer jc & 1 (61 pieces of 1 KB)
+    auto fetch = [&](int jc) {
+        const uint8_t* base = slot(jc);
+        uint8_t* buf = smb + (jc & 1) * Z::kBuf;
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+            const int q = 2 * qq + pw;
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kW), K, buf + Z::oW, q, lane);
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kKD), K, buf + Z::oKD, q, lane);
+            if (WRITE_O)
+                dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kQE), K, buf + Z::oQE, q, lane);
+        }
+        if (WRITE_O)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+                dma_tile_piece<64>(reinterpret_cast<const uint16_t*>(base + L::kMS), kChunk, buf + Z::oMS, 2 * qq + pw,
+                                    lane);
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+            dma_tile_piece<32>(reinterpret_cast<const uint16_t*>(base + L::kU) + v0, V, buf + Z::oU, 2 * qq + pw, lane);
+        if (pw == 1 && lane < 32) dma16(base + L::kGC + 16 * lane, buf + Z::oGC);
+    };
+    // ---- producer: chunk jc's entry state and output rows from staging jc & 1
+    uint16_t* og = static_cast<uint16_t*>(p.o);
+    auto drain = [&](int jc) {
+        // every staging read first, then the stores
+        const uint8_t* sts = sms + (jc & 1) * 8192;
+        const uint8_t* sto = smo + (jc & 1) * 4096;
+        bf16x4_t xs[8], xo[4];
+        if (STORE)
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) xs[kt] = tr4<128>(sts, 16 * pw + 4 * lg, 16 * kt, lane);
+        if (WRITE_O)
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) xo[rq] = tr4<64>(sto, 16 * pw + 4 * lg, 16 * rq, lane);
+        if (STORE) {
+            uint16_t* gS = reinterpret_cast<uint16_t*>(slot(jc) + BwdExtra<128, true>::kS) + v0;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)  // 16 state rows x 16 columns per piece
+                *reinterpret_cast<bf16x4_t*>(gS + (16 * kt + m) * V + 16 * pw + 4 * lg) = xs[kt];
+        }
+        if (WRITE_O) {
+#pragma unroll
+            for (int rq = 0; rq < 4; ++rq) {  // 16 token rows x 16 columns per piece
+                const int row = jc * kChunk + 16 * rq + m;
+                if (row < len)
+                    *reinterpret_cast<bf16x4_t*>(og + ((start + row) * H + h) * V + v0 + 16 * pw + 4 * lg) = xo[rq];
+            }
+        }
+    };
+    // ---- producer: one 4-byte copy per 128-byte line of chunk jc's operands,
+    // all landing on the same 256 bytes of LDS
+    auto warm = [&](int jc) {
+        const uint8_t* base = slot(jc);
+#pragma unroll
+        for (int i = 0; i < NWARM; ++i) {
+            int l = NVB * ((2 * i + pw) * 64 + lane) + vb;
+            l = l < NL ? l : NL - 1;
+            const uint8_t* a;
+            if (l < NL_OP) a = base + (WRITE_O ? L::kQE : L::kW) + 128 * l;
+            else if (WRITE_O && l < NL_OP + 64) a = base + L::kMS + 128 * (l - NL_OP);
+            else if (l < NL - 4) a = base + L::kU + 128 * (l - (NL - 132));
+            else a = base + L::kGC + 128 * (l - (NL - 4));
+            __builtin_amdgcn_global_load_lds(a, (lds_void_t*)smj, 4, 0, 0);
+        }
+    };
+
+    // ---- consumer: state strip, tile t = rows 16 t + 4 lg + r, column 16 w + m
+    f32x4 S[8];
+    // per-lane byte offsets of the operand fragments (loop invariant)
+    int offA[4];      // [64][128] row fragment, k-step s, row tile 0 (+4096 per row tile)
+    int offM[2];      // [64][64] row fragment, k-step s, row tile 0 (+2048 per row tile)
+    int offT[8][2];   // [64][128] transposed fragment halves, column tile t, k-step 0 (+8192 per k-step)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) offA[s] = swz_off<128>(m, 32 * s + 8 * lg);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) offM[s] = swz_off<64>(m, 32 * s + 8 * lg);
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) offT[t][hh] = swz_off<128>(8 * lg + 4 * hh + (m >> 2), 16 * t + 4 * (m & 3));
+    const int offU = (4 * lg + (m >> 2)) * 64 + 32 * w + 8 * (m & 3);
+    auto rdA = [](const uint8_t* tile, int off) { return *reinterpret_cast<const bf16x8*>(tile + off); };
+    auto rdT = [](const uint8_t* tile, int off0, int off1) {
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off0));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off1));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto step = [&](int jc) {
+        const uint8_t* buf = smb + (jc & 1) * Z::kBuf;
+        uint8_t* sts = sms + (jc & 1) * 8192;
+        uint8_t* sto = smo + (jc & 1) * 4096;
+        bf16x8 Sb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) Sb[s] = frag_acc_nat(S[2 * s], S[2 * s + 1]);
+        if (STORE) {  // S^T staging: lane group lg of fragment s holds k = 32 s + 8 lg .. +7
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                *reinterpret_cast<bf16x8*>(sts + swz_off<128>(16 * w + m, 32 * s + 8 * lg)) = Sb[s];
+        }
+        // W S and QE S for the strip's 64 x 16 block
+        f32x4 ws_[4], o[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) ws_[rt] = o[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                ws_[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oW + 4096 * rt, offA[s]), Sb[s], ws_[rt],
+                                                                  0, 0, 0);
+                if (WRITE_O)
+                    o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oQE + 4096 * rt, offA[s]), Sb[s],
+                                                                    o[rt], 0, 0, 0);
+            }
+        // D = U - W S
+        f32x4 d[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+            const bf16x4_t u =
+                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(buf + Z::oU + 1024 * rt + offU));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) d[rt][r] = static_cast<float>(u[r]) - ws_[rt][r];
+        }
+        const bf16x8 Db[2] = {frag_acc_nat(d[0], d[1]), frag_acc_nat(d[2], d[3])};
+        // O = QE S + MS D (MS lower triangular)
+        if (WRITE_O) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int s = 0; s <= (rt >> 1); ++s)
+                    o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oMS + 2048 * rt, offM[s]), Db[s],
+                                                                    o[rt], 0, 0, 0);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                *reinterpret_cast<bf16x4_t*>(sto + swz_off<64>(16 * w + m, 16 * rt + 4 * lg)) =
+                    bf16x4_t{(__bf16)o[rt][0], (__bf16)o[rt][1], (__bf16)o[rt][2], (__bf16)o[rt][3]};
+        }
+        // S' = GC S + KD^T D
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[t][r] *= g[r];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    rdT(buf + Z::oKD + 8192 * s, offT[t][0], offT[t][1]), Db[s], S[t], 0, 0, 0);
+        }
+    };
+
+    if (prod) {
+        if (nc > 0) fetch(0);
+        wait_vmem_all();
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (p.h0) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[t][r] = p.h0[sbase + (16 * t + 4 * lg + r) * V + v0 + 16 * w + m];
+        }
+    }
+    __syncthreads();
+    for (int jc = 0; jc < nc; ++jc) {
+        if (prod) {
+            // staging reads before this step's copies (the compiler would wait
+            // for the copies before any later LDS read); the warm-up loads are
+            // issued last and are the only ones allowed to stay in flight
+            if (jc > 0) drain(jc - 1);
+            if (jc + 1 < nc) fetch(jc + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            warm(jc + 2 < nc ? jc + 2 : jc);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmem<NWARM>();
+        } else {
+            step(jc);
+        }
+        barrier_lds();
+    }
+    if (prod) {
+        if (nc > 0) drain(nc - 1);
+    } else if (p.ht) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p.ht[sbase + (16 * t + 4 * lg + r) * V + v0 + 16 * w + m] = S[t][r];
     }
 }
 
