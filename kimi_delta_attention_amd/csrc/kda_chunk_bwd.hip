@@ -172,6 +172,223 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     }
 }
 
+// Reverse state pass for K = V = 128 in bf16, 32 value columns per workgroup,
+// 256 threads: the producer/consumer form of chunk_state_fwd_pc_kernel.
+// Waves 0-1 (consumers) each own a 16-column strip of dS' over all 128 rows.
+// dD = KD dS' + MS^T dO takes dS' from registers as its B operand.  The
+// token-row products QE^T dO and W^T dD take dO, read transposed, and -dD,
+// formed in registers, as B.  Waves 2-3 (producers) copy each chunk's
+// operand tiles and dO block into LDS a chunk ahead, warm L2 for the chunk
+// after, and store the staged dS' of the chunk before.
+struct StatePcBwd {
+    static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oDO = 57344, oGC = 61440;
+    static constexpr int kBuf = 61952;  // one chunk's operand tiles and dO block
+};
+
+__global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, ChunkGrads gr,
+                                                                 const int32_t* chunk_off, uint8_t* ws,
+                                                                 int64_t slot_bytes) {
+    using Z = StatePcBwd;
+    using L = PrepLayout<128, true>;
+    using X = BwdExtra<128, true>;
+    constexpr int K = 128, V = 128, BV = 32, NVB = V / BV;
+    // L2 warm-up lines of a chunk: QE, W, KD (contiguous), MS, GC, then the
+    // dO rows (two lines per head row), split over the chain's NVB workgroups
+    constexpr int NL = 384 + 64 + 4 + 128;
+    constexpr int NWARM = (NL + NVB * 128 - 1) / (NVB * 128);
+    __shared__ __attribute__((aligned(1024))) uint8_t smb[2 * Z::kBuf];
+    __shared__ __attribute__((aligned(1024))) uint8_t sms[2 * 8192];  // dS'^T staging [32][128] per parity
+    __shared__ __attribute__((aligned(256))) uint8_t smj[256];
+
+    int chain, vb;
+    if (!chain_of_block(blockIdx.x, p.N * p.H, NVB, chain, vb)) return;
+    const int H = p.H;
+    const int n = chain / H, h = chain % H;
+    int64_t start;
+    int len;
+    seq_bounds(p, n, start, len);
+    const int nc = n_chunks(len);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lg = lane >> 4, m = lane & 15;
+    const int v0 = vb * BV;
+    const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
+    const bool prod = w >= 2;
+    const int pw = w - 2;
+    const uint16_t* dOg = static_cast<const uint16_t*>(gr.dO);
+    auto slot = [&](int jc) { return ws + ((slot0 + jc) * H + h) * slot_bytes; };
+    auto rows_in = [&](int jc) { return min(kChunk, len - jc * kChunk); };  // >= 1 for jc < nc
+
+    // ---- producer: chunk jc's operand tiles and dO block into buffer jc & 1
+    auto fetch = [&](int jc) {
+        const uint8_t* base = slot(jc);
+        uint8_t* buf = smb + (jc & 1) * Z::kBuf;
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+            const int q = 2 * qq + pw;
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kKD), K, buf + Z::oKD, q, lane);
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kQE), K, buf + Z::oQE, q, lane);
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kW), K, buf + Z::oW, q, lane);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+            dma_tile_piece<64>(reinterpret_cast<const uint16_t*>(base + L::kMS), kChunk, buf + Z::oMS, 2 * qq + pw,
+                                lane);
+        const uint16_t* dO0 = dOg + ((start + static_cast<int64_t>(jc) * kChunk) * H + h) * V + v0;
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+            dma_tile_piece<32>(dO0, static_cast<int64_t>(H) * V, buf + Z::oDO, 2 * qq + pw, lane, rows_in(jc));
+        if (pw == 1 && lane < 32) dma16(base + L::kGC + 16 * lane, buf + Z::oGC);
+    };
+    // ---- producer: chunk jc's dS' from staging jc & 1 (16 rows x 16 columns per piece)
+    auto drain = [&](int jc) {
+        const uint8_t* st = sms + (jc & 1) * 8192;
+        bf16x4_t xs[8];
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) xs[kt] = tr4<128>(st, 16 * pw + 4 * lg, 16 * kt, lane);
+        uint16_t* gD = reinterpret_cast<uint16_t*>(slot(jc) + X::kDS) + v0;
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+            *reinterpret_cast<bf16x4_t*>(gD + (16 * kt + m) * V + 16 * pw + 4 * lg) = xs[kt];
+    };
+    // ---- producer: one 4-byte copy per 128-byte line of chunk jc's inputs
+    auto warm = [&](int jc) {
+        const uint8_t* base = slot(jc);
+        const int rv = rows_in(jc);
+#pragma unroll
+        for (int i = 0; i < NWARM; ++i) {
+            int l = NVB * ((2 * i + pw) * 64 + lane) + vb;
+            l = l < NL ? l : NL - 1;
+            const void* a;
+            if (l < 384) a = base + L::kQE + 128 * l;
+            else if (l < 448) a = base + L::kMS + 128 * (l - 384);
+            else if (l < 452) a = base + L::kGC + 128 * (l - 448);
+            else {
+                const int r = min((l - 452) >> 1, rv - 1);
+                a = dOg + ((start + static_cast<int64_t>(jc) * kChunk + r) * H + h) * V + 64 * ((l - 452) & 1);
+            }
+            __builtin_amdgcn_global_load_lds(a, (lds_void_t*)smj, 4, 0, 0);
+        }
+    };
+
+    // ---- consumer: dS' strip, tile t = rows 16 t + 4 lg + r, column 16 w + m
+    f32x4 dS[8];
+    int offA[4];      // [64][128] row fragment, k-step s, row tile 0 (+4096 per row tile)
+    int offT[8][2];   // [64][128] transposed fragment halves, column tile t, k-step 0 (+8192 per k-step)
+    int offMT[4][2];  // [64][64] transposed fragment halves, column tile j, k-step 0 (+4096 per k-step)
+    int offD[2];      // [64][32] dO, transposed halves, k-step 0 (+2048 per k-step)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) offA[s] = swz_off<128>(m, 32 * s + 8 * lg);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+        const int r = 8 * lg + 4 * hh + (m >> 2);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) offT[t][hh] = swz_off<128>(r, 16 * t + 4 * (m & 3));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) offMT[j][hh] = swz_off<64>(r, 16 * j + 4 * (m & 3));
+        offD[hh] = swz_off<32>(r, 16 * w + 4 * (m & 3));
+    }
+    auto rdA = [](const uint8_t* tile, int off) { return *reinterpret_cast<const bf16x8*>(tile + off); };
+    auto rdT = [](const uint8_t* tile, int off0, int off1) {
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off0));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off1));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    auto step = [&](int jc) {
+        const uint8_t* buf = smb + (jc & 1) * Z::kBuf;
+        uint8_t* st = sms + (jc & 1) * 8192;
+        bf16x8 Sb[4];  // dS' as the B operand over state rows; also staged for the store
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            Sb[s] = frag_acc_nat(dS[2 * s], dS[2 * s + 1]);
+            *reinterpret_cast<bf16x8*>(st + swz_off<128>(16 * w + m, 32 * s + 8 * lg)) = Sb[s];
+        }
+        // dO block as the B operand over token rows (zero past the sequence end)
+        bf16x8 dOb[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) dOb[s] = rdT(buf + Z::oDO + 2048 * s, offD[0], offD[1]);
+        const int rv = rows_in(jc);
+        if (rv < kChunk) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (32 * s + 8 * lg + j >= rv) dOb[s][j] = static_cast<__bf16>(0.f);
+        }
+        // dD = KD dS' + MS^T dO   (MS^T upper triangular)
+        f32x4 dd[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) dd[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                dd[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oKD + 4096 * rt, offA[s]), Sb[s], dd[rt],
+                                                                 0, 0, 0);
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int s = jt >> 1; s < 2; ++s)
+                dd[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                    rdT(buf + Z::oMS + 4096 * s, offMT[jt][0], offMT[jt][1]), dOb[s], dd[jt], 0, 0, 0);
+        const bf16x8 nDb[2] = {frag_acc_nat(-dd[0], -dd[1]), frag_acc_nat(-dd[2], -dd[3])};
+        // dS = GC dS' + QE^T dO - W^T dD
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dS[t][r] *= g[r];
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                dS[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdT(buf + Z::oQE + 8192 * s, offT[t][0], offT[t][1]),
+                                                                dOb[s], dS[t], 0, 0, 0);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                dS[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdT(buf + Z::oW + 8192 * s, offT[t][0], offT[t][1]),
+                                                                nDb[s], dS[t], 0, 0, 0);
+        }
+    };
+
+    if (prod) {
+        if (nc > 0) fetch(nc - 1);
+        wait_vmem_all();
+    } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) dS[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (gr.dht) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dS[t][r] = gr.dht[sbase + (16 * t + 4 * lg + r) * V + v0 + 16 * w + m];
+        }
+    }
+    __syncthreads();
+    for (int jc = nc - 1; jc >= 0; --jc) {
+        if (prod) {
+            // staging reads before this step's copies (the compiler would wait
+            // for the copies before later LDS reads); the warm-up loads are
+            // issued last and are the only ones allowed to stay in flight
+            if (jc + 1 < nc) drain(jc + 1);
+            if (jc > 0) fetch(jc - 1);
+            __builtin_amdgcn_sched_barrier(0);
+            warm(jc >= 2 ? jc - 2 : jc);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmem<NWARM>();
+        } else {
+            step(jc);
+        }
+        barrier_lds();
+    }
+    if (prod) {
+        if (nc > 0) drain(0);
+    } else if (gr.dh0) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gr.dh0[sbase + (16 * t + 4 * lg + r) * V + v0 + 16 * w + m] = dS[t][r];
+    }
+}
+
 // ------------------------------------------------------------------ V-local gradients
 // Threads of a V-local workgroup (its LDS allows one per CU): the bf16
 // variant takes 8 waves, two per 16-row tile splitting the column tiles, so
@@ -2094,9 +2311,13 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
             hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false>), dim3(cgrid), dim3(kThreads), 0,
                                st, p, chunk_off, slots, sb);
     }
-    if (want(2) && cgrid > 0)
-        hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,
-                           chunk_off, slots, sb);
+    if (want(2) && cgrid > 0) {
+        if constexpr (K == 128 && BF)
+            hipLaunchKernelGGL(chunk_state_bwd_pc_kernel, dim3(cgrid), dim3(256), 0, st, p, gr, chunk_off, slots, sb);
+        else
+            hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,
+                               chunk_off, slots, sb);
+    }
     if (want(3) && nblk > 0)
         hipLaunchKernelGGL((chunk_bwd_vlocal_kernel<K, V, BV, BF>), dim3(static_cast<unsigned>(nblk)),
                            dim3(vlocal_threads(BF)), 0, st, p, gr, chunk_off, slots, sb);

@@ -45,13 +45,17 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 
 // Piece q (1 KB) of a [64][C] bf16 tile whose global rows are `pitch`
 // elements apart: lane L fills LDS chunk L of the piece.
+// Global rows at or past rmax are read from row rmax - 1 instead (the caller
+// masks them), so that no access leaves the source rows.
 template <int C>
-__device__ __forceinline__ void dma_tile_piece(const uint16_t* g, int64_t pitch, uint8_t* lds, int q, int lane) {
+__device__ __forceinline__ void dma_tile_piece(const uint16_t* g, int64_t pitch, uint8_t* lds, int q, int lane,
+                                               int rmax = 1 << 30) {
     constexpr int CPR = C / 8;           // 16-byte chunks per row
     constexpr int RPP = 1024 / (2 * C);  // rows per piece
     const int r = q * RPP + lane / CPR;
     const int c = (lane % CPR) ^ swz<C>(r);
-    dma16(g + r * pitch + c * 8, lds + q * 1024);
+    const int rg = r < rmax ? r : rmax - 1;
+    dma16(g + rg * pitch + c * 8, lds + q * 1024);
 }
 
 // MFMA A fragment (16x16x32, bf16) from a swizzled [R][C] tile, rows m0..m0+15,
