@@ -1697,11 +1697,12 @@ struct KlocW8Smem {
     int unsafe[4];
 };
 
-// fp32 16 x 16 x 16 product with the lane's four B values given (step st
-// uses b[st], the B element at contraction index k0 + 4 (lane / 16) + st);
-// TRANS_A reads A[k][m] instead of A[m][k].
+// fp32 16 x 16 x 16 product accumulated into acc, with the lane's four B
+// values given (step st uses b[st], the B element at contraction index
+// k0 + 4 (lane / 16) + st); TRANS_A reads A[k][m] instead of A[m][k].
 template <bool TRANS_A>
-__device__ __forceinline__ f32x4 mma16_f32_rb(const float* A, int lda, int m0, const float* b, int k0, int lane) {
+__device__ __forceinline__ f32x4 mma16_f32_rb_acc(const float* A, int lda, int m0, const float* b, int k0, int lane,
+                                                  f32x4 acc) {
     const int m = m0 + (lane & 15), kq = k0 + 4 * (lane >> 4);
     float4 a4;
     if (TRANS_A) {
@@ -1712,12 +1713,20 @@ __device__ __forceinline__ f32x4 mma16_f32_rb(const float* A, int lda, int m0, c
     } else {
         a4 = *reinterpret_cast<const float4*>(A + m * lda + kq);
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.x, b[0], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.y, b[1], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.z, b[2], acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4.w, b[3], acc, 0, 0, 0);
     return acc;
+}
+
+// Sum over each row of 16 lanes, in every lane of the row (DPP row rotations).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
+    return v;
 }
 
 constexpr int kKlocW8Threads = 512;
@@ -1762,6 +1771,28 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
         const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
         const float rate = (p.gate_mode == GATE_LOGDECAY) ? 0.f : __expf(p.A_log[h]);
         __syncthreads();  // the previous slot is done with the shared buffers
+
+        // stage 1's operands are requested first, so that their latency
+        // overlaps the prologue's
+        const int rt = w & 3, ch = w >> 2;  // this wave's dA tiles: (rt, ch) and (rt, ch + 2)
+        ET tv[8], tbv[8], msv[8], akv[8];
+        {
+            const ET* gT = reinterpret_cast<const ET*>(base + X::kT);
+            const ET* gTB = reinterpret_cast<const ET*>(base + X::kDTB);
+            const ET* gMS = reinterpret_cast<const ET*>(base + X::kDMS);
+            const ET* gAK = reinterpret_cast<const ET*>(base + X::kAK);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                tv[e] = gT[t + NT * e];
+                tbv[e] = gTB[t + NT * e];
+                msv[e] = gMS[t + NT * e];
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    akv[4 * m + r] = gAK[(16 * rt + 4 * lg + r) * kChunk + 16 * (ch + 2 * m) + lc];
+        }
 
         // ---- 0. prologue (row-wise), cumulative sum, sub-block factors
         {
@@ -1860,25 +1891,6 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
         // ---- 1. dA = -T^T (dTB diag(beta)) T^T and the beta terms of TB and A.
         // Thread t owns column t % 64 of rows t / 64 + 8 e of T, dTB and dMS;
         // wave w owns the dA tiles (w % 4, w / 4) and (w % 4, w / 4 + 2).
-        const int rt = w & 3, ch = w >> 2;
-        ET tv[8], tbv[8], msv[8], akv[8];
-        {
-            const ET* gT = reinterpret_cast<const ET*>(base + X::kT);
-            const ET* gTB = reinterpret_cast<const ET*>(base + X::kDTB);
-            const ET* gMS = reinterpret_cast<const ET*>(base + X::kDMS);
-            const ET* gAK = reinterpret_cast<const ET*>(base + X::kAK);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                tv[e] = gT[t + NT * e];
-                tbv[e] = gTB[t + NT * e];
-                msv[e] = gMS[t + NT * e];
-            }
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    akv[4 * m + r] = gAK[(16 * rt + 4 * lg + r) * kChunk + 16 * (ch + 2 * m) + lc];
-        }
         {
             float part = 0.f;  // column t % 64
 #pragma unroll
@@ -1991,29 +2003,30 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
             for (int J = 0; J < 4; ++J)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) bv[4 * J + r] = ko[4 * J + r] * __expf(Ge[J] - Gc[4 * J + r]);
+            // f(J, I) scales column c of every term, so it is folded into the
+            // B values and the sums over J accumulate in the MFMA
+            f32x4 pq[4], pk[4];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
+            for (int I = 0; I < 4; ++I) pq[I] = pk[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int J = 0; J <= I; ++J) {
+            for (int J = 0; J < 4; ++J)
+#pragma unroll
+                for (int I = J; I < 4; ++I) {
                     const float f = fac(J, I);
-                    const f32x4 aq = mma16_f32_rb<false>(&s.x.sc.dM[0][0], LDD, kSub * I, &bv[4 * J], kSub * J, lane);
-                    const f32x4 ak = mma16_f32_rb<false>(&s.x.sc.dA[0][0], LDD, kSub * I, &bv[4 * J], kSub * J, lane);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        pq[r] += f * aq[r];
-                        pk[r] += f * ak[r];
-                    }
+                    const float bf[4] = {f * bv[4 * J], f * bv[4 * J + 1], f * bv[4 * J + 2], f * bv[4 * J + 3]};
+                    pq[I] = mma16_f32_rb_acc<false>(&s.x.sc.dM[0][0], LDD, kSub * I, bf, kSub * J, lane, pq[I]);
+                    pk[I] = mma16_f32_rb_acc<false>(&s.x.sc.dA[0][0], LDD, kSub * I, bf, kSub * J, lane, pk[I]);
                 }
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float a_ = __expf(Gc[4 * I + r] - Gr[I]);
-                    const float Pq = a_ * pq[r], Pk = a_ * pk[r];
+                    const float Pq = a_ * pq[I][r], Pk = a_ * pk[I][r];
                     dq[I][r] += Pq;
                     dk[I][r] += Pk;
                     dG[I][r] += qo[4 * I + r] * Pq + ko[4 * I + r] * Pk;
                 }
-            }
 
             // R terms: (q a) against dM, then (k a) against dA, a_i = e^(G_i - G_ref(I))
             f32x4 rr[4];
@@ -2032,9 +2045,8 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
 #pragma unroll
                     for (int I = J; I < 4; ++I) {
                         const float f = fac(J, I);
-                        const f32x4 acc = mma16_f32_rb<true>(dX, LDD, kSub * J, &bv[4 * I], kSub * I, lane);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) rr[J][r] += f * acc[r];
+                        const float bf[4] = {f * bv[4 * I], f * bv[4 * I + 1], f * bv[4 * I + 2], f * bv[4 * I + 3]};
+                        rr[J] = mma16_f32_rb_acc<true>(dX, LDD, kSub * J, bf, kSub * I, lane, rr[J]);
                     }
             }
 #pragma unroll
@@ -2181,13 +2193,8 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float vq = qo[4 * I + r] * dq[I][r];
-                    float vk = ko[4 * I + r] * dk[I][r];
-#pragma unroll
-                    for (int o = 1; o < 16; o <<= 1) {
-                        vq += __shfl_xor(vq, o, 64);
-                        vk += __shfl_xor(vk, o, 64);
-                    }
+                    const float vq = row16_sum(qo[4 * I + r] * dq[I][r]);
+                    const float vk = row16_sum(ko[4 * I + r] * dk[I][r]);
                     if (lc == 0) {
                         s.dots[0][w][kSub * I + 4 * lg + r] = vq;
                         s.dots[1][w][kSub * I + 4 * lg + r] = vk;
