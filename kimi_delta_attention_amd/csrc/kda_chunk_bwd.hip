@@ -124,9 +124,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
             const int tt = w + 4 * m;
             if (tt < NST) {
                 const int rt = tt / NCT, ct = tt % NCT;
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    gDS[(16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = MM::from_f32(dS[m][r]);
+                tile_store_t<MM>(gDS + v0 * K, K, 16 * rt, 16 * ct, dS[m], lane);  // dS'^T rows
                 tile_store_t<MM>(&dSt[0][0], LDK, 16 * rt, 16 * ct, dS[m], lane);
             }
         }
@@ -178,8 +176,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
 // dD = KD dS' + MS^T dO takes dS' from registers as its B operand.  The
 // token-row products QE^T dO and W^T dD take dO, read transposed, and -dD,
 // formed in registers, as B.  Waves 2-3 (producers) copy each chunk's
-// operand tiles and dO block into LDS a chunk ahead, warm L2 for the chunk
-// after, and store the staged dS' of the chunk before.
+// operand tiles and dO block into LDS a chunk ahead, warm L2 kWarmAhead
+// chunks ahead, and store the staged dS' of the chunk before.
 struct StatePcBwd {
     static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oDO = 57344, oGC = 61440;
     static constexpr int kBuf = 61952;  // one chunk's operand tiles and dO block
@@ -240,16 +238,17 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
             dma_tile_piece<32>(dO0, static_cast<int64_t>(H) * V, buf + Z::oDO, 2 * qq + pw, lane, rows_in(jc));
         if (pw == 1 && lane < 32) dma16(base + L::kGC + 16 * lane, buf + Z::oGC);
     };
-    // ---- producer: chunk jc's dS' from staging jc & 1 (16 rows x 16 columns per piece)
+    // ---- producer: chunk jc's dS' from staging jc & 1, as whole transposed
+    // rows (column v of dS': 128 values, 256 bytes)
     auto drain = [&](int jc) {
         const uint8_t* st = sms + (jc & 1) * 8192;
-        bf16x4_t xs[8];
+        bf16x8 xs[4];
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt) xs[kt] = tr4<128>(st, 16 * pw + 4 * lg, 16 * kt, lane);
-        uint16_t* gD = reinterpret_cast<uint16_t*>(slot(jc) + X::kDS) + v0;
+        for (int q = 0; q < 4; ++q)  // rows 16 pw + 4 q + lane / 16, 16-byte chunk lane % 16
+            xs[q] = *reinterpret_cast<const bf16x8*>(st + swz_off<128>(16 * pw + 4 * q + lg, 8 * m));
+        uint16_t* gD = reinterpret_cast<uint16_t*>(slot(jc) + X::kDS) + v0 * K;
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
-            *reinterpret_cast<bf16x4_t*>(gD + (16 * kt + m) * V + 16 * pw + 4 * lg) = xs[kt];
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<bf16x8*>(gD + (16 * pw + 4 * q + lg) * K + 8 * m) = xs[q];
     };
     // ---- producer: one 4-byte copy per 128-byte line of chunk jc's inputs
     auto warm = [&](int jc) {
@@ -371,7 +370,7 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
             if (jc + 1 < nc) drain(jc + 1);
             if (jc > 0) fetch(jc - 1);
             __builtin_amdgcn_sched_barrier(0);
-            warm(jc >= 2 ? jc - 2 : jc);
+            warm(jc >= kWarmAhead ? jc - kWarmAhead : jc);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmem<NWARM>();
         } else {
@@ -417,7 +416,7 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     constexpr int NKT = K / 16;    // column tiles of a [64][K] product
     constexpr int VE = 16 / sizeof(ET);          // elements per 16-byte vector
     constexpr int VPR = BV / VE;                 // vectors per block row
-    constexpr int NVS = K * VPR;                 // vectors of an S (or dS') block
+    constexpr int NVS = K * VPR;                 // vectors of an S (or dS') block (rows of S^T, K long)
     constexpr int NVO = kChunk * VPR;            // vectors of a dO block
     constexpr int PS = (NVS + NT - 1) / NT;
     constexpr int PO = (NVO + NT - 1) / NT;
@@ -465,7 +464,8 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     const IT* vg = static_cast<const IT*>(p.v);
     IT* dvg = static_cast<IT*>(gr.dv);
 
-    // next block's operands in registers: S and dS' rows key, dO rows i (16-byte
+    // next block's operands in registers: S and dS' (stored transposed: vector e
+    // holds keys (e / BV) VE .. +VE-1 of column e % BV), dO rows i (16-byte
     // vectors), and v in the accumulator layout of this wave's tiles
     f32x4 rS[PS], rD[PS], rO[PO];
     IT rv[TW][4];  // raw: converted where used, so that the request is not waited on here
@@ -475,9 +475,9 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         for (int m = 0; m < PS; ++m) {
             const int e = t + m * NT;
             if (NVS % NT == 0 || e < NVS) {
-                const int key = e / VPR, c = (e % VPR) * VE;
-                rS[m] = *reinterpret_cast<const f32x4*>(gS + key * V + v0 + c);
-                rD[m] = *reinterpret_cast<const f32x4*>(gDS + key * V + v0 + c);
+                const int c = e % BV, key = (e / BV) * VE;
+                rS[m] = *reinterpret_cast<const f32x4*>(gS + (v0 + c) * K + key);
+                rD[m] = *reinterpret_cast<const f32x4*>(gDS + (v0 + c) * K + key);
             }
         }
 #pragma unroll
@@ -505,15 +505,15 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         for (int m = 0; m < PS; ++m) {
             const int e = t + m * NT;
             if (NVS % NT == 0 || e < NVS) {
-                const int key = e / VPR, c = (e % VPR) * VE;
-                *reinterpret_cast<f32x4*>(&Sn[key][c]) = rS[m];
-                *reinterpret_cast<f32x4*>(&dSn[key][c]) = rD[m];
+                const int c = e % BV, key = (e / BV) * VE;
+                *reinterpret_cast<f32x4*>(&St[c][key]) = rS[m];
+                *reinterpret_cast<f32x4*>(&dSt[c][key]) = rD[m];
                 const ET* se = reinterpret_cast<const ET*>(&rS[m]);
                 const ET* de = reinterpret_cast<const ET*>(&rD[m]);
 #pragma unroll
                 for (int x = 0; x < VE; ++x) {
-                    St[c + x][key] = se[x];
-                    dSt[c + x][key] = de[x];
+                    Sn[key + x][c] = se[x];
+                    dSn[key + x][c] = de[x];
                 }
             }
         }

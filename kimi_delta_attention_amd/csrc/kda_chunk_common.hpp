@@ -123,8 +123,8 @@ struct PrepLayout {
 //   KE   [64][K]  k^ * exp(G)                     (ET)
 //   T    [64][64] (I + A)^-1                      (ET)
 //   AK   [64][64] strict_tril(k^ k^T decayed)      (ET)
-//   S    [K][V]   state entering the chunk         (ET)
-//   DS   [K][V]   gradient of the state leaving it (ET)
+//   S    [V][K]   state entering the chunk, transposed          (ET)
+//   DS   [V][K]   gradient of the state leaving it, transposed (ET)
 //   DQE, DKE, DKD [64][K]  gradients of the QE, KE, KD operands, summed over V (ET)
 //   DMS, DTB      [64][64] gradients of MS and TB, summed over V (ET)
 //   DGAM [K]      gradient of exp(G_last) (fp32)

@@ -612,7 +612,7 @@ struct Seg {
 // Forward state pass.  Per chunk, with the chunk's operands from its slot and
 // the fp32 state S (K x BV columns of this workgroup) in MFMA accumulators:
 //   WS = W S, D = U - WS, O = QE S + MS D, S = GC * S + KD^T D.
-// STORE writes each chunk's entry state (BwdExtra::kS, element type ET) for
+// STORE writes each chunk's entry state (BwdExtra::kS, transposed, element type ET) for
 // the backward; WRITE_O computes and stores the output.  The next chunk's
 // operands are prefetched into registers while the current chunk computes.
 template <int K, int V, int BV, bool BF, bool STORE, bool WRITE_O, int NT = kThreads>
@@ -703,9 +703,7 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
                 const int tt = w + NW * m;
                 if (tt < NST) {
                     const int rt = tt / NCT, ct = tt % NCT;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        gS[(16 * rt + 4 * (lane >> 4) + r) * V + v0 + 16 * ct + (lane & 15)] = MM::from_f32(S[m][r]);
+                    tile_store_t<MM>(gS + v0 * K, K, 16 * rt, 16 * ct, S[m], lane);  // S^T rows
                 }
             }
         }
@@ -817,6 +815,9 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
 // tiles go straight into the other half of a double-buffered LDS area, and the
 // previous chunk's output rows and entry state go out from LDS staging.
 // There is one barrier per chunk.
+// Chunks ahead of use that the state passes warm L2 for.
+constexpr int kWarmAhead = 4;
+
 struct StatePcFwd {
     static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oU = 57344, oGC = 61440;
     static constexpr int kBuf = 61952;  // one chunk's operand tiles
@@ -828,7 +829,8 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
     using Z = StatePcFwd;
     using L = PrepLayout<128, true>;
     constexpr int K = 128, V = 128, BV = 32, NVB = V / BV;
-    // L2 warm-up: the chunk after next, 128-byte lines split over the chain's
+    // L2 warm-up kWarmAhead chunks ahead (HBM latency exceeds a chunk step),
+    // 128-byte lines split over the chain's
     // NVB workgroups, NWARM loads per producer lane
     constexpr int NL_OP = WRITE_O ? 384 : 256;                       // [QE,] W, KD
     constexpr int NL = NL_OP + (WRITE_O ? 64 : 0) + 128 + 4;         // + MS, U, GC
@@ -882,28 +884,35 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
     // ---- producer: chunk jc's entry state and output rows from staging jc & 1
     uint16_t* og = static_cast<uint16_t*>(p.o);
     auto drain = [&](int jc) {
-        // every staging read first, then the stores
+        // every staging read first, then the stores.  The state goes out as
+        // whole transposed rows (column v of S: 128 values, 256 bytes); the
+        // output as 64-byte row segments, its staging read transposed twice
+        // per lane for 8 columns.
         const uint8_t* sts = sms + (jc & 1) * 8192;
         const uint8_t* sto = smo + (jc & 1) * 4096;
-        bf16x4_t xs[8], xo[4];
+        bf16x8 xs[4], xo[2];
         if (STORE)
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) xs[kt] = tr4<128>(sts, 16 * pw + 4 * lg, 16 * kt, lane);
+            for (int q = 0; q < 4; ++q)  // S^T rows 16 pw + 4 q + lane / 16, 16-byte chunk lane % 16
+                xs[q] = *reinterpret_cast<const bf16x8*>(sts + swz_off<128>(16 * pw + 4 * q + lg, 8 * m));
         if (WRITE_O)
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) xo[rq] = tr4<64>(sto, 16 * pw + 4 * lg, 16 * rq, lane);
+            for (int q = 0; q < 2; ++q) {  // token rows 32 pw + 16 q + m, columns 8 lg .. 8 lg + 7
+                const bf16x4_t lo = tr4<64>(sto, 8 * lg, 32 * pw + 16 * q, lane);
+                const bf16x4_t hi = tr4<64>(sto, 8 * lg + 4, 32 * pw + 16 * q, lane);
+                xo[q] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
         if (STORE) {
-            uint16_t* gS = reinterpret_cast<uint16_t*>(slot(jc) + BwdExtra<128, true>::kS) + v0;
+            uint16_t* gS = reinterpret_cast<uint16_t*>(slot(jc) + BwdExtra<128, true>::kS) + v0 * K;
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt)  // 16 state rows x 16 columns per piece
-                *reinterpret_cast<bf16x4_t*>(gS + (16 * kt + m) * V + 16 * pw + 4 * lg) = xs[kt];
+            for (int q = 0; q < 4; ++q)
+                *reinterpret_cast<bf16x8*>(gS + (16 * pw + 4 * q + lg) * K + 8 * m) = xs[q];
         }
         if (WRITE_O) {
 #pragma unroll
-            for (int rq = 0; rq < 4; ++rq) {  // 16 token rows x 16 columns per piece
-                const int row = jc * kChunk + 16 * rq + m;
-                if (row < len)
-                    *reinterpret_cast<bf16x4_t*>(og + ((start + row) * H + h) * V + v0 + 16 * pw + 4 * lg) = xo[rq];
+            for (int q = 0; q < 2; ++q) {
+                const int row = jc * kChunk + 32 * pw + 16 * q + m;
+                if (row < len) *reinterpret_cast<bf16x8*>(og + ((start + row) * H + h) * V + v0 + 8 * lg) = xo[q];
             }
         }
     };
@@ -957,53 +966,96 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
             for (int s = 0; s < 4; ++s)
                 *reinterpret_cast<bf16x8*>(sts + swz_off<128>(16 * w + m, 32 * s + 8 * lg)) = Sb[s];
         }
-        // W S and QE S for the strip's 64 x 16 block
+        // The LDS reads are issued in batches ahead of the products that use
+        // them (scheduling barriers keep that order), so that their latency
+        // overlaps MFMA work rather than stalling each product.
+        // W S and QE S for the strip's 64 x 16 block, one k-step of fragments ahead
+        constexpr int NA = WRITE_O ? 8 : 4;
+        bf16x8 fa[2][NA];
+        auto load_a = [&](int s, bf16x8* f) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f[rt] = rdA(buf + Z::oW + 4096 * rt, offA[s]);
+                if (WRITE_O) f[4 + rt] = rdA(buf + Z::oQE + 4096 * rt, offA[s]);
+            }
+        };
         f32x4 ws_[4], o[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) ws_[rt] = o[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        load_a(0, fa[0]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) load_a(s + 1, fa[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                ws_[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oW + 4096 * rt, offA[s]), Sb[s], ws_[rt],
-                                                                  0, 0, 0);
+                ws_[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][rt], Sb[s], ws_[rt], 0, 0, 0);
                 if (WRITE_O)
-                    o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oQE + 4096 * rt, offA[s]), Sb[s],
-                                                                    o[rt], 0, 0, 0);
+                    o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][4 + rt], Sb[s], o[rt], 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // operands of the remaining products: U rows, MS fragments, decay
+        // factors, and the first KD^T fragments
+        bf16x4_t u[4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            u[rt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(buf + Z::oU + 1024 * rt + offU));
+        bf16x8 fm[6];
+        if (WRITE_O) {
+#pragma unroll
+            for (int rt = 0, q = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int s = 0; s <= (rt >> 1); ++s, ++q) fm[q] = rdA(buf + Z::oMS + 2048 * rt, offM[s]);
+        }
+        f32x4 g[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) g[t] = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg));
+        bf16x8 fk[2][4];  // KD^T fragments of two column tiles, k-steps 0 and 1
+        auto load_k = [&](int t, bf16x8* f) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s) f[s] = rdT(buf + Z::oKD + 8192 * s, offT[t][0], offT[t][1]);
+        };
+        load_k(0, &fk[0][0]);
+        load_k(1, &fk[0][2]);
+        __builtin_amdgcn_sched_barrier(0);
         // D = U - W S
         f32x4 d[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-            const bf16x4_t u =
-                __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(buf + Z::oU + 1024 * rt + offU));
+        for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) d[rt][r] = static_cast<float>(u[r]) - ws_[rt][r];
-        }
+            for (int r = 0; r < 4; ++r) d[rt][r] = static_cast<float>(u[rt][r]) - ws_[rt][r];
         const bf16x8 Db[2] = {frag_acc_nat(d[0], d[1]), frag_acc_nat(d[2], d[3])};
         // O = QE S + MS D (MS lower triangular)
         if (WRITE_O) {
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
+            for (int rt = 0, q = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int s = 0; s <= (rt >> 1); ++s)
-                    o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oMS + 2048 * rt, offM[s]), Db[s],
-                                                                    o[rt], 0, 0, 0);
+                for (int s = 0; s <= (rt >> 1); ++s, ++q)
+                    o[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fm[q], Db[s], o[rt], 0, 0, 0);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
                 *reinterpret_cast<bf16x4_t*>(sto + swz_off<64>(16 * w + m, 16 * rt + 4 * lg)) =
                     bf16x4_t{(__bf16)o[rt][0], (__bf16)o[rt][1], (__bf16)o[rt][2], (__bf16)o[rt][3]};
         }
-        // S' = GC S + KD^T D
+        // S' = GC S + KD^T D, two column tiles at a time, the next two read ahead
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const f32x4 g = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg));
+        for (int tp = 0; tp < 4; ++tp) {
+            if (tp < 3) {
+                load_k(2 * tp + 2, &fk[(tp + 1) & 1][0]);
+                load_k(2 * tp + 3, &fk[(tp + 1) & 1][2]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[t][r] *= g[r];
+            for (int e = 0; e < 2; ++e) {
+                const int t = 2 * tp + e;
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
-                S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    rdT(buf + Z::oKD + 8192 * s, offT[t][0], offT[t][1]), Db[s], S[t], 0, 0, 0);
+                for (int r = 0; r < 4; ++r) S[t][r] *= g[t][r];
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    S[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[tp & 1][2 * e + s], Db[s], S[t], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
@@ -1029,7 +1081,7 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
             if (jc > 0) drain(jc - 1);
             if (jc + 1 < nc) fetch(jc + 1);
             __builtin_amdgcn_sched_barrier(0);
-            warm(jc + 2 < nc ? jc + 2 : jc);
+            warm(jc + kWarmAhead < nc ? jc + kWarmAhead : jc);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmem<NWARM>();
         } else {
