@@ -302,10 +302,28 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
             Sb[s] = frag_acc_nat(dS[2 * s], dS[2 * s + 1]);
             *reinterpret_cast<bf16x8*>(st + swz_off<128>(16 * w + m, 32 * s + 8 * lg)) = Sb[s];
         }
-        // dO block as the B operand over token rows (zero past the sequence end)
+        // The LDS reads are issued in batches ahead of the products that use
+        // them (scheduling barriers keep that order).
+        // dO block as the B operand over token rows (zero past the sequence
+        // end), the MS^T fragments, the decay factors and the first KD fragments
         bf16x8 dOb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) dOb[s] = rdT(buf + Z::oDO + 2048 * s, offD[0], offD[1]);
+        bf16x8 fm[6];
+#pragma unroll
+        for (int jt = 0, q = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int s = jt >> 1; s < 2; ++s, ++q) fm[q] = rdT(buf + Z::oMS + 4096 * s, offMT[jt][0], offMT[jt][1]);
+        f32x4 g[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) g[t] = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg));
+        bf16x8 fa[2][4];
+        auto load_a = [&](int s, bf16x8* f) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) f[rt] = rdA(buf + Z::oKD + 4096 * rt, offA[s]);
+        };
+        load_a(0, fa[0]);
+        __builtin_amdgcn_sched_barrier(0);
         const int rv = rows_in(jc);
         if (rv < kChunk) {
 #pragma unroll
@@ -314,37 +332,50 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
                 for (int j = 0; j < 8; ++j)
                     if (32 * s + 8 * lg + j >= rv) dOb[s][j] = static_cast<__bf16>(0.f);
         }
-        // dD = KD dS' + MS^T dO   (MS^T upper triangular)
+        // dD = KD dS' + MS^T dO   (MS^T upper triangular), KD one k-step ahead
         f32x4 dd[4];
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) dd[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) load_a(s + 1, fa[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-                dd[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdA(buf + Z::oKD + 4096 * rt, offA[s]), Sb[s], dd[rt],
-                                                                 0, 0, 0);
+                dd[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][rt], Sb[s], dd[rt], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // QE^T and W^T fragments of one state-row tile: [QE s0, QE s1, W s0, W s1]
+        bf16x8 fq[2][4];
+        auto load_q = [&](int t, bf16x8* f) {
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt)
+            for (int s = 0; s < 2; ++s) {
+                f[s] = rdT(buf + Z::oQE + 8192 * s, offT[t][0], offT[t][1]);
+                f[2 + s] = rdT(buf + Z::oW + 8192 * s, offT[t][0], offT[t][1]);
+            }
+        };
+        load_q(0, fq[0]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int s = jt >> 1; s < 2; ++s)
-                dd[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                    rdT(buf + Z::oMS + 4096 * s, offMT[jt][0], offMT[jt][1]), dOb[s], dd[jt], 0, 0, 0);
+        for (int jt = 0, q = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int s = jt >> 1; s < 2; ++s, ++q)
+                dd[jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fm[q], dOb[s], dd[jt], 0, 0, 0);
         const bf16x8 nDb[2] = {frag_acc_nat(-dd[0], -dd[1]), frag_acc_nat(-dd[2], -dd[3])};
-        // dS = GC dS' + QE^T dO - W^T dD
+        // dS = GC dS' + QE^T dO - W^T dD, one state-row tile of fragments ahead
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const f32x4 g = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg));
+            if (t < 7) load_q(t + 1, fq[(t + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dS[t][r] *= g[r];
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-                dS[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdT(buf + Z::oQE + 8192 * s, offT[t][0], offT[t][1]),
-                                                                dOb[s], dS[t], 0, 0, 0);
+            for (int r = 0; r < 4; ++r) dS[t][r] *= g[t][r];
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                dS[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rdT(buf + Z::oW + 8192 * s, offT[t][0], offT[t][1]),
-                                                                nDb[s], dS[t], 0, 0, 0);
+                dS[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq[t & 1][s], dOb[s], dS[t], 0, 0, 0);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                dS[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fq[t & 1][2 + s], nDb[s], dS[t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
