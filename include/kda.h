@@ -203,6 +203,38 @@ typedef struct {
 
 kda_status kda_recurrent_step(const kda_step_args *a);
 
+/* Stateful prefill of the short convolution: the conv_update of the
+ * "atlas_core/kimi_k3/kda.rs" page applied to every row of a sequence in
+ * order, carrying the window state in and out, so that a prompt primed here
+ * continues exactly in kda_recurrent_step (the prime -> decode hand-off of the
+ * "memra-engine kda_fixture_gpu.rs" page, GATE 2 and GATE 3).  For each
+ * sequence n and each of the C = 3*H*D channels c, over its rows t in order:
+ *     the window shifts left one slot, x[t, c] enters slot W-1,
+ *     y[t, c] = SiLU(sum_j conv_w[c, j] * window[j])   (no bias)
+ * The window starts as conv_state[n, c, :] (all zeros when conv_state is
+ * NULL) and, on return, conv_state[n, c, :] holds the window after the last
+ * row (unchanged for an empty sequence).  y is written split by channel block
+ * as the [rows, H, D] inputs of kda_chunk_fwd:
+ *     q = y[:, 0 : H*D],  k = y[:, H*D : 2*H*D],  v = y[:, 2*H*D : 3*H*D].
+ * The final states of that forward (output_final_state) and this conv state
+ * are the decode state of kda_recurrent_step.
+ * Every pointer must be 16-byte aligned; q, k and v must not overlap x_qkv or
+ * each other.  Errors as for the other entry points (nothing is launched). */
+typedef struct {
+    int B, T, H, D, W;         /* D in {32, 64, 128}; 1 <= W <= 8 */
+    const int32_t *cu_seqlens; /* device [N+1] for packed input (B = 1), or NULL (dense, N = B) */
+    int N;
+    kda_dtype x_dtype;         /* KDA_F32 or KDA_BF16 */
+    const void *x_qkv;         /* [rows, 3*H*D] pre-conv inputs, [q | k | v] */
+    const float *conv_w;       /* [3*H*D, W], slot 0 oldest */
+    float *conv_state;         /* [N, 3*H*D, W] in/out, oldest -> newest; or NULL */
+    kda_dtype y_dtype;         /* KDA_F32 or KDA_BF16: element type of q, k, v */
+    void *q, *k, *v;           /* [rows, H, D] each */
+    void *stream;              /* hipStream_t */
+} kda_conv_args;
+
+kda_status kda_conv_prefill(const kda_conv_args *a);
+
 /* Static description of a status code.  Thread-safe. */
 const char *kda_status_string(kda_status s);
 

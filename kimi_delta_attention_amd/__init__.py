@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import KDA_GATE_LOGDECAY, KDA_GATE_SAFE, KDA_GATE_SOFTPLUS  # noqa: F401
 
-__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_step", "chunk_fwd_workspace_bytes",
+__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_step", "conv_prefill", "chunk_fwd_workspace_bytes",
            "chunk_bwd_workspace_bytes", "KDA_GATE_LOGDECAY", "KDA_GATE_SAFE", "KDA_GATE_SOFTPLUS"]
 
 
@@ -229,6 +229,64 @@ def recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, *, A_log=None, dt_
     a.stream = _stream()
     _lib.check(_lib.load().kda_recurrent_step(ctypes.byref(a)), "kda_recurrent_step")
     return o
+
+
+def conv_prefill(x_qkv, conv_w, H, D, *, conv_state=None, cu_seqlens=None, out_dtype=None, out=None):
+    """Stateful prefill of the short convolution (kda_conv_prefill).
+
+    x_qkv is [B, T, 3*H*D] (dense) or [T, 3*H*D] with cu_seqlens (packed),
+    in float32 or bfloat16; conv_w is [3*H*D, W] float32; conv_state, if
+    given, is [N, 3*H*D, W] float32 and is updated in place to the window
+    after each sequence's last row (a zero history is used when it is None).
+    Returns (q, k, v), each shaped like x_qkv with H, D in place of its last
+    dimension, in out_dtype (default: x_qkv's dtype) -- the inputs of
+    chunk_kda, whose final states continue with this conv state in
+    recurrent_step."""
+    if conv_w.dim() != 2 or conv_w.shape[0] != 3 * H * D:
+        raise ValueError("conv_w must be [3*H*D, W]")
+    W = conv_w.shape[1]
+    if x_qkv.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("x_qkv must be float32 or bfloat16")
+    if cu_seqlens is not None:
+        if x_qkv.dim() != 2:
+            raise ValueError("packed x_qkv must be [T, 3*H*D]")
+        B, T = 1, x_qkv.shape[0]
+        N = cu_seqlens.numel() - 1
+        lead = (T,)
+    else:
+        if x_qkv.dim() != 3:
+            raise ValueError("dense x_qkv must be [B, T, 3*H*D]")
+        B, T = x_qkv.shape[0], x_qkv.shape[1]
+        N = B
+        lead = (B, T)
+    if x_qkv.shape[-1] != 3 * H * D:
+        raise ValueError("x_qkv's last dimension must be 3*H*D")
+    dev = x_qkv.device
+    _need(x_qkv, "x_qkv", None, dev)
+    _need(conv_w, "conv_w", torch.float32, dev)
+    if conv_state is not None:
+        if tuple(conv_state.shape) != (N, 3 * H * D, W):
+            raise ValueError("conv_state must be [N, 3*H*D, W]")
+        _need(conv_state, "conv_state", torch.float32, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", torch.int32, dev)
+    odt = x_qkv.dtype if out_dtype is None else out_dtype
+    if odt not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = tuple(torch.empty(*lead, H, D, dtype=odt, device=dev) for _ in range(3))
+    for name, t in zip("qkv", out):
+        _need(t, name, odt, dev)
+    a = _lib.ConvArgs()
+    a.B, a.T, a.H, a.D, a.W = B, T, H, D, W
+    a.cu_seqlens, a.N = _ptr(cu_seqlens), N
+    a.x_dtype = _lib.KDA_BF16 if x_qkv.dtype == torch.bfloat16 else _lib.KDA_F32
+    a.x_qkv, a.conv_w, a.conv_state = _ptr(x_qkv), _ptr(conv_w), _ptr(conv_state)
+    a.y_dtype = _lib.KDA_BF16 if odt == torch.bfloat16 else _lib.KDA_F32
+    a.q, a.k, a.v = (_ptr(t) for t in out)
+    a.stream = _stream()
+    _lib.check(_lib.load().kda_conv_prefill(ctypes.byref(a)), "kda_conv_prefill")
+    return out
 
 
 def chunk_bwd_workspace_bytes(q, k, v, g, beta, **kw) -> int:

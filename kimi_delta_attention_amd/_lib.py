@@ -60,10 +60,22 @@ class StepArgs(ctypes.Structure):
     ]
 
 
+class ConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("D", ctypes.c_int), ("W", ctypes.c_int),
+        ("cu_seqlens", _vp), ("N", ctypes.c_int),
+        ("x_dtype", ctypes.c_int),
+        ("x_qkv", _vp), ("conv_w", _vp), ("conv_state", _vp),
+        ("y_dtype", ctypes.c_int),
+        ("q", _vp), ("k", _vp), ("v", _vp),
+        ("stream", _vp),
+    ]
+
+
 # Every symbol include/kda.h declares.
 EXPORTS = ["kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace", "kda_chunk_bwd",
            "kda_chunk_bwd_stage", "kda_chunk_bwd_stages", "kda_chunk_bwd_workspace", "kda_recurrent_step",
-           "kda_status_string", "kda_version"]
+           "kda_conv_prefill", "kda_status_string", "kda_version"]
 
 _lib = None
 
@@ -94,6 +106,8 @@ def load(path: str = LIB_PATH):
     lib.kda_chunk_bwd_workspace.restype = ctypes.c_size_t
     lib.kda_recurrent_step.argtypes = [ctypes.POINTER(StepArgs)]
     lib.kda_recurrent_step.restype = ctypes.c_int
+    lib.kda_conv_prefill.argtypes = [ctypes.POINTER(ConvArgs)]
+    lib.kda_conv_prefill.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []

@@ -176,4 +176,39 @@ kda_status kda_recurrent_step(const kda_step_args* a) {
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_conv_prefill(const kda_conv_args* a) {
+    if (!a) return KDA_ERR_INVALID_ARG;
+    if (a->B <= 0 || a->T < 0 || a->H <= 0 || a->D <= 0 || a->W < 1 || a->W > 8) return KDA_ERR_INVALID_ARG;
+    if (!supported_dim(a->D)) return KDA_ERR_UNSUPPORTED;
+    if ((a->x_dtype != KDA_F32 && a->x_dtype != KDA_BF16) || (a->y_dtype != KDA_F32 && a->y_dtype != KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    int N = a->B;
+    if (a->cu_seqlens) {
+        if (a->B != 1 || a->N <= 0) return KDA_ERR_INVALID_ARG;
+        N = a->N;
+    }
+    const int64_t rows = static_cast<int64_t>(a->B) * a->T;
+    const int64_t C = 3 * static_cast<int64_t>(a->H) * a->D;
+    if (!a->conv_w) return KDA_ERR_INVALID_ARG;
+    if (rows > 0 && (!a->x_qkv || !a->q || !a->k || !a->v)) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {a->x_qkv, a->conv_w, a->conv_state, a->q, a->k, a->v};
+    for (const void* ptr : ptrs)
+        if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    if (rows * C > (int64_t(1) << 40)) return KDA_ERR_UNSUPPORTED;
+    const int64_t nb = (static_cast<int64_t>(a->T) + 63) / 64;
+    const int64_t block_bound = a->cu_seqlens ? nb + N : static_cast<int64_t>(N) * nb;
+    if (block_bound > INT32_MAX || (C / 4 + 255) / 256 > 65535 || N > 65535) return KDA_ERR_UNSUPPORTED;
+    kda::ConvParams p{};
+    p.B = a->B; p.T = a->T; p.H = a->H; p.D = a->D; p.W = a->W;
+    p.N = N;
+    p.cu_seqlens = a->cu_seqlens;
+    p.x_bf16 = a->x_dtype == KDA_BF16;
+    p.y_bf16 = a->y_dtype == KDA_BF16;
+    p.x = a->x_qkv; p.conv_w = a->conv_w; p.conv_state = a->conv_state;
+    p.q = a->q; p.k = a->k; p.v = a->v;
+    p.block_bound = rows > 0 ? static_cast<int>(block_bound) : 0;
+    hipError_t e = kda::launch_conv_prefill(p, static_cast<hipStream_t>(a->stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -29,6 +29,23 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 
+// Stateful short-conv prefill.  Sizes are validated by the caller.
+struct ConvParams {
+    int B, T, H, D, W;
+    int N;                     // number of sequences
+    const int32_t* cu_seqlens; // device [N+1] or nullptr (dense)
+    bool x_bf16, y_bf16;
+    const void* x;             // [rows, 3*H*D]
+    const float* conv_w;       // [3*H*D, W]
+    float* conv_state;         // [N, 3*H*D, W] in/out, or nullptr
+    void* q;                   // [rows, H*D] each
+    void* k;
+    void* v;
+    int block_bound;           // upper bound of the 64-row blocks over all sequences
+};
+
+hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t st);
+
 // Chunked path.  Sizes are validated by the caller.
 struct ChunkParams {
     int B, T, H, K, V;

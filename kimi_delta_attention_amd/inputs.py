@@ -110,6 +110,16 @@ def decode_init(N, H, D, W, *, seed, state_std=0.05, conv_std=0.05, w_std=0.5):
     return dict(conv_w=conv_w, state=state, conv_state=conv_state)
 
 
+def prefill_inputs(rows, H, D, *, seed, dtype=torch.bfloat16, lower_bound=-5.0):
+    """Prompt inputs of a stateful prefill, drawn like the decode steps: x
+    [rows, 3HD] (pre-conv q|k|v), log-decay g [rows, HD], beta logits [rows, H]."""
+    gen = _gen(seed)
+    x = _n(gen, (rows, 3 * H * D)).to(dtype)
+    g = lower_bound * torch.sigmoid(_n(gen, (rows, H * D)))
+    beta = _n(gen, (rows, H))
+    return dict(x=x, g=g.contiguous(), beta=beta)
+
+
 def decode_step_inputs(N, H, D, *, seed, step, dtype=torch.bfloat16, lower_bound=-5.0):
     """Per-step decode inputs: x [N, 3HD] (pre-conv q|k|v), log-decay g
     [N, HD] and beta logits [N, H].  Each step has its own generator seed."""

@@ -80,6 +80,8 @@ def _load():
         lib.or_chunk_fwd_chunked.argtypes = [P, ctypes.c_int, dp, dp, ctypes.c_int]
         lib.or_chunk_bwd.argtypes = [P, dp, dp, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
         lib.or_decode_step.argtypes = [ctypes.POINTER(_Decode), ctypes.c_int]
+        lib.or_conv_prefill.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, ctypes.c_int,
+                                        dp, dp, dp, dp]
         lib.or_gate_values.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp,
                                        ctypes.c_double, dp]
         lib.or_l2norm_rows.argtypes = [dp, ctypes.c_int, ctypes.c_int, ctypes.c_double, dp]
@@ -242,6 +244,37 @@ def decode_step(x, conv_w, conv_state, g, beta, state, *, A_log=None, dt_bias=No
     d.state, d.o = _ptr(st), _ptr(o)
     _load().or_decode_step(ctypes.byref(d), threads or default_threads())
     return o, cs, st
+
+
+def conv_prefill(x, conv_w, conv_state=None, cu_seqlens=None):
+    """Stateful prefill of the short conv: [kda.rs] conv_update applied to each
+    row of each sequence in order, from the sequence's conv state (zeros when
+    conv_state is None) to the window after its last row (the stateful prime
+    of the "memra-engine kda_fixture_gpu.rs" page, GATE 2 and GATE 3).
+
+    x is [B, T, C] (dense) or [T, C] with cu_seqlens (packed); conv_w [C, W];
+    conv_state [N, C, W].  Returns (y shaped like x, new conv_state or None),
+    float64; the inputs are not modified."""
+    x = np.ascontiguousarray(_f64(x))
+    conv_w = np.ascontiguousarray(_f64(conv_w))
+    C, W = conv_w.shape
+    if cu_seqlens is not None:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+        B, T, N = 1, x.shape[0], len(cu) - 1
+        assert x.shape == (T, C) and cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0)
+    else:
+        cu = None
+        B, T = x.shape[0], x.shape[1]
+        N = B
+        assert x.shape == (B, T, C)
+    cs = None
+    if conv_state is not None:
+        cs = np.ascontiguousarray(_f64(conv_state)).copy()
+        assert cs.shape == (N, C, W)
+    y = np.zeros_like(x)
+    _load().or_conv_prefill(B, T, C, W, None if cu is None else cu.ctypes.data, N, _ptr(x), _ptr(conv_w),
+                            _ptr(cs), _ptr(y))
+    return y, cs
 
 
 def gate(x, *, gate_mode, A_log=None, dt_bias=None, lower_bound=None):

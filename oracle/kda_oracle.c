@@ -659,6 +659,40 @@ int or_decode_step(or_decode *Dp, int threads) {
     return 0;
 }
 
+/* ------------------------------------------------------------------ */
+/* Stateful conv prefill: [kda.rs] conv_update applied to each row of a */
+/* sequence in order, starting from the sequence's conv state (zeros    */
+/* when conv_state is NULL) and leaving the window after its last row   */
+/* in it, so that a stateful prime continues exactly in the decode step */
+/* ("memra-engine kda_fixture_gpu.rs" page, GATE 2 and GATE 3).         */
+/* x, y [rows, C]; conv_w [C, W]; conv_state [N, C, W] in/out or NULL.  */
+/* cu NULL: N = B sequences of T rows each.                              */
+/* ------------------------------------------------------------------ */
+int or_conv_prefill(int B, int T, int C, int W, const int32_t *cu, int N, const double *x,
+                    const double *conv_w, double *conv_state, double *y) {
+    double *win = (double *)malloc(sizeof(double) * W);
+    int nseq = cu ? N : B;
+    for (int n = 0; n < nseq; ++n) {
+        long start = cu ? cu[n] : (long)n * T;
+        long len = cu ? (long)cu[n + 1] - cu[n] : T;
+        for (int c = 0; c < C; ++c) {
+            double *st = conv_state ? conv_state + ((size_t)n * C + c) * W : NULL;
+            for (int j = 0; j < W; ++j) win[j] = st ? st[j] : 0.0;
+            for (long t = 0; t < len; ++t) {
+                for (int j = 0; j + 1 < W; ++j) win[j] = win[j + 1];
+                win[W - 1] = x[(size_t)(start + t) * C + c];
+                double acc = 0.0;
+                for (int j = 0; j < W; ++j) acc += conv_w[(size_t)c * W + j] * win[j];
+                y[(size_t)(start + t) * C + c] = acc * or_sigmoid(acc);
+            }
+            if (st)
+                for (int j = 0; j < W; ++j) st[j] = win[j];
+        }
+    }
+    free(win);
+    return 0;
+}
+
 /* Exposed scalar pieces, for the closed-form pins. */
 void or_gate_values(int gate_mode, int H, int K, const double *x, const double *A_log,
                     const double *dt_bias, double lower_bound, double *g_out) {

@@ -151,6 +151,38 @@ def test_recurrent_step_empty_batch_is_noop(lib):
     assert lib.kda_recurrent_step(ctypes.byref(s)) == _lib.KDA_OK
 
 
+def _conv(**over):
+    a = _lib.ConvArgs()
+    a.B, a.T, a.H, a.D, a.W = 2, 100, 2, 128, 4
+    a.N = 0
+    a.x_dtype = a.y_dtype = _lib.KDA_BF16
+    for f in ("x_qkv", "conv_w", "conv_state", "q", "k", "v"):
+        setattr(a, f, FAKE)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(D=96), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(W=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(W=9), _lib.KDA_ERR_INVALID_ARG),
+    (dict(B=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(T=-1), _lib.KDA_ERR_INVALID_ARG),
+    (dict(x_dtype=3), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(y_dtype=3), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(conv_w=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(q=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(x_qkv=FAKE + 8), _lib.KDA_ERR_INVALID_ARG),
+    (dict(conv_state=FAKE + 4), _lib.KDA_ERR_INVALID_ARG),
+    (dict(cu_seqlens=FAKE, B=2, N=2), _lib.KDA_ERR_INVALID_ARG),  # packed input needs B = 1
+    (dict(cu_seqlens=FAKE, B=1, N=0), _lib.KDA_ERR_INVALID_ARG),
+])
+def test_conv_prefill_rejects_before_launch(lib, over, status):
+    a = _conv(**over)
+    assert lib.kda_conv_prefill(ctypes.byref(a)) == status
+
+
 def test_python_binding_rejects_host_tensors():
     import torch
     import kimi_delta_attention_amd as kda

@@ -406,6 +406,91 @@ def test_decode_sequence_equals_chunk_forward_on_conv_output():
     np.testing.assert_allclose(st, S_ref, rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------- conv prefill
+def _silu(a):
+    from scipy.special import expit
+    return a * expit(a)
+
+
+def test_conv_prefill_is_causal_convolution():
+    # the stateful prime is the textbook causal depthwise convolution (np.convolve)
+    # of each channel's input extended by its W-1 history samples; the state left
+    # behind is the last W samples of history ++ input
+    rng = np.random.default_rng(21)
+    C, W = 6, 4
+    w = rng.normal(size=(C, W))
+    lens = [0, 1, 2, 3, 7, 12]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    x = rng.normal(size=(int(cu[-1]), C))
+    s0 = rng.normal(size=(len(lens), C, W))
+    y, s1 = oracle.conv_prefill(x, w, s0, cu_seqlens=cu)
+    for n, L in enumerate(lens):
+        rows = slice(int(cu[n]), int(cu[n + 1]))
+        for c in range(C):
+            full = np.concatenate([s0[n, c], x[rows, c]])
+            np.testing.assert_array_equal(s1[n, c], full[-W:])
+            if L == 0:
+                continue
+            ref = np.convolve(full[1:], w[c, ::-1], mode="valid")  # ref[t] = sum_j w[c, j] full[1 + t + j]
+            np.testing.assert_allclose(y[rows, c], _silu(ref), rtol=1e-13, atol=1e-14)
+    # no state: a zero history, and the dense layout gives the same rows
+    yz, none = oracle.conv_prefill(x[None, :7], w)
+    assert none is None
+    for c in range(C):
+        ref = np.convolve(np.concatenate([np.zeros(W - 1), x[:7, c]]), w[c, ::-1], mode="valid")
+        np.testing.assert_allclose(yz[0, :, c], _silu(ref), rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("split", [0, 1, 2, 3, 5, 9])
+def test_conv_prefill_state_carry_split(split):
+    # memra GATE 3 analogue: one sequence primed in two stateful pieces equals a
+    # single prime, including pieces shorter than the window
+    rng = np.random.default_rng(22)
+    C, W, T = 5, 4, 9
+    w = rng.normal(size=(C, W))
+    x = rng.normal(size=(1, T, C))
+    s0 = rng.normal(size=(1, C, W))
+    y, s = oracle.conv_prefill(x, w, s0)
+    y1, sa = oracle.conv_prefill(x[:, :split], w, s0)
+    y2, sb = oracle.conv_prefill(x[:, split:], w, sa)
+    np.testing.assert_array_equal(np.concatenate([y1, y2], axis=1), y)
+    np.testing.assert_array_equal(sb, s)
+
+
+def test_conv_prefill_then_decode_equals_all_decode():
+    # memra GATE 2 analogue: prime t0 tokens (conv prefill, then the chunk forward
+    # from the decode state), then decode the rest; outputs and both states equal
+    # decoding every token
+    rng = np.random.default_rng(23)
+    N, H, D, W, T, t0 = 2, 2, 4, 4, 8, 5
+    CH = 3 * H * D
+    w = rng.normal(size=(CH, W)) * 0.5
+    cs0 = rng.normal(size=(N, CH, W)) * 0.05
+    st0 = rng.normal(size=(N, H, D, D)) * 0.05
+    xs = rng.normal(size=(N, T, CH))
+    gs = -5.0 / (1.0 + np.exp(-rng.normal(size=(N, T, H * D))))
+    bs = rng.normal(size=(N, T, H))
+    cs, st, outs = cs0.copy(), st0.copy(), []
+    for t in range(T):
+        o, cs, st = oracle.decode_step(xs[:, t], w, cs, gs[:, t], bs[:, t], st)
+        outs.append(o)
+    o_all = np.stack(outs, 1)
+    y, cs1 = oracle.conv_prefill(xs[:, :t0], w, cs0)
+    q = y[..., :H * D].reshape(N, t0, H, D)
+    k = y[..., H * D:2 * H * D].reshape(N, t0, H, D)
+    v = y[..., 2 * H * D:].reshape(N, t0, H, D)
+    o_p, st1 = oracle.chunk_fwd(q, k, v, gs[:, :t0].reshape(N, t0, H, D), bs[:, :t0], initial_state=st0,
+                                use_qk_l2norm=True, use_beta_sigmoid=True)
+    np.testing.assert_allclose(o_p.reshape(N, t0, H * D), o_all[:, :t0], rtol=1e-12, atol=1e-14)
+    outs = []
+    for t in range(t0, T):
+        o, cs1, st1 = oracle.decode_step(xs[:, t], w, cs1, gs[:, t], bs[:, t], st1)
+        outs.append(o)
+    np.testing.assert_allclose(np.stack(outs, 1), o_all[:, t0:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_array_equal(cs1, cs)
+    np.testing.assert_allclose(st1, st, rtol=1e-12, atol=1e-14)
+
+
 def test_shared_input_recipes_have_stated_shapes():
     w = inputs.workload("fwd_small")
     assert tuple(w["q"].shape) == (1, 128, 2, 32) and w["q"].dtype.is_floating_point
