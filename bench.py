@@ -114,6 +114,13 @@ def decode_bytes(N, H, D, W, x_elt):
             + N * H * 4 + 3 * H * D * W * 4 + N * H * D * 4)
 
 
+def conv_bytes(rows, n_seq, H, D, W, elt):
+    """x read once and q, k, v written once (elt bytes each); conv_w read; the
+    conv state read and written once per sequence."""
+    C = 3 * H * D
+    return 2 * rows * C * elt + C * W * 4 + 2 * n_seq * C * W * 4
+
+
 # ---------------------------------------------------------------- workloads
 def make_hybrid(seed, device):
     from kimi_delta_attention_amd import inputs
@@ -210,6 +217,57 @@ def run_decode(steps, warmup, device):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
                      "algorithmic_bytes": algo, "kernel_ms": kern_ms},
+    }
+
+
+def run_prefill(steps, warmup, device):
+    """Stateful prefill of the packed batch: the short conv from a conv state
+    (kda_conv_prefill), then the chunk forward from a decode state with the
+    final states out -- the prime that hands over to decode."""
+    import kimi_delta_attention_amd as kda
+    from kimi_delta_attention_amd import inputs
+    H, D, W = H_H, D_H, 4
+    cu = torch.tensor(HYBRID_CU, dtype=torch.int32, device=device)
+    n_seq = len(HYBRID_CU) - 1
+    pre = inputs.prefill_inputs(T_H, H, D, seed=inputs.SEEDS["decode"] + 1)
+    init = inputs.decode_init(n_seq, H, D, W, seed=inputs.SEEDS["decode"] + 2)
+    x = pre["x"].to(device)
+    g = pre["g"].to(device).reshape(1, T_H, H, D)
+    beta = pre["beta"].to(device).reshape(1, T_H, H)
+    cw = init["conv_w"].to(device)
+    cs = init["conv_state"].to(device)
+    st0 = init["state"].to(device)
+    qkv = tuple(torch.empty(T_H, H, D, dtype=torch.bfloat16, device=device) for _ in range(3))
+    op = kda.ChunkOp(*(t.unsqueeze(0) for t in qkv), g, beta, initial_state=st0, output_final_state=True,
+                     use_qk_l2norm_in_kernel=True, use_beta_sigmoid_in_kernel=True, cu_seqlens=cu)
+    stream = torch.cuda.current_stream()
+
+    def one():
+        kda.conv_prefill(x, cw, H, D, conv_state=cs, cu_seqlens=cu, out=qkv)
+
+    for _ in range(warmup):
+        one()
+        op.forward()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        e[0].record(stream)
+        one()
+        e[1].record(stream)
+        op.forward()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    conv_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    algo = conv_bytes(T_H, n_seq, H, D, W, 2)
+    return {
+        "metric": "stateful prefill tokens/s", "unit": "tokens/s", "value": T_H / ((conv_ms + fwd_ms) * 1e-3),
+        "workload": f"conv{W} prefill + chunk forward from decode states, packed 1024/2048/1024/4096 "
+                    f"(T{T_H}), H{H} d{D}, bf16 x/q/k/v, fp32 states",
+        "conv_ms": conv_ms, "chunk_fwd_ms": fwd_ms,
+        "conv_roofline": {"bound": "hbm", "kernel": "conv_prefill_kernel", "achieved": algo / (conv_ms * 1e-3) / 1e9,
+                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": algo / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": algo},
     }
 
 
@@ -381,6 +439,9 @@ def main():
     if not args.no_decode:
         _log("timing decode")
         line["decode"] = run_decode(max(args.steps, 10), args.warmup, device)
+        _log("timing stateful prefill")
+        line["prefill"] = run_prefill(max(args.steps // 2, 5), min(args.warmup, 3), device)
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         _log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(host0)

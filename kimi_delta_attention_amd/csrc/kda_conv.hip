@@ -24,19 +24,27 @@ namespace kda {
 typedef uint16_t u16x4_ __attribute__((ext_vector_type(4)));
 
 constexpr int kConvRows = 64;     // rows per block
+constexpr int kConvGroup = 8;     // rows whose loads are issued together
 constexpr int kConvThreads = 256;
 constexpr int kConvMaxW = 8;
 
+// Four consecutive elements: Raw is the loaded form (kept until use), f32x4
+// the arithmetic form.
 template <typename T> struct Vec4;
 template <> struct Vec4<float> {
-    __device__ __forceinline__ static f32x4 load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    using Raw = f32x4;
+    __device__ __forceinline__ static Raw raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    __device__ __forceinline__ static f32x4 cvt(Raw r) { return r; }
+    __device__ __forceinline__ static f32x4 load(const float* p) { return raw(p); }
     __device__ __forceinline__ static void store(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
 };
 template <> struct Vec4<uint16_t> {
-    __device__ __forceinline__ static f32x4 load(const uint16_t* p) {
-        const u16x4_ u = *reinterpret_cast<const u16x4_*>(p);
+    using Raw = u16x4_;
+    __device__ __forceinline__ static Raw raw(const uint16_t* p) { return *reinterpret_cast<const u16x4_*>(p); }
+    __device__ __forceinline__ static f32x4 cvt(Raw u) {
         return f32x4{bf16_bits_to_f32(u[0]), bf16_bits_to_f32(u[1]), bf16_bits_to_f32(u[2]), bf16_bits_to_f32(u[3])};
     }
+    __device__ __forceinline__ static f32x4 load(const uint16_t* p) { return cvt(raw(p)); }
     __device__ __forceinline__ static void store(uint16_t* p, f32x4 v) {
         const u16x4_ u = {f32_to_bf16_bits(v[0]), f32_to_bf16_bits(v[1]), f32_to_bf16_bits(v[2]), f32_to_bf16_bits(v[3])};
         *reinterpret_cast<u16x4_*>(p) = u;
@@ -73,7 +81,7 @@ __device__ __forceinline__ bool conv_block(const ConvParams& p, int s, int& n, i
     return false;
 }
 
-template <typename XT, typename YT>
+template <typename XT, typename YT, int M>
 __global__ __launch_bounds__(kConvThreads) void conv_prefill_kernel(ConvParams p) {
     const int64_t HD = static_cast<int64_t>(p.H) * p.D;
     const int64_t C = 3 * HD;
@@ -85,51 +93,60 @@ __global__ __launch_bounds__(kConvThreads) void conv_prefill_kernel(ConvParams p
     const int W = p.W;
     const XT* x = static_cast<const XT*>(p.x);
 
-    f32x4 w[kConvMaxW];  // w[k][e]: weight of window slot k for channel c0 + e
+    // A fixed window of M >= W slots, newest last, so that every register
+    // index is static: slot s holds the input M-1-s rows back, and the W
+    // weights sit in the last W slots (zeros before them).
+    f32x4 w[M];  // w[s][e]: weight of slot s for channel c0 + e
 #pragma unroll
-    for (int k = 0; k < kConvMaxW; ++k)
-        if (k < W)
+    for (int s = 0; s < M; ++s)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[k][e] = p.conv_w[(c0 + e) * W + k];
+        for (int e = 0; e < 4; ++e) w[s][e] = s >= M - W ? p.conv_w[(c0 + e) * W + s - (M - W)] : 0.f;
 
-    // window slots 0 .. W-2 hold the inputs at rows r0 - (W-1) .. r0 - 1
+    // slots 0 .. M-2 hold the inputs at rows r0 - (M-1) .. r0 - 1 (zero where
+    // no weight reads them)
     const int r0 = j * kConvRows;
-    f32x4 win[kConvMaxW];
+    f32x4 win[M];
 #pragma unroll
-    for (int k = 0; k < kConvMaxW - 1; ++k) {
-        if (k < W - 1) {
-            const int tau = r0 - (W - 1) + k;
+    for (int s = 0; s < M - 1; ++s) {
+        const int tau = r0 - (M - 1) + s;
+        win[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s >= M - W) {
             if (tau >= 0) {
-                win[k] = Vec4<XT>::load(x + (start + tau) * C + c0);
+                win[s] = Vec4<XT>::load(x + (start + tau) * C + c0);
             } else if (p.conv_state) {
                 // time tau < 0 sits in slot W + tau of the sequence's state
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    win[k][e] = p.conv_state[(static_cast<int64_t>(n) * C + c0 + e) * W + W + tau];
-            } else {
-                win[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    win[s][e] = p.conv_state[(static_cast<int64_t>(n) * C + c0 + e) * W + W + tau];
             }
         }
     }
 
     const int part = static_cast<int>(c0 / HD);  // 0 q, 1 k, 2 v
     YT* dst = static_cast<YT*>(part == 0 ? p.q : (part == 1 ? p.k : p.v)) + (c0 - part * HD);
+    // rows in groups of kConvGroup, every load of a group issued before its first use
     const int r1 = min(len, r0 + kConvRows);
-    for (int r = r0; r < r1; ++r) {
-        win[W - 1] = Vec4<XT>::load(x + (start + r) * C + c0);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int rb = r0; rb < r1; rb += kConvGroup) {
+        typename Vec4<XT>::Raw xin[kConvGroup];
 #pragma unroll
-        for (int k = 0; k < kConvMaxW; ++k)
-            if (k < W)
+        for (int i = 0; i < kConvGroup; ++i)
+            if (rb + i < r1) xin[i] = Vec4<XT>::raw(x + (start + rb + i) * C + c0);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[e] += w[k][e] * win[k][e];
-        f32x4 y;
+        for (int i = 0; i < kConvGroup; ++i) {
+            if (rb + i >= r1) continue;  // (not break: the loop must unroll)
+            win[M - 1] = Vec4<XT>::cvt(xin[i]);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = acc[e] * sigmoidf_(acc[e]);
-        Vec4<YT>::store(dst + (start + r) * HD, y);
+            for (int s = 0; s < M; ++s)
 #pragma unroll
-        for (int k = 0; k < kConvMaxW - 1; ++k)
-            if (k < W - 1) win[k] = win[k + 1];
+                for (int e = 0; e < 4; ++e) acc[e] += w[s][e] * win[s][e];
+            f32x4 y;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = acc[e] * sigmoidf_(acc[e]);
+            Vec4<YT>::store(dst + (start + rb + i) * HD, y);
+#pragma unroll
+            for (int s = 0; s < M - 1; ++s) win[s] = win[s + 1];
+        }
     }
 }
 
@@ -173,14 +190,17 @@ hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t st) {
     const unsigned gx = static_cast<unsigned>(p.block_bound);
     const unsigned gy = static_cast<unsigned>((C / 4 + kConvThreads - 1) / kConvThreads);
     if (gx > 0) {
+        const dim3 grid(gx, gy), block(kConvThreads);
+        auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, block, 0, st, p); };
+        const bool w4 = p.W <= 4;
         if (p.x_bf16 && p.y_bf16)
-            hipLaunchKernelGGL((conv_prefill_kernel<uint16_t, uint16_t>), dim3(gx, gy), dim3(kConvThreads), 0, st, p);
+            w4 ? go(conv_prefill_kernel<uint16_t, uint16_t, 4>) : go(conv_prefill_kernel<uint16_t, uint16_t, 8>);
         else if (p.x_bf16)
-            hipLaunchKernelGGL((conv_prefill_kernel<uint16_t, float>), dim3(gx, gy), dim3(kConvThreads), 0, st, p);
+            w4 ? go(conv_prefill_kernel<uint16_t, float, 4>) : go(conv_prefill_kernel<uint16_t, float, 8>);
         else if (p.y_bf16)
-            hipLaunchKernelGGL((conv_prefill_kernel<float, uint16_t>), dim3(gx, gy), dim3(kConvThreads), 0, st, p);
+            w4 ? go(conv_prefill_kernel<float, uint16_t, 4>) : go(conv_prefill_kernel<float, uint16_t, 8>);
         else
-            hipLaunchKernelGGL((conv_prefill_kernel<float, float>), dim3(gx, gy), dim3(kConvThreads), 0, st, p);
+            w4 ? go(conv_prefill_kernel<float, float, 4>) : go(conv_prefill_kernel<float, float, 8>);
     }
     if (p.conv_state && p.N > 0) {
         const unsigned sx = static_cast<unsigned>((C + kConvThreads - 1) / kConvThreads);
