@@ -195,7 +195,7 @@ kda_status kda_conv_prefill(const kda_conv_args* a) {
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return KDA_ERR_INVALID_ARG;
     if (rows * C > (int64_t(1) << 40)) return KDA_ERR_UNSUPPORTED;
-    const int64_t nb = (static_cast<int64_t>(a->T) + 63) / 64;
+    const int64_t nb = (static_cast<int64_t>(a->T) + kda::kConvBlockRows - 1) / kda::kConvBlockRows;
     const int64_t block_bound = a->cu_seqlens ? nb + N : static_cast<int64_t>(N) * nb;
     if (block_bound > INT32_MAX || (C / 4 + 255) / 256 > 65535 || N > 65535) return KDA_ERR_UNSUPPORTED;
     kda::ConvParams p{};

@@ -39,7 +39,9 @@ template <> struct Elem<uint16_t> {  // bf16 stored as raw bits
     }
 };
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// The hardware reciprocal (1 ulp) instead of an IEEE divide: the divide's
+// scale/fixup sequence is about ten instructions per call.
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // log(1 + e^x) without overflow: max(x, 0) + log1p(e^-|x|).
 __device__ __forceinline__ float softplusf_(float x) {

@@ -30,6 +30,9 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
 
 // Stateful short-conv prefill.  Sizes are validated by the caller.
+// Rows of one sequence that one conv-prefill workgroup slides over.
+constexpr int kConvBlockRows = 64;
+
 struct ConvParams {
     int B, T, H, D, W;
     int N;                     // number of sequences
@@ -41,7 +44,7 @@ struct ConvParams {
     void* q;                   // [rows, H*D] each
     void* k;
     void* v;
-    int block_bound;           // upper bound of the 64-row blocks over all sequences
+    int block_bound;           // upper bound of the kConvBlockRows-row blocks over all sequences
 };
 
 hipError_t launch_conv_prefill(const ConvParams& p, hipStream_t st);

@@ -23,9 +23,9 @@ def _cu(lens):
                                              (torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)])
 @pytest.mark.parametrize("W", [4, 2, 8])
 def test_conv_prefill_packed(x_dtype, y_dtype, W):
-    # ragged lengths: empty, shorter than the window, and across 64-row blocks
+    # ragged lengths: empty, shorter than the window, and across the 32-row blocks
     H, D = 2, 64
-    lens = [0, 1, 2, 3, 63, 64, 65, 130]
+    lens = [0, 1, 2, 3, 31, 32, 33, 63, 64, 65, 130]
     cu = _cu(lens)
     T, N, HD = int(cu[-1]), len(lens), H * D
     print(f"conv prefill packed lens={lens} H={H} D={D} W={W} x={x_dtype} y={y_dtype}", flush=True)
@@ -141,7 +141,7 @@ def test_prime_then_decode_equals_decode(dtype, D):
     check("conv_state", cs, cs_ref, TOL_F32)
 
 
-@pytest.mark.parametrize("split", [1, 2, 3, 63, 64, 65, 127])
+@pytest.mark.parametrize("split", [1, 2, 3, 31, 33, 63, 64, 65, 127])
 def test_two_piece_prime_equals_one(split):
     # GATE 3: one 130-token prompt primed in two stateful pieces equals a single prime
     H, D, W, total = 2, 32, 4, 130
