@@ -215,7 +215,7 @@ def run_decode(steps, warmup, device):
         "ms_per_step": wall * 1e3, "workload": f"decode N{N} H{H} d{D} conv{W} bf16 x, fp32 state",
         "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": algo / (kern_ms * 1e-3) / 1e9,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": None,
+                     "frac": algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": stored_traffic("decode"),
                      "algorithmic_bytes": algo, "kernel_ms": kern_ms},
     }
 
@@ -267,7 +267,8 @@ def run_prefill(steps, warmup, device):
         "conv_ms": conv_ms, "chunk_fwd_ms": fwd_ms,
         "conv_roofline": {"bound": "hbm", "kernel": "conv_prefill_kernel", "achieved": algo / (conv_ms * 1e-3) / 1e9,
                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": algo / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": algo},
+                          "frac": algo / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": algo,
+                          "traffic": stored_traffic("prefill.conv")},
     }
 
 
