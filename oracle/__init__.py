@@ -82,6 +82,8 @@ def _load():
         lib.or_decode_step.argtypes = [ctypes.POINTER(_Decode), ctypes.c_int]
         lib.or_conv_prefill.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, ctypes.c_int,
                                         dp, dp, dp, dp]
+        lib.or_output_gate.argtypes = [ctypes.c_int64, ctypes.c_int, dp, dp, ctypes.c_double, dp]
+        lib.or_output_gate_bwd.argtypes = [ctypes.c_int64, ctypes.c_int, dp, dp, ctypes.c_double, dp, dp, dp]
         lib.or_gate_values.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, dp, dp, dp,
                                        ctypes.c_double, dp]
         lib.or_l2norm_rows.argtypes = [dp, ctypes.c_int, ctypes.c_int, ctypes.c_double, dp]
@@ -275,6 +277,33 @@ def conv_prefill(x, conv_w, conv_state=None, cu_seqlens=None):
     _load().or_conv_prefill(B, T, C, W, None if cu is None else cu.ctypes.data, N, _ptr(x), _ptr(conv_w),
                             _ptr(cs), _ptr(y))
     return y, cs
+
+
+def output_gate(o, g, eps=1e-5):
+    """Full-rank output gate ([kda.rs] full_rank_output_gate): per head,
+    sigmoid(g) * o / sqrt(mean(o^2) + eps).  o and g are [..., V] with the head
+    dimension last; eps defaults to the gated output norm's 1e-5 of the
+    "memra-engine kda_fixture_gpu.rs" page.  Returns float64 like o."""
+    o = np.ascontiguousarray(_f64(o))
+    g = np.ascontiguousarray(_f64(g))
+    assert o.shape == g.shape
+    V = o.shape[-1]
+    y = np.zeros_like(o)
+    _load().or_output_gate(o.size // V, V, _ptr(o), _ptr(g), float(eps), _ptr(y))
+    return y
+
+
+def output_gate_bwd(o, g, dy, eps=1e-5):
+    """Reverse mode of output_gate: returns (dO, dg) for the upstream dy."""
+    o = np.ascontiguousarray(_f64(o))
+    g = np.ascontiguousarray(_f64(g))
+    dy = np.ascontiguousarray(_f64(dy))
+    assert o.shape == g.shape == dy.shape
+    V = o.shape[-1]
+    dO = np.zeros_like(o)
+    dg = np.zeros_like(o)
+    _load().or_output_gate_bwd(o.size // V, V, _ptr(o), _ptr(g), float(eps), _ptr(dy), _ptr(dO), _ptr(dg))
+    return dO, dg
 
 
 def gate(x, *, gate_mode, A_log=None, dt_bias=None, lower_bound=None):

@@ -15,6 +15,8 @@
  *              chunk_kda argument list, flag semantics and gate formulas.
  *   [Primus]   "KDA <=> FLA Parity in Primus": section "What changed and why",
  *              table A (in-kernel gate fused with its cumulative sum).
+ *   [kda.rs] also gives full_rank_output_gate, the per-head gated RMS norm
+ *              of the output; "memra-engine kda_fixture_gpu.rs" gives its eps.
  *
  * Parity status of every function is given in its comment; all of them are
  * pinned by the CPU tests (hand-worked recurrence, closed forms, invariants,
@@ -690,6 +692,51 @@ int or_conv_prefill(int B, int T, int C, int W, const int32_t *cu, int N, const 
         }
     }
     free(win);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Full-rank output gate: [kda.rs] full_rank_output_gate.  For each of  */
+/* the n_vec = rows*H vectors of length V (one head of one row):        */
+/*     ms = (1/V) sum_v o[v]^2,   r = 1 / sqrt(ms + eps),               */
+/*     y[v] = sigmoid(g[v]) * o[v] * r.                                 */
+/* eps is that of the gated output norm ("memra-engine                  */
+/* kda_fixture_gpu.rs" page: 1e-5), supplied by the caller.             */
+/* ------------------------------------------------------------------ */
+int or_output_gate(int64_t n_vec, int V, const double *o, const double *g, double eps, double *y) {
+    for (int64_t i = 0; i < n_vec; ++i) {
+        const double *oi = o + i * V, *gi = g + i * V;
+        double ss = 0.0;
+        for (int v = 0; v < V; ++v) ss += oi[v] * oi[v];
+        const double r = 1.0 / sqrt(ss / V + eps);
+        for (int v = 0; v < V; ++v) y[i * V + v] = or_sigmoid(gi[v]) * oi[v] * r;
+    }
+    return 0;
+}
+
+/* Reverse mode of or_output_gate (chain rule written out; no page prints */
+/* it).  With a = sigmoid(g), r as above and the upstream dy:            */
+/*     dg[v] = dy[v] * o[v] * r * a[v] (1 - a[v])                         */
+/*     do[v] = r a[v] dy[v]  +  o[v] * dr/dms * (2/V) * sum_u a[u] dy[u] o[u] */
+/* where dr/dms = -r^3 / 2, so the second term is                         */
+/*     -(r^3 / V) * o[v] * sum_u a[u] dy[u] o[u].                          */
+int or_output_gate_bwd(int64_t n_vec, int V, const double *o, const double *g, double eps,
+                       const double *dy, double *dO, double *dg) {
+    for (int64_t i = 0; i < n_vec; ++i) {
+        const double *oi = o + i * V, *gi = g + i * V, *di = dy + i * V;
+        double ss = 0.0, sa = 0.0;
+        for (int v = 0; v < V; ++v) {
+            ss += oi[v] * oi[v];
+            sa += or_sigmoid(gi[v]) * di[v] * oi[v];
+        }
+        const double r = 1.0 / sqrt(ss / V + eps);
+        const double dr_dms = -0.5 * r * r * r;
+        for (int v = 0; v < V; ++v) {
+            const double a = or_sigmoid(gi[v]);
+            dg[i * V + v] = di[v] * oi[v] * r * a * (1.0 - a);
+            dO[i * V + v] = r * a * di[v] + oi[v] * dr_dms * (2.0 / V) * sa;
+        }
+    }
     return 0;
 }
 

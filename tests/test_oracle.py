@@ -497,3 +497,77 @@ def test_shared_input_recipes_have_stated_shapes():
     assert float(w["g"].max()) <= 0.0 and float(w["g"].min()) >= -5.0
     d = inputs.decode_step_inputs(2, 3, 4, seed=1, step=0)
     assert tuple(d["x"].shape) == (2, 36)
+
+
+# ---------------------------------------------------------------- output gate
+# [kda.rs] full_rank_output_gate: per head, sigmoid(g) * o / sqrt(mean(o^2) + eps).
+
+def test_output_gate_hand_worked_vector():
+    # o = (3, 4): mean of squares 12.5; with eps = 0, r = 1/sqrt(12.5).
+    # g = (0, ln 3): sigmoid = (1/2, 3/4).
+    y = oracle.output_gate(np.array([[3.0, 4.0]]), np.array([[0.0, math.log(3.0)]]), eps=0.0)
+    r = 1.0 / math.sqrt(12.5)
+    np.testing.assert_allclose(y, [[0.5 * 3.0 * r, 0.75 * 4.0 * r]], rtol=1e-15)
+
+
+def test_output_gate_constant_row_closed_form():
+    # a row of one value c: y[v] = sigmoid(g[v]) * c / sqrt(c^2 + eps)
+    c, eps, V = -2.5, 1e-5, 8
+    g = np.linspace(-3, 3, V)
+    y = oracle.output_gate(np.full((1, V), c), g[None, :], eps=eps)
+    want = [1.0 / (1.0 + math.exp(-gv)) * c / math.sqrt(c * c + eps) for gv in g]
+    np.testing.assert_allclose(y[0], want, rtol=1e-14)
+
+
+def test_output_gate_is_per_head_and_scale_free():
+    rng = np.random.default_rng(5)
+    o = rng.standard_normal((3, 2, 16))
+    g = rng.standard_normal((3, 2, 16))
+    y = oracle.output_gate(o, g, eps=0.0)
+    # with eps = 0 the norm removes any positive scale of a head's vector
+    o2 = o.copy()
+    o2[:, 1] *= 7.0
+    y2 = oracle.output_gate(o2, g, eps=0.0)
+    np.testing.assert_allclose(y2, y, rtol=1e-13, atol=1e-15)
+    # changing head 1 leaves head 0 alone: the norm does not mix heads
+    o3 = o.copy()
+    o3[:, 1] = rng.standard_normal((3, 16))
+    y3 = oracle.output_gate(o3, g, eps=1e-5)
+    np.testing.assert_array_equal(y3[:, 0], oracle.output_gate(o, g, eps=1e-5)[:, 0])
+
+
+def test_output_gate_open_gate_is_rms_norm():
+    # g -> +inf opens the gate: mean(y^2) = ms / (ms + eps)
+    rng = np.random.default_rng(6)
+    o = 0.01 * rng.standard_normal((4, 32))
+    eps = 1e-5
+    y = oracle.output_gate(o, np.full_like(o, 60.0), eps=eps)
+    ms = (o ** 2).mean(axis=1)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), ms / (ms + eps), rtol=1e-12)
+
+
+def test_output_gate_bwd_central_differences():
+    rng = np.random.default_rng(7)
+    o = rng.standard_normal((3, 2, 8))
+    g = rng.standard_normal((3, 2, 8))
+    dy = rng.standard_normal((3, 2, 8))
+    eps, h = 0.3, 1e-6  # a large eps keeps both terms of dO of similar size
+    dO, dg = oracle.output_gate_bwd(o, g, dy, eps=eps)
+    loss = lambda oo, gg: float((dy * oracle.output_gate(oo, gg, eps=eps)).sum())
+    for idx in [(0, 0, 0), (1, 1, 3), (2, 0, 7), (2, 1, 5)]:
+        e = np.zeros_like(o)
+        e[idx] = h
+        fd_o = (loss(o + e, g) - loss(o - e, g)) / (2 * h)
+        fd_g = (loss(o, g + e) - loss(o, g - e)) / (2 * h)
+        assert abs(fd_o - dO[idx]) < 1e-8 * max(1.0, abs(fd_o)), (idx, fd_o, dO[idx])
+        assert abs(fd_g - dg[idx]) < 1e-8 * max(1.0, abs(fd_g)), (idx, fd_g, dg[idx])
+
+
+def test_output_gate_bwd_is_orthogonal_to_o_at_zero_eps():
+    # scaling o does not change y when eps = 0, so the gradient has no component along o
+    rng = np.random.default_rng(8)
+    o = rng.standard_normal((5, 64))
+    g = rng.standard_normal((5, 64))
+    dy = rng.standard_normal((5, 64))
+    dO, _ = oracle.output_gate_bwd(o, g, dy, eps=0.0)
+    np.testing.assert_allclose((dO * o).sum(axis=1), 0.0, atol=1e-12)
