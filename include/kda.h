@@ -180,7 +180,10 @@ int kda_chunk_bwd_stages(void);
  *       window[c] shifts left one slot (slot 0 leaves), x[c] enters slot W-1,
  *       y[c] = SiLU(sum_j conv_w[c, j] * window[c, j])   (no bias)
  *   then per head the recurrence step above on (q, k, v) = y, writing
- *   o [N, H*D] (fp32) and updating state in place. */
+ *   o [N, H*D] (fp32) and updating state in place.
+ * With out_gate set, o receives the full-rank output gate of the step's
+ * output instead (kda_output_gate below, same page: full_rank_output_gate),
+ * computed in the same kernel. */
 typedef struct {
     int N, H, D, W;          /* D = head dim (K = V = D) in {32, 64, 128}; 1 <= W <= 8 */
     kda_dtype x_dtype;       /* KDA_F32 or KDA_BF16 */
@@ -199,6 +202,8 @@ typedef struct {
     float *state;            /* [N, H, D, D] in/out, key index major */
     float *o;                /* [N, H*D] fp32 */
     void *stream;            /* hipStream_t */
+    const void *out_gate;    /* [N, H*D] in x_dtype, or NULL: o is the plain output */
+    float out_gate_eps;      /* NaN means 1e-5; must be >= 0 */
 } kda_step_args;
 
 kda_status kda_recurrent_step(const kda_step_args *a);
@@ -234,6 +239,35 @@ typedef struct {
 } kda_conv_args;
 
 kda_status kda_conv_prefill(const kda_conv_args *a);
+
+/* Full-rank output gate (full_rank_output_gate of the
+ * "atlas_core/kimi_k3/kda.rs" page), per head of every row:
+ *     r = 1 / sqrt(mean_v(o[v]^2) + eps),   y[v] = sigmoid(g[v]) * o[v] * r
+ * over the V values of the head (no weight).  The gated output norm of the
+ * "memra-engine kda_fixture_gpu.rs" page uses eps = 1e-5, the default here.
+ * o is the output of kda_chunk_fwd or kda_recurrent_step; y feeds the output
+ * projection.  y may be o (in place); any other overlap is not allowed.
+ * Every pointer must be 16-byte aligned.  Nothing is launched on error. */
+typedef struct {
+    int rows, H, V;            /* V in {32, 64, 128, 256}; rows >= 0 */
+    kda_dtype o_dtype;         /* KDA_F32 or KDA_BF16: o, y (and dy, dO) */
+    kda_dtype g_dtype;         /* KDA_F32 or KDA_BF16: g (and dg) */
+    float eps;                 /* NaN means 1e-5; must be >= 0 */
+    const void *o;             /* [rows, H, V] */
+    const void *g;             /* [rows, H, V] gate input (before the sigmoid) */
+    void *y;                   /* [rows, H, V] */
+    void *stream;              /* hipStream_t */
+} kda_gate_args;
+
+kda_status kda_output_gate(const kda_gate_args *a);
+
+/* Reverse mode of kda_output_gate (the chain rule written out; no page prints
+ * it): with a = sigmoid(g) and r as above, for the upstream gradient dy,
+ *     dg[v] = dy[v] * o[v] * r * a[v] * (1 - a[v])
+ *     dO[v] = r * a[v] * dy[v] - (r^3 / V) * o[v] * sum_u a[u] * dy[u] * o[u].
+ * a->y is not read.  dy and dO have o_dtype, dg has g_dtype; dO may be dy and
+ * dg may be g (in place); no other overlap.  dO is the dO of kda_chunk_bwd. */
+kda_status kda_output_gate_bwd(const kda_gate_args *a, const void *dy, void *dO, void *dg);
 
 /* Static description of a status code.  Thread-safe. */
 const char *kda_status_string(kda_status s);

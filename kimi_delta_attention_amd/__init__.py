@@ -20,7 +20,8 @@ import torch
 from . import _lib
 from ._lib import KDA_GATE_LOGDECAY, KDA_GATE_SAFE, KDA_GATE_SOFTPLUS  # noqa: F401
 
-__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_step", "conv_prefill", "chunk_fwd_workspace_bytes",
+__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_step", "conv_prefill", "output_gate", "output_gate_bwd",
+           "chunk_fwd_workspace_bytes",
            "chunk_bwd_workspace_bytes", "KDA_GATE_LOGDECAY", "KDA_GATE_SAFE", "KDA_GATE_SOFTPLUS"]
 
 
@@ -193,10 +194,11 @@ def chunk_kda_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bi
 
 def recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, *, A_log=None, dt_bias=None, lower_bound=None,
                    use_gate_in_kernel=False, safe_gate=False, gate_mode=None, use_qk_l2norm=True,
-                   use_beta_sigmoid=True, scale=None, out=None):
+                   use_beta_sigmoid=True, scale=None, out=None, out_gate=None, out_gate_eps=None):
     """One decode token per sequence with the short-conv update
     (kda_recurrent_step).  conv_state and state are updated in place.
-    Returns o [N, H*D] fp32."""
+    Returns o [N, H*D] fp32; with out_gate ([N, H*D], x_qkv's dtype) it is the
+    full-rank output gate of the step's output, computed in the same kernel."""
     if state.dim() != 4 or state.shape[2] != state.shape[3]:
         raise ValueError("state must be [N, H, D, D]")
     N, H, D, _ = state.shape
@@ -227,8 +229,60 @@ def recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, *, A_log=None, dt_
     a.scale = float("nan") if scale is None else float(scale)
     a.state, a.o = _ptr(state), _ptr(o)
     a.stream = _stream()
+    if out_gate is not None:
+        if tuple(out_gate.shape) != (N, H * D):
+            raise ValueError("out_gate must be [N, H*D]")
+        _need(out_gate, "out_gate", x_qkv.dtype, dev)
+        a.out_gate = _ptr(out_gate)
+    a.out_gate_eps = float("nan") if out_gate_eps is None else float(out_gate_eps)
     _lib.check(_lib.load().kda_recurrent_step(ctypes.byref(a)), "kda_recurrent_step")
     return o
+
+
+def _gate_args(o, g, eps):
+    if o.dim() < 2 or tuple(g.shape) != tuple(o.shape):
+        raise ValueError("o and g must have one shape [..., H, V]")
+    for name, t in (("o", o), ("g", g)):
+        if t.dtype not in (torch.float32, torch.bfloat16):
+            raise ValueError(f"{name} must be float32 or bfloat16")
+        _need(t, name, None, o.device)
+    a = _lib.GateArgs()
+    a.H, a.V = o.shape[-2], o.shape[-1]
+    a.rows = o.numel() // (a.H * a.V) if o.numel() else 0
+    a.o_dtype = _lib.KDA_BF16 if o.dtype == torch.bfloat16 else _lib.KDA_F32
+    a.g_dtype = _lib.KDA_BF16 if g.dtype == torch.bfloat16 else _lib.KDA_F32
+    a.eps = float("nan") if eps is None else float(eps)
+    a.o, a.g = _ptr(o), _ptr(g)
+    a.stream = _stream()
+    return a
+
+
+def output_gate(o, g, *, eps=None, out=None):
+    """Full-rank output gate (kda_output_gate): per head, sigmoid(g) * o /
+    sqrt(mean(o^2) + eps) over the last dimension V of o [..., H, V]; eps
+    defaults to 1e-5.  out may be o itself (in place)."""
+    a = _gate_args(o, g, eps)
+    y = out if out is not None else torch.empty_like(o)
+    if tuple(y.shape) != tuple(o.shape):
+        raise ValueError("out must have o's shape")
+    _need(y, "out", o.dtype, o.device)
+    a.y = _ptr(y)
+    _lib.check(_lib.load().kda_output_gate(ctypes.byref(a)), "kda_output_gate")
+    return y
+
+
+def output_gate_bwd(o, g, dy, *, eps=None):
+    """Reverse mode of output_gate (kda_output_gate_bwd): returns (dO, dg) for
+    the upstream gradient dy, in o's and g's dtypes."""
+    a = _gate_args(o, g, eps)
+    if tuple(dy.shape) != tuple(o.shape):
+        raise ValueError("dy must have o's shape")
+    _need(dy, "dy", o.dtype, o.device)
+    dO = torch.empty_like(o)
+    dg = torch.empty_like(g)
+    _lib.check(_lib.load().kda_output_gate_bwd(ctypes.byref(a), _ptr(dy), _ptr(dO), _ptr(dg)),
+               "kda_output_gate_bwd")
+    return dO, dg
 
 
 def conv_prefill(x_qkv, conv_w, H, D, *, conv_state=None, cu_seqlens=None, out_dtype=None, out=None):

@@ -57,6 +57,7 @@ class StepArgs(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("state", _vp), ("o", _vp),
         ("stream", _vp),
+        ("out_gate", _vp), ("out_gate_eps", ctypes.c_float),
     ]
 
 
@@ -72,10 +73,20 @@ class ConvArgs(ctypes.Structure):
     ]
 
 
+class GateArgs(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int), ("H", ctypes.c_int), ("V", ctypes.c_int),
+        ("o_dtype", ctypes.c_int), ("g_dtype", ctypes.c_int),
+        ("eps", ctypes.c_float),
+        ("o", _vp), ("g", _vp), ("y", _vp),
+        ("stream", _vp),
+    ]
+
+
 # Every symbol include/kda.h declares.
 EXPORTS = ["kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace", "kda_chunk_bwd",
            "kda_chunk_bwd_stage", "kda_chunk_bwd_stages", "kda_chunk_bwd_workspace", "kda_recurrent_step",
-           "kda_conv_prefill", "kda_status_string", "kda_version"]
+           "kda_conv_prefill", "kda_output_gate", "kda_output_gate_bwd", "kda_status_string", "kda_version"]
 
 _lib = None
 
@@ -108,6 +119,10 @@ def load(path: str = LIB_PATH):
     lib.kda_recurrent_step.restype = ctypes.c_int
     lib.kda_conv_prefill.argtypes = [ctypes.POINTER(ConvArgs)]
     lib.kda_conv_prefill.restype = ctypes.c_int
+    lib.kda_output_gate.argtypes = [ctypes.POINTER(GateArgs)]
+    lib.kda_output_gate.restype = ctypes.c_int
+    lib.kda_output_gate_bwd.argtypes = [ctypes.POINTER(GateArgs), _vp, _vp, _vp]
+    lib.kda_output_gate_bwd.restype = ctypes.c_int
     lib.kda_status_string.argtypes = [ctypes.c_int]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_conv.hip", "kda_chunk_fwd.hip", "kda_chunk_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_conv.hip", "kda_gate.hip", "kda_chunk_fwd.hip", "kda_chunk_bwd.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 arithmetic is disabled for all device code (see the comment in

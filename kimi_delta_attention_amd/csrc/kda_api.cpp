@@ -14,6 +14,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 bool supported_dim(int d) { return d == 32 || d == 64 || d == 128; }
 
+// eps of the gated output norm when the caller passes NaN: the value the
+// "memra-engine kda_fixture_gpu.rs" page uses for it.
+constexpr float kGateEpsDefault = 1e-5f;
+
 // Shared validation of the chunk arguments; fills the internal launch params.
 kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forward) {
     if (!a) return KDA_ERR_INVALID_ARG;
@@ -172,7 +176,61 @@ kda_status kda_recurrent_step(const kda_step_args* a) {
     p.use_qk_l2norm = a->use_qk_l2norm; p.use_beta_sigmoid = a->use_beta_sigmoid;
     p.scale = (std::isnan(a->scale) || a->scale <= 0.f) ? 1.0f / std::sqrt(static_cast<float>(a->D)) : a->scale;
     p.state = a->state; p.o = a->o;
+    if (a->out_gate) {
+        if (!(std::isnan(a->out_gate_eps) || a->out_gate_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
+        p.out_gate = a->out_gate;
+        p.out_gate_eps = std::isnan(a->out_gate_eps) ? kGateEpsDefault : a->out_gate_eps;
+    }
     hipError_t e = kda::launch_decode(p, static_cast<hipStream_t>(a->stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+static kda_status check_gate(const kda_gate_args* a, kda::GateParams& p) {
+    if (!a) return KDA_ERR_INVALID_ARG;
+    if (a->rows < 0 || a->H <= 0 || a->V <= 0) return KDA_ERR_INVALID_ARG;
+    if (a->V != 32 && a->V != 64 && a->V != 128 && a->V != 256) return KDA_ERR_UNSUPPORTED;
+    if ((a->o_dtype != KDA_F32 && a->o_dtype != KDA_BF16) || (a->g_dtype != KDA_F32 && a->g_dtype != KDA_BF16))
+        return KDA_ERR_UNSUPPORTED;
+    if (!(std::isnan(a->eps) || a->eps >= 0.f)) return KDA_ERR_INVALID_ARG;
+    p = kda::GateParams{};
+    p.n_vec = static_cast<int64_t>(a->rows) * a->H;
+    p.V = a->V;
+    p.o_bf16 = a->o_dtype == KDA_BF16;
+    p.g_bf16 = a->g_dtype == KDA_BF16;
+    p.eps = std::isnan(a->eps) ? kGateEpsDefault : a->eps;
+    p.o = a->o;
+    p.g = a->g;
+    if (p.n_vec * a->V > (int64_t(1) << 40)) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+kda_status kda_output_gate(const kda_gate_args* a) {
+    kda::GateParams p;
+    kda_status s = check_gate(a, p);
+    if (s != KDA_OK) return s;
+    if (p.n_vec == 0) return KDA_OK;
+    if (!a->o || !a->g || !a->y) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {a->o, a->g, a->y};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    p.y = a->y;
+    hipError_t e = kda::launch_output_gate(p, static_cast<hipStream_t>(a->stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_output_gate_bwd(const kda_gate_args* a, const void* dy, void* dO, void* dg) {
+    kda::GateParams p;
+    kda_status s = check_gate(a, p);
+    if (s != KDA_OK) return s;
+    if (p.n_vec == 0) return KDA_OK;
+    if (!a->o || !a->g || !dy || !dO || !dg) return KDA_ERR_INVALID_ARG;
+    const void* ptrs[] = {a->o, a->g, dy, dO, dg};
+    for (const void* ptr : ptrs)
+        if (!aligned16(ptr)) return KDA_ERR_INVALID_ARG;
+    p.dy = dy;
+    p.dO = dO;
+    p.dg = dg;
+    hipError_t e = kda::launch_output_gate_bwd(p, static_cast<hipStream_t>(a->stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -17,7 +17,7 @@
 //
 // Bytes per (sequence, head) at D = 128, W = 4: state 2 x 64 KiB, conv state
 // 2 x 6 KiB, x 768 B (bf16), g 512 B, conv_w 6 KiB (shared by all sequences),
-// o 512 B, beta 4 B.
+// o 512 B, beta 4 B, and with the output gate its input, 256 B (bf16).
 #include "kda_device.hpp"
 #include "kda_launch.hpp"
 
@@ -48,6 +48,7 @@ __global__ __launch_bounds__(decode_threads<D>()) void decode_step_kernel(Decode
     __shared__ float red_q[RG][D];    // partial S~^T q
     __shared__ float delta[D];
     __shared__ float scal[4];         // 1/|q|, 1/|k|, q^.k^
+    __shared__ float osq[(D + kWave - 1) / kWave];  // per-wave sums of o^2 (output gate)
 
     // ---- issue the state loads first: they do not depend on the conv.
     float* Sg = p.state + (static_cast<int64_t>(n) * H + h) * D * D;
@@ -142,7 +143,11 @@ __global__ __launch_bounds__(decode_threads<D>()) void decode_step_kernel(Decode
         red_q[rg][4 * cq + j] = pq[j];
     }
     __syncthreads();
+    const int64_t oi = static_cast<int64_t>(n) * HD + static_cast<int64_t>(h) * D + t;
+    const XT* og = static_cast<const XT*>(p.out_gate);
+    float ov = 0.0f, gv = 0.0f;
     if (t < D) {
+        if (og) gv = Elem<XT>::load(og, oi);
         float a = 0.0f, b = 0.0f;
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
@@ -151,9 +156,22 @@ __global__ __launch_bounds__(decode_threads<D>()) void decode_step_kernel(Decode
         }
         const float d = beta * (ys[2][t] - a);
         delta[t] = d;
-        p.o[static_cast<int64_t>(n) * HD + static_cast<int64_t>(h) * D + t] = p.scale * (b + kq * d);
+        ov = p.scale * (b + kq * d);
+        if (!og) p.o[oi] = ov;
+    }
+    // full-rank output gate of the same page: sigmoid(g) * o / sqrt(mean(o^2) + eps)
+    // over the head's D outputs, which are the first D threads
+    if (og && t / kWave < (D + kWave - 1) / kWave) {
+        const float s2 = wave_sum(ov * ov);  // threads t >= D hold 0
+        if (t % kWave == 0) osq[t / kWave] = s2;
     }
     __syncthreads();
+    if (og && t < D) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int w = 0; w < (D + kWave - 1) / kWave; ++w) ss += osq[w];
+        p.o[oi] = sigmoidf_(gv) * ov * rsqrtf(ss * (1.0f / D) + p.out_gate_eps);
+    }
 
     // ---- rank-1 write and store
     const f32x4 dq = *reinterpret_cast<const f32x4*>(&delta[4 * cq]);

@@ -56,6 +56,31 @@ __device__ __forceinline__ float gate_eff(int mode, float x, float rate, float b
     return -rate * softplusf_(z);
 }
 
+typedef uint16_t u16x4_ __attribute__((ext_vector_type(4)));
+
+// Four consecutive elements: Raw is the loaded form (kept until use), f32x4
+// the arithmetic form.
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    using Raw = f32x4;
+    __device__ __forceinline__ static Raw raw(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+    __device__ __forceinline__ static f32x4 cvt(Raw r) { return r; }
+    __device__ __forceinline__ static f32x4 load(const float* p) { return raw(p); }
+    __device__ __forceinline__ static void store(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+};
+template <> struct Vec4<uint16_t> {
+    using Raw = u16x4_;
+    __device__ __forceinline__ static Raw raw(const uint16_t* p) { return *reinterpret_cast<const u16x4_*>(p); }
+    __device__ __forceinline__ static f32x4 cvt(Raw u) {
+        return f32x4{bf16_bits_to_f32(u[0]), bf16_bits_to_f32(u[1]), bf16_bits_to_f32(u[2]), bf16_bits_to_f32(u[3])};
+    }
+    __device__ __forceinline__ static f32x4 load(const uint16_t* p) { return cvt(raw(p)); }
+    __device__ __forceinline__ static void store(uint16_t* p, f32x4 v) {
+        const u16x4_ u = {f32_to_bf16_bits(v[0]), f32_to_bf16_bits(v[1]), f32_to_bf16_bits(v[2]), f32_to_bf16_bits(v[3])};
+        *reinterpret_cast<u16x4_*>(p) = u;
+    }
+};
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);

@@ -25,9 +25,29 @@ struct DecodeParams {
     float scale;
     float* state;
     float* o;
+    const void* out_gate;      // [N, H*D] in x's element type, or nullptr (plain output)
+    float out_gate_eps;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);
+
+// Full-rank output gate over n_vec head vectors of V values.  Sizes are
+// validated by the caller.
+struct GateParams {
+    int64_t n_vec;             // rows * H
+    int V;                     // 32, 64, 128 or 256
+    bool o_bf16, g_bf16;       // element types of o / y / dy / dO, and of g / dg
+    float eps;
+    const void* o;
+    const void* g;
+    void* y;                   // forward output
+    const void* dy;            // reverse mode: upstream gradient and outputs
+    void* dO;
+    void* dg;
+};
+
+hipError_t launch_output_gate(const GateParams& p, hipStream_t st);
+hipError_t launch_output_gate_bwd(const GateParams& p, hipStream_t st);
 
 // Stateful short-conv prefill.  Sizes are validated by the caller.
 // Rows of one sequence that one conv-prefill workgroup slides over.

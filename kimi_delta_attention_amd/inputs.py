@@ -120,6 +120,16 @@ def prefill_inputs(rows, H, D, *, seed, dtype=torch.bfloat16, lower_bound=-5.0):
     return dict(x=x, g=g.contiguous(), beta=beta)
 
 
+def gate_inputs(rows, H, V, *, seed, dtype=torch.bfloat16, g_dtype=None):
+    """Output-gate inputs: the attention output o, the gate input g and an
+    upstream gradient dy, each [rows, H, V] ~ N(0, 1) (g in g_dtype, default dtype)."""
+    gen = _gen(seed)
+    o = _n(gen, (rows, H, V)).to(dtype)
+    g = _n(gen, (rows, H, V)).to(g_dtype or dtype)
+    dy = _n(gen, (rows, H, V)).to(dtype)
+    return dict(o=o, g=g, dy=dy)
+
+
 def decode_step_inputs(N, H, D, *, seed, step, dtype=torch.bfloat16, lower_bound=-5.0):
     """Per-step decode inputs: x [N, 3HD] (pre-conv q|k|v), log-decay g
     [N, HD] and beta logits [N, H].  Each step has its own generator seed."""

@@ -189,3 +189,50 @@ def test_python_binding_rejects_host_tensors():
     x = torch.zeros(1, 4, 1, 32)
     with pytest.raises(ValueError):
         kda.chunk_kda(x, x, x, x, torch.zeros(1, 4, 1))
+
+
+def _gate(**over):
+    a = _lib.GateArgs()
+    a.rows, a.H, a.V = 4, 2, 128
+    a.o_dtype = a.g_dtype = _lib.KDA_BF16
+    a.eps = float("nan")
+    for f in ("o", "g", "y"):
+        setattr(a, f, FAKE)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(V=48), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(V=512), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(o_dtype=3), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(g_dtype=3), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(rows=-1), _lib.KDA_ERR_INVALID_ARG),
+    (dict(H=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(eps=-1e-5), _lib.KDA_ERR_INVALID_ARG),
+    (dict(y=None), _lib.KDA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 8), _lib.KDA_ERR_INVALID_ARG),
+])
+def test_output_gate_rejects_before_launch(lib, over, status):
+    a = _gate(**over)
+    assert lib.kda_output_gate(ctypes.byref(a)) == status
+
+
+def test_output_gate_bwd_rejects_before_launch(lib):
+    a = _gate()
+    assert lib.kda_output_gate_bwd(ctypes.byref(a), None, FAKE, FAKE) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_output_gate_bwd(ctypes.byref(a), FAKE, FAKE + 4, FAKE) == _lib.KDA_ERR_INVALID_ARG
+    assert lib.kda_output_gate_bwd(ctypes.byref(_gate(eps=-1.0)), FAKE, FAKE, FAKE) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_output_gate_empty_is_noop(lib):
+    # no rows: nothing to read, nothing launched, null pointers allowed
+    a = _gate(rows=0, o=None, g=None, y=None)
+    assert lib.kda_output_gate(ctypes.byref(a)) == _lib.KDA_OK
+    assert lib.kda_output_gate_bwd(ctypes.byref(a), None, None, None) == _lib.KDA_OK
+
+
+def test_recurrent_step_rejects_negative_gate_eps(lib):
+    s = _step(out_gate=FAKE, out_gate_eps=-0.5)
+    assert lib.kda_recurrent_step(ctypes.byref(s)) == _lib.KDA_ERR_INVALID_ARG
