@@ -114,6 +114,11 @@ def decode_bytes(N, H, D, W, x_elt):
             + N * H * 4 + 3 * H * D * W * 4 + N * H * D * 4)
 
 
+def gate_bytes(rows, H, V, elt):
+    """Output gate: o and g read, y written once (elt bytes each)."""
+    return 3 * rows * H * V * elt
+
+
 def conv_bytes(rows, n_seq, H, D, W, elt):
     """x read once and q, k, v written once (elt bytes each); conv_w read; the
     conv state read and written once per sequence."""
@@ -210,6 +215,25 @@ def run_decode(steps, warmup, device):
     kern_ms = sum(evs[t].elapsed_time(evs[t + 1]) for t in range(steps)) / steps
     wall = (t1 - t0) / steps
     algo = decode_bytes(N, H, D, W, 2)
+    # the same steps with the full-rank output gate fused into the step
+    gates = [inputs.gate_inputs(N, H, D, seed=seed + 10 + t)["g"].reshape(N, H * D).to(device) for t in range(2)]
+    for t in range(warmup):
+        s = ins[t % n_in]
+        kda.recurrent_step(s["x"], cw, cs, s["g"], s["beta"], st, out=o, out_gate=gates[t % 2])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(steps):
+        s = ins[(warmup + t) % n_in]
+        evs[t].record(stream)
+        kda.recurrent_step(s["x"], cw, cs, s["g"], s["beta"], st, out=o, out_gate=gates[t % 2])
+    evs[steps].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gk_ms = sum(evs[t].elapsed_time(evs[t + 1]) for t in range(steps)) / steps
+    galgo = algo + N * H * D * 2
+    gated = {"value": N * steps / (t1 - t0), "unit": "seq/s", "kernel_ms": gk_ms, "algorithmic_bytes": galgo,
+             "frac": galgo / (gk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+             "workload": "the same decode steps with the full-rank output gate (bf16 gate input) fused"}
     return {
         "metric": "decode sequence-steps/s", "unit": "seq/s", "value": N / wall,
         "ms_per_step": wall * 1e3, "workload": f"decode N{N} H{H} d{D} conv{W} bf16 x, fp32 state",
@@ -217,13 +241,15 @@ def run_decode(steps, warmup, device):
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": stored_traffic("decode"),
                      "algorithmic_bytes": algo, "kernel_ms": kern_ms},
+        "with_output_gate": gated,
     }
 
 
 def run_prefill(steps, warmup, device):
     """Stateful prefill of the packed batch: the short conv from a conv state
-    (kda_conv_prefill), then the chunk forward from a decode state with the
-    final states out -- the prime that hands over to decode."""
+    (kda_conv_prefill), the chunk forward from a decode state with the final
+    states out -- the prime that hands over to decode -- and the full-rank
+    output gate on its output (kda_output_gate)."""
     import kimi_delta_attention_amd as kda
     from kimi_delta_attention_amd import inputs
     H, D, W = H_H, D_H, 4
@@ -238,6 +264,8 @@ def run_prefill(steps, warmup, device):
     cs = init["conv_state"].to(device)
     st0 = init["state"].to(device)
     qkv = tuple(torch.empty(T_H, H, D, dtype=torch.bfloat16, device=device) for _ in range(3))
+    g_out = inputs.gate_inputs(T_H, H, D, seed=inputs.SEEDS["decode"] + 3)["g"].to(device)
+    y = torch.empty(T_H, H, D, dtype=torch.bfloat16, device=device)
     op = kda.ChunkOp(*(t.unsqueeze(0) for t in qkv), g, beta, initial_state=st0, output_final_state=True,
                      use_qk_l2norm_in_kernel=True, use_beta_sigmoid_in_kernel=True, cu_seqlens=cu)
     stream = torch.cuda.current_stream()
@@ -245,30 +273,45 @@ def run_prefill(steps, warmup, device):
     def one():
         kda.conv_prefill(x, cw, H, D, conv_state=cs, cu_seqlens=cu, out=qkv)
 
+    o = op.o.reshape(T_H, H, D)
+
+    def gate():
+        kda.output_gate(o, g_out, out=y)
+
     for _ in range(warmup):
         one()
         op.forward()
+        gate()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for e in ev:
         e[0].record(stream)
         one()
         e[1].record(stream)
         op.forward()
         e[2].record(stream)
+        gate()
+        e[3].record(stream)
     torch.cuda.synchronize()
     conv_ms = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     fwd_ms = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    gate_ms = sum(e[2].elapsed_time(e[3]) for e in ev) / steps
     algo = conv_bytes(T_H, n_seq, H, D, W, 2)
+    galgo = gate_bytes(T_H, H, D, 2)
+
+    def roof(kernel, nbytes, ms, stage):
+        return {"bound": "hbm", "kernel": kernel, "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": nbytes,
+                "traffic": stored_traffic(stage)}
+
     return {
-        "metric": "stateful prefill tokens/s", "unit": "tokens/s", "value": T_H / ((conv_ms + fwd_ms) * 1e-3),
-        "workload": f"conv{W} prefill + chunk forward from decode states, packed 1024/2048/1024/4096 "
-                    f"(T{T_H}), H{H} d{D}, bf16 x/q/k/v, fp32 states",
-        "conv_ms": conv_ms, "chunk_fwd_ms": fwd_ms,
-        "conv_roofline": {"bound": "hbm", "kernel": "conv_prefill_kernel", "achieved": algo / (conv_ms * 1e-3) / 1e9,
-                          "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                          "frac": algo / (conv_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": algo,
-                          "traffic": stored_traffic("prefill.conv")},
+        "metric": "stateful prefill tokens/s", "unit": "tokens/s",
+        "value": T_H / ((conv_ms + fwd_ms + gate_ms) * 1e-3),
+        "workload": f"conv{W} prefill + chunk forward from decode states + output gate, packed "
+                    f"1024/2048/1024/4096 (T{T_H}), H{H} d{D}, bf16 x/q/k/v/o/gate, fp32 states",
+        "conv_ms": conv_ms, "chunk_fwd_ms": fwd_ms, "gate_ms": gate_ms,
+        "conv_roofline": roof("conv_prefill_kernel", algo, conv_ms, "prefill.conv"),
+        "gate_roofline": roof("output_gate_kernel", galgo, gate_ms, "prefill.gate"),
     }
 
 
