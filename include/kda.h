@@ -183,7 +183,14 @@ int kda_chunk_bwd_stages(void);
  *   o [N, H*D] (fp32) and updating state in place.
  * With out_gate set, o receives the full-rank output gate of the step's
  * output instead (kda_output_gate below, same page: full_rank_output_gate),
- * computed in the same kernel. */
+ * computed in the same kernel.
+ * Slot-indexed states (resuming sequences from saved snapshots, the
+ * prefix-hit restore of the same page's test prefix_hit_wrong_slot_diverges):
+ * with state_slots given, state is a pool [S, H, D, D] and conv_state a pool
+ * [S, 3*H*D, W] (S = n_slots), and sequence n reads and updates slot
+ * state_slots[n]; x, g, beta, out_gate and o stay indexed by n.  Slots must
+ * be distinct within a call (two sequences on one slot race).  A slot outside
+ * [0, S) leaves every state unchanged and sets that sequence's o to NaN. */
 typedef struct {
     int N, H, D, W;          /* D = head dim (K = V = D) in {32, 64, 128}; 1 <= W <= 8 */
     kda_dtype x_dtype;       /* KDA_F32 or KDA_BF16 */
@@ -204,6 +211,8 @@ typedef struct {
     void *stream;            /* hipStream_t */
     const void *out_gate;    /* [N, H*D] in x_dtype, or NULL: o is the plain output */
     float out_gate_eps;      /* NaN means 1e-5; must be >= 0 */
+    const int32_t *state_slots; /* device [N] or NULL; see below */
+    int n_slots;             /* pool size S when state_slots is given */
 } kda_step_args;
 
 kda_status kda_recurrent_step(const kda_step_args *a);

@@ -194,19 +194,23 @@ def chunk_kda_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bi
 
 def recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, *, A_log=None, dt_bias=None, lower_bound=None,
                    use_gate_in_kernel=False, safe_gate=False, gate_mode=None, use_qk_l2norm=True,
-                   use_beta_sigmoid=True, scale=None, out=None, out_gate=None, out_gate_eps=None):
+                   use_beta_sigmoid=True, scale=None, out=None, out_gate=None, out_gate_eps=None,
+                   state_slots=None):
     """One decode token per sequence with the short-conv update
     (kda_recurrent_step).  conv_state and state are updated in place.
     Returns o [N, H*D] fp32; with out_gate ([N, H*D], x_qkv's dtype) it is the
-    full-rank output gate of the step's output, computed in the same kernel."""
+    full-rank output gate of the step's output, computed in the same kernel.
+    With state_slots (int32 [N], distinct), state [S, H, D, D] and conv_state
+    [S, 3*H*D, W] are pools and sequence n uses slot state_slots[n]."""
     if state.dim() != 4 or state.shape[2] != state.shape[3]:
         raise ValueError("state must be [N, H, D, D]")
-    N, H, D, _ = state.shape
+    S, H, D, _ = state.shape
+    N = x_qkv.shape[0] if state_slots is not None else S
     if conv_w.dim() != 2 or conv_w.shape[0] != 3 * H * D:
         raise ValueError("conv_w must be [3*H*D, W]")
     W = conv_w.shape[1]
-    if tuple(x_qkv.shape) != (N, 3 * H * D) or tuple(conv_state.shape) != (N, 3 * H * D, W):
-        raise ValueError("x_qkv must be [N, 3*H*D] and conv_state [N, 3*H*D, W]")
+    if tuple(x_qkv.shape) != (N, 3 * H * D) or tuple(conv_state.shape) != (S, 3 * H * D, W):
+        raise ValueError("x_qkv must be [N, 3*H*D] and conv_state [S, 3*H*D, W]")
     if tuple(g.shape) != (N, H * D) or tuple(beta.shape) != (N, H):
         raise ValueError("g must be [N, H*D] and beta [N, H]")
     dev = state.device
@@ -235,6 +239,11 @@ def recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, *, A_log=None, dt_
         _need(out_gate, "out_gate", x_qkv.dtype, dev)
         a.out_gate = _ptr(out_gate)
     a.out_gate_eps = float("nan") if out_gate_eps is None else float(out_gate_eps)
+    if state_slots is not None:
+        if tuple(state_slots.shape) != (N,):
+            raise ValueError("state_slots must be [N]")
+        _need(state_slots, "state_slots", torch.int32, dev)
+        a.state_slots, a.n_slots = _ptr(state_slots), S
     _lib.check(_lib.load().kda_recurrent_step(ctypes.byref(a)), "kda_recurrent_step")
     return o
 

@@ -58,6 +58,7 @@ class StepArgs(ctypes.Structure):
         ("state", _vp), ("o", _vp),
         ("stream", _vp),
         ("out_gate", _vp), ("out_gate_eps", ctypes.c_float),
+        ("state_slots", _vp), ("n_slots", ctypes.c_int),
     ]
 
 

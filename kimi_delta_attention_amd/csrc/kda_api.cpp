@@ -176,6 +176,11 @@ kda_status kda_recurrent_step(const kda_step_args* a) {
     p.use_qk_l2norm = a->use_qk_l2norm; p.use_beta_sigmoid = a->use_beta_sigmoid;
     p.scale = (std::isnan(a->scale) || a->scale <= 0.f) ? 1.0f / std::sqrt(static_cast<float>(a->D)) : a->scale;
     p.state = a->state; p.o = a->o;
+    if (a->state_slots) {
+        if (a->n_slots <= 0) return KDA_ERR_INVALID_ARG;
+        p.state_slots = a->state_slots;
+        p.n_slots = a->n_slots;
+    }
     if (a->out_gate) {
         if (!(std::isnan(a->out_gate_eps) || a->out_gate_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
         p.out_gate = a->out_gate;

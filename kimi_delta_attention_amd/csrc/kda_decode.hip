@@ -7,6 +7,12 @@
 // then kda_recurrent_step (L2-normalised q and k, sigmoid of the beta logit,
 // key-axis decay, delta-rule write, read-out after the write).
 //
+// With a slot map, sequence n reads and writes the states of slot
+// state_slots[n] of the state pools, so that a batch can resume sequences
+// from saved snapshots (the prefix-hit restore that the same page's test
+// prefix_hit_wrong_slot_diverges exercises); x, g, beta, o and the gate input
+// stay indexed by n.
+//
 // Mapping: one workgroup per (sequence, head), 512 threads at D = 128 (256
 // below; measured faster than 256 or 1024 at the production geometry).  The
 // D x D state tile (64 KiB at D = 128) is held in registers: thread t owns column quad
@@ -50,8 +56,21 @@ __global__ __launch_bounds__(decode_threads<D>()) void decode_step_kernel(Decode
     __shared__ float scal[4];         // 1/|q|, 1/|k|, q^.k^
     __shared__ float osq[(D + kWave - 1) / kWave];  // per-wave sums of o^2 (output gate)
 
+    // The sequence's states live in slot sn of the state pools (slot n
+    // without a slot map).  A slot outside the pool leaves every state alone
+    // and writes NaN outputs, so the error is visible.
+    int sn = n;
+    if (p.state_slots) {
+        sn = p.state_slots[n];
+        if (sn < 0 || sn >= p.n_slots) {
+            for (int c = t; c < D; c += NT)
+                p.o[static_cast<int64_t>(n) * HD + static_cast<int64_t>(h) * D + c] = __builtin_nanf("");
+            return;
+        }
+    }
+
     // ---- issue the state loads first: they do not depend on the conv.
-    float* Sg = p.state + (static_cast<int64_t>(n) * H + h) * D * D;
+    float* Sg = p.state + (static_cast<int64_t>(sn) * H + h) * D * D;
     const int cq = t % CQ;
     const int rg = t / CQ;
     f32x4 s[RPT];
@@ -67,7 +86,7 @@ __global__ __launch_bounds__(decode_threads<D>()) void decode_step_kernel(Decode
         const int part = j / D;
         const int c = j % D;
         const int64_t ch = part * HD + static_cast<int64_t>(h) * D + c;
-        float* win = p.conv_state + (static_cast<int64_t>(n) * CH + ch) * W;
+        float* win = p.conv_state + (static_cast<int64_t>(sn) * CH + ch) * W;
         const float* w = p.conv_w + ch * W;
         const float xin = Elem<XT>::load(x, ch);
         float acc;

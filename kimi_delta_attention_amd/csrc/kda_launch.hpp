@@ -27,6 +27,8 @@ struct DecodeParams {
     float* o;
     const void* out_gate;      // [N, H*D] in x's element type, or nullptr (plain output)
     float out_gate_eps;
+    const int32_t* state_slots;  // [N] slot of each sequence in the state pools, or nullptr (slot n)
+    int n_slots;                 // pool size when state_slots is given
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t st);

@@ -236,3 +236,8 @@ def test_output_gate_empty_is_noop(lib):
 def test_recurrent_step_rejects_negative_gate_eps(lib):
     s = _step(out_gate=FAKE, out_gate_eps=-0.5)
     assert lib.kda_recurrent_step(ctypes.byref(s)) == _lib.KDA_ERR_INVALID_ARG
+
+
+def test_recurrent_step_slot_map_needs_a_pool_size(lib):
+    s = _step(state_slots=FAKE, n_slots=0)
+    assert lib.kda_recurrent_step(ctypes.byref(s)) == _lib.KDA_ERR_INVALID_ARG

@@ -113,3 +113,53 @@ def test_decode_production_geometry_sampled():
                 check(f"state step {t} unit {u}", st[n, h], ost[u][1][0, 0], TOL_F32)
                 check(f"conv step {t} unit {u}", cs[n][chan(h)], ost[u][0][0], TOL_F32)
             print(f"  step {t + 1} ok", flush=True)
+
+
+def test_decode_slot_indexed_states():
+    """Sequences resume from slots of a state pool (the prefix-hit restore of the
+    kda.rs page's test prefix_hit_wrong_slot_diverges): the right slots give the
+    oracle's steps from those states, other slots stay untouched, the wrong slot
+    diverges, and a slot outside the pool is refused by the kernel."""
+    S, N, H, D, W, T = 5, 3, 2, 64, 4, 3
+    init = inputs.decode_init(S, H, D, W, seed=21)
+    steps = [inputs.decode_step_inputs(N, H, D, seed=22, step=t) for t in range(T)]
+    slots = [3, 0, 4]
+    print(f"decode slots S={S} N={N} H={H} D={D} slots={slots}", flush=True)
+    cw = dev(init["conv_w"])
+    cs = dev(init["conv_state"]).clone()
+    st = dev(init["state"]).clone()
+    sl = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    outs = []
+    for s in steps:
+        outs.append(kda.recurrent_step(dev(s["x"]), cw, cs, dev(s["g"]), dev(s["beta"]), st,
+                                       state_slots=sl).clone())
+    torch.cuda.synchronize()
+    ocs, ost = init["conv_state"][slots], init["state"][slots]
+    for t, s in enumerate(steps):
+        o, ocs, ost = oracle.decode_step(s["x"], init["conv_w"], ocs, s["g"], s["beta"], ost)
+        check(f"o[{t}]", outs[t], o, TOL_F32)
+    check("state slots", st[slots], ost, TOL_F32)
+    check("conv_state slots", cs[slots], ocs, TOL_F32)
+    for u in (1, 2):  # not in the map: bit-identical
+        assert torch.equal(st[u].cpu(), init["state"][u]) and torch.equal(cs[u].cpu(), init["conv_state"][u])
+
+    # the wrong slot for sequence 0 (its neighbour's state) gives a different output
+    cs2 = dev(init["conv_state"]).clone()
+    st2 = dev(init["state"]).clone()
+    wrong = torch.tensor([0, 3, 4], dtype=torch.int32, device="cuda")
+    o_wrong = kda.recurrent_step(dev(steps[0]["x"]), cw, cs2, dev(steps[0]["g"]), dev(steps[0]["beta"]), st2,
+                                 state_slots=wrong)
+    torch.cuda.synchronize()
+    assert float((o_wrong[0] - outs[0][0]).abs().max()) > 1e-3
+
+    # a slot outside the pool: NaN output for that sequence, its neighbours as usual
+    cs3 = dev(init["conv_state"]).clone()
+    st3 = dev(init["state"]).clone()
+    bad = torch.tensor([S + 2, 0, 4], dtype=torch.int32, device="cuda")
+    o_bad = kda.recurrent_step(dev(steps[0]["x"]), cw, cs3, dev(steps[0]["g"]), dev(steps[0]["beta"]), st3,
+                               state_slots=bad)
+    torch.cuda.synchronize()
+    assert torch.isnan(o_bad[0]).all()
+    assert torch.equal(o_bad[1:], outs[0][1:])
+    for u in (1, 2, 3):
+        assert torch.equal(st3[u].cpu(), init["state"][u]) and torch.equal(cs3[u].cpu(), init["conv_state"][u])
