@@ -257,11 +257,12 @@ def _loss(args, kw, dO, dSf):
     return float((o * dO).sum() + (S * dSf).sum())
 
 
-@pytest.mark.parametrize("mode,beta_logits", [(oracle.GATE_LOGDECAY, False),
-                                              (oracle.GATE_SAFE, True),
-                                              (oracle.GATE_SOFTPLUS, True)])
-def test_backward_matches_finite_differences(mode, beta_logits):
-    B, T, H, K, V = 1, 16, 1, 8, 8
+@pytest.mark.parametrize("mode,beta_logits,K,V", [(oracle.GATE_LOGDECAY, False, 8, 8),
+                                                  (oracle.GATE_SAFE, True, 8, 8),
+                                                  (oracle.GATE_SOFTPLUS, True, 8, 8),
+                                                  (oracle.GATE_LOGDECAY, False, 4, 6)])
+def test_backward_matches_finite_differences(mode, beta_logits, K, V):
+    B, T, H = 1, 16, 1
     args, kw = _rand_problem(77 + mode, B=B, T=T, H=H, K=K, V=V, gate_mode=mode,
                              beta_logits=beta_logits)
     rng = np.random.default_rng(5)
