@@ -141,7 +141,9 @@ typedef struct {
  * (api.py chunk_kda; the chunk form's use of I + tril(A_kk * beta) is named in
  * its l2-norm warning).  K = V in {32, 64, 128} for KDA_BF16 q/k/v and
  * {32, 64} for KDA_F32 (the fp32 operand tiles of K = 128 exceed the 160 KiB
- * of LDS a workgroup can hold); anything else is KDA_ERR_UNSUPPORTED.
+ * of LDS a workgroup can hold), and the narrow-key pair K = 32, V = 64 of the
+ * "KDA <=> FLA Parity in Primus" page's 300M configuration (key head dim 32,
+ * value head dim 64) in both dtypes; anything else is KDA_ERR_UNSUPPORTED.
  * An empty sequence writes final_state = initial_state. */
 kda_status kda_chunk_fwd(const kda_chunk_args *a);
 size_t kda_chunk_fwd_workspace(const kda_chunk_args *a);

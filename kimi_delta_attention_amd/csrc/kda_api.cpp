@@ -24,7 +24,9 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forwar
     if (a->B <= 0 || a->T < 0 || a->H <= 0 || a->K <= 0 || a->V <= 0) return KDA_ERR_INVALID_ARG;
     if (a->qkv_dtype != KDA_F32 && a->qkv_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
     if (a->chunk_size != 64) return KDA_ERR_UNSUPPORTED;
-    if (!supported_dim(a->K) || a->K != a->V) return KDA_ERR_UNSUPPORTED;
+    // K = V in {32, 64, 128}, or the narrow-key pair K = 32, V = 64
+    const bool kv_ok = (supported_dim(a->K) && a->K == a->V) || (a->K == 32 && a->V == 64);
+    if (!kv_ok) return KDA_ERR_UNSUPPORTED;
     if (a->qkv_dtype == KDA_F32 && a->K > 64) return KDA_ERR_UNSUPPORTED;  // LDS budget
     if (a->gate_mode < KDA_GATE_LOGDECAY || a->gate_mode > KDA_GATE_SOFTPLUS) return KDA_ERR_INVALID_ARG;
     if (a->use_qk_l2norm != 0 && a->use_qk_l2norm != 1) return KDA_ERR_INVALID_ARG;

@@ -48,8 +48,8 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
-    using L = PrepLayout<K, BF>;
-    using X = BwdExtra<K, BF>;
+    using L = PrepLayout<K, BF, V>;
+    using X = BwdExtra<K, BF, V>;
     constexpr int LDK = K + MM::PAD;
     constexpr int LDC = kChunk + MM::PAD;
     constexpr int NCT = BV / 16;
@@ -436,8 +436,8 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
-    using L = PrepLayout<K, BF>;
-    using X = BwdExtra<K, BF>;
+    using L = PrepLayout<K, BF, V>;
+    using X = BwdExtra<K, BF, V>;
     constexpr int NT = vlocal_threads(BF);
     constexpr int WPR = NT / 256;  // waves per 16-row tile
     constexpr int LDK = K + MM::PAD;
@@ -700,14 +700,14 @@ struct KlocSmem {
     float gpa[kThreads / 64];
 };
 
-template <int K, bool BF>
+template <int K, bool BF, int V = K>
 __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_kernel(ChunkParams p, ChunkGrads gr,
                                                                     const int32_t* chunk_off, uint8_t* ws,
                                                                     int64_t slot_bytes) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
-    using X = BwdExtra<K, BF>;
+    using X = BwdExtra<K, BF, V>;
     using SM = KlocSmem<K, BF>;
     constexpr int LDC = SM::LDC;
     constexpr int CPT = K / 4;
@@ -1119,13 +1119,13 @@ __device__ __forceinline__ f32x4 mma16_f32(const float* A, int lda, int m0, cons
     return acc;
 }
 
-template <int K>
+template <int K, int V = K>
 __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkParams p, ChunkGrads gr,
                                                                          const int32_t* chunk_off, uint8_t* ws,
                                                                          int64_t slot_bytes, int nblk) {
     using MM = Mma<true>;
     using ET = uint16_t;
-    using X = BwdExtra<K, true>;
+    using X = BwdExtra<K, true, V>;
     using SM = KlocMfmaSmem<K>;
     constexpr int LDC = SM::LDC;
     constexpr int LDF = SM::LDF;
@@ -2305,12 +2305,14 @@ __global__ void gate_param_reduce_kernel(ChunkParams p, ChunkGrads gr, const int
 }
 
 // ------------------------------------------------------------------ host side
-template <int K, bool BF>
+template <int K, bool BF, int V = K>
 static size_t bwd_bytes(const ChunkParams& p) {
-    return chunk_off_bytes(p) + static_cast<size_t>(p.total_chunks_bound) * p.H * BwdExtra<K, BF>::kBytes;
+    return chunk_off_bytes(p) + static_cast<size_t>(p.total_chunks_bound) * p.H * BwdExtra<K, BF, V>::kBytes;
 }
 
 size_t chunk_bwd_workspace(const ChunkParams& p) {
+    if (p.K == 32 && p.V == 64) return p.bf16 ? bwd_bytes<32, true, 64>(p) : bwd_bytes<32, false, 64>(p);
+    if (p.K != p.V) return 0;
     switch (p.K) {
         case 32: return p.bf16 ? bwd_bytes<32, true>(p) : bwd_bytes<32, false>(p);
         case 64: return p.bf16 ? bwd_bytes<64, true>(p) : bwd_bytes<64, false>(p);
@@ -2319,10 +2321,9 @@ size_t chunk_bwd_workspace(const ChunkParams& p) {
     }
 }
 
-template <int K, int BV, bool BF>
+template <int K, int BV, bool BF, int V = K>
 static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st, int stage) {
-    constexpr int V = K;
-    using X = BwdExtra<K, BF>;
+    using X = BwdExtra<K, BF, V>;
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     int32_t* chunk_off = reinterpret_cast<int32_t*>(w8);
     uint8_t* slots = w8 + chunk_off_bytes(p);
@@ -2335,11 +2336,11 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
         if (p.cu_seqlens)
             hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
         if (nblk > 0)
-            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true>), dim3(static_cast<unsigned>(nblk)), dim3(prep_threads(K)), 0,
-                               st, p, chunk_off, slots, sb);
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true, V>), dim3(static_cast<unsigned>(nblk)),
+                               dim3(prep_threads(K)), 0, st, p, chunk_off, slots, sb);
     }
     if (want(1) && cgrid > 0) {
-        if constexpr (K == 128 && BF)
+        if constexpr (K == 128 && V == 128 && BF)
             hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<true, false>), dim3(cgrid), dim3(256), 0, st, p, chunk_off,
                                slots, sb);
         else if (cgrid <= kPersistentGrid)  // few chains: 8 waves per chain (see the forward)
@@ -2350,7 +2351,7 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                st, p, chunk_off, slots, sb);
     }
     if (want(2) && cgrid > 0) {
-        if constexpr (K == 128 && BF)
+        if constexpr (K == 128 && V == 128 && BF)
             hipLaunchKernelGGL(chunk_state_bwd_pc_kernel, dim3(cgrid), dim3(256), 0, st, p, gr, chunk_off, slots, sb);
         else
             hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,
@@ -2361,16 +2362,16 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                            dim3(vlocal_threads(BF)), 0, st, p, gr, chunk_off, slots, sb);
     if (want(4)) {
         if (nblk > 0) {
-            if constexpr (BF && K == 128)
+            if constexpr (BF && K == 128 && V == 128)
                 hipLaunchKernelGGL(chunk_bwd_klocal_w8_kernel,
                                    dim3(static_cast<unsigned>(nblk < kPersistentGrid ? nblk : kPersistentGrid)),
                                    dim3(kKlocW8Threads), 0, st, p, gr, chunk_off, slots, sb, static_cast<int>(nblk));
             else if constexpr (BF)
-                hipLaunchKernelGGL((chunk_bwd_klocal_mfma_kernel<K>),
+                hipLaunchKernelGGL((chunk_bwd_klocal_mfma_kernel<K, V>),
                                    dim3(static_cast<unsigned>(nblk < kPersistentGrid ? nblk : kPersistentGrid)),
                                    dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb, static_cast<int>(nblk));
             else
-                hipLaunchKernelGGL((chunk_bwd_klocal_kernel<K, BF>), dim3(static_cast<unsigned>(nblk)),
+                hipLaunchKernelGGL((chunk_bwd_klocal_kernel<K, BF, V>), dim3(static_cast<unsigned>(nblk)),
                                    dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb);
         }
         if (p.gate_mode != GATE_LOGDECAY && (gr.dA_log || gr.ddt_bias))
@@ -2381,6 +2382,8 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
 }
 
 hipError_t launch_chunk_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, hipStream_t st, int stage) {
+    if (p.K == 32 && p.V == 64)
+        return p.bf16 ? run_bwd<32, 32, true, 64>(p, gr, ws, st, stage) : run_bwd<32, 16, false, 64>(p, gr, ws, st, stage);
     if (p.K != p.V) return hipErrorInvalidValue;
     switch (p.K) {
         case 32: return p.bf16 ? run_bwd<32, 32, true>(p, gr, ws, st, stage) : run_bwd<32, 16, false>(p, gr, ws, st, stage);

@@ -105,10 +105,9 @@ __device__ __forceinline__ int n_chunks(int len) { return (len + kChunk - 1) / k
 //   GC  [K]      exp(G_last)                             (fp32)
 // G is the inclusive cumulative log-decay inside the chunk.  With S the state
 // entering the chunk, D = U - W S, O = QE S + MS D and S' = GC * S + KD^T D.
-template <int K, bool BF>
+template <int K, bool BF, int V = K>
 struct PrepLayout {
     using ET = typename Mma<BF>::ET;
-    static constexpr int V = K;
     static constexpr size_t kQE = 0;
     static constexpr size_t kW = kQE + sizeof(ET) * kChunk * K;
     static constexpr size_t kKD = kW + sizeof(ET) * kChunk * K;
@@ -129,11 +128,10 @@ struct PrepLayout {
 //   DMS, DTB      [64][64] gradients of MS and TB, summed over V (ET)
 //   DGAM [K]      gradient of exp(G_last) (fp32)
 //   GP   [K + 1]  this chunk's share of d(dt_bias) and d(A_log) (fp32)
-template <int K, bool BF>
+template <int K, bool BF, int V = K>
 struct BwdExtra {
     using ET = typename Mma<BF>::ET;
-    static constexpr int V = K;
-    static constexpr size_t kKE = PrepLayout<K, BF>::kBytes;
+    static constexpr size_t kKE = PrepLayout<K, BF, V>::kBytes;
     static constexpr size_t kT = kKE + sizeof(ET) * kChunk * K;
     static constexpr size_t kAK = kT + sizeof(ET) * kChunk * kChunk;
     static constexpr size_t kS = kAK + sizeof(ET) * kChunk * kChunk;

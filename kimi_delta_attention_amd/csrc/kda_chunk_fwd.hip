@@ -5,13 +5,16 @@
 namespace kda {
 
 // ------------------------------------------------------------------ host side
-template <int K, bool BF>
+template <int K, bool BF, int V = K>
 static size_t prep_bytes(const ChunkParams& p) {
-    return static_cast<size_t>(p.total_chunks_bound) * p.H * PrepLayout<K, BF>::kBytes;
+    return static_cast<size_t>(p.total_chunks_bound) * p.H * PrepLayout<K, BF, V>::kBytes;
 }
 
 size_t chunk_fwd_workspace(const ChunkParams& p) {
     size_t prep = 0;
+    if (p.K == 32 && p.V == 64)
+        return chunk_off_bytes(p) + (p.bf16 ? prep_bytes<32, true, 64>(p) : prep_bytes<32, false, 64>(p));
+    if (p.K != p.V) return 0;
     switch (p.K) {
         case 32: prep = p.bf16 ? prep_bytes<32, true>(p) : prep_bytes<32, false>(p); break;
         case 64: prep = p.bf16 ? prep_bytes<64, true>(p) : prep_bytes<64, false>(p); break;
@@ -29,20 +32,20 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     int32_t* chunk_off = reinterpret_cast<int32_t*>(w8);
     uint8_t* prep = w8 + chunk_off_bytes(p);
-    const int64_t sb = static_cast<int64_t>(KEEP ? BwdExtra<K, BF>::kBytes : PrepLayout<K, BF>::kBytes);
+    const int64_t sb = static_cast<int64_t>(KEEP ? BwdExtra<K, BF, V>::kBytes : PrepLayout<K, BF, V>::kBytes);
     if (stage < 0 || stage == 0) {
         if (p.cu_seqlens)
             hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
         const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
         if (nblk > 0)
-            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, KEEP>), dim3(static_cast<unsigned>(nblk)), dim3(prep_threads(K)),
-                               0, st, p, chunk_off, prep, sb);
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, KEEP, V>), dim3(static_cast<unsigned>(nblk)),
+                               dim3(prep_threads(K)), 0, st, p, chunk_off, prep, sb);
     }
     if (stage < 0 || stage == 1) {
         // few chains (no more workgroups than CUs): 8 waves per chain shorten
         // each chunk step; otherwise 4 waves let two chains share a CU
         const int grid = chain_grid(p.N * p.H, V / BV);
-        if constexpr (K == 128 && BF) {
+        if constexpr (K == 128 && V == 128 && BF) {
             if (grid > 0)
                 hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<KEEP, true>), dim3(grid), dim3(256), 0, st, p, chunk_off,
                                    prep, sb);
@@ -62,6 +65,8 @@ static hipError_t run_fwd_any(const ChunkParams& p, void* ws, hipStream_t st, in
 }
 
 hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage) {
+    if (p.K == 32 && p.V == 64)
+        return p.bf16 ? run_fwd_any<32, 64, 16, true>(p, ws, st, stage) : run_fwd_any<32, 64, 16, false>(p, ws, st, stage);
     if (p.K != p.V) return hipErrorInvalidValue;
     switch (p.K) {
         case 32:

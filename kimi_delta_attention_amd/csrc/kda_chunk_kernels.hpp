@@ -127,7 +127,7 @@ __device__ __forceinline__ f32x4 gemm(const typename MM::ET* A, int lda, int m0,
 // LDS and memory chains with another's work.
 __host__ __device__ constexpr int prep_threads(int K) { return K >= 64 ? 512 : 256; }
 
-template <int K, bool BF, bool BWD>
+template <int K, bool BF, bool BWD, int V = K>
 struct PrepSmem {
     using ET = typename Mma<BF>::ET;
     static constexpr int LDE = K + Mma<BF>::PAD;
@@ -142,7 +142,7 @@ struct PrepSmem {
         struct {
             ET TB[kChunk][kChunk + Mma<BF>::PAD];  // T diag(beta): A operand of W and U
             ET KEt[K][kChunk + Mma<BF>::PAD];      // (k^ exp(G))^T
-            ET Vt[K][kChunk + Mma<BF>::PAD];       // v^T (V = K)
+            ET Vt[V][kChunk + Mma<BF>::PAD];       // v^T
         } wu;
     } u;
     float A[kChunk][kChunk + 4];  // 16-byte aligned rows (MFMA A operand)
@@ -163,20 +163,23 @@ struct PrepSmem {
 
 // BWD additionally writes T = (I + A)^-1 and the un-scaled strictly lower
 // k-k score matrix (BwdExtra layout) for the backward kernels.
-template <int K, bool BF, bool BWD>
+template <int K, bool BF, bool BWD, int V = K>
 __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams p, const int32_t* chunk_off,
                                                               uint8_t* ws, int64_t slot_bytes) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;  // q/k/v element
-    using L = PrepLayout<K, BF>;
+    using L = PrepLayout<K, BF, V>;
+    using X = BwdExtra<K, BF, V>;
     constexpr int NT = prep_threads(K);
     constexpr int NW = NT / 64;     // waves
     constexpr int TPR = NT / kChunk;  // threads per row in row-wise phases
     constexpr int CPT = K / TPR;      // channels per thread in row-wise phases
     static_assert(CPT % 8 == 0, "row segments are whole 16-byte vectors");
-    constexpr int LDE = PrepSmem<K, BF, BWD>::LDE;
-    __shared__ __attribute__((aligned(16))) PrepSmem<K, BF, BWD> s;
+    constexpr int CPTV = V / TPR;     // value channels per thread
+    static_assert(CPTV % 8 == 0, "row segments are whole 16-byte vectors");
+    constexpr int LDE = PrepSmem<K, BF, BWD, V>::LDE;
+    __shared__ __attribute__((aligned(16))) PrepSmem<K, BF, BWD, V> s;
 
     const int H = p.H;
     const int slot = blockIdx.x / H;
@@ -336,7 +339,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         store_row<CPT>(gQE + i * K + c0, o_);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) ke_[c] = kh[c] * a_[c] * s.Er[I][c0 + c];
-        if (BWD) store_row<CPT>(reinterpret_cast<ET*>(out + BwdExtra<K, BF>::kKE) + i * K + c0, ke_);
+        if (BWD) store_row<CPT>(reinterpret_cast<ET*>(out + X::kKE) + i * K + c0, ke_);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * e_[c] * s.Ec[I][c0 + c];
         store_row<CPT>(gKD + i * K + c0, o_);
@@ -469,8 +472,8 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     }
     for (int c = t; c < K; c += NT) gGC[c] = s.gC[c];
     if (BWD) {
-        ET* gT = reinterpret_cast<ET*>(out + BwdExtra<K, BF>::kT);
-        ET* gAK = reinterpret_cast<ET*>(out + BwdExtra<K, BF>::kAK);
+        ET* gT = reinterpret_cast<ET*>(out + X::kT);
+        ET* gAK = reinterpret_cast<ET*>(out + X::kAK);
         for (int e = t; e < kChunk * kChunk; e += NT) {
             const int a = e / kChunk, b = e % kChunk;
             gT[e] = MM::from_f32(s.u.T[a][b]);
@@ -487,36 +490,38 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             const int e = t + m * NT;
             s.u.wu.TB[e / kChunk][e % kChunk] = MM::from_f32(tbr[m]);
         }
-        float vv[CPT];
+        const int cv0 = pq * CPTV;
+        float vv[CPTV];
         if (valid) {
-            load_row<CPT>(static_cast<const IT*>(p.v) + (grow * H + h) * K + c0, vv);
+            load_row<CPTV>(static_cast<const IT*>(p.v) + (grow * H + h) * V + cv0, vv);
         } else {
 #pragma unroll
-            for (int c = 0; c < CPT; ++c) vv[c] = 0.f;
+            for (int c = 0; c < CPTV; ++c) vv[c] = 0.f;
         }
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            s.u.wu.KEt[c0 + c][i] = MM::from_f32(ke_[c]);
-            s.u.wu.Vt[c0 + c][i] = MM::from_f32(vv[c]);
-        }
+        for (int c = 0; c < CPT; ++c) s.u.wu.KEt[c0 + c][i] = MM::from_f32(ke_[c]);
+#pragma unroll
+        for (int c = 0; c < CPTV; ++c) s.u.wu.Vt[cv0 + c][i] = MM::from_f32(vv[c]);
         __syncthreads();
         ET* gW = reinterpret_cast<ET*>(out + L::kW);
         ET* gU = reinterpret_cast<ET*>(out + L::kU);
-        // wave w: row tile w % 4, every (NW / 4)-th column tile from w / 4
+        // wave w: row tile w % 4, every (NW / 4)-th column tile from w / 4;
+        // W has K / 16 column tiles and U has V / 16
+        constexpr int NCTWU = (K > V ? K : V) / 16;
         const int rt = w & 3;
 #pragma unroll 2
-        for (int ct = w >> 2; ct < K / 16; ct += NW / 4) {
+        for (int ct = w >> 2; ct < NCTWU; ct += NW / 4) {
             f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < 16 * (rt + 1); k0 += MM::KS) {
                 const auto a = MM::load(&s.u.wu.TB[0][0], LDC, 16 * rt, k0, lane);
-                aw = MM::mma(a, MM::load(&s.u.wu.KEt[0][0], LDC, 16 * ct, k0, lane), aw);
-                au = MM::mma(a, MM::load(&s.u.wu.Vt[0][0], LDC, 16 * ct, k0, lane), au);
+                if (K == V || ct < K / 16) aw = MM::mma(a, MM::load(&s.u.wu.KEt[0][0], LDC, 16 * ct, k0, lane), aw);
+                if (K == V || ct < V / 16) au = MM::mma(a, MM::load(&s.u.wu.Vt[0][0], LDC, 16 * ct, k0, lane), au);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 16 * rt + 4 * (lane >> 4) + r, col = 16 * ct + (lane & 15);
-                gW[row * K + col] = MM::from_f32(aw[r]);
-                gU[row * K + col] = MM::from_f32(au[r]);
+                if (K == V || ct < K / 16) gW[row * K + col] = MM::from_f32(aw[r]);
+                if (K == V || ct < V / 16) gU[row * V + col] = MM::from_f32(au[r]);
             }
         }
     }
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
-    using L = PrepLayout<K, BF>;
+    using L = PrepLayout<K, BF, V>;
     constexpr int LDK = K + MM::PAD;
     constexpr int LDC = kChunk + MM::PAD;
     constexpr int LDB = BV + MM::PAD;
@@ -697,7 +702,7 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
         sGC.store(&gC[0], K, t);
         if (STORE) {
             uint8_t* base = ws + ((slot0 + jc) * H + h) * slot_bytes;
-            ET* gS = reinterpret_cast<ET*>(base + BwdExtra<K, BF>::kS);
+            ET* gS = reinterpret_cast<ET*>(base + BwdExtra<K, BF, V>::kS);
 #pragma unroll
             for (int m = 0; m < SPW; ++m) {
                 const int tt = w + NW * m;

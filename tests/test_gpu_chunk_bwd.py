@@ -47,18 +47,19 @@ def _compare(w, tag, names=NAMES):
 
 
 @pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 130])
-@pytest.mark.parametrize("dtype,K", [(torch.float32, 32), (torch.float32, 64), (torch.bfloat16, 32),
-                                     (torch.bfloat16, 64), (torch.bfloat16, 128)])
-def test_bwd_boundary_lengths(T, dtype, K):
-    w = inputs.chunk_inputs(2, T, 2, K, K, seed=300 + T + K, dtype=dtype, h0_std=0.1, with_grad_out=True,
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.float32, 64, 64), (torch.bfloat16, 32, 32),
+                                       (torch.bfloat16, 64, 64), (torch.bfloat16, 128, 128),
+                                       (torch.float32, 32, 64), (torch.bfloat16, 32, 64)])
+def test_bwd_boundary_lengths(T, dtype, K, V):
+    w = inputs.chunk_inputs(2, T, 2, K, V, seed=300 + T + K + V, dtype=dtype, h0_std=0.1, with_grad_out=True,
                             dfinal_std=0.1)
-    _compare(w, f"T={T} K={K}")
+    _compare(w, f"T={T} K={K} V={V}")
 
 
 @pytest.mark.parametrize("mode", [inputs.GATE_SAFE, inputs.GATE_SOFTPLUS])
-@pytest.mark.parametrize("dtype,K", [(torch.float32, 32), (torch.bfloat16, 128)])
-def test_bwd_in_kernel_gates(mode, dtype, K):
-    w = inputs.chunk_inputs(2, 150, 2, K, K, seed=17 + mode, dtype=dtype, gate_mode=mode, beta_logits=True,
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.bfloat16, 128, 128), (torch.bfloat16, 32, 64)])
+def test_bwd_in_kernel_gates(mode, dtype, K, V):
+    w = inputs.chunk_inputs(2, 150, 2, K, V, seed=17 + mode, dtype=dtype, gate_mode=mode, beta_logits=True,
                             h0_std=0.1, with_grad_out=True, dfinal_std=0.1)
     _compare(w, f"gate {mode}")
 
@@ -119,6 +120,39 @@ def test_bwd_train_geometry_sampled_units():
     check("train dh0", got, o["dh0"], 2e-2)
 
 
+def test_bwd_narrow_key_geometry_sampled_units():
+    """The narrow-key head geometry of the Primus 300M configuration (8 heads,
+    key dim 32, value dim 64, T2048, its unbounded softplus gate in kernel and
+    beta logits), bf16, 16 sequences of its micro-batch: the whole batch runs
+    on the GPU, the oracle checks 3 sampled sequences of one head in the
+    forward and the backward."""
+    w = inputs.chunk_inputs(16, 2048, 8, 32, 64, seed=75, dtype=torch.bfloat16, gate_mode=inputs.GATE_SOFTPLUS,
+                            beta_logits=True, with_grad_out=True)
+    print("narrow-key geometry B16 T2048 H8 K32 V64", flush=True)
+    g = _gpu_bwd(w)
+    kw = dict(A_log=dev(w["A_log"]), dt_bias=dev(w["dt_bias"]), scale=w["scale"],
+              use_qk_l2norm_in_kernel=True, gate_mode=w["gate_mode"], use_beta_sigmoid_in_kernel=True)
+    o_gpu, _ = kda.chunk_kda(dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["g"]), dev(w["beta"]), **kw)
+    torch.cuda.synchronize()
+    # units of one head, so that its A_log and dt_bias apply to the whole slice
+    hd, K = 5, 32
+    units = [(0, hd), (7, hd), (15, hd)]
+    sub, bs, hs = _slice_units(w, units)
+    sub["A_log"] = w["A_log"][hd:hd + 1]
+    sub["dt_bias"] = w["dt_bias"][hd * K:(hd + 1) * K]
+    o = _oracle_bwd(sub)
+    for name in ["dq", "dk", "dv", "dg"]:
+        got = torch.stack([g[name][b, :, h] for b, h in units], 0).unsqueeze(2)
+        check(f"narrow {name}", got, o[name], 2e-2)
+    got = torch.stack([g["dbeta"][b, :, h] for b, h in units], 0).unsqueeze(2)
+    check("narrow dbeta", got, o["dbeta"], 2e-2)
+    of, _ = oracle.chunk_fwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], A_log=sub["A_log"],
+                             dt_bias=sub["dt_bias"], scale=sub["scale"], use_qk_l2norm=True,
+                             gate_mode=sub["gate_mode"], use_beta_sigmoid=True)
+    got = torch.stack([o_gpu[b, :, h] for b, h in units], 0).unsqueeze(2)
+    check("narrow o", got, of, 2e-2)
+
+
 def test_bwd_hybrid_varlen_sampled_heads():
     """Packed 1024/2048/1024/4096, H16 K=V=128 bf16, dO ~ N(0,1): 3 heads checked."""
     w = inputs.chunk_inputs(1, 8192, 16, 128, 128, seed=inputs.SEEDS["fwd_hybrid"], dtype=torch.bfloat16,
@@ -144,7 +178,8 @@ def test_bwd_deterministic():
         assert torch.equal(a[name], b[name]), name
 
 
-@pytest.mark.parametrize("case", ["bf16_128_varlen_tail", "f32_32_softplus_h0", "bf16_64_safe_dfinal"])
+@pytest.mark.parametrize("case", ["bf16_128_varlen_tail", "f32_32_softplus_h0", "bf16_64_safe_dfinal",
+                                  "bf16_32x64_softplus_varlen"])
 def test_bwd_reuses_saved_forward(case):
     """A forward with keep_for_backward writes what the backward's first two
     stages compute; the backward with the flag skips them.  Same kernels, same
@@ -156,9 +191,13 @@ def test_bwd_reuses_saved_forward(case):
     elif case == "f32_32_softplus_h0":
         w = inputs.chunk_inputs(2, 130, 2, 32, 32, seed=72, gate_mode=inputs.GATE_SOFTPLUS, beta_logits=True,
                                 h0_std=0.1, with_grad_out=True, dfinal_std=0.1)
-    else:
+    elif case == "bf16_64_safe_dfinal":
         w = inputs.chunk_inputs(2, 97, 2, 64, 64, seed=73, dtype=torch.bfloat16, gate_mode=inputs.GATE_SAFE,
                                 with_grad_out=True, dfinal_std=0.1)
+    else:
+        w = inputs.chunk_inputs(1, 260, 2, 32, 64, seed=74, dtype=torch.bfloat16, gate_mode=inputs.GATE_SOFTPLUS,
+                                beta_logits=True, cu_seqlens=[0, 0, 130, 260], with_grad_out=True, h0_std=0.1,
+                                dfinal_std=0.1)
     print(f"saved-forward {case}", flush=True)
     kw = dict(A_log=dev(w["A_log"]), dt_bias=dev(w["dt_bias"]), scale=w["scale"],
               initial_state=dev(w["initial_state"]), use_qk_l2norm_in_kernel=True, gate_mode=w["gate_mode"],

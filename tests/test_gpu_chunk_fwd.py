@@ -70,18 +70,19 @@ def test_fwd_hybrid_bf16_varlen_sampled_heads():
 
 
 @pytest.mark.parametrize("T", [1, 7, 63, 64, 65, 130])
-@pytest.mark.parametrize("dtype,K", [(torch.float32, 32), (torch.float32, 64), (torch.bfloat16, 32),
-                                     (torch.bfloat16, 64), (torch.bfloat16, 128)])
-def test_fwd_boundary_lengths(T, dtype, K):
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.float32, 64, 64), (torch.bfloat16, 32, 32),
+                                       (torch.bfloat16, 64, 64), (torch.bfloat16, 128, 128),
+                                       (torch.float32, 32, 64), (torch.bfloat16, 32, 64)])
+def test_fwd_boundary_lengths(T, dtype, K, V):
     """Lengths straddling the 64-token chunk (memra gate 1 lengths), random initial state."""
-    w = inputs.chunk_inputs(2, T, 3, K, K, seed=100 + T + K, dtype=dtype, h0_std=0.1)
-    _compare(w, f"T={T} K={K}")
+    w = inputs.chunk_inputs(2, T, 3, K, V, seed=100 + T + K + V, dtype=dtype, h0_std=0.1)
+    _compare(w, f"T={T} K={K} V={V}")
 
 
 @pytest.mark.parametrize("mode", [inputs.GATE_SAFE, inputs.GATE_SOFTPLUS])
-@pytest.mark.parametrize("dtype,K", [(torch.float32, 32), (torch.bfloat16, 128)])
-def test_fwd_in_kernel_gates(mode, dtype, K):
-    w = inputs.chunk_inputs(1, 200, 2, K, K, seed=7 + mode, dtype=dtype, gate_mode=mode, beta_logits=True,
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.bfloat16, 128, 128), (torch.bfloat16, 32, 64)])
+def test_fwd_in_kernel_gates(mode, dtype, K, V):
+    w = inputs.chunk_inputs(1, 200, 2, K, V, seed=7 + mode, dtype=dtype, gate_mode=mode, beta_logits=True,
                             h0_std=0.1)
     _compare(w, f"gate {mode}")
 
