@@ -479,10 +479,9 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     const int slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
     int n, j;
-    if (!slot_to_chunk(p, chunk_off, slot, n, j)) return;
     int64_t start;
     int len;
-    seq_bounds(p, n, start, len);
+    if (!slot_locate(p, chunk_off, slot, n, j, start, len)) return;
     const int rows = min(kChunk, len - j * kChunk);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int rt = w & 3, hv = w >> 2;  // 16-row tile and column-tile phase of this wave
@@ -719,10 +718,9 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_kernel(ChunkParams 
     const int slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
     int n, j;
-    if (!slot_to_chunk(p, chunk_off, slot, n, j)) return;
     int64_t start;
     int len;
-    seq_bounds(p, n, start, len);
+    if (!slot_locate(p, chunk_off, slot, n, j, start, len)) return;
     const int rows = min(kChunk, len - j * kChunk);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
@@ -1145,10 +1143,9 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         const int slot = blk / H;
         const int h = blk % H;
         int n, j;
-        if (!slot_to_chunk(p, chunk_off, slot, n, j)) break;  // slots past the last chunk are all empty
         int64_t start;
         int len;
-        seq_bounds(p, n, start, len);
+        if (!slot_locate(p, chunk_off, slot, n, j, start, len)) break;  // slots past the last chunk are all empty
         const int rows = min(kChunk, len - j * kChunk);
         uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
         const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
@@ -1793,10 +1790,9 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
         const int slot = blk / H;
         const int h = blk % H;
         int n, j;
-        if (!slot_to_chunk(p, chunk_off, slot, n, j)) break;  // slots past the last chunk are all empty
         int64_t start;
         int len;
-        seq_bounds(p, n, start, len);
+        if (!slot_locate(p, chunk_off, slot, n, j, start, len)) break;  // slots past the last chunk are all empty
         const int rows = min(kChunk, len - j * kChunk);
         uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
         const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
@@ -2334,7 +2330,8 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
     auto want = [stage, &p](int s) { return (stage < 0 || stage == s) && !(p.keep && s < 2); };
     if (want(0)) {
         if (p.cu_seqlens)
-            hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
+            hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(kPlanThreads), 0, st, p.cu_seqlens, p.N, p.T, chunk_off,
+                               p.total_chunks_bound);
         if (nblk > 0)
             hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true, V>), dim3(static_cast<unsigned>(nblk)),
                                dim3(prep_threads(K)), 0, st, p, chunk_off, slots, sb);

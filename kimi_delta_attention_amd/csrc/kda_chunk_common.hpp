@@ -148,8 +148,20 @@ struct BwdExtra {
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// The plan at the head of the workspace (packed input only):
+//   chunk_off [N + 1]  int32, chunk_off[n] = chunks of sequences 0..n-1;
+//   slot map  [bound]  int4 {n, j, start, len} per chunk slot (256-byte
+//                      aligned), n = -1 for slots past the last chunk,
+// written by plan_chunks_kernel, so that a parallel kernel locates its slot
+// with one 16-byte load instead of a search over chunk_off and cu_seqlens.
+__host__ __device__ inline size_t plan_map_offset(int N) {
+    return align256(sizeof(int32_t) * (static_cast<size_t>(N) + 1));
+}
+
 __host__ inline size_t chunk_off_bytes(const ChunkParams& p) {
-    return align256(sizeof(int32_t) * (static_cast<size_t>(p.N) + 1));
+    size_t b = plan_map_offset(p.N);
+    if (p.cu_seqlens) b += align256(sizeof(int32_t) * 4 * static_cast<size_t>(p.total_chunks_bound));
+    return b;
 }
 
 // Chunk slot of chunk j of sequence n (slots are numbered over all sequences).
@@ -159,26 +171,26 @@ __device__ __forceinline__ int64_t chunk_slot(const ChunkParams& p, const int32_
     return base + j;
 }
 
-// Inverse of chunk_slot for the parallel kernels: slot c -> (n, j); returns
+// Slot c -> (sequence n, chunk j, sequence start row, sequence length);
 // false when c is past the last chunk.
-__device__ __forceinline__ bool slot_to_chunk(const ChunkParams& p, const int32_t* chunk_off, int c,
-                                              int& n, int& j) {
+__device__ __forceinline__ bool slot_locate(const ChunkParams& p, const int32_t* chunk_off, int c, int& n, int& j,
+                                            int64_t& start, int& len) {
     if (!p.cu_seqlens) {
         const int nc = n_chunks(p.T);
         if (nc == 0) return false;
         n = c / nc;
         j = c % nc;
+        start = static_cast<int64_t>(n) * p.T;
+        len = p.T;
         return n < p.N;
     }
-    if (c >= chunk_off[p.N]) return false;
-    int lo = 0, hi = p.N - 1;  // last n with chunk_off[n] <= c
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
-    }
-    n = lo;
-    j = c - chunk_off[lo];
-    return true;
+    const int4 e = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(chunk_off) +
+                                                 plan_map_offset(p.N))[c];
+    n = e.x;
+    j = e.y;
+    start = e.z;
+    len = e.w;
+    return n >= 0;
 }
 
 // Column-block grid remap: all V-column blocks of one (sequence, head) chain

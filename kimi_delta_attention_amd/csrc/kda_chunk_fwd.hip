@@ -35,7 +35,8 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
     const int64_t sb = static_cast<int64_t>(KEEP ? BwdExtra<K, BF, V>::kBytes : PrepLayout<K, BF, V>::kBytes);
     if (stage < 0 || stage == 0) {
         if (p.cu_seqlens)
-            hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(64), 0, st, p.cu_seqlens, p.N, p.T, chunk_off);
+            hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(kPlanThreads), 0, st, p.cu_seqlens, p.N, p.T, chunk_off,
+                               p.total_chunks_bound);
         const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
         if (nblk > 0)
             hipLaunchKernelGGL((chunk_prep_kernel<K, BF, KEEP, V>), dim3(static_cast<unsigned>(nblk)),

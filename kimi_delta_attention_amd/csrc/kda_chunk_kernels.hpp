@@ -38,18 +38,59 @@
 namespace kda {
 
 // ------------------------------------------------------------------ plan
-// chunk_off[n] = number of chunks in sequences 0..n-1 (packed input only).
-static __global__ void plan_chunks_kernel(const int32_t* cu, int N, int T, int32_t* chunk_off) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    int acc = 0;
-    for (int n = 0; n < N; ++n) {
-        chunk_off[n] = acc;
-        int a = cu[n], b = cu[n + 1];
+// The plan of a packed call (layout at plan_map_offset): chunk_off by a
+// block-wide scan of the sequences' chunk counts, then the slot map.  One
+// workgroup of kPlanThreads; sequence offsets are clamped into [0, T] as in
+// seq_bounds.
+constexpr int kPlanThreads = 1024;
+static __global__ __launch_bounds__(kPlanThreads) void plan_chunks_kernel(const int32_t* cu, int N, int T,
+                                                                          int32_t* chunk_off, int bound) {
+    __shared__ int part[kPlanThreads];
+    const int t = threadIdx.x;
+    auto clamp_seq = [&](int n, int& a, int& b) {
+        a = cu[n];
+        b = cu[n + 1];
         a = a < 0 ? 0 : (a > T ? T : a);
         b = b < a ? a : (b > T ? T : b);
-        acc += n_chunks(b - a);
+    };
+    int carry = 0;
+    for (int base = 0; base < N; base += kPlanThreads) {
+        const int n = base + t;
+        int c = 0;
+        if (n < N) {
+            int a, b;
+            clamp_seq(n, a, b);
+            c = n_chunks(b - a);
+        }
+        part[t] = c;
+        __syncthreads();
+        for (int o = 1; o < kPlanThreads; o <<= 1) {  // inclusive scan
+            const int v = t >= o ? part[t - o] : 0;
+            __syncthreads();
+            part[t] += v;
+            __syncthreads();
+        }
+        if (n < N) chunk_off[n] = carry + part[t] - c;
+        carry += part[kPlanThreads - 1];
+        __syncthreads();
     }
-    chunk_off[N] = acc;
+    if (t == 0) chunk_off[N] = carry;
+    __syncthreads();  // chunk_off is read back below by other threads of this workgroup
+    int4* map = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(chunk_off) + plan_map_offset(N));
+    for (int c = t; c < bound; c += kPlanThreads) {
+        int4 e = {-1, 0, 0, 0};
+        if (c < carry) {
+            int lo = 0, hi = N - 1;  // last n with chunk_off[n] <= c
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+            }
+            int a, b;
+            clamp_seq(lo, a, b);
+            e = int4{lo, c - chunk_off[lo], a, b - a};
+        }
+        map[c] = e;
+    }
 }
 
 // Vector load of CPT consecutive elements into fp32 registers.
@@ -121,6 +162,36 @@ __device__ __forceinline__ f32x4 gemm(const typename MM::ET* A, int lda, int m0,
     return acc;
 }
 
+// MFMA operands for a product whose B operand is a row-major [k][n] LDS tile.
+// bf16: B is read with the transposing LDS read (lane (n, g), g = lane / 16,
+// receives rows k0 + 4g .. + 3 and k0 + 16 + 4g .. + 3 of column n0 + n), and
+// the A fragment supplies the same contraction indices.  fp32: one element
+// per lane, k = k0 + lane / 16.
+template <class MM>
+__device__ __forceinline__ typename MM::Frag load_ap(const typename MM::ET* base, int ld, int r0, int k0, int lane) {
+    if constexpr (sizeof(typename MM::ET) == 2) {
+        const uint16_t* row = base + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+        const u16x4 lo = *reinterpret_cast<const u16x4*>(row);
+        const u16x4 hi = *reinterpret_cast<const u16x4*>(row + 16);
+        const u16x8 u = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(typename MM::Frag, u);
+    } else {
+        return MM::load(base, ld, r0, k0, lane);
+    }
+}
+template <class MM>
+__device__ __forceinline__ typename MM::Frag load_kn(const typename MM::ET* base, int ld, int k0, int n0, int lane) {
+    if constexpr (sizeof(typename MM::ET) == 2) {
+        const int i = lane & 15, g = lane >> 4;
+        const uint16_t* a0 = base + (k0 + 4 * g + (i >> 2)) * ld + n0 + 4 * (i & 3);
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a0);
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(a0 + 16 * ld));
+        return typename MM::Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+        return base[(k0 + (lane >> 4)) * ld + n0 + (lane & 15)];
+    }
+}
+
 // ------------------------------------------------------------------ prep
 // Threads of a prep workgroup: its LDS allows one workgroup per CU, so wide
 // channels take 8 waves (two per SIMD) to overlap the latency of one wave's
@@ -141,8 +212,8 @@ struct PrepSmem {
         float T[kChunk][kChunk + 4];  // 16-byte aligned rows (MFMA A operand)
         struct {
             ET TB[kChunk][kChunk + Mma<BF>::PAD];  // T diag(beta): A operand of W and U
-            ET KEt[K][kChunk + Mma<BF>::PAD];      // (k^ exp(G))^T
-            ET Vt[V][kChunk + Mma<BF>::PAD];       // v^T
+            ET KE[kChunk][K + Mma<BF>::PAD];       // k^ exp(G), row-major (B operand, read transposed)
+            ET Vr[kChunk][V + Mma<BF>::PAD];       // v, row-major (B operand, read transposed)
         } wu;
     } u;
     float A[kChunk][kChunk + 4];  // 16-byte aligned rows (MFMA A operand)
@@ -185,10 +256,9 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     const int slot = blockIdx.x / H;
     const int h = blockIdx.x % H;
     int n, j;
-    if (!slot_to_chunk(p, chunk_off, slot, n, j)) return;
     int64_t start;
     int len;
-    seq_bounds(p, n, start, len);
+    if (!slot_locate(p, chunk_off, slot, n, j, start, len)) return;
     const int rows = min(kChunk, len - j * kChunk);  // >= 1 by construction
 
     const int t = threadIdx.x;
@@ -205,17 +275,30 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     const int i = t / TPR;
     const int pq = t % TPR;
     const int c0 = pq * CPT;
+    const int cv0 = pq * CPTV;
     const bool valid = i < rows;
     const int64_t grow = start + static_cast<int64_t>(j) * kChunk + i;
     float qh[CPT], kh[CPT], gv[CPT];
+    // beta and this thread's part of the v row are requested with q, k and g
+    // and held as loaded (v is first used by the WY products of step 8)
+    constexpr int VEI = 16 / static_cast<int>(sizeof(IT));
+    constexpr int NVV = CPTV / VEI;
+    f32x4 vraw[NVV];
+    float braw = 0.f;
     if (valid) {
         const int64_t off = (grow * H + h) * K + c0;
         load_row<CPT>(static_cast<const IT*>(p.q) + off, qh);
         load_row<CPT>(static_cast<const IT*>(p.k) + off, kh);
         load_row<CPT>(p.g + off, gv);
+        braw = p.beta[grow * H + h];
+        const IT* vsrc = static_cast<const IT*>(p.v) + (grow * H + h) * V + cv0;
+#pragma unroll
+        for (int m = 0; m < NVV; ++m) vraw[m] = *reinterpret_cast<const f32x4*>(vsrc + VEI * m);
     } else {
 #pragma unroll
         for (int c = 0; c < CPT; ++c) qh[c] = kh[c] = gv[c] = 0.0f;
+#pragma unroll
+        for (int m = 0; m < NVV; ++m) vraw[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     float ssq = 0.f, ssk = 0.f;
 #pragma unroll
@@ -251,19 +334,13 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     if (pq == 0) {
         s.rq[i] = rq;
         s.rk[i] = rk;
-        float b = 0.f;
-        if (valid) {
-            b = p.beta[grow * H + h];
-            if (p.use_beta_sigmoid) b = sigmoidf_(b);
-        }
+        float b = braw;
+        if (valid && p.use_beta_sigmoid) b = sigmoidf_(b);
         s.beta[i] = b;
     }
     if (t < 4) s.unsafe[t] = 0;
-    for (int e = t; e < kChunk * (kChunk + 4); e += NT) (&s.A[0][0])[e] = 0.f;
-    for (int e = t; e < kChunk * (kChunk + 1); e += NT) {
-        (&s.M[0][0])[e] = 0.f;
-        if (BWD) (&s.Ak[0][0])[e] = 0.f;
-    }
+    // A, M and Ak are not cleared: every entry that step 6 or 7 reads is
+    // written in step 5 (blocks above the diagonal are masked in step 7)
     __syncthreads();
 
     // ---- 2. inclusive cumulative sum over the 64 rows, per channel
@@ -310,6 +387,11 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         s.gC[c] = __expf(Glast);
     }
     __syncthreads();
+
+    // v has arrived long ago: take its wait here, before step 4 issues
+    // stores (a wait after them would also wait for the stores)
+#pragma unroll
+    for (int m = 0; m < NVV; ++m) asm volatile("" ::"v"(vraw[m]));
 
     // ---- 4. factored operands (LDS) and the chunk's outputs QE, KD (workspace);
     //         k^ exp(G) stays in registers for W
@@ -392,7 +474,12 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             int a = 0, b = pr;
             while (b > a) { b -= a + 1; ++a; }
             const int ri = kSub * I + a, rj = kSub * I + b;
-            if (ri >= rows) continue;  // padding rows stay zero
+            if (ri >= rows) {  // padding rows
+                s.M[ri][rj] = 0.f;
+                s.A[ri][rj] = 0.f;
+                if (BWD) s.Ak[ri][rj] = 0.f;
+                continue;
+            }
             const int64_t oi = ((start + static_cast<int64_t>(j) * kChunk + ri) * H + h) * K;
             const int64_t oj = ((start + static_cast<int64_t>(j) * kChunk + rj) * H + h) * K;
             float sa = 0.f, sm = 0.f;
@@ -410,8 +497,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     __syncthreads();
 
     // ---- 6. T = (I + A)^-1: diagonal sub-blocks by forward substitution ...
-    for (int e = t; e < kChunk * (kChunk + 4); e += NT) (&s.u.T[0][0])[e] = 0.f;
-    __syncthreads();
+    // (T above the diagonal is never read before step 7, which masks it)
     if (w < 4 && lane < kSub) {
         const int I = w;
         const int jc = lane;
@@ -466,9 +552,10 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     for (int m = 0; m < TPT; ++m) {
         const int e = t + m * NT;
         const int a = e / kChunk, b = e % kChunk;
-        tbr[m] = s.u.T[a][b] * s.beta[b];
+        const bool up = b > a;  // above the diagonal: zero (never written in LDS)
+        tbr[m] = up ? 0.f : s.u.T[a][b] * s.beta[b];
         gTB[e] = MM::from_f32(tbr[m]);
-        gMS[e] = MM::from_f32(p.scale * s.M[a][b]);
+        gMS[e] = MM::from_f32(up ? 0.f : p.scale * s.M[a][b]);
     }
     for (int c = t; c < K; c += NT) gGC[c] = s.gC[c];
     if (BWD) {
@@ -476,8 +563,8 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         ET* gAK = reinterpret_cast<ET*>(out + X::kAK);
         for (int e = t; e < kChunk * kChunk; e += NT) {
             const int a = e / kChunk, b = e % kChunk;
-            gT[e] = MM::from_f32(s.u.T[a][b]);
-            gAK[e] = MM::from_f32(s.Ak[a][b]);
+            gT[e] = MM::from_f32(b > a ? 0.f : s.u.T[a][b]);
+            gAK[e] = MM::from_f32(b >= a ? 0.f : s.Ak[a][b]);
         }
     }
     __syncthreads();
@@ -490,18 +577,10 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             const int e = t + m * NT;
             s.u.wu.TB[e / kChunk][e % kChunk] = MM::from_f32(tbr[m]);
         }
-        const int cv0 = pq * CPTV;
-        float vv[CPTV];
-        if (valid) {
-            load_row<CPTV>(static_cast<const IT*>(p.v) + (grow * H + h) * V + cv0, vv);
-        } else {
+        // KE and v rows as they are (v exactly as loaded: IT is ET)
+        store_row<CPT>(&s.u.wu.KE[i][c0], ke_);
 #pragma unroll
-            for (int c = 0; c < CPTV; ++c) vv[c] = 0.f;
-        }
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) s.u.wu.KEt[c0 + c][i] = MM::from_f32(ke_[c]);
-#pragma unroll
-        for (int c = 0; c < CPTV; ++c) s.u.wu.Vt[cv0 + c][i] = MM::from_f32(vv[c]);
+        for (int m = 0; m < NVV; ++m) *reinterpret_cast<f32x4*>(&s.u.wu.Vr[i][cv0 + VEI * m]) = vraw[m];
         __syncthreads();
         ET* gW = reinterpret_cast<ET*>(out + L::kW);
         ET* gU = reinterpret_cast<ET*>(out + L::kU);
@@ -513,9 +592,9 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         for (int ct = w >> 2; ct < NCTWU; ct += NW / 4) {
             f32x4 aw = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
             for (int k0 = 0; k0 < 16 * (rt + 1); k0 += MM::KS) {
-                const auto a = MM::load(&s.u.wu.TB[0][0], LDC, 16 * rt, k0, lane);
-                if (K == V || ct < K / 16) aw = MM::mma(a, MM::load(&s.u.wu.KEt[0][0], LDC, 16 * ct, k0, lane), aw);
-                if (K == V || ct < V / 16) au = MM::mma(a, MM::load(&s.u.wu.Vt[0][0], LDC, 16 * ct, k0, lane), au);
+                const auto a = load_ap<MM>(&s.u.wu.TB[0][0], LDC, 16 * rt, k0, lane);
+                if (K == V || ct < K / 16) aw = MM::mma(a, load_kn<MM>(&s.u.wu.KE[0][0], LDE, k0, 16 * ct, lane), aw);
+                if (K == V || ct < V / 16) au = MM::mma(a, load_kn<MM>(&s.u.wu.Vr[0][0], V + MM::PAD, k0, 16 * ct, lane), au);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
