@@ -2333,8 +2333,8 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
             hipLaunchKernelGGL(plan_chunks_kernel, dim3(1), dim3(kPlanThreads), 0, st, p.cu_seqlens, p.N, p.T, chunk_off,
                                p.total_chunks_bound);
         if (nblk > 0)
-            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true, V>), dim3(static_cast<unsigned>(nblk)),
-                               dim3(prep_threads(K)), 0, st, p, chunk_off, slots, sb);
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, true, V>), dim3(prep_grid<K, BF, true, V>(nblk)),
+                               dim3(prep_threads(K)), 0, st, p, chunk_off, slots, sb, nblk);
     }
     if (want(1) && cgrid > 0) {
         if constexpr (K == 128 && V == 128 && BF)

@@ -39,8 +39,8 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
                                p.total_chunks_bound);
         const int64_t nblk = static_cast<int64_t>(p.total_chunks_bound) * p.H;
         if (nblk > 0)
-            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, KEEP, V>), dim3(static_cast<unsigned>(nblk)),
-                               dim3(prep_threads(K)), 0, st, p, chunk_off, prep, sb);
+            hipLaunchKernelGGL((chunk_prep_kernel<K, BF, KEEP, V>), dim3(prep_grid<K, BF, KEEP, V>(nblk)),
+                               dim3(prep_threads(K)), 0, st, p, chunk_off, prep, sb, nblk);
     }
     if (stage < 0 || stage == 1) {
         // few chains (no more workgroups than CUs): 8 waves per chain shorten

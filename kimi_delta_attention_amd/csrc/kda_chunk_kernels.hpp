@@ -162,6 +162,24 @@ __device__ __forceinline__ f32x4 gemm(const typename MM::ET* A, int lda, int m0,
     return acc;
 }
 
+// Widen N elements held as loaded (16-byte vectors of IT) to fp32.
+template <typename IT, int N>
+__device__ __forceinline__ void widen_row(const f32x4* r, float* dst) {
+    if constexpr (sizeof(IT) == 2) {
+#pragma unroll
+        for (int m = 0; m < N / 8; ++m) {
+            const u16x8 u = __builtin_bit_cast(u16x8, r[m]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dst[8 * m + e] = bf16_bits_to_f32(u[e]);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < N / 4; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[4 * m + e] = r[m][e];
+    }
+}
+
 // MFMA operands for a product whose B operand is a row-major [k][n] LDS tile.
 // bf16: B is read with the transposing LDS read (lane (n, g), g = lane / 16,
 // receives rows k0 + 4g .. + 3 and k0 + 16 + 4g .. + 3 of column n0 + n), and
@@ -232,11 +250,29 @@ struct PrepSmem {
     int unsafe[4];
 };
 
+// Persistent grid of the prep kernel: as many workgroups as fit on the 256
+// CUs at once (160 KiB of LDS and 2048 threads per CU), at most one per item.
+template <int K, bool BF, bool BWD, int V = K>
+__host__ inline unsigned prep_grid(int64_t n_items) {
+    constexpr size_t lds = sizeof(PrepSmem<K, BF, BWD, V>);
+    constexpr int by_lds = static_cast<int>((160 * 1024) / lds);
+    constexpr int by_threads = 2048 / prep_threads(K);
+    constexpr int per_cu = by_lds < by_threads ? by_lds : by_threads;
+    const int64_t cap = static_cast<int64_t>(kPersistentGrid) * (per_cu > 0 ? per_cu : 1);
+    return static_cast<unsigned>(n_items < cap ? n_items : cap);
+}
+
 // BWD additionally writes T = (I + A)^-1 and the un-scaled strictly lower
 // k-k score matrix (BwdExtra layout) for the backward kernels.
+//
+// Persistent over the (slot, head) items, item = slot * H + h: workgroup b
+// takes items b, b + gridDim.x, ...  While an item computes, the next item's
+// q, k, g and beta (requested once the prologue has consumed the current
+// ones) and v (requested once the current v is in LDS) are in flight, and
+// the current item's stores drain behind the next item's work.
 template <int K, bool BF, bool BWD, int V = K>
 __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams p, const int32_t* chunk_off,
-                                                              uint8_t* ws, int64_t slot_bytes) {
+                                                              uint8_t* ws, int64_t slot_bytes, int64_t n_items) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;  // q/k/v element
@@ -253,15 +289,97 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     __shared__ __attribute__((aligned(16))) PrepSmem<K, BF, BWD, V> s;
 
     const int H = p.H;
-    const int slot = blockIdx.x / H;
-    const int h = blockIdx.x % H;
+    const int64_t GS = gridDim.x;
+    constexpr int VEI = 16 / static_cast<int>(sizeof(IT));  // q/k/v elements per 16-byte vector
+    constexpr int NQV = CPT / VEI;
+    constexpr int NGV = CPT / 4;
+    constexpr int NVV = CPTV / VEI;
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+    // slot-map entry of an item (packed input; unused for dense input)
+    auto map_entry = [&](int64_t item) -> int4 {
+        int4 e = {-1, 0, 0, 0};
+        if (p.cu_seqlens && item < n_items)
+            e = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(chunk_off) + plan_map_offset(p.N))[item / H];
+        return e;
+    };
+    auto decode = [&](int64_t item, int4 e, int& n, int& j, int64_t& start, int& len) -> bool {
+        if (item >= n_items) return false;
+        if (p.cu_seqlens) {
+            n = e.x;
+            j = e.y;
+            start = e.z;
+            len = e.w;
+            return n >= 0;
+        }
+        const int nc = n_chunks(p.T);
+        const int slot = static_cast<int>(item / H);
+        n = slot / nc;
+        j = slot % nc;
+        start = static_cast<int64_t>(n) * p.T;
+        len = p.T;
+        return n < p.N;
+    };
+    // this thread's raw inputs of one item (row i, channel parts pq)
+    f32x4 qraw[NQV], kraw[NQV], graw[NGV], vraw[NVV];
+    float braw = 0.f;
+    auto fetch_qkgb = [&](bool ok, int64_t rowh, int i_, int pq_, int rows_) {
+        const bool vr = ok && i_ < rows_;
+        const IT* qs = static_cast<const IT*>(p.q) + rowh * K + pq_ * CPT;
+        const IT* ks = static_cast<const IT*>(p.k) + rowh * K + pq_ * CPT;
+        const float* gs = p.g + rowh * K + pq_ * CPT;
+#pragma unroll
+        for (int m = 0; m < NQV; ++m) {
+            qraw[m] = vr ? *reinterpret_cast<const f32x4*>(qs + VEI * m) : zero4;
+            kraw[m] = vr ? *reinterpret_cast<const f32x4*>(ks + VEI * m) : zero4;
+        }
+#pragma unroll
+        for (int m = 0; m < NGV; ++m) graw[m] = vr ? *reinterpret_cast<const f32x4*>(gs + 4 * m) : zero4;
+        braw = vr ? p.beta[rowh] : 0.f;
+    };
+    auto fetch_v = [&](bool ok, int64_t rowh, int i_, int pq_, int rows_) {
+        const bool vr = ok && i_ < rows_;
+        const IT* vs = static_cast<const IT*>(p.v) + rowh * V + pq_ * CPTV;
+#pragma unroll
+        for (int m = 0; m < NVV; ++m) vraw[m] = vr ? *reinterpret_cast<const f32x4*>(vs + VEI * m) : zero4;
+    };
+
+    // the first item: its inputs, waited for here (so that the loop's waits
+    // only ever count requests made one item earlier)
+    int4 mcur = map_entry(blockIdx.x);
+    int4 mnext = map_entry(blockIdx.x + GS);
+    {
+        int n0 = 0, j0 = 0, len0 = 0;
+        int64_t st0 = 0;
+        const bool ok0 = decode(blockIdx.x, mcur, n0, j0, st0, len0);
+        const int i0 = static_cast<int>(threadIdx.x) / TPR, pq0 = static_cast<int>(threadIdx.x) % TPR;
+        const int rows0 = ok0 ? min(kChunk, len0 - j0 * kChunk) : 0;
+        const int64_t rowh0 = (st0 + static_cast<int64_t>(j0) * kChunk + i0) * H + blockIdx.x % H;
+        fetch_qkgb(ok0, rowh0, i0, pq0, rows0);
+        fetch_v(ok0, rowh0, i0, pq0, rows0);
+#pragma unroll
+        for (int m = 0; m < NQV; ++m) asm volatile("" ::"v"(qraw[m]), "v"(kraw[m]));
+#pragma unroll
+        for (int m = 0; m < NGV; ++m) asm volatile("" ::"v"(graw[m]));
+#pragma unroll
+        for (int m = 0; m < NVV; ++m) asm volatile("" ::"v"(vraw[m]));
+        asm volatile("" ::"v"(braw));
+    }
+
+    for (int64_t item = blockIdx.x; item < n_items; item += GS) {
     int n, j;
     int64_t start;
     int len;
-    if (!slot_locate(p, chunk_off, slot, n, j, start, len)) return;
+    if (!decode(item, mcur, n, j, start, len)) break;  // items past the last chunk are all empty
+    const int slot = static_cast<int>(item / H);
+    const int h = static_cast<int>(item % H);
     const int rows = min(kChunk, len - j * kChunk);  // >= 1 by construction
 
-    const int t = threadIdx.x;
+    // thread coordinates from an opaque copy of the thread id, so that the
+    // body's per-thread LDS addresses are not hoisted out of the item loop
+    // (each would hold a register for the whole loop)
+    int tid = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid));
+    const int t = tid;
     const int lane = t & 63;
     const int w = t >> 6;
     uint8_t* out = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
@@ -277,29 +395,10 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     const int c0 = pq * CPT;
     const int cv0 = pq * CPTV;
     const bool valid = i < rows;
-    const int64_t grow = start + static_cast<int64_t>(j) * kChunk + i;
     float qh[CPT], kh[CPT], gv[CPT];
-    // beta and this thread's part of the v row are requested with q, k and g
-    // and held as loaded (v is first used by the WY products of step 8)
-    constexpr int VEI = 16 / static_cast<int>(sizeof(IT));
-    constexpr int NVV = CPTV / VEI;
-    f32x4 vraw[NVV];
-    float braw = 0.f;
-    if (valid) {
-        const int64_t off = (grow * H + h) * K + c0;
-        load_row<CPT>(static_cast<const IT*>(p.q) + off, qh);
-        load_row<CPT>(static_cast<const IT*>(p.k) + off, kh);
-        load_row<CPT>(p.g + off, gv);
-        braw = p.beta[grow * H + h];
-        const IT* vsrc = static_cast<const IT*>(p.v) + (grow * H + h) * V + cv0;
-#pragma unroll
-        for (int m = 0; m < NVV; ++m) vraw[m] = *reinterpret_cast<const f32x4*>(vsrc + VEI * m);
-    } else {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) qh[c] = kh[c] = gv[c] = 0.0f;
-#pragma unroll
-        for (int m = 0; m < NVV; ++m) vraw[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    widen_row<IT, CPT>(qraw, qh);
+    widen_row<IT, CPT>(kraw, kh);
+    widen_row<float, CPT>(graw, gv);
     float ssq = 0.f, ssk = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
@@ -338,6 +437,16 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         if (valid && p.use_beta_sigmoid) b = sigmoidf_(b);
         s.beta[i] = b;
     }
+    // the next item: where it is, and its q, k, g and beta (this item's are
+    // consumed); the slot-map entry of the item after it
+    int nn = 0, jn = 0, lenn = 0;
+    int64_t stn = 0;
+    const bool okn = decode(item + GS, mnext, nn, jn, stn, lenn);
+    const int rowsn = okn ? min(kChunk, lenn - jn * kChunk) : 0;
+    const int64_t rowhn = (stn + static_cast<int64_t>(jn) * kChunk + i) * H + static_cast<int>((item + GS) % H);
+    const int4 mnext2 = map_entry(item + 2 * GS);
+    fetch_qkgb(okn, rowhn, i, pq, rowsn);
+    asm volatile("" ::: "memory");  // keeps the requests here (not sunk to the loop's end)
     if (t < 4) s.unsafe[t] = 0;
     // A, M and Ak are not cleared: every entry that step 6 or 7 reads is
     // written in step 5 (blocks above the diagonal are masked in step 7)
@@ -387,11 +496,6 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         s.gC[c] = __expf(Glast);
     }
     __syncthreads();
-
-    // v has arrived long ago: take its wait here, before step 4 issues
-    // stores (a wait after them would also wait for the stores)
-#pragma unroll
-    for (int m = 0; m < NVV; ++m) asm volatile("" ::"v"(vraw[m]));
 
     // ---- 4. factored operands (LDS) and the chunk's outputs QE, KD (workspace);
     //         k^ exp(G) stays in registers for W
@@ -581,6 +685,8 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         store_row<CPT>(&s.u.wu.KE[i][c0], ke_);
 #pragma unroll
         for (int m = 0; m < NVV; ++m) *reinterpret_cast<f32x4*>(&s.u.wu.Vr[i][cv0 + VEI * m]) = vraw[m];
+        fetch_v(okn, rowhn, i, pq, rowsn);
+        asm volatile("" ::: "memory");
         __syncthreads();
         ET* gW = reinterpret_cast<ET*>(out + L::kW);
         ET* gU = reinterpret_cast<ET*>(out + L::kU);
@@ -604,6 +710,9 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             }
         }
     }
+    mcur = mnext;
+    mnext = mnext2;
+    }  // items
 }
 
 // ------------------------------------------------------------------ state
