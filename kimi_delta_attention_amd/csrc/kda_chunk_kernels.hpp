@@ -162,6 +162,30 @@ __device__ __forceinline__ f32x4 gemm(const typename MM::ET* A, int lda, int m0,
     return acc;
 }
 
+// N fp32 values rounded to the element type ET, in 16-byte vectors (the
+// rounding of store_row), and the store of such vectors.
+template <typename ET, int N>
+__device__ __forceinline__ void pack_row(const float* src, f32x4* dst) {
+    if constexpr (sizeof(ET) == 2) {
+#pragma unroll
+        for (int m = 0; m < N / 8; ++m) {
+            u16x8 u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = f32_to_bf16_bits(src[8 * m + e]);
+            dst[m] = __builtin_bit_cast(f32x4, u);
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < N / 4; ++m) dst[m] = f32x4{src[4 * m], src[4 * m + 1], src[4 * m + 2], src[4 * m + 3]};
+    }
+}
+template <typename ET, int N>
+__device__ __forceinline__ void store_packed(ET* dst, const f32x4* v) {
+    constexpr int E = 16 / static_cast<int>(sizeof(ET));
+#pragma unroll
+    for (int m = 0; m < N / E; ++m) *reinterpret_cast<f32x4*>(dst + E * m) = v[m];
+}
+
 // Widen N elements held as loaded (16-byte vectors of IT) to fp32.
 template <typename IT, int N>
 __device__ __forceinline__ void widen_row(const f32x4* r, float* dst) {
@@ -497,9 +521,11 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     }
     __syncthreads();
 
-    // ---- 4. factored operands (LDS) and the chunk's outputs QE, KD (workspace);
+    // ---- 4. factored operands (LDS) and the chunk's outputs QE, KD (and KE);
+    //         those three are stored after step 5's products are issued, and
     //         k^ exp(G) stays in registers for W
-    float ke_[CPT];
+    constexpr int PV = CPT * static_cast<int>(sizeof(ET)) / 16;
+    f32x4 pQE[PV], pKE[PV], pKD[PV];
     {
         const int I = i / kSub;
         float a_[CPT], e_[CPT], o_[CPT];
@@ -522,13 +548,13 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         store_row<CPT>(&s.u.op.kbe[i][c0], o_);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) o_[c] = p.scale * qh[c] * a_[c] * s.Er[I][c0 + c];
-        store_row<CPT>(gQE + i * K + c0, o_);
+        pack_row<ET, CPT>(o_, pQE);
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) ke_[c] = kh[c] * a_[c] * s.Er[I][c0 + c];
-        if (BWD) store_row<CPT>(reinterpret_cast<ET*>(out + X::kKE) + i * K + c0, ke_);
+        for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * a_[c] * s.Er[I][c0 + c];
+        pack_row<ET, CPT>(o_, pKE);
 #pragma unroll
         for (int c = 0; c < CPT; ++c) o_[c] = kh[c] * e_[c] * s.Ec[I][c0 + c];
-        store_row<CPT>(gKD + i * K + c0, o_);
+        pack_row<ET, CPT>(o_, pKD);
     }
     __syncthreads();
 
@@ -569,6 +595,9 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             }
         }
     }
+    store_packed<ET, CPT>(gQE + i * K + c0, pQE);
+    if (BWD) store_packed<ET, CPT>(reinterpret_cast<ET*>(out + X::kKE) + i * K + c0, pKE);
+    store_packed<ET, CPT>(gKD + i * K + c0, pKD);
     // pairwise diagonal sub-blocks whose decay span is too wide to factorise
     for (int I = 0; I < 4; ++I) {
         if (!s.unsafe[I]) continue;
@@ -649,40 +678,45 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         __syncthreads();
     }
 
-    // ---- 7. T diag(beta) and scale * M to the workspace
-    constexpr int TPT = kChunk * kChunk / NT;
-    float tbr[TPT];
+    // ---- 7. T diag(beta) and scale * M to the workspace; thread t owns EPT
+    //         consecutive entries of one row (entries above the diagonal are
+    //         zero: they were never written in LDS)
+    constexpr int EPT = kChunk * kChunk / NT;
+    static_assert(EPT % 8 == 0, "whole 16-byte vectors per thread");
+    const int e7 = t * EPT, a7 = e7 / kChunk, b7 = e7 % kChunk;
+    float tbr[EPT];
+    {
+        float ms[EPT];
 #pragma unroll
-    for (int m = 0; m < TPT; ++m) {
-        const int e = t + m * NT;
-        const int a = e / kChunk, b = e % kChunk;
-        const bool up = b > a;  // above the diagonal: zero (never written in LDS)
-        tbr[m] = up ? 0.f : s.u.T[a][b] * s.beta[b];
-        gTB[e] = MM::from_f32(tbr[m]);
-        gMS[e] = MM::from_f32(up ? 0.f : p.scale * s.M[a][b]);
+        for (int x = 0; x < EPT; ++x) {
+            const int b = b7 + x;
+            const bool up = b > a7;
+            tbr[x] = up ? 0.f : s.u.T[a7][b] * s.beta[b];
+            ms[x] = up ? 0.f : p.scale * s.M[a7][b];
+        }
+        store_row<EPT>(gTB + e7, tbr);
+        store_row<EPT>(gMS + e7, ms);
     }
     for (int c = t; c < K; c += NT) gGC[c] = s.gC[c];
     if (BWD) {
-        ET* gT = reinterpret_cast<ET*>(out + X::kT);
-        ET* gAK = reinterpret_cast<ET*>(out + X::kAK);
-        for (int e = t; e < kChunk * kChunk; e += NT) {
-            const int a = e / kChunk, b = e % kChunk;
-            gT[e] = MM::from_f32(b > a ? 0.f : s.u.T[a][b]);
-            gAK[e] = MM::from_f32(b >= a ? 0.f : s.Ak[a][b]);
+        float tt[EPT], ak[EPT];
+#pragma unroll
+        for (int x = 0; x < EPT; ++x) {
+            const int b = b7 + x;
+            tt[x] = b > a7 ? 0.f : s.u.T[a7][b];
+            ak[x] = b >= a7 ? 0.f : s.Ak[a7][b];
         }
+        store_row<EPT>(reinterpret_cast<ET*>(out + X::kT) + e7, tt);
+        store_row<EPT>(reinterpret_cast<ET*>(out + X::kAK) + e7, ak);
     }
     __syncthreads();
 
     // ---- 8. the WY pair W = T diag(beta) (k^ exp(G)), U = T diag(beta) v on MFMA
     {
         constexpr int LDC = kChunk + MM::PAD;
-#pragma unroll
-        for (int m = 0; m < TPT; ++m) {
-            const int e = t + m * NT;
-            s.u.wu.TB[e / kChunk][e % kChunk] = MM::from_f32(tbr[m]);
-        }
+        store_row<EPT>(&s.u.wu.TB[a7][b7], tbr);
         // KE and v rows as they are (v exactly as loaded: IT is ET)
-        store_row<CPT>(&s.u.wu.KE[i][c0], ke_);
+        store_packed<ET, CPT>(&s.u.wu.KE[i][c0], pKE);
 #pragma unroll
         for (int m = 0; m < NVV; ++m) *reinterpret_cast<f32x4*>(&s.u.wu.Vr[i][cv0 + VEI * m]) = vraw[m];
         fetch_v(okn, rowhn, i, pq, rowsn);
