@@ -428,7 +428,10 @@ __host__ __device__ constexpr int vlocal_threads(bool bf) { return bf ? 512 : 25
 // Per V-column block of BV columns: Y = v - KE S, dD = KD dS' + MS^T dO,
 // D = TB Y, dY = TB^T dD (= dv), and the V-summed products dQE, dKE, dKD,
 // dMS, dTB, dgam accumulate over the blocks.  The next block's S, dS', dO and
-// v are requested before the current block's products.
+// v are requested before the current block's products.  Every operand stays
+// in LDS in the layout it arrives in: products that need a transposed operand
+// (MS^T, TB^T, and S, dS', dO, Y, dD as [k][n] B operands) read it through
+// the transposing LDS read (load_kn).
 template <int K, int V, int BV, bool BF>
 __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(ChunkParams p, ChunkGrads gr,
                                                                               const int32_t* chunk_off,
@@ -460,20 +463,14 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     __shared__ __attribute__((aligned(16))) ET KEn[kChunk][LDK];
     __shared__ __attribute__((aligned(16))) ET KDn[kChunk][LDK];
     __shared__ __attribute__((aligned(16))) ET TBn[kChunk][LDC];
-    __shared__ __attribute__((aligned(16))) ET TBt[kChunk][LDC];
-    __shared__ __attribute__((aligned(16))) ET MSt[kChunk][LDC];
-    __shared__ __attribute__((aligned(16))) ET St[BV][LDK];
+    __shared__ __attribute__((aligned(16))) ET MSn[kChunk][LDC];
+    __shared__ __attribute__((aligned(16))) ET St[BV][LDK];   // S^T block: row = value column, K keys
     __shared__ __attribute__((aligned(16))) ET dSt[BV][LDK];
-    __shared__ __attribute__((aligned(16))) ET Sn[K][LDB];
-    __shared__ __attribute__((aligned(16))) ET dSn[K][LDB];
     __shared__ __attribute__((aligned(16))) ET dOn[kChunk][LDB];
     __shared__ __attribute__((aligned(16))) ET Yn[kChunk][LDB];
     __shared__ __attribute__((aligned(16))) ET Dn[kChunk][LDB];
     __shared__ __attribute__((aligned(16))) ET dDn[kChunk][LDB];
     __shared__ __attribute__((aligned(16))) ET dYn[kChunk][LDB];
-    __shared__ __attribute__((aligned(16))) ET dOt[BV][LDC];
-    __shared__ __attribute__((aligned(16))) ET Yt[BV][LDC];
-    __shared__ __attribute__((aligned(16))) ET dDt[BV][LDC];
 
     const int H = p.H;
     const int slot = blockIdx.x / H;
@@ -538,13 +535,6 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
                 const int c = e % BV, key = (e / BV) * VE;
                 *reinterpret_cast<f32x4*>(&St[c][key]) = rS[m];
                 *reinterpret_cast<f32x4*>(&dSt[c][key]) = rD[m];
-                const ET* se = reinterpret_cast<const ET*>(&rS[m]);
-                const ET* de = reinterpret_cast<const ET*>(&rD[m]);
-#pragma unroll
-                for (int x = 0; x < VE; ++x) {
-                    Sn[key + x][c] = se[x];
-                    dSn[key + x][c] = de[x];
-                }
             }
         }
 #pragma unroll
@@ -553,9 +543,6 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
             if (NVO % NT == 0 || e < NVO) {
                 const int i = e / VPR, c = (e % VPR) * VE;
                 *reinterpret_cast<f32x4*>(&dOn[i][c]) = rO[m];
-                const ET* oe = reinterpret_cast<const ET*>(&rO[m]);
-#pragma unroll
-                for (int x = 0; x < VE; ++x) dOt[c + x][i] = oe[x];
             }
         }
     };
@@ -563,8 +550,7 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     copy_in<ET, kChunk, K, NT>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + X::kKE), t);
     copy_in<ET, kChunk, K, NT>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
     copy_in<ET, kChunk, kChunk, NT>(&TBn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-    copy_in_t<ET, kChunk, kChunk, NT>(&TBt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-    copy_in_t<ET, kChunk, kChunk, NT>(&MSt[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
+    copy_in<ET, kChunk, kChunk, NT>(&MSn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
     fetch(0);  // after the copies, whose stores would otherwise wait for it too
 
     f32x4 aQE[AW], aKE[AW], aKD[AW], aMS[CW], aTB[CW];
@@ -597,12 +583,12 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = vcur[m][r] - pp[r];
             tile_store<MM>(&Yn[0][0], LDB, 16 * rt, 16 * ct, y, lane);
-            tile_store_t<MM>(&Yt[0][0], LDC, 16 * rt, 16 * ct, y, lane);
             f32x4 dd = {0.f, 0.f, 0.f, 0.f};
             dd = gemm<MM>(&KDn[0][0], LDK, 16 * rt, &dSt[0][0], LDK, 16 * ct, 0, K, dd, lane);
-            dd = gemm<MM>(&MSt[0][0], LDC, 16 * rt, &dOt[0][0], LDC, 16 * ct, klo, kChunk, dd, lane);
+            for (int k0 = klo; k0 < kChunk; k0 += MM::KS)  // MS^T is upper triangular
+                dd = MM::mma(load_kn<MM>(&MSn[0][0], LDC, k0, 16 * rt, lane),
+                             load_kn<MM>(&dOn[0][0], LDB, k0, 16 * ct, lane), dd);
             tile_store<MM>(&dDn[0][0], LDB, 16 * rt, 16 * ct, dd, lane);
-            tile_store_t<MM>(&dDt[0][0], LDC, 16 * rt, 16 * ct, dd, lane);
         }
         __syncthreads();
 
@@ -612,10 +598,14 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
             const int ct = hv + WPR * m;
             if (ct >= NCT) continue;
             f32x4 d = {0.f, 0.f, 0.f, 0.f};
-            d = gemm<MM>(&TBn[0][0], LDC, 16 * rt, &Yt[0][0], LDC, 16 * ct, 0, 16 * (rt + 1), d, lane);
+            for (int k0 = 0; k0 < 16 * (rt + 1); k0 += MM::KS)  // TB is lower triangular
+                d = MM::mma(load_ap<MM>(&TBn[0][0], LDC, 16 * rt, k0, lane),
+                            load_kn<MM>(&Yn[0][0], LDB, k0, 16 * ct, lane), d);
             tile_store<MM>(&Dn[0][0], LDB, 16 * rt, 16 * ct, d, lane);
             f32x4 dy = {0.f, 0.f, 0.f, 0.f};
-            dy = gemm<MM>(&TBt[0][0], LDC, 16 * rt, &dDt[0][0], LDC, 16 * ct, klo, kChunk, dy, lane);
+            for (int k0 = klo; k0 < kChunk; k0 += MM::KS)
+                dy = MM::mma(load_kn<MM>(&TBn[0][0], LDC, k0, 16 * rt, lane),
+                             load_kn<MM>(&dDn[0][0], LDB, k0, 16 * ct, lane), dy);
             tile_store<MM>(&dYn[0][0], LDB, 16 * rt, 16 * ct, dy, lane);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -625,13 +615,19 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         }
         __syncthreads();
 
-        // V-summed products over this column block
+        // V-summed products over this column block (contraction over the block's
+        // value columns; S and dS' enter as [v][key] B operands)
 #pragma unroll
         for (int m = 0; m < AW; ++m) {
             const int c = hv + WPR * m;
-            aQE[m] = gemm<MM>(&dOn[0][0], LDB, 16 * rt, &Sn[0][0], LDB, 16 * c, 0, BV, aQE[m], lane);
-            aKE[m] = gemm<MM>(&dYn[0][0], LDB, 16 * rt, &Sn[0][0], LDB, 16 * c, 0, BV, aKE[m], lane);
-            aKD[m] = gemm<MM>(&Dn[0][0], LDB, 16 * rt, &dSn[0][0], LDB, 16 * c, 0, BV, aKD[m], lane);
+#pragma unroll
+            for (int k0 = 0; k0 < BV; k0 += MM::KS) {
+                const auto bs = load_kn<MM>(&St[0][0], LDK, k0, 16 * c, lane);
+                aQE[m] = MM::mma(load_ap<MM>(&dOn[0][0], LDB, 16 * rt, k0, lane), bs, aQE[m]);
+                aKE[m] = MM::mma(load_ap<MM>(&dYn[0][0], LDB, 16 * rt, k0, lane), bs, aKE[m]);
+                aKD[m] = MM::mma(load_ap<MM>(&Dn[0][0], LDB, 16 * rt, k0, lane),
+                                 load_kn<MM>(&dSt[0][0], LDK, k0, 16 * c, lane), aKD[m]);
+            }
         }
 #pragma unroll
         for (int m = 0; m < CW; ++m) {
@@ -641,7 +637,7 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         }
         for (int key = t; key < K; key += NT)
 #pragma unroll 4
-            for (int c = 0; c < BV; ++c) dgam += MM::to_f32(Sn[key][c]) * MM::to_f32(dSn[key][c]);
+            for (int c = 0; c < BV; ++c) dgam += MM::to_f32(St[c][key]) * MM::to_f32(dSt[c][key]);
         __syncthreads();
     }
 
