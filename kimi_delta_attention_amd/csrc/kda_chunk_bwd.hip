@@ -432,10 +432,22 @@ __host__ __device__ constexpr int vlocal_threads(bool bf) { return bf ? 512 : 25
 // in LDS in the layout it arrives in: products that need a transposed operand
 // (MS^T, TB^T, and S, dS', dO, Y, dD as [k][n] B operands) read it through
 // the transposing LDS read (load_kn).
+//
+// Persistent over the (slot, head) items like the prep kernel: the next
+// item's KE, KD, TB and MS are requested once the current ones are in LDS,
+// and its first block's S, dS', dO and v during the current item's last
+// block.
+// One persistent workgroup per CU: at K = 128 the LDS allows no second one,
+// and at smaller K the registers of the item loop do not.
+__host__ inline unsigned vlocal_grid(int64_t n_items) {
+    return static_cast<unsigned>(n_items < kPersistentGrid ? n_items : kPersistentGrid);
+}
+
 template <int K, int V, int BV, bool BF>
 __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(ChunkParams p, ChunkGrads gr,
                                                                               const int32_t* chunk_off,
-                                                                              uint8_t* ws, int64_t slot_bytes) {
+                                                                              uint8_t* ws, int64_t slot_bytes,
+                                                                              int64_t n_items) {
     using MM = Mma<BF>;
     using ET = typename MM::ET;
     using IT = typename std::conditional<BF, uint16_t, float>::type;
@@ -473,34 +485,80 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     __shared__ __attribute__((aligned(16))) ET dYn[kChunk][LDB];
 
     const int H = p.H;
-    const int slot = blockIdx.x / H;
-    const int h = blockIdx.x % H;
-    int n, j;
-    int64_t start;
-    int len;
-    if (!slot_locate(p, chunk_off, slot, n, j, start, len)) return;
-    const int rows = min(kChunk, len - j * kChunk);
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int rt = w & 3, hv = w >> 2;  // 16-row tile and column-tile phase of this wave
-    uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
-    const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
-
-    const ET* gS = reinterpret_cast<const ET*>(base + X::kS);
-    const ET* gDS = reinterpret_cast<const ET*>(base + X::kDS);
+    const int64_t GS = gridDim.x;
     const IT* dOg = static_cast<const IT*>(gr.dO);
     const IT* vg = static_cast<const IT*>(p.v);
     IT* dvg = static_cast<IT*>(gr.dv);
 
-    // next block's operands in registers: S and dS' (stored transposed: vector e
+    // where an item is
+    struct Loc {
+        bool ok;
+        int h, rows;
+        int64_t rbase;  // global row of the chunk's first row
+        uint8_t* base;  // the item's workspace slot
+    };
+    auto map_entry = [&](int64_t item) -> int4 {
+        int4 e = {-1, 0, 0, 0};
+        if (p.cu_seqlens && item < n_items)
+            e = reinterpret_cast<const int4*>(reinterpret_cast<const uint8_t*>(chunk_off) + plan_map_offset(p.N))[item / H];
+        return e;
+    };
+    auto decode = [&](int64_t item, int4 e) -> Loc {
+        Loc l{false, 0, 0, 0, ws};
+        if (item >= n_items) return l;
+        int n, j, len;
+        int64_t start;
+        const int slot = static_cast<int>(item / H);
+        if (p.cu_seqlens) {
+            n = e.x;
+            j = e.y;
+            start = e.z;
+            len = e.w;
+            if (n < 0) return l;
+        } else {
+            const int nc = n_chunks(p.T);
+            n = slot / nc;
+            j = slot % nc;
+            start = static_cast<int64_t>(n) * p.T;
+            len = p.T;
+            if (n >= p.N) return l;
+        }
+        l.ok = true;
+        l.h = static_cast<int>(item % H);
+        l.rows = min(kChunk, len - j * kChunk);
+        l.rbase = start + static_cast<int64_t>(j) * kChunk;
+        l.base = ws + (static_cast<int64_t>(slot) * H + l.h) * slot_bytes;
+        return l;
+    };
+
+    // an item's KE, KD, TB and MS in registers on their way to LDS
+    Seg<ET, kChunk, K, false, NT> cKE, cKD;
+    Seg<ET, kChunk, kChunk, false, NT> cTB, cMS;
+    auto fetch_copy = [&](const Loc& l, int t_) {
+        if (!l.ok) return;
+        cKE.load(reinterpret_cast<const ET*>(l.base + X::kKE), K, t_);
+        cKD.load(reinterpret_cast<const ET*>(l.base + L::kKD), K, t_);
+        cTB.load(reinterpret_cast<const ET*>(l.base + L::kTB), kChunk, t_);
+        cMS.load(reinterpret_cast<const ET*>(l.base + L::kMS), kChunk, t_);
+    };
+
+    // a block's operands in registers: S and dS' (stored transposed: vector e
     // holds keys (e / BV) VE .. +VE-1 of column e % BV), dO rows i (16-byte
-    // vectors), and v in the accumulator layout of this wave's tiles
+    // vectors), and v in the accumulator layout of a wave's tiles
     f32x4 rS[PS], rD[PS], rO[PO];
-    IT rv[TW][4];  // raw: converted where used, so that the request is not waited on here
-    auto fetch = [&](int vb) {
+    // raw, one 32-bit register each (16-bit values are not packed in pairs,
+    // which would wait for the request), converted where used
+    using RT = typename std::conditional<BF, uint32_t, float>::type;
+    RT rv[TW][4];
+    auto fetch = [&](const Loc& l, int vb, int t_) {
+        if (!l.ok) return;
+        const int lane_ = t_ & 63, rt_ = (t_ >> 6) & 3, hv_ = t_ >> 8;
         const int v0 = vb * BV;
+        const ET* gS = reinterpret_cast<const ET*>(l.base + X::kS);
+        const ET* gDS = reinterpret_cast<const ET*>(l.base + X::kDS);
 #pragma unroll
         for (int m = 0; m < PS; ++m) {
-            const int e = t + m * NT;
+            const int e = t_ + m * NT;
             if (NVS % NT == 0 || e < NVS) {
                 const int c = e % BV, key = (e / BV) * VE;
                 rS[m] = *reinterpret_cast<const f32x4*>(gS + (v0 + c) * K + key);
@@ -509,28 +567,30 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         }
 #pragma unroll
         for (int m = 0; m < PO; ++m) {
-            const int e = t + m * NT;
+            const int e = t_ + m * NT;
             if (NVO % NT == 0 || e < NVO) {
                 const int i = e / VPR, c = (e % VPR) * VE;
-                rO[m] = i < rows ? *reinterpret_cast<const f32x4*>(dOg + ((rbase + i) * H + h) * V + v0 + c)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+                rO[m] = i < l.rows ? *reinterpret_cast<const f32x4*>(dOg + ((l.rbase + i) * H + l.h) * V + v0 + c)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
 #pragma unroll
         for (int m = 0; m < TW; ++m) {
-            const int ct = hv + WPR * m;
+            const int ct = hv_ + WPR * m;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * rt + 4 * (lane >> 4) + r;
-                rv[m][r] = (ct < NCT && i < rows) ? vg[((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15)]
-                                                  : IT(0);
+                const int i = 16 * rt_ + 4 * (lane_ >> 4) + r;
+                rv[m][r] = (ct < NCT && i < l.rows)
+                               ? static_cast<RT>(vg[((l.rbase + i) * H + l.h) * V + v0 + 16 * ct + (lane_ & 15)])
+                               : RT(0);
             }
         }
     };
-    auto stage = [&]() {
+
+    auto stage = [&](int t_) {
 #pragma unroll
         for (int m = 0; m < PS; ++m) {
-            const int e = t + m * NT;
+            const int e = t_ + m * NT;
             if (NVS % NT == 0 || e < NVS) {
                 const int c = e % BV, key = (e / BV) * VE;
                 *reinterpret_cast<f32x4*>(&St[c][key]) = rS[m];
@@ -539,7 +599,7 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         }
 #pragma unroll
         for (int m = 0; m < PO; ++m) {
-            const int e = t + m * NT;
+            const int e = t_ + m * NT;
             if (NVO % NT == 0 || e < NVO) {
                 const int i = e / VPR, c = (e % VPR) * VE;
                 *reinterpret_cast<f32x4*>(&dOn[i][c]) = rO[m];
@@ -547,11 +607,35 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
         }
     };
 
-    copy_in<ET, kChunk, K, NT>(&KEn[0][0], LDK, reinterpret_cast<const ET*>(base + X::kKE), t);
-    copy_in<ET, kChunk, K, NT>(&KDn[0][0], LDK, reinterpret_cast<const ET*>(base + L::kKD), t);
-    copy_in<ET, kChunk, kChunk, NT>(&TBn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kTB), t);
-    copy_in<ET, kChunk, kChunk, NT>(&MSn[0][0], LDC, reinterpret_cast<const ET*>(base + L::kMS), t);
-    fetch(0);  // after the copies, whose stores would otherwise wait for it too
+    // the first item: everything requested and waited for here, so that the
+    // loop's waits only count requests made one item (or one block) earlier
+    int4 mnext = map_entry(blockIdx.x + GS);
+    Loc lc = decode(blockIdx.x, map_entry(blockIdx.x));
+    fetch_copy(lc, threadIdx.x);
+    fetch(lc, 0, threadIdx.x);
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+
+    for (int64_t item = blockIdx.x; item < n_items; item += GS) {
+    if (!lc.ok) break;  // items past the last chunk are all empty
+    // thread coordinates from an opaque copy of the thread id (keeps the
+    // body's LDS addresses from being hoisted out of the item loop)
+    int tid = static_cast<int>(threadIdx.x);
+    asm volatile("" : "+v"(tid));
+    const int t = tid, lane = t & 63, w = t >> 6;
+    const int rt = w & 3, hv = w >> 2;  // 16-row tile and column-tile phase of this wave
+    const int rows = lc.rows;
+    const int h = lc.h;
+    const int64_t rbase = lc.rbase;
+    uint8_t* base = lc.base;
+
+    cKE.store(&KEn[0][0], LDK, t);
+    cKD.store(&KDn[0][0], LDK, t);
+    cTB.store(&TBn[0][0], LDC, t);
+    cMS.store(&MSn[0][0], LDC, t);
+    const Loc ln = decode(item + GS, mnext);
+    const int4 mnext2 = map_entry(item + 2 * GS);
+    fetch_copy(ln, t);
+    asm volatile("" ::: "memory");  // keeps the requests here
 
     f32x4 aQE[AW], aKE[AW], aKD[AW], aMS[CW], aTB[CW];
 #pragma unroll
@@ -563,13 +647,25 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
 
     for (int vb = 0; vb < V / BV; ++vb) {
         const int v0 = vb * BV;
-        stage();
+        stage(t);
         float vcur[TW][4];
 #pragma unroll
         for (int m = 0; m < TW; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) vcur[m][r] = Elem<IT>::load(&rv[m][r], 0);
-        if (vb + 1 < V / BV) fetch(vb + 1);
+            for (int r = 0; r < 4; ++r) {
+                RT x = rv[m][r];
+                asm volatile("" : "+v"(x));  // converted here, not right after the request
+                if constexpr (BF) vcur[m][r] = bf16_bits_to_f32(static_cast<uint16_t>(x));
+                else vcur[m][r] = x;
+            }
+        {
+            // the next block of this item, or the first block of the next
+            // item: one request sequence (a branch per case would land them
+            // in different registers and copy them, waiting for the data)
+            const bool last = vb + 1 == V / BV;
+            fetch(last ? ln : lc, last ? 0 : vb + 1, t);
+        }
+        asm volatile("" ::: "memory");
         __syncthreads();
 
         // Y = v - KE S and dD = KD dS' + MS^T dO on this wave's tiles
@@ -664,6 +760,9 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
             gTB[i * kChunk + col] = MM::from_f32(aTB[m][r]);
         }
     for (int key = t; key < K; key += NT) reinterpret_cast<float*>(base + X::kDGAM)[key] = dgam;
+    lc = ln;
+    mnext = mnext2;
+    }  // items
 }
 
 // ------------------------------------------------------------------ K-local gradients
@@ -2351,8 +2450,8 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                chunk_off, slots, sb);
     }
     if (want(3) && nblk > 0)
-        hipLaunchKernelGGL((chunk_bwd_vlocal_kernel<K, V, BV, BF>), dim3(static_cast<unsigned>(nblk)),
-                           dim3(vlocal_threads(BF)), 0, st, p, gr, chunk_off, slots, sb);
+        hipLaunchKernelGGL((chunk_bwd_vlocal_kernel<K, V, BV, BF>), dim3(vlocal_grid(nblk)),
+                           dim3(vlocal_threads(BF)), 0, st, p, gr, chunk_off, slots, sb, nblk);
     if (want(4)) {
         if (nblk > 0) {
             if constexpr (BF && K == 128 && V == 128)
