@@ -1807,6 +1807,10 @@ struct KlocW8Smem {
             float dM[kChunk][LDD];  // scale * dMS (lower incl. diagonal)
             float dA[kChunk][LDD];  // diag(beta) dA (strictly lower)
         } sc;
+        struct {
+            ET dq[kChunk][LDE];     // the slot's dq and dk rows on their way out
+            ET dk[kChunk][LDE];
+        } out;
     } x;
     ET ew[8][kChunk][16];
     float invP[4][K];
@@ -2335,23 +2339,34 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
         }
         __syncthreads();
         {
-            uint16_t* dqg = static_cast<uint16_t*>(gr.dq);
-            uint16_t* dkg = static_cast<uint16_t*>(gr.dk);
+            // dq and dk through LDS (the union's score gradients are done),
+            // then out as 16-byte row segments
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
-                    if (i >= rows) continue;
                     float oq = dq[I][r], ok = dk[I][r];
                     if (p.use_qk_l2norm) {
                         oq = s.rq[i] * (oq - MM::to_f32(s.qh[i][c]) * s.dots[0][0][i]);
                         ok = s.rk[i] * (ok - MM::to_f32(s.kh[i][c]) * s.dots[1][0][i]);
                     }
-                    const int64_t gi = ((rbase + i) * H + h) * K + c;
-                    dqg[gi] = f32_to_bf16_bits(oq);
-                    dkg[gi] = f32_to_bf16_bits(ok);
+                    s.x.out.dq[i][c] = f32_to_bf16_bits(oq);
+                    s.x.out.dk[i][c] = f32_to_bf16_bits(ok);
                 }
+            __syncthreads();
+            uint16_t* dqg = static_cast<uint16_t*>(gr.dq);
+            uint16_t* dkg = static_cast<uint16_t*>(gr.dk);
+            constexpr int SEG = K / 8;  // 16-byte segments per row
+#pragma unroll
+            for (int m = 0; m < kChunk * SEG / NT; ++m) {
+                const int e = t + NT * m, i = e / SEG, c8 = 8 * (e % SEG);
+                if (i < rows) {
+                    const int64_t gi = ((rbase + i) * H + h) * K + c8;
+                    *reinterpret_cast<u16x8*>(dqg + gi) = *reinterpret_cast<const u16x8*>(&s.x.out.dq[i][c8]);
+                    *reinterpret_cast<u16x8*>(dkg + gi) = *reinterpret_cast<const u16x8*>(&s.x.out.dk[i][c8]);
+                }
+            }
         }
         if (t < kChunk && t < rows) {
             float db = s.dbr[0][t] + s.dbr[1][t];
