@@ -1804,8 +1804,9 @@ struct KlocW8Smem {
             ET Zn[kChunk][LDC];
         } mm;
         struct {
-            float dM[kChunk][LDD];  // scale * dMS (lower incl. diagonal)
-            float dA[kChunk][LDD];  // diag(beta) dA (strictly lower)
+            ET dM[kChunk][LDC];   // dMS (lower incl. diagonal) as stored: bf16, exact
+            ET dA[kChunk][LDC];   // diag(beta) dA (strictly lower), bf16 high part
+            ET dAl[kChunk][LDC];  // and the bf16 remainder, so that hi + lo holds 16 bits
         } sc;
         struct {
             ET dq[kChunk][LDE];     // the slot's dq and dk rows on their way out
@@ -2055,7 +2056,10 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                     const int i = 16 * rt + 4 * lg + r, jj = 16 * (ch + 2 * m) + lc;
                     const float dAv = (jj < i) ? -da[m][r] : 0.f;
                     rowp[r] += dAv * MM::to_f32(akv[4 * m + r]);
-                    s.x.sc.dA[i][jj] = dAv * s.beta[i];
+                    const float x_ = dAv * s.beta[i];
+                    const ET hi = MM::from_f32(x_);
+                    s.x.sc.dA[i][jj] = hi;
+                    s.x.sc.dAl[i][jj] = MM::from_f32(x_ - MM::to_f32(hi));
                 }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -2069,7 +2073,7 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int a = (t >> 6) + 8 * e, b = t & 63;
-                s.x.sc.dM[a][b] = (b <= a) ? p.scale * MM::to_f32(msv[e]) : 0.f;
+                s.x.sc.dM[a][b] = (b <= a) ? msv[e] : ET(0);  // the scale is applied to the products
             }
         }
         __syncthreads();
@@ -2130,25 +2134,46 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
 #pragma unroll
                 for (int r = 0; r < 4; ++r) bv[4 * J + r] = ko[4 * J + r] * __expf(Ge[J] - Gc[4 * J + r]);
             // f(J, I) scales column c of every term, so it is folded into the
-            // B values and the sums over J accumulate in the MFMA
+            // B values and the sums over J accumulate in the MFMA.  bf16 products
+            // with two sub-blocks J, J + 1 per contraction step (contraction order
+            // of load_ap): the lane's B values are its own rows of both.  B is
+            // split into bf16 high and low parts, and so is dA (dMS is exact in
+            // bf16), so that the products keep about 16 bits of their operands.
+            auto pair_b = [&](float f0, int b0, float f1, int b1, MM::Frag& hi, MM::Frag& lo) {
+                u16x8 uh, ul;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x_ = e < 4 ? f0 * bv[4 * b0 + e] : f1 * bv[4 * b1 + e - 4];
+                    uh[e] = MM::from_f32(x_);
+                    ul[e] = MM::from_f32(x_ - MM::to_f32(uh[e]));
+                }
+                hi = __builtin_bit_cast(MM::Frag, uh);
+                lo = __builtin_bit_cast(MM::Frag, ul);
+            };
             f32x4 pq[4], pk[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) pq[I] = pk[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int J = 0; J < 4; ++J)
+            for (int I = 0; I < 4; ++I)
 #pragma unroll
-                for (int I = J; I < 4; ++I) {
-                    const float f = fac(J, I);
-                    const float bf[4] = {f * bv[4 * J], f * bv[4 * J + 1], f * bv[4 * J + 2], f * bv[4 * J + 3]};
-                    pq[I] = mma16_f32_rb_acc<false>(&s.x.sc.dM[0][0], LDD, kSub * I, bf, kSub * J, lane, pq[I]);
-                    pk[I] = mma16_f32_rb_acc<false>(&s.x.sc.dA[0][0], LDD, kSub * I, bf, kSub * J, lane, pk[I]);
+                for (int Jp = 0; Jp <= I; Jp += 2) {
+                    MM::Frag bh, bl;
+                    pair_b(fac(Jp, I), Jp, Jp + 1 <= I ? fac(Jp + 1, I) : 0.f, Jp + 1, bh, bl);
+                    const auto am = load_ap<MM>(&s.x.sc.dM[0][0], LDC, kSub * I, kSub * Jp, lane);
+                    const auto ah = load_ap<MM>(&s.x.sc.dA[0][0], LDC, kSub * I, kSub * Jp, lane);
+                    const auto al = load_ap<MM>(&s.x.sc.dAl[0][0], LDC, kSub * I, kSub * Jp, lane);
+                    pq[I] = MM::mma(am, bh, pq[I]);
+                    pq[I] = MM::mma(am, bl, pq[I]);
+                    pk[I] = MM::mma(ah, bh, pk[I]);
+                    pk[I] = MM::mma(ah, bl, pk[I]);
+                    pk[I] = MM::mma(al, bh, pk[I]);
                 }
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float a_ = __expf(Gc[4 * I + r] - Gr[I]);
-                    const float Pq = a_ * pq[I][r], Pk = a_ * pk[I][r];
+                    const float Pq = a_ * p.scale * pq[I][r], Pk = a_ * pk[I][r];
                     dq[I][r] += Pq;
                     dk[I][r] += Pk;
                     dG[I][r] += qo[4 * I + r] * Pq + ko[4 * I + r] * Pk;
@@ -2164,15 +2189,27 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                 for (int I = 0; I < 4; ++I)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        bv[4 * I + r] = (pass == 0 ? qo[4 * I + r] : ko[4 * I + r]) * __expf(Gc[4 * I + r] - Gr[I]);
-                const float* dX = pass == 0 ? &s.x.sc.dM[0][0] : &s.x.sc.dA[0][0];
+                        bv[4 * I + r] = (pass == 0 ? p.scale * qo[4 * I + r] : ko[4 * I + r]) *
+                                        __expf(Gc[4 * I + r] - Gr[I]);
+                // A = dX^T (transposing read); sub-blocks I < J contribute nothing
 #pragma unroll
                 for (int J = 0; J < 4; ++J)
 #pragma unroll
-                    for (int I = J; I < 4; ++I) {
-                        const float f = fac(J, I);
-                        const float bf[4] = {f * bv[4 * I], f * bv[4 * I + 1], f * bv[4 * I + 2], f * bv[4 * I + 3]};
-                        rr[J] = mma16_f32_rb_acc<true>(dX, LDD, kSub * J, bf, kSub * I, lane, rr[J]);
+                    for (int Ip = 0; Ip < 4; Ip += 2) {
+                        if (Ip + 1 < J) continue;
+                        MM::Frag bh, bl;
+                        pair_b(Ip >= J ? fac(J, Ip) : 0.f, Ip, fac(J, Ip + 1), Ip + 1, bh, bl);
+                        if (pass == 0) {
+                            const auto am = load_kn<MM>(&s.x.sc.dM[0][0], LDC, kSub * Ip, kSub * J, lane);
+                            rr[J] = MM::mma(am, bh, rr[J]);
+                            rr[J] = MM::mma(am, bl, rr[J]);
+                        } else {
+                            const auto ah = load_kn<MM>(&s.x.sc.dA[0][0], LDC, kSub * Ip, kSub * J, lane);
+                            const auto al = load_kn<MM>(&s.x.sc.dAl[0][0], LDC, kSub * Ip, kSub * J, lane);
+                            rr[J] = MM::mma(ah, bh, rr[J]);
+                            rr[J] = MM::mma(ah, bl, rr[J]);
+                            rr[J] = MM::mma(al, bh, rr[J]);
+                        }
                     }
             }
 #pragma unroll
@@ -2200,13 +2237,14 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                             const float Gj = s.G[jr][c];
                             if (y <= xr) {
                                 const float e = __expf(Gi - Gj) * MM::to_f32(s.kh[jr][c]);
-                                Pq += s.x.sc.dM[i][jr] * e;
-                                Pk += s.x.sc.dA[i][jr] * e;
+                                Pq += p.scale * MM::to_f32(s.x.sc.dM[i][jr]) * e;
+                                Pk += (MM::to_f32(s.x.sc.dA[i][jr]) + MM::to_f32(s.x.sc.dAl[i][jr])) * e;
                             }
                             if (y >= xr) {
                                 const float e = __expf(Gj - Gi);
-                                R += (s.x.sc.dM[jr][i] * MM::to_f32(s.qh[jr][c]) +
-                                      s.x.sc.dA[jr][i] * MM::to_f32(s.kh[jr][c])) * e;
+                                R += (p.scale * MM::to_f32(s.x.sc.dM[jr][i]) * MM::to_f32(s.qh[jr][c]) +
+                                      (MM::to_f32(s.x.sc.dA[jr][i]) + MM::to_f32(s.x.sc.dAl[jr][i])) *
+                                          MM::to_f32(s.kh[jr][c])) * e;
                             }
                         }
                         const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
