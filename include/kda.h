@@ -98,7 +98,12 @@ typedef struct {
                                 boundary warns that un-normalised keys can drive the
                                 exact result to inf. */
     int use_beta_sigmoid;    /* beta <- sigmoid(beta) */
-    int chunk_size;          /* must be 64 */
+    int chunk_size;          /* >= 1: a tiling request.  The chunked form is exact for any
+                                chunk size, and the api.py dispatch maps the request to
+                                each backend's own tiling (a divisor of T for its
+                                reference, 32 or 64 for its Triton kernels); these
+                                kernels always tile with 64 rows, so every request
+                                gives the same result.  <= 0 is KDA_ERR_INVALID_ARG. */
     /* state */
     const float *initial_state; /* [N, H, K, V] or NULL (zeros) */
     int output_final_state;
@@ -136,7 +141,7 @@ typedef struct {
     float *ddt_bias;             /* [H*K] or NULL; SAFE / SOFTPLUS only */
 } kda_chunk_grads;
 
-/* Chunked forward (chunk size 64): writes o and, if requested, final_state.
+/* Chunked forward (64-row chunks): writes o and, if requested, final_state.
  * Computes exactly the recurrence above, in chunkwise-parallel form
  * (api.py chunk_kda; the chunk form's use of I + tril(A_kk * beta) is named in
  * its l2-norm warning).  K = V in {32, 64, 128} for KDA_BF16 q/k/v and

@@ -23,7 +23,7 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forwar
     if (!a) return KDA_ERR_INVALID_ARG;
     if (a->B <= 0 || a->T < 0 || a->H <= 0 || a->K <= 0 || a->V <= 0) return KDA_ERR_INVALID_ARG;
     if (a->qkv_dtype != KDA_F32 && a->qkv_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if (a->chunk_size != 64) return KDA_ERR_UNSUPPORTED;
+    if (a->chunk_size <= 0) return KDA_ERR_INVALID_ARG;  // a tiling request: the kernels tile with 64 rows
     // K = V in {32, 64, 128}, or the narrow-key pair K = 32, V = 64
     const bool kv_ok = (supported_dim(a->K) && a->K == a->V) || (a->K == 32 && a->V == 64);
     if (!kv_ok) return KDA_ERR_UNSUPPORTED;

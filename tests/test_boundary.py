@@ -58,7 +58,8 @@ def _args(**over):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(chunk_size=32), _lib.KDA_ERR_UNSUPPORTED),
+    (dict(chunk_size=0), _lib.KDA_ERR_INVALID_ARG),
+    (dict(chunk_size=-64), _lib.KDA_ERR_INVALID_ARG),
     (dict(K=48, V=48), _lib.KDA_ERR_UNSUPPORTED),
     (dict(K=64, V=32), _lib.KDA_ERR_UNSUPPORTED),              # only the narrow-key pair 32/64 is built
     (dict(K=64, V=128), _lib.KDA_ERR_UNSUPPORTED),
@@ -89,7 +90,7 @@ def test_workspace_query_is_host_only(lib):
     a.workspace = FAKE
     a.workspace_bytes = need - 1
     assert lib.kda_chunk_fwd(ctypes.byref(a)) == _lib.KDA_ERR_WORKSPACE
-    bad = _args(chunk_size=16)
+    bad = _args(chunk_size=0)
     assert lib.kda_chunk_fwd_workspace(ctypes.byref(bad)) == 0
 
 

@@ -137,3 +137,18 @@ def test_fwd_no_final_state_and_deterministic():
     o2, _ = _run_gpu(w, output_final_state=False)
     assert f1 is None
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("chunk_size", [1, 16, 32, 100])
+def test_fwd_chunk_size_is_a_tiling_request(chunk_size):
+    """Any chunk size >= 1 is accepted as a tiling request, as the api.py dispatch
+    maps it to each backend's own tiling: these kernels always tile with 64 rows, so
+    the result is bit-identical to the default request and matches the oracle."""
+    w = inputs.chunk_inputs(1, 130, 2, 64, 64, seed=90 + chunk_size, dtype=torch.bfloat16, h0_std=0.1,
+                            cu_seqlens=[0, 33, 130])
+    o64, fs64 = _run_gpu(w)
+    o, fs = _run_gpu(w, chunk_size=chunk_size)
+    assert torch.equal(o, o64) and torch.equal(fs, fs64)
+    oo, ofs = _run_oracle(w)
+    check(f"chunk_size={chunk_size} o", o, oo, tol_for(w["q"].dtype))
+    check(f"chunk_size={chunk_size} final_state", fs, ofs, tol_for(w["q"].dtype))
