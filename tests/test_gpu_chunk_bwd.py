@@ -219,3 +219,18 @@ def test_bwd_reuses_saved_forward(case):
         o = _oracle_bwd(w)
         for name in NAMES:
             check(f"saved {name}", got[name], o[name], tol_for(w["q"].dtype))
+
+
+def test_bwd_many_short_sequences():
+    """1,500 packed sequences of 0..70 tokens (more than the 1,024 the plan
+    kernel's scan takes per round, empty ones among them), H2 K=V=32 bf16:
+    the plan's chunk offsets and slot map, forward and backward, against the
+    oracle."""
+    gen = torch.Generator().manual_seed(61)
+    lens = torch.randint(0, 71, (1500,), generator=gen)
+    lens[::97] = 0
+    cu = [0] + torch.cumsum(lens, 0).tolist()
+    w = inputs.chunk_inputs(1, cu[-1], 2, 32, 32, seed=62, dtype=torch.bfloat16, cu_seqlens=cu, h0_std=0.1,
+                            with_grad_out=True, dfinal_std=0.1)
+    print(f"many short: N={len(cu) - 1} T={cu[-1]}", flush=True)
+    _compare(w, "many-short")
