@@ -398,6 +398,28 @@ def run_train(steps, warmup, device):
             "path_mfma_frac": pf * th / sec / 1e12 / PEAK_BF16_TFLOPS}
 
 
+def run_variant(B, T, H, K, V, cu, gate, steps, warmup, device, seed, what):
+    """Forward + backward of another geometry or gate form, timed like the main
+    step (forward saving for the backward, stages timed on the launch stream),
+    two alternating input sets.  In-kernel gates also produce dA_log and
+    d(dt_bias)."""
+    from kimi_delta_attention_amd import inputs
+    import kimi_delta_attention_amd as kda
+    ops = []
+    for sd in (seed, seed + 1000):
+        w = inputs.chunk_inputs(B, T, H, K, V, seed=sd, dtype=torch.bfloat16, cu_seqlens=cu, gate_mode=gate,
+                                beta_logits=gate != inputs.GATE_LOGDECAY, with_grad_out=True)
+        d = {k: (v.to(device) if hasattr(v, "to") else v) for k, v in w.items()}
+        ops.append(kda.ChunkOp(d["q"], d["k"], d["v"], d["g"], d["beta"], A_log=d["A_log"], dt_bias=d["dt_bias"],
+                               scale=d["scale"], output_final_state=True, use_qk_l2norm_in_kernel=True,
+                               gate_mode=gate, use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"],
+                               lower_bound=d["lower_bound"], cu_seqlens=d["cu_seqlens"], dO=d["dO"],
+                               keep_for_backward=True))
+    sec, per_stage = time_chunk(ops, steps, warmup, True, _lib_stages())
+    tokens = B * T if cu is None else cu[-1]
+    return {"workload": what, "tokens_per_s": tokens / sec, "ms_per_step": sec * 1e3, "stages_ms": per_stage}
+
+
 def _lib_stages():
     from kimi_delta_attention_amd import _lib
     return _lib.load().kda_chunk_bwd_stages()
@@ -411,6 +433,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip the dense B8 x T4096 training shape")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the in-kernel gate and narrow-key (K32/V64) fwd+bwd legs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -479,6 +503,20 @@ def main():
     if not args.no_train:
         _log("timing chunk path (dense B8 x T4096)")
         line["train"] = run_train(max(args.steps // 2, 3), min(args.warmup, 3), device)
+        torch.cuda.empty_cache()
+    if not args.no_variants:
+        from kimi_delta_attention_amd import inputs
+        _log("timing chunk path (packed T8192) with the in-kernel softplus gate")
+        line["gated"] = run_variant(1, T_H, H_H, D_H, D_H, HYBRID_CU, inputs.GATE_SOFTPLUS, max(args.steps // 2, 5),
+                                    min(args.warmup, 3), device, 1013,
+                                    "chunk_kda fwd+bwd, packed 1024/2048/1024/4096 (T8192), H16, K=V=128, bf16, "
+                                    "softplus gate and beta sigmoid in kernel, dA_log and d(dt_bias) produced")
+        torch.cuda.empty_cache()
+        _log("timing chunk path, narrow-key geometry (K32, V64)")
+        line["narrow_key"] = run_variant(16, 2048, 8, 32, 64, None, inputs.GATE_SOFTPLUS, max(args.steps // 2, 5),
+                                         min(args.warmup, 3), device, 1015,
+                                         "chunk_kda fwd+bwd, dense B16 x T2048, H8, K=32, V=64 (the 300M model's "
+                                         "heads), bf16, softplus gate and beta sigmoid in kernel")
         torch.cuda.empty_cache()
     if not args.no_decode:
         _log("timing decode")

@@ -2429,21 +2429,55 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
     }
 }
 
-// d(A_log) and d(dt_bias): deterministic sums of the per-chunk shares.
+// d(A_log) and d(dt_bias): deterministic sums of the per-chunk shares.  One
+// workgroup per head; thread (slot lane sl, column lane cl) sums the slots
+// sl, sl + 8, ... of its columns with four requests in flight, and the eight
+// slot lanes' sums are added in a fixed order, so results are run-to-run
+// identical without atomics.
+constexpr int kGateReduceThreads = 1024;
 template <int K>
-__global__ void gate_param_reduce_kernel(ChunkParams p, ChunkGrads gr, const int32_t* chunk_off, const uint8_t* ws,
-                                         int64_t slot_bytes, size_t gp_off) {
+__global__ __launch_bounds__(kGateReduceThreads) void gate_param_reduce_kernel(ChunkParams p, ChunkGrads gr,
+                                                                              const int32_t* chunk_off,
+                                                                              const uint8_t* ws, int64_t slot_bytes,
+                                                                              size_t gp_off) {
+    constexpr int CL = 128;                      // column lanes
+    constexpr int SL = kGateReduceThreads / CL;  // slot lanes
+    constexpr int NCOL = K + 1;                  // K d(dt_bias) shares and the d(A_log) share
+    constexpr int CPL = (NCOL + CL - 1) / CL;    // columns per column lane
+    __shared__ float part[SL][CPL * CL];
     const int h = blockIdx.x;
     const int H = p.H;
     const int nslots = p.cu_seqlens ? chunk_off[p.N] : p.N * n_chunks(p.T);
-    for (int c = threadIdx.x; c <= K; c += blockDim.x) {
+    const int cl = threadIdx.x % CL, sl = threadIdx.x / CL;
+#pragma unroll
+    for (int m = 0; m < CPL; ++m) {
+        const int c = cl + CL * m;
         float acc = 0.f;
-        for (int sl = 0; sl < nslots; ++sl)
-            acc += reinterpret_cast<const float*>(ws + (static_cast<int64_t>(sl) * H + h) * slot_bytes + gp_off)[c];
+        if (c < NCOL) {
+            auto share = [&](int s_) {
+                return reinterpret_cast<const float*>(ws + (static_cast<int64_t>(s_) * H + h) * slot_bytes + gp_off)[c];
+            };
+            int s_ = sl;
+            for (; s_ + 3 * SL < nslots; s_ += 4 * SL) {
+                const float a0 = share(s_), a1 = share(s_ + SL), a2 = share(s_ + 2 * SL), a3 = share(s_ + 3 * SL);
+                acc += a0;
+                acc += a1;
+                acc += a2;
+                acc += a3;
+            }
+            for (; s_ < nslots; s_ += SL) acc += share(s_);
+        }
+        part[sl][c] = acc;
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < NCOL; c += kGateReduceThreads) {
+        float tot = 0.f;
+#pragma unroll
+        for (int q = 0; q < SL; ++q) tot += part[q][c];
         if (c < K) {
-            if (gr.ddt_bias) gr.ddt_bias[h * K + c] = acc;
+            if (gr.ddt_bias) gr.ddt_bias[h * K + c] = tot;
         } else if (gr.dA_log) {
-            gr.dA_log[h] = acc;
+            gr.dA_log[h] = tot;
         }
     }
 }
@@ -2520,7 +2554,8 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                    dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb);
         }
         if (p.gate_mode != GATE_LOGDECAY && (gr.dA_log || gr.ddt_bias))
-            hipLaunchKernelGGL((gate_param_reduce_kernel<K>), dim3(p.H), dim3(256), 0, st, p, gr, chunk_off, slots, sb,
+            hipLaunchKernelGGL((gate_param_reduce_kernel<K>), dim3(p.H), dim3(kGateReduceThreads), 0, st, p, gr,
+                               chunk_off, slots, sb,
                                X::kGP);
     }
     return hipGetLastError();

@@ -447,11 +447,15 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     }
     if (valid && p.gate_mode != GATE_LOGDECAY) {
         const float rate = __expf(p.A_log[h]);
+        float bias[CPT];  // requested as whole vectors, waited for once
+        if (p.dt_bias) {
+            load_row<CPT>(p.dt_bias + h * K + c0, bias);
+        } else {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-            const float bias = p.dt_bias ? p.dt_bias[h * K + c0 + c] : 0.f;
-            gv[c] = gate_eff(p.gate_mode, gv[c], rate, bias, p.lower_bound);
+            for (int c = 0; c < CPT; ++c) bias[c] = 0.f;
         }
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) gv[c] = gate_eff(p.gate_mode, gv[c], rate, bias[c], p.lower_bound);
     }
     store_row<CPT>(&s.G[i][c0], gv);
     if (pq == 0) {
