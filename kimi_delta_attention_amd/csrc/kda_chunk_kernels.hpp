@@ -602,33 +602,50 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     store_packed<ET, CPT>(gQE + i * K + c0, pQE);
     if (BWD) store_packed<ET, CPT>(reinterpret_cast<ET*>(out + X::kKE) + i * K + c0, pKE);
     store_packed<ET, CPT>(gKD + i * K + c0, pKD);
-    // pairwise diagonal sub-blocks whose decay span is too wide to factorise
-    for (int I = 0; I < 4; ++I) {
-        if (!s.unsafe[I]) continue;
+    // pairwise diagonal sub-blocks whose decay span is too wide to factorise:
+    // PL consecutive lanes per (row, column) pair of a block, 16 channels each
+    // (q and k rows re-read from the input as vectors), summed by lane shuffles
+    if (s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3]) {
+        constexpr int CPL = 16;
+        constexpr int PL = K / CPL;
+        constexpr int NPAIR = kSub * (kSub + 1) / 2;
         const IT* qg = static_cast<const IT*>(p.q);
         const IT* kg = static_cast<const IT*>(p.k);
-        for (int pr = t; pr < kSub * (kSub + 1) / 2; pr += NT) {
+        for (int u = t; u < 4 * NPAIR * PL; u += NT) {
+            const int I = u / (NPAIR * PL);
+            if (!s.unsafe[I]) continue;  // uniform over a pair's lanes
+            const int pl = u % PL, pr = (u / PL) % NPAIR;
             int a = 0, b = pr;
             while (b > a) { b -= a + 1; ++a; }
             const int ri = kSub * I + a, rj = kSub * I + b;
-            if (ri >= rows) {  // padding rows
-                s.M[ri][rj] = 0.f;
-                s.A[ri][rj] = 0.f;
-                if (BWD) s.Ak[ri][rj] = 0.f;
-                continue;
-            }
-            const int64_t oi = ((start + static_cast<int64_t>(j) * kChunk + ri) * H + h) * K;
-            const int64_t oj = ((start + static_cast<int64_t>(j) * kChunk + rj) * H + h) * K;
             float sa = 0.f, sm = 0.f;
-            for (int c = 0; c < K; ++c) {
-                const float e = __expf(s.G[ri][c] - s.G[rj][c]);
-                const float kj = Elem<IT>::load(kg, oj + c) * s.rk[rj];
-                sa += Elem<IT>::load(kg, oi + c) * s.rk[ri] * kj * e;
-                sm += Elem<IT>::load(qg, oi + c) * s.rq[ri] * kj * e;
+            if (ri < rows) {  // padding rows stay zero
+                const int cu = pl * CPL;
+                const int64_t oi = ((start + static_cast<int64_t>(j) * kChunk + ri) * H + h) * K + cu;
+                const int64_t oj = ((start + static_cast<int64_t>(j) * kChunk + rj) * H + h) * K + cu;
+                float qi[CPL], ki[CPL], kj[CPL];
+                load_row<CPL>(qg + oi, qi);
+                load_row<CPL>(kg + oi, ki);
+                load_row<CPL>(kg + oj, kj);
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    const float e = __expf(s.G[ri][cu + c] - s.G[rj][cu + c]);
+                    sa += ki[c] * kj[c] * e;
+                    sm += qi[c] * kj[c] * e;
+                }
+                sa *= s.rk[ri] * s.rk[rj];
+                sm *= s.rq[ri] * s.rk[rj];
             }
-            s.M[ri][rj] = sm;
-            s.A[ri][rj] = (rj < ri) ? sa * s.beta[ri] : 0.f;
-            if (BWD) s.Ak[ri][rj] = (rj < ri) ? sa : 0.f;
+#pragma unroll
+            for (int o = 1; o < PL; o <<= 1) {
+                sa += __shfl_xor(sa, o, 64);
+                sm += __shfl_xor(sm, o, 64);
+            }
+            if (pl == 0) {
+                s.M[ri][rj] = sm;
+                s.A[ri][rj] = (rj < ri) ? sa * s.beta[ri] : 0.f;
+                if (BWD) s.Ak[ri][rj] = (rj < ri) ? sa : 0.f;
+            }
         }
     }
     __syncthreads();
