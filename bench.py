@@ -344,7 +344,18 @@ def csrc_digest():
 def stored_traffic(stage):
     """HBM bytes per launch of `stage` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summary, or None when there is none or the kernels changed since it was taken."""
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "hbm_traffic_T8192_H16_D128.txt")
+    return _stored("hbm_traffic_T8192_H16_D128.txt", f"hbm_bytes_per_launch[{stage}]")
+
+
+def stored_mfma_util(stage):
+    """MFMA busy fraction of `stage` from the committed rocprofv3 MFMA counter summary
+    (SQ_VALU_MFMA_BUSY_CYCLES over the launch's cycles x 1,024 SIMDs), or None when
+    there is none or the kernels changed since it was taken."""
+    return _stored("mfma_util_T8192_H16_D128.txt", f"mfma_util[{stage}]")
+
+
+def _stored(name, key):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -355,7 +366,7 @@ def stored_traffic(stage):
                 kv[k.strip()] = v.strip()
     if kv.get("csrc_sha256") != csrc_digest():
         return None
-    v = kv.get(f"hbm_bytes_per_launch[{stage}]")
+    v = kv.get(key)
     return float(v) if v else None
 
 
@@ -472,6 +483,7 @@ def main():
     roof = stage_roofline(dom, work[dom], per_stage[dom])
     tr = stored_traffic(dom)
     roof["traffic"] = tr
+    roof["mfma_util"] = stored_mfma_util(dom)
     th = tokens * H_H
     pb, pf = PATH_FWDBWD
     fb, ff = PATH_FWD
@@ -489,7 +501,8 @@ def main():
                    "global_batch": n_seq, "seq_len": tokens, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "stages_ms": per_stage,
-        "stage_roofline": {k: {kk: v[kk] for kk in ("bound", "achieved", "unit", "frac")}
+        "stage_roofline": {k: dict({kk: v[kk] for kk in ("bound", "achieved", "unit", "frac")},
+                                   mfma_util=stored_mfma_util(k))
                            for k, v in ((n, stage_roofline(n, work[n], per_stage[n])) for n in per_stage)},
         "path_roofline": {"fwd+bwd_hbm_frac": pb * th / sec / 1e9 / PEAK_HBM_GBS,
                           "fwd+bwd_mfma_frac": pf * th / sec / 1e12 / PEAK_BF16_TFLOPS,
