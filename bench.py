@@ -144,7 +144,8 @@ def chunk_op(d, with_bwd, keep=True):
 
 
 def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages, keep=True):
-    """Mean seconds per fwd(+bwd) step and mean ms per stage.  With keep the
+    """Mean seconds per fwd(+bwd) step, timed over whole calls, and mean ms per
+    stage from a second run of the same steps stage by stage.  With keep the
     forward saves what the backward's stages 0 and 1 would recompute, and those
     stages (which then launch nothing) are not called."""
     stream = torch.cuda.current_stream()
@@ -165,16 +166,28 @@ def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages, keep=True):
                 k += 1
         evs[k].record(stream)
 
+    def whole(op):
+        op.forward()
+        if with_bwd:
+            op.backward()
+
+    # the timed steps: whole kda_chunk_fwd / kda_chunk_bwd calls, as a caller makes them
     for i in range(warmup):
-        one(ops[i % len(ops)], [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)])
-    torch.cuda.synchronize()
-    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+        whole(ops[i % len(ops)])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        one(ops[i % len(ops)], all_evs[i])
+        whole(ops[i % len(ops)])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # then the same steps stage by stage, with events between the stages, for the breakdown
+    for i in range(min(warmup, 2)):
+        one(ops[i % len(ops)], [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)])
+    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        one(ops[i % len(ops)], all_evs[i])
+    torch.cuda.synchronize()
     per = {n: [] for n in names}
     for evs in all_evs:
         for j, n in enumerate(names):
