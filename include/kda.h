@@ -77,7 +77,10 @@ typedef struct {
     int B, T, H, K, V;
     /* Variable-length packing: device int32 [N+1] prefix offsets with
      * cu_seqlens[0] = 0 and cu_seqlens[N] = T, non-decreasing; requires B = 1.
-     * NULL means dense input with N = B sequences of length T. */
+     * NULL means dense input with N = B sequences of length T.  The values
+     * are read on the device only: offsets that break these rules are
+     * clamped so that every access stays inside the tensors and the
+     * workspace, and the results are then unspecified. */
     const int32_t *cu_seqlens;
     int N;
     /* inputs */

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     int64_t start;
     int len;
     seq_bounds(p, n, start, len);
-    const int nc = n_chunks(len);
+    const int nc = chain_chunks(p, chunk_off, n, len);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     const int v0 = vb * BV;
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
     int64_t start;
     int len;
     seq_bounds(p, n, start, len);
-    const int nc = n_chunks(len);
+    const int nc = chain_chunks(p, chunk_off, n, len);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lg = lane >> 4, m = lane & 15;
     const int v0 = vb * BV;
@@ -2447,7 +2447,7 @@ __global__ __launch_bounds__(kGateReduceThreads) void gate_param_reduce_kernel(C
     __shared__ float part[SL][CPL * CL];
     const int h = blockIdx.x;
     const int H = p.H;
-    const int nslots = p.cu_seqlens ? chunk_off[p.N] : p.N * n_chunks(p.T);
+    const int nslots = p.cu_seqlens ? min(chunk_off[p.N], p.total_chunks_bound) : p.N * n_chunks(p.T);
     const int cl = threadIdx.x % CL, sl = threadIdx.x / CL;
 #pragma unroll
     for (int m = 0; m < CPL; ++m) {

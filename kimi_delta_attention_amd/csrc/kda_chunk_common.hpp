@@ -171,6 +171,17 @@ __device__ __forceinline__ int64_t chunk_slot(const ChunkParams& p, const int32_
     return base + j;
 }
 
+// Chunks of sequence n that the state passes walk.  For packed offsets that
+// break the non-decreasing rule the clamped lengths can add up to more chunks
+// than there are slots; a chain then stops at the last slot, so that every
+// workspace access stays inside it (the results are unspecified).
+__device__ __forceinline__ int chain_chunks(const ChunkParams& p, const int32_t* chunk_off, int n, int len) {
+    const int nc = n_chunks(len);
+    if (!p.cu_seqlens) return nc;
+    const int room = p.total_chunks_bound - chunk_off[n];
+    return nc < room ? nc : (room > 0 ? room : 0);
+}
+
 // Slot c -> (sequence n, chunk j, sequence start row, sequence length);
 // false when c is past the last chunk.
 __device__ __forceinline__ bool slot_locate(const ChunkParams& p, const int32_t* chunk_off, int c, int& n, int& j,

@@ -897,7 +897,7 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
     int64_t start;
     int len;
     seq_bounds(p, n, start, len);
-    const int nc = n_chunks(len);
+    const int nc = chain_chunks(p, chunk_off, n, len);
     const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     // 16-row tile and first column tile of this wave (4 waves: every column tile)
     const int rw = NW > 4 ? (w & 3) : w, cw = NW > 4 ? (w >> 2) : 0;
@@ -1097,7 +1097,7 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
     int64_t start;
     int len;
     seq_bounds(p, n, start, len);
-    const int nc = n_chunks(len);
+    const int nc = chain_chunks(p, chunk_off, n, len);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int lg = lane >> 4, m = lane & 15;
     const int v0 = vb * BV;
