@@ -1646,33 +1646,59 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 carry = __shfl(dG[I][0], lc, 64);  // suffix sum from row 16 I
             }
 
-            // gate chain rule
+            // gate chain rule.  Every gate input is requested before the first
+            // d(gate) store, one sub-block ahead of its use: loads and stores
+            // share one in-order counter, so a load issued behind a store would
+            // also wait for that store.  dG becomes d(gate input) in place.
             const float bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias[h * K + c] : 0.f;
             float ddt = 0.f;
+            if (p.gate_mode != GATE_LOGDECAY) {
+                float zc[4], zn[4];
+                auto zload = [&](int I, float (&z)[4]) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = kSub * I + 4 * lg + r;
+                        const int ic = i < rows ? i : rows - 1;  // a slot holds at least one row
+                        z[r] = p.g[((rbase + ic) * H + h) * K + c];
+                    }
+                };
+                zload(0, zc);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    if (I < 3) zload(I + 1, zn);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = kSub * I + 4 * lg + r;
+                        const float dge = dG[I][r];
+                        const float z = zc[r] + bias;
+                        float dx, da;
+                        if (p.gate_mode == GATE_SAFE) {
+                            const float sg = sigmoidf_(rate * z);
+                            const float b_ = p.lower_bound * sg * (1.f - sg);
+                            dx = dge * b_ * rate;
+                            da = dx * z;
+                        } else {
+                            dx = -dge * rate * sigmoidf_(z);
+                            da = -dge * rate * softplusf_(z);
+                        }
+                        if (i < rows) {
+                            ddt += dx;
+                            dal += da;
+                        }
+                        dG[I][r] = dx;
+                    }
+                    if (I < 3) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) zc[r] = zn[r];
+                    }
+                }
+            }
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
-                    if (i < rows) {
-                        const int64_t gi = ((rbase + i) * H + h) * K + c;
-                        const float dge = dG[I][r];
-                        float dx = dge;
-                        if (p.gate_mode != GATE_LOGDECAY) {
-                            const float z = p.g[gi] + bias;
-                            if (p.gate_mode == GATE_SAFE) {
-                                const float sg = sigmoidf_(rate * z);
-                                const float b_ = p.lower_bound * sg * (1.f - sg);
-                                dx = dge * b_ * rate;
-                                dal += dge * b_ * rate * z;
-                            } else {
-                                dx = -dge * rate * sigmoidf_(z);
-                                dal += -dge * rate * softplusf_(z);
-                            }
-                            ddt += dx;
-                        }
-                        gr.dg[gi] = dx;
-                    }
+                    if (i < rows) gr.dg[((rbase + i) * H + h) * K + c] = dG[I][r];
                 }
             ddt += __shfl_xor(ddt, 16, 64);
             ddt += __shfl_xor(ddt, 32, 64);
@@ -2320,33 +2346,59 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                 carry = __shfl(dG[I][0], lc, 64);  // suffix sum from row 16 I
             }
 
-            // gate chain rule
+            // gate chain rule.  Every gate input is requested before the first
+            // d(gate) store, one sub-block ahead of its use: loads and stores
+            // share one in-order counter, so a load issued behind a store would
+            // also wait for that store.  dG becomes d(gate input) in place.
             const float bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias[h * K + c] : 0.f;
             float ddt = 0.f;
+            if (p.gate_mode != GATE_LOGDECAY) {
+                float zc[4], zn[4];
+                auto zload = [&](int I, float (&z)[4]) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = kSub * I + 4 * lg + r;
+                        const int ic = i < rows ? i : rows - 1;  // a slot holds at least one row
+                        z[r] = p.g[((rbase + ic) * H + h) * K + c];
+                    }
+                };
+                zload(0, zc);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    if (I < 3) zload(I + 1, zn);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = kSub * I + 4 * lg + r;
+                        const float dge = dG[I][r];
+                        const float z = zc[r] + bias;
+                        float dx, da;
+                        if (p.gate_mode == GATE_SAFE) {
+                            const float sg = sigmoidf_(rate * z);
+                            const float b_ = p.lower_bound * sg * (1.f - sg);
+                            dx = dge * b_ * rate;
+                            da = dx * z;
+                        } else {
+                            dx = -dge * rate * sigmoidf_(z);
+                            da = -dge * rate * softplusf_(z);
+                        }
+                        if (i < rows) {
+                            ddt += dx;
+                            dal += da;
+                        }
+                        dG[I][r] = dx;
+                    }
+                    if (I < 3) {
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) zc[r] = zn[r];
+                    }
+                }
+            }
 #pragma unroll
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
-                    if (i < rows) {
-                        const int64_t gi = ((rbase + i) * H + h) * K + c;
-                        const float dge = dG[I][r];
-                        float dx = dge;
-                        if (p.gate_mode != GATE_LOGDECAY) {
-                            const float z = p.g[gi] + bias;
-                            if (p.gate_mode == GATE_SAFE) {
-                                const float sg = sigmoidf_(rate * z);
-                                const float b_ = p.lower_bound * sg * (1.f - sg);
-                                dx = dge * b_ * rate;
-                                dal += dge * b_ * rate * z;
-                            } else {
-                                dx = -dge * rate * sigmoidf_(z);
-                                dal += -dge * rate * softplusf_(z);
-                            }
-                            ddt += dx;
-                        }
-                        gr.dg[gi] = dx;
-                    }
+                    if (i < rows) gr.dg[((rbase + i) * H + h) * K + c] = dG[I][r];
                 }
             ddt += __shfl_xor(ddt, 16, 64);
             ddt += __shfl_xor(ddt, 32, 64);
