@@ -11,6 +11,12 @@ synthetic (see kimi_delta_attention_amd/inputs.py) and resident in HBM before
 the timed region; two input sets alternate so that the 256 MiB Infinity Cache
 cannot serve one step from the previous one.
 
+The headline `roofline` is the whole fwd+bwd step against its operator-level
+bytes (every operator input and output crossing HBM once: 4,364 B per
+token-head at d = 128 in bf16, plus the states), with each stage's share next
+to the HBM bytes its kernel was counted moving.  The bytes this design's
+kernels pass each other through the workspace are a labelled secondary figure.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -108,6 +114,55 @@ PATH_FWD = (1540, 141013)
 PATH_FWDBWD = (4364, 423039)
 
 
+def path_shares(K, V, elt):
+    """Operator-level HBM bytes per token-head of one fwd+bwd step, each operator
+    input and output crossing HBM once, assigned to the stage that first reads
+    or writes it: the prep reads q, k, v, g, beta; the state pass writes o; the
+    reverse state pass reads dO; V-local reads v and writes dv; K-local reads q,
+    k, g, beta again and writes dq, dk, dg, dbeta.  At K = V = 128 in bf16 these
+    are 1,284 + 256 + 256 + 512 + 2,056 = 4,364 B."""
+    return {
+        "fwd.prep": (2 * K + V) * elt + 4 * K + 4,
+        "fwd.state": V * elt,
+        "bwd.2": V * elt,
+        "bwd.3": 2 * V * elt,
+        "bwd.4": 2 * K * elt + 4 * K + 4 + 2 * K * elt + 4 * K + 4,
+    }
+
+
+def path_roofline(stage_ms, step_ms, token_heads, K, V, elt, state_bytes, design):
+    """Headline roofline of the whole fwd+bwd step against its operator-level
+    bytes (path_shares per token-head, plus the final state written by the
+    forward and d(initial state) written by the backward), over the measured
+    step time.  Each stage carries its own share next to the counted HBM bytes
+    of its kernel; the bytes this design's kernels hand each other through the
+    workspace are the secondary `design_bytes` figure."""
+    shares = path_shares(K, V, elt)
+    per = {}
+    total_share = 0
+    traffic = 0.0
+    for n, ms in stage_ms.items():
+        share = shares.get(n, 0) * token_heads
+        if n == "fwd.state":
+            share += state_bytes
+        if n == "bwd.2":
+            share += state_bytes
+        total_share += share
+        tr = stored_traffic(n)
+        traffic = None if (traffic is None or tr is None) else traffic + tr
+        per[n] = {"kernel_ms": ms, "share_bytes": share, "share_frac": share / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "design_bytes": design[n][0],
+                  "design_frac": design[n][0] / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                  "traffic": tr, "traffic_ratio": None if tr is None else tr / share if share else None,
+                  "mfma_util": stored_mfma_util(n)}
+    ach = total_share / (step_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "kernel": "fwd+bwd path (every stage of kda_chunk_fwd + kda_chunk_bwd)",
+            "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+            "traffic": traffic, "traffic_ratio": None if traffic is None else traffic / total_share,
+            "algorithmic_bytes": total_share, "step_ms": step_ms,
+            "stage_sum_ms": sum(stage_ms.values()), "stages": per}
+
+
 def decode_bytes(N, H, D, W, x_elt):
     """State and conv state read + written once; x, g, beta, conv_w read; o written."""
     return (2 * N * H * D * D * 4 + 2 * N * 3 * H * D * W * 4 + N * 3 * H * D * x_elt + N * H * D * 4
@@ -144,8 +199,9 @@ def chunk_op(d, with_bwd, keep=True):
 
 
 def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages, keep=True):
-    """Mean seconds per fwd(+bwd) step, timed over whole calls, and mean ms per
-    stage from a second run of the same steps stage by stage.  With keep the
+    """Mean seconds per fwd(+bwd) step, timed over whole calls (host clock), mean
+    ms per stage from a second run of the same steps stage by stage, and the
+    mean ms per whole step from HIP events on the launch stream.  With keep the
     forward saves what the backward's stages 0 and 1 would recompute, and those
     stages (which then launch nothing) are not called."""
     stream = torch.cuda.current_stream()
@@ -175,11 +231,16 @@ def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages, keep=True):
     for i in range(warmup):
         whole(ops[i % len(ops)])
     torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(steps):
         whole(ops[i % len(ops)])
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    step_ms = ev0.elapsed_time(ev1) / steps  # HIP events on the launch stream
     # then the same steps stage by stage, with events between the stages, for the breakdown
     for i in range(min(warmup, 2)):
         one(ops[i % len(ops)], [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)])
@@ -192,7 +253,7 @@ def time_chunk(ops, steps, warmup, with_bwd, n_bwd_stages, keep=True):
     for evs in all_evs:
         for j, n in enumerate(names):
             per[n].append(evs[j].elapsed_time(evs[j + 1]))
-    return (t1 - t0) / steps, {n: sum(v) / len(v) for n, v in per.items()}
+    return (t1 - t0) / steps, {n: sum(v) / len(v) for n, v in per.items()}, step_ms
 
 
 def run_decode(steps, warmup, device):
@@ -409,7 +470,7 @@ def run_train(steps, warmup, device):
                      output_final_state=True, use_qk_l2norm_in_kernel=True, gate_mode=d["gate_mode"],
                      use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"], lower_bound=d["lower_bound"], dO=d["dO"],
                      keep_for_backward=True)
-    sec, per_stage = time_chunk([op], steps, warmup, True, _lib_stages())
+    sec, per_stage, _ = time_chunk([op], steps, warmup, True, _lib_stages())
     tokens = B * T
     fwd_ms = per_stage["fwd.prep"] + per_stage["fwd.state"]
     pb, pf = PATH_FWDBWD
@@ -439,7 +500,7 @@ def run_variant(B, T, H, K, V, cu, gate, steps, warmup, device, seed, what):
                                gate_mode=gate, use_beta_sigmoid_in_kernel=d["use_beta_sigmoid"],
                                lower_bound=d["lower_bound"], cu_seqlens=d["cu_seqlens"], dO=d["dO"],
                                keep_for_backward=True))
-    sec, per_stage = time_chunk(ops, steps, warmup, True, _lib_stages())
+    sec, per_stage, _ = time_chunk(ops, steps, warmup, True, _lib_stages())
     tokens = B * T if cu is None else cu[-1]
     return {"workload": what, "tokens_per_s": tokens / sec, "ms_per_step": sec * 1e3, "stages_ms": per_stage}
 
@@ -479,27 +540,31 @@ def main():
     _, d1 = make_hybrid(2003, device)
     ops = [chunk_op(d0, True), chunk_op(d1, True)]
     _log("timing chunk path (packed T8192)")
-    sec, per_stage = time_chunk(ops, args.steps, args.warmup, True, n_bwd)
+    sec, per_stage, step_ms = time_chunk(ops, args.steps, args.warmup, True, n_bwd)
     del ops
     torch.cuda.empty_cache()
     _log("timing chunk path (packed T8192), backward recomputing the forward's operands")
     ops = [chunk_op(d0, True, keep=False), chunk_op(d1, True, keep=False)]
-    sec_r, per_stage_r = time_chunk(ops, args.steps, args.warmup, True, n_bwd, keep=False)
+    sec_r, per_stage_r, _ = time_chunk(ops, args.steps, args.warmup, True, n_bwd, keep=False)
     tokens = T_H
     n_seq = len(HYBRID_CU) - 1
     # the inference forward (nothing saved) is the recomputing run's forward
     fwd_ms = per_stage_r["fwd.prep"] + per_stage_r["fwd.state"]
     slots = sum((HYBRID_CU[i + 1] - HYBRID_CU[i] + C - 1) // C for i in range(n_seq)) * H_H
     work = stage_work(slots, n_seq, H_H, D_H, D_H, 2)
-    # dominant kernel: the stage with the largest mean duration
-    dom = max(per_stage, key=per_stage.get)
-    roof = stage_roofline(dom, work[dom], per_stage[dom])
-    tr = stored_traffic(dom)
-    roof["traffic"] = tr
-    roof["mfma_util"] = stored_mfma_util(dom)
     th = tokens * H_H
+    # headline: the whole fwd+bwd step against its operator-level bytes (final
+    # state written by the forward, d(initial state) by the backward)
+    state_bytes = n_seq * H_H * D_H * D_H * 4
+    roof = path_roofline(per_stage, step_ms, th, D_H, D_H, 2, state_bytes, work)
+    # the slowest stage against the bytes this design moves through the workspace
+    dom = max(per_stage, key=per_stage.get)
+    slowest = stage_roofline(dom, work[dom], per_stage[dom])
+    slowest["traffic"] = stored_traffic(dom)
+    slowest["mfma_util"] = stored_mfma_util(dom)
     pb, pf = PATH_FWDBWD
     fb, ff = PATH_FWD
+    roof["inference_fwd_mfma_frac"] = ff * th / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
     line = {
         "metric": "chunk_kda fwd+bwd tokens/s (H16,D128,T8192) + decode seq/s; % MFMA/HBM peak",
         "value": tokens / sec,
@@ -514,14 +579,12 @@ def main():
                    "global_batch": n_seq, "seq_len": tokens, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "stages_ms": per_stage,
-        "stage_roofline": {k: dict({kk: v[kk] for kk in ("bound", "achieved", "unit", "frac")},
-                                   mfma_util=stored_mfma_util(k))
-                           for k, v in ((n, stage_roofline(n, work[n], per_stage[n])) for n in per_stage)},
-        "path_roofline": {"fwd+bwd_hbm_frac": pb * th / sec / 1e9 / PEAK_HBM_GBS,
-                          "fwd+bwd_mfma_frac": pf * th / sec / 1e12 / PEAK_BF16_TFLOPS,
-                          "fwd_tokens_per_s": tokens / (fwd_ms * 1e-3),
-                          "fwd_hbm_frac": fb * th / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                          "fwd_mfma_frac": ff * th / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "slowest_stage_design_bytes": slowest,
+        "path_roofline": {"fwd+bwd_hbm_frac": pb * th / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "fwd+bwd_mfma_frac": pf * th / (step_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                          "inference_fwd_tokens_per_s": tokens / (fwd_ms * 1e-3),
+                          "inference_fwd_hbm_frac": fb * th / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "inference_fwd_mfma_frac": ff * th / (fwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
         "recompute": {"tokens_per_s": tokens / sec_r, "ms_per_step": sec_r * 1e3, "stages_ms": per_stage_r},
     }
     del ops, d0, d1
@@ -547,6 +610,7 @@ def main():
     if not args.no_decode:
         _log("timing decode")
         line["decode"] = run_decode(max(args.steps, 10), args.warmup, device)
+        line["roofline"]["decode_hbm_frac"] = line["decode"]["roofline"]["frac"]
         _log("timing stateful prefill")
         line["prefill"] = run_prefill(max(args.steps // 2, 5), min(args.warmup, 3), device)
         torch.cuda.empty_cache()

@@ -91,10 +91,10 @@ typedef struct {
     const float *A_log;      /* [H]; required for SAFE / SOFTPLUS, ignored otherwise */
     const float *dt_bias;    /* [H*K] or NULL (= 0); SAFE / SOFTPLUS only */
     float scale;             /* <= 0 or NaN means K^-1/2 */
-    float lower_bound;       /* NaN means "none".  Required for SAFE.  In LOGDECAY
-                                mode a finite value promises g >= lower_bound on
-                                every element; kernels may use it to pick a
-                                faster overflow-safe factorisation. */
+    float lower_bound;       /* NaN means "none".  Required for SAFE (the gate's
+                                floor); not read in the other modes, where any
+                                log-decay is handled by the run-time per-block
+                                span check of the kernels. */
     int gate_mode;           /* kda_gate_mode */
     int use_qk_l2norm;       /* q <- q (sum q^2 + 1e-6)^-1/2, same for k.  With 0 the
                                 caller must supply well-scaled keys: the api.py
@@ -199,7 +199,9 @@ int kda_chunk_bwd_stages(void);
  * with state_slots given, state is a pool [S, H, D, D] and conv_state a pool
  * [S, 3*H*D, W] (S = n_slots), and sequence n reads and updates slot
  * state_slots[n]; x, g, beta, out_gate and o stay indexed by n.  Slots must
- * be distinct within a call (two sequences on one slot race).  A slot outside
+ * be distinct within a call: the library does not check this (the indices are
+ * device data), and two sequences on one slot race, leaving that slot's
+ * states and both outputs undefined.  A slot outside
  * [0, S) leaves every state unchanged and sets that sequence's o to NaN. */
 typedef struct {
     int N, H, D, W;          /* D = head dim (K = V = D) in {32, 64, 128}; 1 <= W <= 8 */

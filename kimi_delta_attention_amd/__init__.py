@@ -102,6 +102,13 @@ def _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, output_f
     return a, (B, T, H, K, V, N, dev)
 
 
+def _check_grad_shapes(dO, d_final_state, B, T, H, K, V, N):
+    if dO is None or tuple(dO.shape) != (B, T, H, V):
+        raise ValueError(f"dO must be [{B}, {T}, {H}, {V}]")
+    if d_final_state is not None and tuple(d_final_state.shape) != (N, H, K, V):
+        raise ValueError(f"d_final_state must be [{N}, {H}, {K}, {V}]")
+
+
 def _workspace(nbytes, dev, workspace):
     if nbytes == 0:
         return None
@@ -115,8 +122,12 @@ def _workspace(nbytes, dev, workspace):
 def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
               output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
               use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
-              cu_seqlens=None, gate_mode=None, workspace=None, out=None, keep_for_backward=False):
+              cu_seqlens=None, gate_mode=None, workspace=None, out=None, keep_for_backward=False,
+              final_state_out=None):
     """Chunked KDA forward (kda_chunk_fwd).  Returns (o, final_state or None).
+
+    out ([B, T, H, V], q's dtype) and final_state_out ([N, H, K, V], float32)
+    are optional preallocated outputs.
 
     keep_for_backward=True also stores in ``workspace`` what the backward would
     recompute; pass the same workspace, unchanged inputs and
@@ -131,7 +142,15 @@ def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial
     lib = _lib.load()
     o = out if out is not None else torch.empty(B, T, H, V, dtype=q.dtype, device=dev)
     _need(o, "out", q.dtype, dev)
-    fs = torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if output_final_state else None
+    if tuple(o.shape) != (B, T, H, V):
+        raise ValueError(f"out must be [{B}, {T}, {H}, {V}]")
+    fs = None
+    if output_final_state:
+        fs = final_state_out if final_state_out is not None else torch.empty(N, H, K, V, dtype=torch.float32,
+                                                                             device=dev)
+        _need(fs, "final_state_out", torch.float32, dev)
+        if tuple(fs.shape) != (N, H, K, V):
+            raise ValueError(f"final_state_out must be [{N}, {H}, {K}, {V}]")
     a.o, a.final_state = _ptr(o), _ptr(fs)
     ws = _workspace(lib.kda_chunk_fwd_workspace(ctypes.byref(a)), dev, workspace)
     a.workspace = _ptr(ws)
@@ -153,13 +172,15 @@ def chunk_kda_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bi
                   initial_state=None, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
                   use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
                   cu_seqlens=None, gate_mode=None, need_d_initial_state=True, workspace=None,
-                  keep_for_backward=False):
+                  keep_for_backward=False, out=None):
     """Chunked KDA backward (kda_chunk_bwd): gradients of <o, dO> + <final_state,
     d_final_state> w.r.t. q, k, v, g and beta as passed, the initial state and,
     for in-kernel gates, A_log and dt_bias.  Returns a dict.
 
     keep_for_backward=True reuses what a chunk_kda(..., keep_for_backward=True)
-    call stored in the same ``workspace``."""
+    call stored in the same ``workspace``.  ``out`` may hold preallocated
+    gradient tensors under the returned dict's keys (each of the shape and
+    dtype that would be allocated); the missing ones are allocated."""
     gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
     a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, False,
                                              use_qk_l2norm_in_kernel, gm, use_beta_sigmoid_in_kernel,
@@ -169,17 +190,27 @@ def chunk_kda_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bi
     a.keep_for_backward = int(bool(keep_for_backward))
     _need(dO, "dO", q.dtype, dev)
     _need(d_final_state, "d_final_state", torch.float32, dev)
+    _check_grad_shapes(dO, d_final_state, B, T, H, K, V, N)
     lib = _lib.load()
-    out = {
-        "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
-        "dg": torch.empty(B, T, H, K, dtype=torch.float32, device=dev),
-        "dbeta": torch.empty(B, T, H, dtype=torch.float32, device=dev),
-        "dh0": torch.empty(N, H, K, V, dtype=torch.float32, device=dev) if need_d_initial_state else None,
-        "dA_log": None, "ddt_bias": None,
-    }
-    if gm != KDA_GATE_LOGDECAY:
-        out["dA_log"] = torch.empty(H, dtype=torch.float32, device=dev)
-        out["ddt_bias"] = torch.empty(H * K, dtype=torch.float32, device=dev)
+    given = out or {}
+    spec = {"dq": ((B, T, H, K), q.dtype), "dk": ((B, T, H, K), q.dtype), "dv": ((B, T, H, V), q.dtype),
+            "dg": ((B, T, H, K), torch.float32), "dbeta": ((B, T, H), torch.float32),
+            "dh0": ((N, H, K, V), torch.float32) if need_d_initial_state else None,
+            "dA_log": ((H,), torch.float32) if gm != KDA_GATE_LOGDECAY else None,
+            "ddt_bias": ((H * K,), torch.float32) if gm != KDA_GATE_LOGDECAY else None}
+    out = {}
+    for name, sd in spec.items():
+        if sd is None:
+            out[name] = None
+            continue
+        shape, dt = sd
+        t = given.get(name)
+        if t is None:
+            t = torch.empty(*shape, dtype=dt, device=dev)
+        _need(t, name, dt, dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {list(shape)}")
+        out[name] = t
     gr = _lib.ChunkGrads()
     gr.dO, gr.d_final_state = _ptr(dO), _ptr(d_final_state)
     gr.dq, gr.dk, gr.dv = _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"])
@@ -220,8 +251,14 @@ def recurrent_step(x_qkv, conv_w, conv_state, g, beta, state, *, A_log=None, dt_
     for name, t in (("conv_w", conv_w), ("conv_state", conv_state), ("g", g), ("beta", beta), ("state", state),
                     ("A_log", A_log), ("dt_bias", dt_bias)):
         _need(t, name, torch.float32, dev)
+    if A_log is not None and A_log.numel() != H:
+        raise ValueError("A_log must have H elements")
+    if dt_bias is not None and dt_bias.numel() != H * D:
+        raise ValueError("dt_bias must have H*D elements")
     o = out if out is not None else torch.empty(N, H * D, dtype=torch.float32, device=dev)
     _need(o, "out", torch.float32, dev)
+    if tuple(o.shape) != (N, H * D):
+        raise ValueError(f"out must be [{N}, {H * D}]")
     a = _lib.StepArgs()
     a.N, a.H, a.D, a.W = N, H, D, W
     a.x_dtype = _lib.KDA_BF16 if x_qkv.dtype == torch.bfloat16 else _lib.KDA_F32
@@ -280,15 +317,19 @@ def output_gate(o, g, *, eps=None, out=None):
     return y
 
 
-def output_gate_bwd(o, g, dy, *, eps=None):
+def output_gate_bwd(o, g, dy, *, eps=None, out=None):
     """Reverse mode of output_gate (kda_output_gate_bwd): returns (dO, dg) for
-    the upstream gradient dy, in o's and g's dtypes."""
+    the upstream gradient dy, in o's and g's dtypes.  out, if given, is a
+    preallocated (dO, dg) pair."""
     a = _gate_args(o, g, eps)
     if tuple(dy.shape) != tuple(o.shape):
         raise ValueError("dy must have o's shape")
     _need(dy, "dy", o.dtype, o.device)
-    dO = torch.empty_like(o)
-    dg = torch.empty_like(g)
+    dO, dg = out if out is not None else (torch.empty_like(o), torch.empty_like(g))
+    if tuple(dO.shape) != tuple(o.shape) or tuple(dg.shape) != tuple(g.shape):
+        raise ValueError("out must be (dO, dg) shaped like o and g")
+    _need(dO, "dO", o.dtype, o.device)
+    _need(dg, "dg", g.dtype, o.device)
     _lib.check(_lib.load().kda_output_gate_bwd(ctypes.byref(a), _ptr(dy), _ptr(dO), _ptr(dg)),
                "kda_output_gate_bwd")
     return dO, dg
@@ -394,6 +435,7 @@ class ChunkOp:
         if dO is not None:
             _need(dO, "dO", q.dtype, dev)
             _need(d_final_state, "d_final_state", torch.float32, dev)
+            _check_grad_shapes(dO, d_final_state, B, T, H, K, V, N)
             nb = max(nb, lib.kda_chunk_bwd_workspace(ctypes.byref(a)))
             self.grads = {
                 "dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),

@@ -61,7 +61,6 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forwar
     p.gate_mode = a->gate_mode;
     p.use_qk_l2norm = a->use_qk_l2norm;
     p.use_beta_sigmoid = a->use_beta_sigmoid;
-    p.bounded = false;
     p.h0 = a->initial_state;
     p.o = forward ? a->o : nullptr;
     p.ht = (forward && a->output_final_state) ? a->final_state : nullptr;

@@ -89,7 +89,6 @@ struct ChunkParams {
     int gate_mode;
     int use_qk_l2norm;
     int use_beta_sigmoid;
-    bool bounded;              // every log-decay is >= lower_bound with 16*|lb| <= 80
     const float* h0;           // [N,H,K,V] or nullptr
     void* o;
     float* ht;                 // [N,H,K,V] or nullptr

@@ -212,18 +212,26 @@ def chunk_bwd(q, k, v, g, beta, dO, *, d_final_state=None, A_log=None, dt_bias=N
 
 def decode_step(x, conv_w, conv_state, g, beta, state, *, A_log=None, dt_bias=None, scale=None,
                 use_qk_l2norm=True, gate_mode=GATE_LOGDECAY, use_beta_sigmoid=True,
-                lower_bound=None, threads=None):
+                lower_bound=None, threads=None, inplace=False):
     """One decode token per sequence ([kda.rs] kda_decode_token): the causal
     depthwise short-conv update with SiLU over the [q|k|v] channels
     ([kda.rs] conv_update), then one recurrent step ([kda.rs] kda_recurrent_step).
 
     x [N, 3*H*D]; conv_w [3*H*D, W]; conv_state [N, 3*H*D, W]; g [N, H*D];
     beta [N, H]; state [N, H, D, D].  Returns (o [N, H*D], new conv_state,
-    new state), all float64; the inputs are not modified."""
+    new state), all float64; the inputs are not modified, except with
+    inplace=True, where conv_state and state must be C-contiguous float64
+    numpy arrays and are updated in place (no copy of a large state)."""
     x = _f64(x)
     conv_w = _f64(conv_w)
-    cs = _f64(conv_state).copy()
-    st = _f64(state).copy()
+    if inplace:
+        for name, arr in (("conv_state", conv_state), ("state", state)):
+            if not (isinstance(arr, np.ndarray) and arr.dtype == np.float64 and arr.flags.c_contiguous):
+                raise ValueError(f"inplace decode needs {name} as a C-contiguous float64 array")
+        cs, st = conv_state, state
+    else:
+        cs = _f64(conv_state).copy()
+        st = _f64(state).copy()
     g = _f64(g)
     beta = _f64(beta)
     A_log, dt_bias = _f64(A_log), _f64(dt_bias)

@@ -28,3 +28,9 @@ def check(name, got, want, tol):
 
 def dev(x, device="cuda"):
     return None if x is None else x.to(device).contiguous()
+
+
+def nan_full(shape, dtype, device="cuda"):
+    """An output buffer filled with NaN before a GPU call, so that any element
+    the kernels fail to write fails the finiteness check."""
+    return torch.full(tuple(shape), float("nan"), dtype=dtype, device=device)

@@ -7,7 +7,7 @@ import torch
 import oracle
 import kimi_delta_attention_amd as kda
 from kimi_delta_attention_amd import inputs
-from parity import check, dev, tol_for
+from parity import check, dev, tol_for, nan_full
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +21,18 @@ def _gpu_bwd(w, **over):
               lower_bound=w["lower_bound"], cu_seqlens=dev(w["cu_seqlens"]),
               d_final_state=dev(w.get("d_final_state")))
     kw.update(over)
+    # gradients start as NaN, so that an element the kernels do not write fails the check
+    B, T, H, K = w["q"].shape
+    V = w["v"].shape[-1]
+    N = B if w["cu_seqlens"] is None else len(w["cu_seqlens"]) - 1
+    dt = w["q"].dtype
+    pre = {"dq": nan_full((B, T, H, K), dt), "dk": nan_full((B, T, H, K), dt), "dv": nan_full((B, T, H, V), dt),
+           "dg": nan_full((B, T, H, K), torch.float32), "dbeta": nan_full((B, T, H), torch.float32),
+           "dh0": nan_full((N, H, K, V), torch.float32)}
+    if w["gate_mode"] != inputs.GATE_LOGDECAY:
+        pre["dA_log"] = nan_full((H,), torch.float32)
+        pre["ddt_bias"] = nan_full((H * K,), torch.float32)
+    kw.setdefault("out", pre)
     out = kda.chunk_kda_bwd(dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["g"]), dev(w["beta"]), dev(w["dO"]), **kw)
     torch.cuda.synchronize()
     return out
@@ -84,90 +96,43 @@ def test_bwd_varlen_empty_and_tiny():
     _compare(w, "varlen")
 
 
-def _slice_units(w, units):
-    """Inputs restricted to the (batch row, head) units listed; units are
-    independent, so the oracle's result on the slice is exact for them."""
-    out = {}
-    bs = [b for b, _ in units]
-    hs = [h for _, h in units]
-    for key in ("q", "k", "v", "g", "dO"):
-        out[key] = torch.stack([w[key][b, :, h] for b, h in units], 0).unsqueeze(2)
-    out["beta"] = torch.stack([w["beta"][b, :, h] for b, h in units], 0).unsqueeze(2)
-    out["initial_state"] = torch.stack([w["initial_state"][b, h] for b, h in units], 0).unsqueeze(1)
-    out["d_final_state"] = None
-    for key in ("scale", "use_qk_l2norm", "gate_mode", "use_beta_sigmoid", "lower_bound"):
-        out[key] = w[key]
-    out["A_log"] = out["dt_bias"] = None
-    out["cu_seqlens"] = None
-    return out, bs, hs
-
-
-def test_bwd_train_geometry_sampled_units():
-    """B8 T4096 H16 K=V=128 bf16 with dO ~ N(0,1): the whole batch runs on the
-    GPU; the oracle checks 4 sampled (sequence, head) units."""
+def test_bwd_train_geometry_whole_batch():
+    """B8 T4096 H16 K=V=128 bf16 with dO ~ N(0,1), in the launch configuration
+    the bench times: every gradient of all 128 (sequence, head) units against
+    the oracle."""
     w = inputs.workload("train")
-    print("train geometry", flush=True)
+    print("train geometry: whole batch", flush=True)
     g = _gpu_bwd(w)
-    units = [(0, 0), (3, 7), (5, 12), (7, 15)]
-    sub, bs, hs = _slice_units(w, units)
-    o = _oracle_bwd(sub)
-    for name in ["dq", "dk", "dv", "dg"]:
-        got = torch.stack([g[name][b, :, h] for b, h in units], 0).unsqueeze(2)
-        check(f"train {name}", got, o[name], 2e-2)
-    got = torch.stack([g["dbeta"][b, :, h] for b, h in units], 0).unsqueeze(2)
-    check("train dbeta", got, o["dbeta"], 2e-2)
-    got = torch.stack([g["dh0"][b, h] for b, h in units], 0).unsqueeze(1)
-    check("train dh0", got, o["dh0"], 2e-2)
+    o = _oracle_bwd(w)
+    for name in NAMES:
+        check(f"train {name}", g[name], o[name], 2e-2)
 
 
-def test_bwd_narrow_key_geometry_sampled_units():
+def test_bwd_narrow_key_geometry_whole_batch():
     """The narrow-key head geometry of the Primus 300M configuration (8 heads,
     key dim 32, value dim 64, T2048, its unbounded softplus gate in kernel and
-    beta logits), bf16, 16 sequences of its micro-batch: the whole batch runs
-    on the GPU, the oracle checks 3 sampled sequences of one head in the
-    forward and the backward."""
+    beta logits), bf16, 16 sequences of its micro-batch: every element of the
+    forward and the backward (dA_log and d(dt_bias) included) against the
+    oracle."""
     w = inputs.chunk_inputs(16, 2048, 8, 32, 64, seed=75, dtype=torch.bfloat16, gate_mode=inputs.GATE_SOFTPLUS,
                             beta_logits=True, with_grad_out=True)
-    print("narrow-key geometry B16 T2048 H8 K32 V64", flush=True)
-    g = _gpu_bwd(w)
+    print("narrow-key geometry B16 T2048 H8 K32 V64: whole batch", flush=True)
+    _compare(w, "narrow")
     kw = dict(A_log=dev(w["A_log"]), dt_bias=dev(w["dt_bias"]), scale=w["scale"],
               use_qk_l2norm_in_kernel=True, gate_mode=w["gate_mode"], use_beta_sigmoid_in_kernel=True)
     o_gpu, _ = kda.chunk_kda(dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["g"]), dev(w["beta"]), **kw)
     torch.cuda.synchronize()
-    # units of one head, so that its A_log and dt_bias apply to the whole slice
-    hd, K = 5, 32
-    units = [(0, hd), (7, hd), (15, hd)]
-    sub, bs, hs = _slice_units(w, units)
-    sub["A_log"] = w["A_log"][hd:hd + 1]
-    sub["dt_bias"] = w["dt_bias"][hd * K:(hd + 1) * K]
-    o = _oracle_bwd(sub)
-    for name in ["dq", "dk", "dv", "dg"]:
-        got = torch.stack([g[name][b, :, h] for b, h in units], 0).unsqueeze(2)
-        check(f"narrow {name}", got, o[name], 2e-2)
-    got = torch.stack([g["dbeta"][b, :, h] for b, h in units], 0).unsqueeze(2)
-    check("narrow dbeta", got, o["dbeta"], 2e-2)
-    of, _ = oracle.chunk_fwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], A_log=sub["A_log"],
-                             dt_bias=sub["dt_bias"], scale=sub["scale"], use_qk_l2norm=True,
-                             gate_mode=sub["gate_mode"], use_beta_sigmoid=True)
-    got = torch.stack([o_gpu[b, :, h] for b, h in units], 0).unsqueeze(2)
-    check("narrow o", got, of, 2e-2)
+    of, _ = oracle.chunk_fwd(w["q"], w["k"], w["v"], w["g"], w["beta"], A_log=w["A_log"], dt_bias=w["dt_bias"],
+                             scale=w["scale"], use_qk_l2norm=True, gate_mode=w["gate_mode"], use_beta_sigmoid=True)
+    check("narrow o", o_gpu, of, 2e-2)
 
 
-def test_bwd_hybrid_varlen_sampled_heads():
-    """Packed 1024/2048/1024/4096, H16 K=V=128 bf16, dO ~ N(0,1): 3 heads checked."""
+def test_bwd_hybrid_varlen_whole_batch():
+    """Packed 1024/2048/1024/4096, H16 K=V=128 bf16, dO ~ N(0,1): every head."""
     w = inputs.chunk_inputs(1, 8192, 16, 128, 128, seed=inputs.SEEDS["fwd_hybrid"], dtype=torch.bfloat16,
                             cu_seqlens=[0, 1024, 3072, 4096, 8192], with_grad_out=True)
-    g = _gpu_bwd(w)
-    heads = [1, 8, 14]
-    sub = dict(w)
-    for key in ("q", "k", "v", "g", "dO"):
-        sub[key] = w[key][:, :, heads]
-    sub["beta"] = w["beta"][:, :, heads]
-    sub["initial_state"] = w["initial_state"][:, heads]
-    o = _oracle_bwd(sub)
-    for name in ["dq", "dk", "dv", "dg", "dbeta"]:
-        check(f"hybrid {name}", g[name][:, :, heads], o[name], 2e-2)
-    check("hybrid dh0", g["dh0"][:, heads], o["dh0"], 2e-2)
+    print("hybrid backward: whole batch", flush=True)
+    _compare(w, "hybrid")
 
 
 def test_bwd_deterministic():

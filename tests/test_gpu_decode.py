@@ -6,7 +6,7 @@ import torch
 import oracle
 import kimi_delta_attention_amd as kda
 from kimi_delta_attention_amd import inputs
-from parity import check, dev, TOL_F32
+from parity import check, dev, TOL_F32, nan_full
 
 pytestmark = pytest.mark.gpu
 
@@ -17,7 +17,9 @@ def _gpu_steps(init, steps, N, H, D, x_dtype, **kw):
     st = dev(init["state"]).clone()
     outs = []
     for s in steps:
-        o = kda.recurrent_step(dev(s["x"].to(x_dtype)), cw, cs, dev(s["g"]), dev(s["beta"]), st, **kw)
+        # the output starts as NaN, so that an element the kernel does not write fails the check
+        o = kda.recurrent_step(dev(s["x"].to(x_dtype)), cw, cs, dev(s["g"]), dev(s["beta"]), st,
+                               out=nan_full((N, H * D), torch.float32), **kw)
         outs.append(o.clone())
     torch.cuda.synchronize()
     return outs, cs, st
@@ -76,42 +78,33 @@ def test_decode_gate_modes_and_flags(mode):
     check("state/noflags", gst, ost, TOL_F32)
 
 
-def test_decode_production_geometry_sampled():
-    """64 sequences x 96 heads x d128, 256 consecutive steps in place; sampled
-    (sequence, head) units are compared with the oracle after every 32 steps.
-    Units are independent, so the oracle runs on the sampled units alone."""
+def test_decode_production_geometry_whole_batch():
+    """64 sequences x 96 heads x d128, 256 consecutive steps in place, in the
+    launch configuration the bench times: after every 32 steps the outputs,
+    recurrent states and conv states of all 6,144 (sequence, head) units are
+    compared with the oracle, which steps the whole batch in place alongside."""
     shp = inputs.DECODE_SHAPE
     N, H, D, W = shp["N"], shp["H"], shp["D"], shp["W"]
     seed = inputs.SEEDS["decode"]
     init = inputs.decode_init(N, H, D, W, seed=seed)
-    units = [(0, 0), (5, 17), (33, 95), (63, 48), (17, 3), (48, 64)]
-    HD = H * D
-    # per-unit oracle state
-    def chan(h):
-        return np.concatenate([np.arange(p * HD + h * D, p * HD + h * D + D) for p in range(3)])
-    ost = {u: (init["conv_state"][u[0]][chan(u[1])].double().numpy()[None],
-               init["state"][u[0], u[1]].double().numpy()[None, None]) for u in units}
+    ocs = init["conv_state"].double().numpy().copy()
+    ost = init["state"].double().numpy().copy()
     cw = dev(init["conv_w"])
     cs = dev(init["conv_state"])
     st = dev(init["state"])
-    print("decode production geometry: 256 steps", flush=True)
+    o = nan_full((N, H * D), torch.float32)
+    print("decode production geometry: 256 steps, whole batch", flush=True)
     for t in range(256):
         s = inputs.decode_step_inputs(N, H, D, seed=seed, step=t)
-        o = kda.recurrent_step(dev(s["x"]), cw, cs, dev(s["g"]), dev(s["beta"]), st)
-        for u in units:
-            n, h = u
-            c = chan(h)
-            oo, ocs, ostt = oracle.decode_step(s["x"][n:n + 1, c], init["conv_w"][c], ost[u][0],
-                                               s["g"][n:n + 1, h * D:(h + 1) * D], s["beta"][n:n + 1, h:h + 1],
-                                               ost[u][1], threads=1)
-            ost[u] = (ocs, ostt)
-            if (t + 1) % 32 == 0:
-                check(f"o step {t} unit {u}", o[n, h * D:(h + 1) * D], oo[0], TOL_F32)
         if (t + 1) % 32 == 0:
-            for u in units:
-                n, h = u
-                check(f"state step {t} unit {u}", st[n, h], ost[u][1][0, 0], TOL_F32)
-                check(f"conv step {t} unit {u}", cs[n][chan(h)], ost[u][0][0], TOL_F32)
+            o.fill_(float("nan"))
+        kda.recurrent_step(dev(s["x"]), cw, cs, dev(s["g"]), dev(s["beta"]), st, out=o)
+        oo, _, _ = oracle.decode_step(s["x"], init["conv_w"], ocs, s["g"], s["beta"], ost, inplace=True)
+        if (t + 1) % 32 == 0:
+            torch.cuda.synchronize()
+            check(f"o step {t + 1}", o, oo, TOL_F32)
+            check(f"state step {t + 1}", st, ost, TOL_F32)
+            check(f"conv state step {t + 1}", cs, ocs, TOL_F32)
             print(f"  step {t + 1} ok", flush=True)
 
 

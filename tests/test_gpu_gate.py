@@ -6,7 +6,7 @@ import torch
 import oracle
 import kimi_delta_attention_amd as kda
 from kimi_delta_attention_amd import inputs
-from parity import check, dev, tol_for, TOL_F32
+from parity import check, dev, tol_for, TOL_F32, nan_full
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +22,7 @@ def test_output_gate_forward(o_dtype, g_dtype, V):
     print(f"output gate rows={rows} H={H} V={V} o={o_dtype} g={g_dtype}", flush=True)
     x = inputs.gate_inputs(rows, H, V, seed=50 + V, dtype=o_dtype, g_dtype=g_dtype)
     for eps in (1e-5, 0.3):
-        y = kda.output_gate(dev(x["o"]), dev(x["g"]), eps=eps)
+        y = kda.output_gate(dev(x["o"]), dev(x["g"]), eps=eps, out=nan_full(x["o"].shape, o_dtype))
         torch.cuda.synchronize()
         assert y.dtype == o_dtype
         want = oracle.output_gate(x["o"], x["g"], eps=eps)
@@ -36,7 +36,8 @@ def test_output_gate_backward(o_dtype, g_dtype, V):
     rows, H = 29, 2
     print(f"output gate bwd rows={rows} H={H} V={V} o={o_dtype} g={g_dtype}", flush=True)
     x = inputs.gate_inputs(rows, H, V, seed=60 + V, dtype=o_dtype, g_dtype=g_dtype)
-    dO, dg = kda.output_gate_bwd(dev(x["o"]), dev(x["g"]), dev(x["dy"]), eps=0.3)
+    pre = (nan_full(x["o"].shape, o_dtype), nan_full(x["g"].shape, g_dtype))  # unwritten elements fail the check
+    dO, dg = kda.output_gate_bwd(dev(x["o"]), dev(x["g"]), dev(x["dy"]), eps=0.3, out=pre)
     torch.cuda.synchronize()
     assert dO.dtype == o_dtype and dg.dtype == g_dtype
     want_dO, want_dg = oracle.output_gate_bwd(x["o"], x["g"], x["dy"], eps=0.3)

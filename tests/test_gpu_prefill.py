@@ -10,7 +10,7 @@ import torch
 import oracle
 import kimi_delta_attention_amd as kda
 from kimi_delta_attention_amd import inputs
-from parity import check, dev, TOL_F32, TOL_BF16
+from parity import check, dev, TOL_F32, TOL_BF16, nan_full
 
 pytestmark = pytest.mark.gpu
 
@@ -32,8 +32,9 @@ def test_conv_prefill_packed(x_dtype, y_dtype, W):
     x = inputs.prefill_inputs(T, H, D, seed=31 + W, dtype=x_dtype)["x"]
     init = inputs.decode_init(N, H, D, W, seed=32 + W)
     cs = dev(init["conv_state"]).clone()
+    pre = tuple(nan_full((T, H, D), y_dtype) for _ in range(3))  # unwritten elements fail the check
     q, k, v = kda.conv_prefill(dev(x), dev(init["conv_w"]), H, D, conv_state=cs, cu_seqlens=dev(cu),
-                               out_dtype=y_dtype)
+                               out_dtype=y_dtype, out=pre)
     torch.cuda.synchronize()
     y_ref, cs_ref = oracle.conv_prefill(x, init["conv_w"], init["conv_state"], cu_seqlens=cu.numpy())
     tol = TOL_BF16 if y_dtype == torch.bfloat16 else TOL_F32
