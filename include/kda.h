@@ -156,6 +156,28 @@ typedef struct {
 kda_status kda_chunk_fwd(const kda_chunk_args *a);
 size_t kda_chunk_fwd_workspace(const kda_chunk_args *a);
 
+/* Chunked forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Identical to kda_chunk_fwd, except that its workspace is the
+ * library's own device array of KDA_NOALLOC_SCRATCH_BYTES bytes, one per GPU,
+ * held from the library's load on that GPU until the process ends;
+ * a->workspace and a->workspace_bytes are ignored.  It calls no hipMalloc,
+ * hipFree or other allocating routine.
+ *   - If kda_chunk_fwd_workspace(a) exceeds KDA_NOALLOC_SCRATCH_BYTES the call
+ *     returns KDA_ERR_WORKSPACE and launches nothing (192 MiB holds, e.g.,
+ *     the packed 8192-token, 16-head, K = V = 128 bf16 prefill).
+ *   - keep_for_backward must be 0 (else KDA_ERR_INVALID_ARG): the array is
+ *     shared by every call on the GPU, so saved operands would not survive.
+ *   - Every call on a GPU shares that GPU's array, which keeps the last
+ *     call's contents (nothing in it needs to start at zero).  Calls that
+ *     overlap in time on one GPU (unordered streams or threads) race on it
+ *     and their results are undefined; calls ordered on one stream are safe.
+ *   - The first call on each device looks up the array's device address
+ *     (hipGetSymbolAddress, not a stream operation); later calls reuse it.
+ *     A failure of that lookup returns KDA_ERR_HIP. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_args *a);
+
 /* Stage-split forward, for profilers that time each kernel with stream
  * events.  Calling stage 0 then stage 1 with the same arguments (and the
  * same workspace) on one stream is identical to kda_chunk_fwd:

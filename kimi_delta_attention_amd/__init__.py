@@ -20,7 +20,7 @@ import torch
 from . import _lib
 from ._lib import KDA_GATE_LOGDECAY, KDA_GATE_SAFE, KDA_GATE_SOFTPLUS  # noqa: F401
 
-__all__ = ["chunk_kda", "chunk_kda_bwd", "recurrent_step", "conv_prefill", "output_gate", "output_gate_bwd",
+__all__ = ["chunk_kda", "chunk_kda_noalloc", "chunk_kda_bwd", "recurrent_step", "conv_prefill", "output_gate", "output_gate_bwd",
            "chunk_fwd_workspace_bytes",
            "chunk_bwd_workspace_bytes", "KDA_GATE_LOGDECAY", "KDA_GATE_SAFE", "KDA_GATE_SOFTPLUS"]
 
@@ -156,6 +156,36 @@ def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial
     a.workspace = _ptr(ws)
     a.workspace_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _lib.check(lib.kda_chunk_fwd(ctypes.byref(a)), "kda_chunk_fwd")
+    return o, fs
+
+
+def chunk_kda_noalloc(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
+                      output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
+                      use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
+                      cu_seqlens=None, gate_mode=None, out=None, final_state_out=None):
+    """kda_chunk_fwd_noalloc: the chunked forward with its workspace in the
+    library's own device array (no device allocation by the library).  With
+    ``out`` and (if requested) ``final_state_out`` given, this call allocates
+    nothing on the device either.  Calls on one GPU share the array: calls
+    that overlap in time race.  Returns (o, final_state or None)."""
+    gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
+    a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
+                                             output_final_state, use_qk_l2norm_in_kernel, gm,
+                                             use_beta_sigmoid_in_kernel, lower_bound, chunk_size, cu_seqlens)
+    lib = _lib.load()
+    o = out if out is not None else torch.empty(B, T, H, V, dtype=q.dtype, device=dev)
+    _need(o, "out", q.dtype, dev)
+    if tuple(o.shape) != (B, T, H, V):
+        raise ValueError(f"out must be [{B}, {T}, {H}, {V}]")
+    fs = None
+    if output_final_state:
+        fs = final_state_out if final_state_out is not None else torch.empty(N, H, K, V, dtype=torch.float32,
+                                                                             device=dev)
+        _need(fs, "final_state_out", torch.float32, dev)
+        if tuple(fs.shape) != (N, H, K, V):
+            raise ValueError(f"final_state_out must be [{N}, {H}, {K}, {V}]")
+    a.o, a.final_state = _ptr(o), _ptr(fs)
+    _lib.check(lib.kda_chunk_fwd_noalloc(ctypes.byref(a)), "kda_chunk_fwd_noalloc")
     return o, fs
 
 

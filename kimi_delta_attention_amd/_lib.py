@@ -18,6 +18,9 @@ KDA_GATE_LOGDECAY, KDA_GATE_SAFE, KDA_GATE_SOFTPLUS = 0, 1, 2
 
 _vp = ctypes.c_void_p
 
+# Size of the library's own device scratch used by kda_chunk_fwd_noalloc.
+KDA_NOALLOC_SCRATCH_BYTES = 192 << 20
+
 
 class ChunkArgs(ctypes.Structure):
     _fields_ = [
@@ -85,7 +88,7 @@ class GateArgs(ctypes.Structure):
 
 
 # Every symbol include/kda.h declares.
-EXPORTS = ["kda_chunk_fwd", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace", "kda_chunk_bwd",
+EXPORTS = ["kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_stage", "kda_chunk_fwd_workspace", "kda_chunk_bwd",
            "kda_chunk_bwd_stage", "kda_chunk_bwd_stages", "kda_chunk_bwd_workspace", "kda_recurrent_step",
            "kda_conv_prefill", "kda_output_gate", "kda_output_gate_bwd", "kda_status_string", "kda_version"]
 
@@ -104,6 +107,8 @@ def load(path: str = LIB_PATH):
     CA = ctypes.POINTER(ChunkArgs)
     lib.kda_chunk_fwd.argtypes = [CA]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [CA]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_stage.argtypes = [CA, ctypes.c_int]
     lib.kda_chunk_fwd_stage.restype = ctypes.c_int
     lib.kda_chunk_fwd_workspace.argtypes = [CA]

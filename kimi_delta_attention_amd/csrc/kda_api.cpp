@@ -110,6 +110,21 @@ static kda_status chunk_fwd_impl(const kda_chunk_args* a, int stage) {
 
 kda_status kda_chunk_fwd(const kda_chunk_args* a) { return chunk_fwd_impl(a, -1); }
 
+static_assert(kda::kNoAllocScratchBytes == KDA_NOALLOC_SCRATCH_BYTES, "kda.h and the library agree on the size");
+
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_args* a) {
+    kda::ChunkParams p{};
+    kda_status st = check_chunk(a, p, true);
+    if (st != KDA_OK) return st;
+    if (p.keep) return KDA_ERR_INVALID_ARG;  // saved operands would not survive the next call
+    const size_t need = kda::chunk_fwd_workspace(p);
+    if (need > kda::kNoAllocScratchBytes) return KDA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0 && kda::noalloc_workspace(&ws) != hipSuccess) return KDA_ERR_HIP;
+    hipError_t e = kda::launch_chunk_fwd(p, ws, static_cast<hipStream_t>(a->stream), -1);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_chunk_fwd_stage(const kda_chunk_args* a, int stage) {
     if (stage < 0 || stage > 1) return KDA_ERR_INVALID_ARG;
     return chunk_fwd_impl(a, stage);

@@ -111,6 +111,13 @@ struct ChunkGrads {
 };
 
 size_t chunk_fwd_workspace(const ChunkParams& p);  // of the forward's own layout
+
+// Bytes of the library's own device scratch (kda_noalloc.hip), one array per
+// GPU; kda.h states the same value as KDA_NOALLOC_SCRATCH_BYTES.
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(192) << 20;
+// Device address of the current device's scratch array (looked up once per
+// device, thread-safe).
+hipError_t noalloc_workspace(void** ptr);
 // stage < 0 runs every stage; 0 = prep, 1 = state pass.  With p.keep the
 // forward writes the backward's layout (chunk_bwd_workspace bytes).
 hipError_t launch_chunk_fwd(const ChunkParams& p, void* ws, hipStream_t st, int stage = -1);
