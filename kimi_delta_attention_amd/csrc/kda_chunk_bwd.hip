@@ -31,8 +31,11 @@
 //   3 vlocal     per (chunk, head): dv and the V-summed operand gradients;
 //   4 klocal     per (chunk, head): dq, dk, dg, dbeta (and the gate-parameter
 //                shares), plus the reduction of d(A_log), d(dt_bias).
-// The score rule is formed pairwise (every exponent <= 0), so it is exact for
-// any gate without the sub-block factorisation.
+// The score rule runs on MFMA products with the per-sub-block factorisation of
+// the forward: sub-block pairs through the row before the later block, diagonal
+// sub-blocks through the row before them when their decay span allows, else by
+// the level decomposition (every factor at most 1), so any gate is exact.  The
+// fp32 kernel forms the score rule pairwise instead.
 #include "kda_chunk_kernels.hpp"
 
 namespace kda {
@@ -1212,6 +1215,43 @@ __device__ __forceinline__ f32x4 mma16_f32(const float* A, int lda, int m0, cons
     return acc;
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// C += A B over a 16-row contraction with bf16 operands (4 per lane: lane l
+// supplies A[l % 16][4 (l / 16) .. + 3] and B[4 (l / 16) .. + 3][l % 16]).
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                      0, 0, 0);
+}
+
+// Transposing LDS read of four bf16 values (the lo half of load_kn).
+__device__ __forceinline__ u32x2 read_tr16(const uint16_t* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)p));
+}
+
+// Four fp32 values as bf16 high parts and bf16 remainders, so that the pair
+// holds about 16 bits of each value.
+__device__ __forceinline__ void split_hi_lo4(const float (&x)[4], u32x2& hi, u32x2& lo) {
+    const bf16x2_t h0 = {static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1])};
+    const bf16x2_t h1 = {static_cast<__bf16>(x[2]), static_cast<__bf16>(x[3])};
+    const bf16x2_t l0 = {static_cast<__bf16>(x[0] - static_cast<float>(h0[0])),
+                         static_cast<__bf16>(x[1] - static_cast<float>(h0[1]))};
+    const bf16x2_t l1 = {static_cast<__bf16>(x[2] - static_cast<float>(h1[0])),
+                         static_cast<__bf16>(x[3] - static_cast<float>(h1[1]))};
+    hi = u32x2{__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1)};
+    lo = u32x2{__builtin_bit_cast(uint32_t, l0), __builtin_bit_cast(uint32_t, l1)};
+}
+
+// AND masks over four bf16 entries (two per word) that keep the entries e of
+// level_keep(pos, base, h, row_is_later) and clear the others.
+__device__ __forceinline__ u32x2 level_words(int pos, int base, int h, bool row_is_later) {
+    const unsigned m = level_keep(pos, base, h, row_is_later);
+    return u32x2{((m & 1u) ? 0x0000FFFFu : 0u) | ((m & 2u) ? 0xFFFF0000u : 0u),
+                 ((m & 4u) ? 0x0000FFFFu : 0u) | ((m & 8u) ? 0xFFFF0000u : 0u)};
+}
+
 template <int K, int V = K>
 __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkParams p, ChunkGrads gr,
                                                                          const int32_t* chunk_off, uint8_t* ws,
@@ -1565,40 +1605,114 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 }
             }
 
-            // diagonal sub-blocks too wide to factorise: pairwise from G
+            // diagonal sub-blocks too wide to factorise through one reference row:
+            // the level decomposition (kda_chunk_common.hpp), every factor <= 1, as
+            // 16 x 16 x 16 bf16 products over the block's own 16 rows with the fp32
+            // score gradients and the B values (each lane's own rows of the
+            // block) split into bf16 high and low parts, the A entries of other
+            // levels masked; the diagonal entries directly.  Block values are
+            // selected into registers and the contributions added back by
+            // selection (no run-time register indexing).
             if (any_unsafe) {
 #pragma unroll 1
                 for (int I = 0; I < 4; ++I) {
-                    if (!s.unsafe[I]) continue;
+                    if (!s.unsafe[I]) continue;  // uniform over the workgroup
+                    const int b0 = kSub * I;
+                    float gI[4], qI[4], kI[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int x = 4 * lg + r, i = kSub * I + x;
-                        const float Gi = s.G[i][c];
-                        float Pq = 0.f, Pk = 0.f, R = 0.f;
-#pragma unroll 1
-                        for (int y = 0; y < kSub; ++y) {
-                            const int jr = kSub * I + y;
-                            const float Gj = s.G[jr][c];
-                            if (y <= x) {
-                                const float e = __expf(Gi - Gj) * MM::to_f32(s.kh[jr][c]);
-                                Pq += s.x.sc.dM[i][jr] * e;
-                                Pk += s.x.sc.dA[i][jr] * e;
-                            }
-                            if (y >= x) {
-                                const float e = __expf(Gj - Gi);
-                                R += (s.x.sc.dM[jr][i] * MM::to_f32(s.qh[jr][c]) +
-                                      s.x.sc.dA[jr][i] * MM::to_f32(s.kh[jr][c])) * e;
-                            }
-                        }
-                        const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
-#pragma unroll
-                        for (int II = 0; II < 4; ++II)
-                            if (II == I) {
-                                dq[II][r] += Pq;
-                                dk[II][r] += Pk + R;
-                                dG[II][r] += q_ * Pq + k_ * Pk - k_ * R;
-                            }
+                        gI[r] = I == 0 ? Gc[r] : I == 1 ? Gc[4 + r] : I == 2 ? Gc[8 + r] : Gc[12 + r];
+                        qI[r] = MM::to_f32(s.qh[b0 + 4 * lg + r][c]);
+                        kI[r] = MM::to_f32(s.kh[b0 + 4 * lg + r][c]);
                     }
+                    const float g8 = s.G[b0 + 7][c];
+                    const float g4 = s.G[b0 + 4 * (lg & 2) + 3][c];
+                    // A operands: rows b0 + lc against contraction rows b0 + 4 lg + e,
+                    // and transposed (rows b0 + 4 lg + e of column b0 + lc)
+                    float am[4], ak[4], tm[4], tk[4];
+                    {
+                        const float4 a4 = *reinterpret_cast<const float4*>(&s.x.sc.dM[b0 + lc][b0 + 4 * lg]);
+                        const float4 k4 = *reinterpret_cast<const float4*>(&s.x.sc.dA[b0 + lc][b0 + 4 * lg]);
+                        am[0] = a4.x; am[1] = a4.y; am[2] = a4.z; am[3] = a4.w;
+                        ak[0] = k4.x; ak[1] = k4.y; ak[2] = k4.z; ak[3] = k4.w;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            tm[e] = s.x.sc.dM[b0 + 4 * lg + e][b0 + lc];
+                            tk[e] = s.x.sc.dA[b0 + 4 * lg + e][b0 + lc];
+                        }
+                    }
+                    u32x2 amh, aml, akh, akl, tmh, tml, tkh, tkl;
+                    split_hi_lo4(am, amh, aml);
+                    split_hi_lo4(ak, akh, akl);
+                    split_hi_lo4(tm, tmh, tml);
+                    split_hi_lo4(tk, tkh, tkl);
+                    f32x4 dqI = {0.f, 0.f, 0.f, 0.f}, dkI = dqI, dGI = dqI;
+#pragma unroll 1
+                    for (int lv = 0; lv < 4; ++lv) {
+                        const int hh = 8 >> lv;
+                        float f[4];
+                        bool later[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float gref = hh == 8 ? g8 : hh == 4 ? g4 : hh == 2 ? gI[1] : gI[r & 2];
+                            later[r] = (4 * lg + r) & hh;
+                            f[r] = __expf(later[r] ? gI[r] - gref : gref - gI[r]);
+                        }
+                        const u32x2 wP = level_words(lc, 4 * lg, hh, true);
+                        const u32x2 wR = level_words(lc, 4 * lg, hh, false);
+                        float b4[4];
+                        u32x2 bh, bl;
+                        // P terms (dM carries the scale)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? 0.f : kI[r] * f[r];
+                        split_hi_lo4(b4, bh, bl);
+                        f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
+                        pq = mfma16x16x16(amh & wP, bh, pq);
+                        pq = mfma16x16x16(amh & wP, bl, pq);
+                        pq = mfma16x16x16(aml & wP, bh, pq);
+                        pk = mfma16x16x16(akh & wP, bh, pk);
+                        pk = mfma16x16x16(akh & wP, bl, pk);
+                        pk = mfma16x16x16(akl & wP, bh, pk);
+                        // R terms: q against dM, then k against dA
+                        f32x4 rr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? qI[r] * f[r] : 0.f;
+                        split_hi_lo4(b4, bh, bl);
+                        rr = mfma16x16x16(tmh & wR, bh, rr);
+                        rr = mfma16x16x16(tmh & wR, bl, rr);
+                        rr = mfma16x16x16(tml & wR, bh, rr);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? kI[r] * f[r] : 0.f;
+                        split_hi_lo4(b4, bh, bl);
+                        rr = mfma16x16x16(tkh & wR, bh, rr);
+                        rr = mfma16x16x16(tkh & wR, bl, rr);
+                        rr = mfma16x16x16(tkl & wR, bh, rr);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float Pq = later[r] ? f[r] * pq[r] : 0.f;
+                            const float Pk = later[r] ? f[r] * pk[r] : 0.f;
+                            const float R = later[r] ? 0.f : f[r] * rr[r];
+                            dqI[r] += Pq;
+                            dkI[r] += Pk + R;
+                            dGI[r] += qI[r] * Pq + kI[r] * (Pk - R);
+                        }
+                    }
+                    // the diagonal entries (no decay): dM_ii enters both rules and
+                    // their dG terms cancel; dA is strictly lower
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = b0 + 4 * lg + r;
+                        const float dmii = s.x.sc.dM[i][i];
+                        dqI[r] += dmii * kI[r];
+                        dkI[r] += dmii * qI[r];
+                    }
+#pragma unroll
+                    for (int II = 0; II < 4; ++II)
+                        if (II == I) {
+                            dq[II] += dqI;
+                            dk[II] += dkI;
+                            dG[II] += dGI;
+                        }
                 }
             }
 
@@ -2247,41 +2361,106 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                     dG[J][r] -= ko[4 * J + r] * R;
                 }
 
-            // diagonal sub-blocks too wide to factorise: pairwise from G
+            // diagonal sub-blocks too wide to factorise through one reference row:
+            // the level decomposition (kda_chunk_common.hpp), every factor <= 1, as
+            // 16 x 16 x 16 bf16 products over the block's own 16 rows (each lane's
+            // four B values are its own rows of the block), with the A entries of
+            // other levels masked; the diagonal entries directly.  One copy of the
+            // code serves every block: the block's register values are selected
+            // in and its contributions added back by selection, so that no
+            // register array is indexed at run time.
             if (s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3]) {
 #pragma unroll 1
                 for (int I = 0; I < 4; ++I) {
-                    if (!s.unsafe[I]) continue;
+                    if (!s.unsafe[I]) continue;  // uniform over the workgroup
+                    float gI[4], qI[4], kI[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int xr = 4 * lg + r, i = kSub * I + xr;
-                        const float Gi = s.G[i][c];
-                        float Pq = 0.f, Pk = 0.f, R = 0.f;
-#pragma unroll 1
-                        for (int y = 0; y < kSub; ++y) {
-                            const int jr = kSub * I + y;
-                            const float Gj = s.G[jr][c];
-                            if (y <= xr) {
-                                const float e = __expf(Gi - Gj) * MM::to_f32(s.kh[jr][c]);
-                                Pq += p.scale * MM::to_f32(s.x.sc.dM[i][jr]) * e;
-                                Pk += (MM::to_f32(s.x.sc.dA[i][jr]) + MM::to_f32(s.x.sc.dAl[i][jr])) * e;
-                            }
-                            if (y >= xr) {
-                                const float e = __expf(Gj - Gi);
-                                R += (p.scale * MM::to_f32(s.x.sc.dM[jr][i]) * MM::to_f32(s.qh[jr][c]) +
-                                      (MM::to_f32(s.x.sc.dA[jr][i]) + MM::to_f32(s.x.sc.dAl[jr][i])) *
-                                          MM::to_f32(s.kh[jr][c])) * e;
-                            }
-                        }
-                        const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
-#pragma unroll
-                        for (int II = 0; II < 4; ++II)
-                            if (II == I) {
-                                dq[II][r] += Pq;
-                                dk[II][r] += Pk + R;
-                                dG[II][r] += q_ * Pq + k_ * Pk - k_ * R;
-                            }
+                        gI[r] = I == 0 ? Gc[r] : I == 1 ? Gc[4 + r] : I == 2 ? Gc[8 + r] : Gc[12 + r];
+                        qI[r] = I == 0 ? qo[r] : I == 1 ? qo[4 + r] : I == 2 ? qo[8 + r] : qo[12 + r];
+                        kI[r] = I == 0 ? ko[r] : I == 1 ? ko[4 + r] : I == 2 ? ko[8 + r] : ko[12 + r];
                     }
+                    const int b0 = kSub * I;
+                    const float g8 = s.G[b0 + 7][c];
+                    const float g4 = s.G[b0 + 4 * (lg & 2) + 3][c];
+                    // A operands of the block: rows b0 + lc against contraction rows
+                    // b0 + 4 lg + e, and the transposed reads (rows b0 + 4 lg + e of
+                    // column b0 + lc) for the column-side rule
+                    const u32x2 am0 = *reinterpret_cast<const u32x2*>(&s.x.sc.dM[b0 + lc][b0 + 4 * lg]);
+                    const u32x2 ah0 = *reinterpret_cast<const u32x2*>(&s.x.sc.dA[b0 + lc][b0 + 4 * lg]);
+                    const u32x2 al0 = *reinterpret_cast<const u32x2*>(&s.x.sc.dAl[b0 + lc][b0 + 4 * lg]);
+                    const int tro = (b0 + 4 * lg + (lc >> 2)) * LDC + b0 + 4 * (lc & 3);
+                    const u32x2 tm0 = read_tr16(&s.x.sc.dM[0][0] + tro);
+                    const u32x2 th0 = read_tr16(&s.x.sc.dA[0][0] + tro);
+                    const u32x2 tl0 = read_tr16(&s.x.sc.dAl[0][0] + tro);
+                    f32x4 dqI = {0.f, 0.f, 0.f, 0.f}, dkI = dqI, dGI = dqI;
+#pragma unroll
+                    for (int lv = 0; lv < 4; ++lv) {
+                        const int hh = 8 >> lv;
+                        float f[4];
+                        bool later[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float gref = hh == 8 ? g8 : hh == 4 ? g4 : hh == 2 ? gI[1] : gI[r & 2];
+                            later[r] = (4 * lg + r) & hh;
+                            f[r] = __expf(later[r] ? gI[r] - gref : gref - gI[r]);
+                        }
+                        const u32x2 wP = level_words(lc, 4 * lg, hh, true);
+                        const u32x2 wR = level_words(lc, 4 * lg, hh, false);
+                        // P terms: rows i (later half) against columns j (earlier half)
+                        float b4[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? 0.f : kI[r] * f[r];
+                        u32x2 bh, bl;
+                        split_hi_lo4(b4, bh, bl);
+                        const u32x2 am = am0 & wP, ah = ah0 & wP, al = al0 & wP;
+                        f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
+                        pq = mfma16x16x16(am, bh, pq);
+                        pq = mfma16x16x16(am, bl, pq);
+                        pk = mfma16x16x16(ah, bh, pk);
+                        pk = mfma16x16x16(ah, bl, pk);
+                        pk = mfma16x16x16(al, bh, pk);
+                        // R terms: columns j (earlier half) against rows i (later half)
+                        f32x4 rr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? p.scale * qI[r] * f[r] : 0.f;
+                        split_hi_lo4(b4, bh, bl);
+                        const u32x2 tm = tm0 & wR;
+                        rr = mfma16x16x16(tm, bh, rr);
+                        rr = mfma16x16x16(tm, bl, rr);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? kI[r] * f[r] : 0.f;
+                        split_hi_lo4(b4, bh, bl);
+                        const u32x2 th = th0 & wR, tl = tl0 & wR;
+                        rr = mfma16x16x16(th, bh, rr);
+                        rr = mfma16x16x16(th, bl, rr);
+                        rr = mfma16x16x16(tl, bh, rr);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float Pq = later[r] ? f[r] * p.scale * pq[r] : 0.f;
+                            const float Pk = later[r] ? f[r] * pk[r] : 0.f;
+                            const float R = later[r] ? 0.f : f[r] * rr[r];
+                            dqI[r] += Pq;
+                            dkI[r] += Pk + R;
+                            dGI[r] += qI[r] * Pq + kI[r] * (Pk - R);
+                        }
+                    }
+                    // the diagonal entries (no decay): dM_ii enters both rules and
+                    // their dG terms cancel; dA is strictly lower
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = b0 + 4 * lg + r;
+                        const float dmii = p.scale * MM::to_f32(s.x.sc.dM[i][i]);
+                        dqI[r] += dmii * kI[r];
+                        dkI[r] += dmii * qI[r];
+                    }
+#pragma unroll
+                    for (int II = 0; II < 4; ++II)
+                        if (II == I) {
+                            dq[II] += dqI;
+                            dk[II] += dkI;
+                            dG[II] += dGI;
+                        }
                 }
             }
 

@@ -20,7 +20,8 @@ constexpr int kThreads = 256;
 constexpr int kPersistentGrid = 256;
 // Diagonal 16-row sub-blocks whose accumulated decay span stays under this
 // bound are factorised through the row before the block (factors up to
-// e^kSpanLimit, finite in fp32); wider spans are formed pairwise.
+// e^kSpanLimit, finite in fp32); wider spans go through the level
+// decomposition below, whose factors are all at most 1.
 constexpr float kSpanLimit = 85.0f;
 
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
@@ -55,6 +56,13 @@ template <> struct Mma<true> {        // bf16 inputs, fp32 accumulate
     }
     __device__ __forceinline__ static ET from_f32(float x) { return f32_to_bf16_bits(x); }
     __device__ __forceinline__ static float to_f32(ET x) { return bf16_bits_to_f32(x); }
+    // KPL fp32 values rounded into one fragment
+    __device__ __forceinline__ static Frag pack(const float (&x)[KPL]) {
+        u16x8 u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = f32_to_bf16_bits(x[e]);
+        return __builtin_bit_cast(Frag, u);
+    }
 };
 
 template <> struct Mma<false> {       // fp32 inputs, fp32 accumulate
@@ -72,7 +80,42 @@ template <> struct Mma<false> {       // fp32 inputs, fp32 accumulate
     __device__ __forceinline__ static Frag scale(Frag f, const float* s) { return f * s[0]; }
     __device__ __forceinline__ static ET from_f32(float x) { return x; }
     __device__ __forceinline__ static float to_f32(ET x) { return x; }
+    __device__ __forceinline__ static Frag pack(const float (&x)[KPL]) { return x[0]; }
 };
+
+// ---- level decomposition of a diagonal 16-row sub-block
+// The score X_ij = sum_c x_ic k_jc e^(G_ic - G_jc) of a row pair (i, j), j < i,
+// inside one 16-row sub-block is factorised through a reference row that lies
+// between them, so that both factors are at most 1 for any decay span: with
+// positions a = i mod 16 and b = j mod 16, the pair belongs to level h, the
+// highest bit in which a and b differ (h in {8, 4, 2, 1}); i lies in the later
+// half (bit h set) and j in the earlier half of the same 2h-row group, and the
+// reference is that group's row (a & ~(2h - 1)) + h - 1, the last row of the
+// earlier half.  Each level is one product with the rows of the later half as
+// left operand (factor e^(G_i - G_ref)) and the rows of the earlier half as
+// right operand (factor e^(G_ref - G_j)); the diagonal i = j carries no decay.
+
+// Factor of row position pos at level h: e^(G_pos - G_ref) in the later half,
+// e^(G_ref - G_pos) in the earlier half.
+__device__ __forceinline__ float level_fac(int pos, int h, float g_pos, float g_ref) {
+    return (pos & h) ? __expf(g_pos - g_ref) : __expf(g_ref - g_pos);
+}
+
+// True when (a, b) is a pair of level h with a in the later half.
+__device__ __forceinline__ bool level_pair(int a, int b, int h) {
+    return (a & h) && !(b & h) && ((a ^ b) < 2 * h);
+}
+
+// 4-bit mask over the positions base .. base + 3 of the other index: with
+// row_is_later, bit e is level_pair(pos, base + e, h) (pos the later row), else
+// level_pair(base + e, pos, h) (pos the earlier row).
+__device__ __forceinline__ unsigned level_keep(int pos, int base, int h, bool row_is_later) {
+    unsigned m = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (row_is_later ? level_pair(pos, base + e, h) : level_pair(base + e, pos, h)) m |= 1u << e;
+    return m;
+}
 
 // ---------------------------------------------------------------- geometry
 // Sequence bounds: dense input (cu == nullptr) or packed offsets.  Offsets are

@@ -29,7 +29,9 @@
 // that no factor exceeds 1, except on the diagonal 16x16 sub-blocks, where the
 // reference is the row before the block and the opposite factor is at most
 // exp(span of the block).  A block whose span exceeds kSpanLimit for any
-// channel (possible only with unbounded gates) is formed pairwise instead.
+// channel (possible only with unbounded gates) is formed by the level
+// decomposition instead (kda_chunk_common.hpp): four more products, each with
+// a reference row between the rows it pairs, so every factor is at most 1.
 #pragma once
 
 #include "kda_chunk_common.hpp"
@@ -562,14 +564,55 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     }
     __syncthreads();
 
-    // ---- 5. A and M sub-block tiles on MFMA (job = (matrix, I, J<=I)); 20 jobs
+    // Level job of diagonal sub-block I (one wave): the pairs of level hh of the
+    // level decomposition (level_pair; hh = 0: the diagonal) of A (and the
+    // un-scaled Ak) and M, from the normalised q and k rows that step 5 leaves
+    // in the qL and kL tiles, each element times its factor (at most 1).
+    auto level_job = [&](int hh, int I, int lane_) {
+        const int pr = lane_ & 15;  // this lane's operand row in the block
+        const int row = kSub * I + pr;
+        const bool later = hh == 0 || (pr & hh), earlier = hh == 0 || !(pr & hh);
+        const int ref = hh == 0 ? row : kSub * I + (pr & ~(2 * hh - 1)) + hh - 1;
+        f32x4 accM = {0.f, 0.f, 0.f, 0.f}, accA = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int k0 = 0; k0 < K; k0 += MM::KS) {
+            const int ch = k0 + (lane_ >> 4) * MM::KPL;
+            float fa[MM::KPL], fb[MM::KPL];
+#pragma unroll
+            for (int e = 0; e < MM::KPL; ++e) {
+                const float f = hh == 0 ? 1.f : level_fac(pr, hh, s.G[row][ch + e], s.G[ref][ch + e]);
+                fa[e] = later ? f : 0.f;
+                fb[e] = earlier ? f : 0.f;
+            }
+            const auto xq = MM::load(&s.u.op.qL[0][0], LDE, kSub * I, k0, lane_);
+            const auto xk = MM::load(&s.u.op.kL[0][0], LDE, kSub * I, k0, lane_);
+            const auto bK = MM::scale(xk, fb);
+            accM = MM::mma(MM::scale(xq, fa), bK, accM);
+            if (hh) accA = MM::mma(MM::scale(xk, fa), bK, accA);
+        }
+        const int b_ = lane_ & 15, colg = kSub * I + b_;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int a_ = 4 * (lane_ >> 4) + r, rowg = kSub * I + a_;
+            if (hh == 0 ? a_ == b_ : level_pair(a_, b_, hh)) {
+                s.M[rowg][colg] = accM[r];
+                s.A[rowg][colg] = accA[r] * s.beta[rowg];  // 0 on the diagonal
+                if (BWD) s.Ak[rowg][colg] = accA[r];
+            }
+        }
+    };
+
+    // ---- 5. A and M sub-block tiles on MFMA (job = (matrix, I, J<=I)); 20 jobs,
+    //         then for each diagonal sub-block too wide to factorise through one
+    //         reference row, its level jobs (level_job: levels 8, 4, 2, 1 and the
+    //         diagonal)
     for (int job = w; job < 20; job += NW) {
         const bool isM = job >= 10;
         int tj = isM ? job - 10 : job;
         int I = 0;
         while (tj > I) { tj -= I + 1; ++I; }
         const int J = tj;
-        if (J == I && s.unsafe[I]) continue;  // formed pairwise below
+        if (J == I && s.unsafe[I]) continue;  // formed by its level jobs
         const float* fac = nullptr;
         if (J == I) fac = s.invP[I];
         else if (I == 2 && J == 0) fac = s.F20;
@@ -602,50 +645,14 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     store_packed<ET, CPT>(gQE + i * K + c0, pQE);
     if (BWD) store_packed<ET, CPT>(reinterpret_cast<ET*>(out + X::kKE) + i * K + c0, pKE);
     store_packed<ET, CPT>(gKD + i * K + c0, pKD);
-    // pairwise diagonal sub-blocks whose decay span is too wide to factorise:
-    // PL consecutive lanes per (row, column) pair of a block, 16 channels each
-    // (q and k rows re-read from the input as vectors), summed by lane shuffles
-    if (s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3]) {
-        constexpr int CPL = 16;
-        constexpr int PL = K / CPL;
-        constexpr int NPAIR = kSub * (kSub + 1) / 2;
-        const IT* qg = static_cast<const IT*>(p.q);
-        const IT* kg = static_cast<const IT*>(p.k);
-        for (int u = t; u < 4 * NPAIR * PL; u += NT) {
-            const int I = u / (NPAIR * PL);
-            if (!s.unsafe[I]) continue;  // uniform over a pair's lanes
-            const int pl = u % PL, pr = (u / PL) % NPAIR;
-            int a = 0, b = pr;
-            while (b > a) { b -= a + 1; ++a; }
-            const int ri = kSub * I + a, rj = kSub * I + b;
-            float sa = 0.f, sm = 0.f;
-            if (ri < rows) {  // padding rows stay zero
-                const int cu = pl * CPL;
-                const int64_t oi = ((start + static_cast<int64_t>(j) * kChunk + ri) * H + h) * K + cu;
-                const int64_t oj = ((start + static_cast<int64_t>(j) * kChunk + rj) * H + h) * K + cu;
-                float qi[CPL], ki[CPL], kj[CPL];
-                load_row<CPL>(qg + oi, qi);
-                load_row<CPL>(kg + oi, ki);
-                load_row<CPL>(kg + oj, kj);
-#pragma unroll
-                for (int c = 0; c < CPL; ++c) {
-                    const float e = __expf(s.G[ri][cu + c] - s.G[rj][cu + c]);
-                    sa += ki[c] * kj[c] * e;
-                    sm += qi[c] * kj[c] * e;
-                }
-                sa *= s.rk[ri] * s.rk[rj];
-                sm *= s.rq[ri] * s.rk[rj];
-            }
-#pragma unroll
-            for (int o = 1; o < PL; o <<= 1) {
-                sa += __shfl_xor(sa, o, 64);
-                sm += __shfl_xor(sm, o, 64);
-            }
-            if (pl == 0) {
-                s.M[ri][rj] = sm;
-                s.A[ri][rj] = (rj < ri) ? sa * s.beta[ri] : 0.f;
-                if (BWD) s.Ak[ri][rj] = (rj < ri) ? sa : 0.f;
-            }
+    if (s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3]) {  // uniform
+        __syncthreads();  // the factored tiles are read
+        store_row<CPT>(&s.u.op.qL[i][c0], qh);
+        store_row<CPT>(&s.u.op.kL[i][c0], kh);
+        __syncthreads();
+        for (int job = w; job < 20; job += NW) {
+            const int I = job / 5, lv = job % 5;
+            if (s.unsafe[I]) level_job(lv < 4 ? (8 >> lv) : 0, I, lane);
         }
     }
     __syncthreads();
