@@ -60,6 +60,9 @@ typedef enum {
     KDA_ERR_HIP = 5            /* a kernel launch reported an error */
 } kda_status;
 
+/* Element types.  The args structs hold them (like the flags and the gate
+ * mode) in plain int fields, so that any value a caller stores is a valid
+ * object in both C and C++; the library rejects values outside this set. */
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 
 /* How g is turned into the per-channel log-decay (api.py chunk_kda gate
@@ -84,7 +87,7 @@ typedef struct {
     const int32_t *cu_seqlens;
     int N;
     /* inputs */
-    kda_dtype qkv_dtype;     /* dtype of q, k, v (and o, dq, dk, dv, dO) */
+    int qkv_dtype;           /* kda_dtype of q, k, v (and o, dq, dk, dv, dO) */
     const void *q, *k, *v;
     const float *g;          /* [rows, H, K] log-decay or raw gate input (see gate_mode) */
     const float *beta;       /* [rows, H] value, or logit when use_beta_sigmoid */
@@ -227,7 +230,7 @@ int kda_chunk_bwd_stages(void);
  * [0, S) leaves every state unchanged and sets that sequence's o to NaN. */
 typedef struct {
     int N, H, D, W;          /* D = head dim (K = V = D) in {32, 64, 128}; 1 <= W <= 8 */
-    kda_dtype x_dtype;       /* KDA_F32 or KDA_BF16 */
+    int x_dtype;             /* kda_dtype: KDA_F32 or KDA_BF16 */
     const void *x_qkv;       /* [N, 3*H*D] pre-conv inputs, [q | k | v] */
     const float *conv_w;     /* [3*H*D, W], slot 0 oldest */
     float *conv_state;       /* [N, 3*H*D, W] in/out, oldest -> newest */
@@ -272,11 +275,11 @@ typedef struct {
     int B, T, H, D, W;         /* D in {32, 64, 128}; 1 <= W <= 8 */
     const int32_t *cu_seqlens; /* device [N+1] for packed input (B = 1), or NULL (dense, N = B) */
     int N;
-    kda_dtype x_dtype;         /* KDA_F32 or KDA_BF16 */
+    int x_dtype;               /* kda_dtype: KDA_F32 or KDA_BF16 */
     const void *x_qkv;         /* [rows, 3*H*D] pre-conv inputs, [q | k | v] */
     const float *conv_w;       /* [3*H*D, W], slot 0 oldest */
     float *conv_state;         /* [N, 3*H*D, W] in/out, oldest -> newest; or NULL */
-    kda_dtype y_dtype;         /* KDA_F32 or KDA_BF16: element type of q, k, v */
+    int y_dtype;               /* kda_dtype: KDA_F32 or KDA_BF16, element type of q, k, v */
     void *q, *k, *v;           /* [rows, H, D] each */
     void *stream;              /* hipStream_t */
 } kda_conv_args;
@@ -293,8 +296,8 @@ kda_status kda_conv_prefill(const kda_conv_args *a);
  * Every pointer must be 16-byte aligned.  Nothing is launched on error. */
 typedef struct {
     int rows, H, V;            /* V in {32, 64, 128, 256}; rows >= 0 */
-    kda_dtype o_dtype;         /* KDA_F32 or KDA_BF16: o, y (and dy, dO) */
-    kda_dtype g_dtype;         /* KDA_F32 or KDA_BF16: g (and dg) */
+    int o_dtype;               /* kda_dtype: KDA_F32 or KDA_BF16, for o, y (and dy, dO) */
+    int g_dtype;               /* kda_dtype: KDA_F32 or KDA_BF16, for g (and dg) */
     float eps;                 /* NaN means 1e-5; must be >= 0 */
     const void *o;             /* [rows, H, V] */
     const void *g;             /* [rows, H, V] gate input (before the sigmoid) */

@@ -22,7 +22,13 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
-_LIB = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_SANITIZE=1 builds and loads a copy instrumented with
+# AddressSanitizer and UndefinedBehaviorSanitizer (the process must then have
+# the ASan runtime preloaded; tests/test_sanitizers.py does this).
+_SANITIZE = os.environ.get("KDA_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "libkda_oracle_san.so" if _SANITIZE else "libkda_oracle.so")
+_SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+              "-fno-sanitize-recover=all"]
 
 GATE_LOGDECAY, GATE_SAFE, GATE_SOFTPLUS = 0, 1, 2
 L2_EPS = 1e-6  # [kda.rs] KDA_L2_EPS: the in-kernel q/k normalisation epsilon
@@ -32,8 +38,9 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc into ``oracle/libkda_oracle.so``."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC",
-                               "-shared", "-o", tmp, _SRC, "-lm", "-lpthread"])
+        opt = _SAN_FLAGS if _SANITIZE else ["-O2"]
+        subprocess.check_call(["gcc"] + opt + ["-std=c99", "-D_POSIX_C_SOURCE=200809L", "-fPIC",
+                                               "-shared", "-o", tmp, _SRC, "-lm", "-lpthread"])
         os.replace(tmp, _LIB)
     return _LIB
 

@@ -54,44 +54,78 @@ typedef struct {
 } or_problem;
 
 /* ------------------------------------------------------------------ */
+/* Dense vector / matrix primitives (row-major, K x V matrices S with   */
+/* S[kk * V + vv]), so that the recurrence below reads as its matrix     */
+/* equations.                                                           */
+/* ------------------------------------------------------------------ */
+static double la_dot(int n, const double *x, const double *y) {
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i) acc += x[i] * y[i];
+    return acc;
+}
+
+/* out = a * x (out may be x) */
+static void la_scale(int n, double a, const double *x, double *out) {
+    for (int i = 0; i < n; ++i) out[i] = a * x[i];
+}
+
+/* out = S^T x  (S is K x V, x has K entries, out has V) */
+static void la_tmatvec(int K, int V, const double *S, const double *x, double *out) {
+    for (int vv = 0; vv < V; ++vv) out[vv] = 0.0;
+    for (int kk = 0; kk < K; ++kk)
+        for (int vv = 0; vv < V; ++vv) out[vv] += S[kk * V + vv] * x[kk];
+}
+
+/* S = diag(d) S: row kk of S times d[kk] */
+static void la_diag_rows(int K, int V, const double *d, double *S) {
+    for (int kk = 0; kk < K; ++kk) la_scale(V, d[kk], S + (size_t)kk * V, S + (size_t)kk * V);
+}
+
+/* S = S + a b^T */
+static void la_rank1(int K, int V, const double *a, const double *b, double *S) {
+    for (int kk = 0; kk < K; ++kk)
+        for (int vv = 0; vv < V; ++vv) S[kk * V + vv] += a[kk] * b[vv];
+}
+
+/* ------------------------------------------------------------------ */
 /* Scalar pieces of the prologue                                       */
 /* ------------------------------------------------------------------ */
 
-/* Logistic function; [kda.rs] `sigmoid`. */
+/* Logistic function 1 / (1 + e^-x). */
 static double or_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
-/* Overflow-free log(1+e^x) as max(x,0) + log1p(e^{-|x|}); [kda.rs] `softplus`. */
-static double or_softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+/* softplus(x) = log(1 + e^x) ([kda.rs] `softplus`, which evaluates it in an
+ * overflow-free form).  Here: for x > 0, log(1 + e^x) = x + log(1 + e^-x); for
+ * x <= 0 it is log(1 + e^x) directly; both log1p arguments are in (0, 1]. */
+static double or_softplus(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
 
-/* Row L2 normalisation x * (sum x^2 + eps)^{-1/2}; [kda.rs] `l2norm_rows`
- * with the in-kernel eps constant KDA_L2_EPS = 1e-6. */
+/* x / ||x||_eps with ||x||_eps = sqrt(x . x + eps): the L2 normalisation of
+ * [kda.rs] `l2norm_rows` with the in-kernel eps 1e-6. */
 static void or_l2norm(const double *x, int d, double eps, double *out) {
-    double ss = 0.0;
-    for (int i = 0; i < d; ++i) ss += x[i] * x[i];
-    double inv = 1.0 / sqrt(ss + eps);
-    for (int i = 0; i < d; ++i) out[i] = x[i] * inv;
+    la_scale(d, 1.0 / sqrt(la_dot(d, x, x) + eps), x, out);
 }
 
-/* Per-channel log-decay of head h from the raw gate input x (one token).
- * LOGDECAY: g = x (the decay is passed in log space, [api.py] default path).
- * SAFE:     g = lb * sigmoid(exp(A_log_h) * (x + dt_bias))   ([kda.rs] bounded_gate, Some(lb);
- *                                                           [api.py] safe_gate branch)
- * SOFTPLUS: g = -exp(A_log_h) * softplus(x + dt_bias)     ([kda.rs] bounded_gate, None;
- *                                                           [api.py] unbounded branch)
- * dt_bias is indexed [h*K + c] ([api.py] views it as g.shape[-2:]); NULL means 0. */
+/* Per-channel log-decay of head h from the raw gate input x (one token):
+ * with the pre-activation z = x + dt_bias (dt_bias indexed [h*K + c], NULL
+ * meaning 0, as [api.py] views it with g's trailing shape) and the rate
+ * a = exp(A_log_h),
+ *   LOGDECAY: g = x                       ([api.py] default path: the decay
+ *                                          is passed in log space)
+ *   SAFE:     g = lower_bound * sigma(a z) ([kda.rs] bounded_gate with a bound;
+ *                                          [api.py] safe_gate branch)
+ *   SOFTPLUS: g = -a * softplus(z)        ([kda.rs] bounded_gate without one;
+ *                                          [api.py] unbounded branch) */
 static void or_gate(const or_problem *P, int h, const double *x, double *g) {
-    int K = P->K;
+    const int K = P->K;
     if (P->gate_mode == OR_GATE_LOGDECAY) {
-        for (int c = 0; c < K; ++c) g[c] = x[c];
+        memcpy(g, x, sizeof(double) * K);
         return;
     }
-    double rate = exp(P->A_log[h]);
+    const double a = exp(P->A_log[h]);
+    const double *bias = P->dt_bias ? P->dt_bias + (size_t)h * K : NULL;
     for (int c = 0; c < K; ++c) {
-        double z = x[c] + (P->dt_bias ? P->dt_bias[h * K + c] : 0.0);
-        if (P->gate_mode == OR_GATE_SAFE)
-            g[c] = P->lower_bound * or_sigmoid(rate * z);
-        else
-            g[c] = -rate * or_softplus(z);
+        const double z = x[c] + (bias ? bias[c] : 0.0);
+        g[c] = P->gate_mode == OR_GATE_SAFE ? P->lower_bound * or_sigmoid(a * z) : -a * or_softplus(z);
     }
 }
 
@@ -126,35 +160,28 @@ static void or_prologue(const or_problem *P, int64_t row, int h, double *qh, dou
 }
 
 /* ------------------------------------------------------------------ */
-/* One step of the recurrence ([kda.rs] module doc "Recurrence" and     */
-/* kda_recurrent_step):                                                */
-/*   S~ = diag(exp(g)) S          decay acts on the key axis (rows)    */
-/*   p  = S~^T k                                                         */
-/*   d  = beta * (v - p)                                                 */
-/*   S  = S~ + k d^T                                                     */
-/*   o  = scale * S^T q           read after the write                  */
+/* One token of the recurrence, written as the matrix equations of the  */
+/* [kda.rs] module doc "Recurrence" (its kda_recurrent_step evaluates   */
+/* the same step):                                                      */
+/*   S~ = diag(exp(g)) S        the decay acts on the key axis (rows)   */
+/*   d  = beta (v - S~^T k)     the delta against the prediction for k  */
+/*   S  = S~ + k d^T            the rank-1 write                         */
+/*   o  = scale S^T q           the read-out after the write            */
+/* p receives S~^T k and d the delta (both kept for the backward).      */
 /* ------------------------------------------------------------------ */
 static void or_step(int K, int V, double *S, const double *qh, const double *kh,
                     const double *vt, double b, const double *gt, double scale,
                     double *p, double *d, double *o) {
-    for (int kk = 0; kk < K; ++kk) {
-        double e = exp(gt[kk]);
-        for (int vv = 0; vv < V; ++vv) S[kk * V + vv] *= e;
-    }
-    for (int vv = 0; vv < V; ++vv) {
-        double acc = 0.0;
-        for (int kk = 0; kk < K; ++kk) acc += S[kk * V + vv] * kh[kk];
-        p[vv] = acc;
-        d[vv] = b * (vt[vv] - acc);
-    }
-    for (int kk = 0; kk < K; ++kk)
-        for (int vv = 0; vv < V; ++vv) S[kk * V + vv] += kh[kk] * d[vv];
+    double *decay = (double *)malloc(sizeof(double) * K);
+    for (int kk = 0; kk < K; ++kk) decay[kk] = exp(gt[kk]);
+    la_diag_rows(K, V, decay, S);
+    free(decay);
+    la_tmatvec(K, V, S, kh, p);
+    for (int vv = 0; vv < V; ++vv) d[vv] = b * (vt[vv] - p[vv]);
+    la_rank1(K, V, kh, d, S);
     if (o) {
-        for (int vv = 0; vv < V; ++vv) {
-            double acc = 0.0;
-            for (int kk = 0; kk < K; ++kk) acc += S[kk * V + vv] * qh[kk];
-            o[vv] = scale * acc;
-        }
+        la_tmatvec(K, V, S, qh, o);
+        la_scale(V, scale, o, o);
     }
 }
 
@@ -604,6 +631,23 @@ int or_chunk_bwd(const or_problem *P, const double *dO, const double *dS_final, 
 /* conv_update: shift the window left by one (slot 0 leaves), write x  */
 /* into the last slot, y = SiLU(sum_j w[c,j] * window[c,j]).            */
 /* ------------------------------------------------------------------ */
+/* SiLU(x) = x sigma(x). */
+static double or_silu(double x) { return x * or_sigmoid(x); }
+
+/* The causal depthwise convolution at the newest token x of one channel:
+ * sum_j w[j] u[j] over the W most recent inputs u, oldest first (u = the
+ * W - 1 newest entries of the window `win`, then x): [kda.rs] conv_update's
+ * output, no bias. */
+static double or_conv_tap(int W, const double *w, const double *win, double x) {
+    return la_dot(W - 1, w, win + 1) + w[W - 1] * x;
+}
+
+/* The window after x enters: the oldest entry leaves, x becomes the newest. */
+static void or_window_push(int W, double *win, double x) {
+    memmove(win, win + 1, sizeof(double) * (W - 1));
+    win[W - 1] = x;
+}
+
 typedef struct {
     int N, H, D, W;
     const double *x;       /* [N, 3*H*D] */
@@ -626,12 +670,9 @@ static void or_decode_seq(void *vctx, int n) {
     const double *xn = Dp->x + (size_t)n * CH;
     double *cs = Dp->conv_state + (size_t)n * CH * W;
     for (int c = 0; c < CH; ++c) {
-        double *row = cs + (size_t)c * W;
-        for (int j = 0; j + 1 < W; ++j) row[j] = row[j + 1];
-        row[W - 1] = xn[c];
-        double acc = 0.0;
-        for (int j = 0; j < W; ++j) acc += Dp->conv_w[(size_t)c * W + j] * row[j];
-        y[c] = acc * or_sigmoid(acc);
+        double *win = cs + (size_t)c * W;  /* the last W inputs, oldest first */
+        y[c] = or_silu(or_conv_tap(W, Dp->conv_w + (size_t)c * W, win, xn[c]));
+        or_window_push(W, win, xn[c]);
     }
     /* the recurrent step on the post-conv [q|k|v] */
     or_problem P;
@@ -672,26 +713,25 @@ int or_decode_step(or_decode *Dp, int threads) {
 /* ------------------------------------------------------------------ */
 int or_conv_prefill(int B, int T, int C, int W, const int32_t *cu, int N, const double *x,
                     const double *conv_w, double *conv_state, double *y) {
-    double *win = (double *)malloc(sizeof(double) * W);
+    /* Per sequence and channel, the inputs extended on the left by the W
+     * entries of the incoming window: u = [window ; x_0 .. x_{L-1}], so that
+     * y_t = SiLU(sum_j w[j] u[t + 1 + j]) and the outgoing window is the last
+     * W entries of u. */
     int nseq = cu ? N : B;
     for (int n = 0; n < nseq; ++n) {
         long start = cu ? cu[n] : (long)n * T;
         long len = cu ? (long)cu[n + 1] - cu[n] : T;
+        double *u = (double *)malloc(sizeof(double) * (size_t)(W + len));
         for (int c = 0; c < C; ++c) {
             double *st = conv_state ? conv_state + ((size_t)n * C + c) * W : NULL;
-            for (int j = 0; j < W; ++j) win[j] = st ? st[j] : 0.0;
-            for (long t = 0; t < len; ++t) {
-                for (int j = 0; j + 1 < W; ++j) win[j] = win[j + 1];
-                win[W - 1] = x[(size_t)(start + t) * C + c];
-                double acc = 0.0;
-                for (int j = 0; j < W; ++j) acc += conv_w[(size_t)c * W + j] * win[j];
-                y[(size_t)(start + t) * C + c] = acc * or_sigmoid(acc);
-            }
-            if (st)
-                for (int j = 0; j < W; ++j) st[j] = win[j];
+            for (int j = 0; j < W; ++j) u[j] = st ? st[j] : 0.0;
+            for (long t = 0; t < len; ++t) u[W + t] = x[(size_t)(start + t) * C + c];
+            for (long t = 0; t < len; ++t)
+                y[(size_t)(start + t) * C + c] = or_silu(la_dot(W, conv_w + (size_t)c * W, u + t + 1));
+            if (st) memcpy(st, u + len, sizeof(double) * W);
         }
+        free(u);
     }
-    free(win);
     return 0;
 }
 
@@ -706,10 +746,10 @@ int or_conv_prefill(int B, int T, int C, int W, const int32_t *cu, int N, const 
 int or_output_gate(int64_t n_vec, int V, const double *o, const double *g, double eps, double *y) {
     for (int64_t i = 0; i < n_vec; ++i) {
         const double *oi = o + i * V, *gi = g + i * V;
-        double ss = 0.0;
-        for (int v = 0; v < V; ++v) ss += oi[v] * oi[v];
-        const double r = 1.0 / sqrt(ss / V + eps);
-        for (int v = 0; v < V; ++v) y[i * V + v] = or_sigmoid(gi[v]) * oi[v] * r;
+        double *yi = y + i * V;
+        /* RMS normalisation of the head's vector, then the elementwise gate */
+        la_scale(V, 1.0 / sqrt(la_dot(V, oi, oi) / V + eps), oi, yi);
+        for (int v = 0; v < V; ++v) yi[v] *= or_sigmoid(gi[v]);
     }
     return 0;
 }
