@@ -131,6 +131,19 @@ typedef struct {
      * the two calls the caller keeps the workspace and every input unchanged;
      * the library cannot check this. */
     int keep_for_backward;
+    /* Fused full-rank output gate (forward only; the "atlas_core/kimi_k3/kda.rs"
+     * page, full_rank_output_gate).  With out_gate given, o receives, per row
+     * and head, y = sigmoid(out_gate) * o / sqrt(mean_v(o^2) + eps) over the
+     * head's V values -- kda_output_gate applied to the output -- computed in
+     * the state pass before the row is stored, so that o never makes a round
+     * trip through memory.  out_gate is [rows, H, V] in out_gate_dtype,
+     * 16-byte aligned.  Inference only: keep_for_backward must be 0 and
+     * kda_chunk_bwd rejects a set out_gate (KDA_ERR_INVALID_ARG); training
+     * calls the forward without it and kda_output_gate / kda_output_gate_bwd.
+     * The state pass then runs one workgroup per (sequence, head). */
+    const void *out_gate;     /* [rows, H, V] gate input, or NULL (o is the plain output) */
+    int out_gate_dtype;       /* kda_dtype of out_gate */
+    float out_gate_eps;       /* NaN means 1e-5; must be >= 0 */
 } kda_chunk_args;
 
 /* Gradients for kda_chunk_bwd.  dq, dk, dv are in qkv_dtype; the others fp32.

@@ -102,6 +102,20 @@ def _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state, output_f
     return a, (B, T, H, K, V, N, dev)
 
 
+def _set_out_gate(a, out_gate, out_gate_eps, B, T, H, V, dev):
+    """The fused full-rank output gate of the forward (kda_chunk_args.out_gate)."""
+    a.out_gate_eps = float("nan") if out_gate_eps is None else float(out_gate_eps)
+    if out_gate is None:
+        return
+    if tuple(out_gate.shape) != (B, T, H, V):
+        raise ValueError(f"out_gate must be [{B}, {T}, {H}, {V}]")
+    if out_gate.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_gate must be float32 or bfloat16")
+    _need(out_gate, "out_gate", None, dev)
+    a.out_gate = _ptr(out_gate)
+    a.out_gate_dtype = _lib.KDA_BF16 if out_gate.dtype == torch.bfloat16 else _lib.KDA_F32
+
+
 def _check_grad_shapes(dO, d_final_state, B, T, H, K, V, N):
     if dO is None or tuple(dO.shape) != (B, T, H, V):
         raise ValueError(f"dO must be [{B}, {T}, {H}, {V}]")
@@ -123,11 +137,14 @@ def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial
               output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
               use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
               cu_seqlens=None, gate_mode=None, workspace=None, out=None, keep_for_backward=False,
-              final_state_out=None):
+              final_state_out=None, out_gate=None, out_gate_eps=None):
     """Chunked KDA forward (kda_chunk_fwd).  Returns (o, final_state or None).
 
     out ([B, T, H, V], q's dtype) and final_state_out ([N, H, K, V], float32)
-    are optional preallocated outputs.
+    are optional preallocated outputs.  With out_gate ([B, T, H, V], float32
+    or bfloat16) the returned o is the full-rank output gate of the output,
+    sigmoid(out_gate) * o / sqrt(mean_V(o^2) + eps) per head (eps default
+    1e-5), computed in the forward's state pass (inference only).
 
     keep_for_backward=True also stores in ``workspace`` what the backward would
     recompute; pass the same workspace, unchanged inputs and
@@ -139,6 +156,7 @@ def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial
     if keep_for_backward and workspace is None:
         raise ValueError("keep_for_backward needs a caller-owned workspace (chunk_bwd_workspace_bytes)")
     a.keep_for_backward = int(bool(keep_for_backward))
+    _set_out_gate(a, out_gate, out_gate_eps, B, T, H, V, dev)
     lib = _lib.load()
     o = out if out is not None else torch.empty(B, T, H, V, dtype=q.dtype, device=dev)
     _need(o, "out", q.dtype, dev)
@@ -162,7 +180,8 @@ def chunk_kda(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial
 def chunk_kda_noalloc(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None, initial_state=None,
                       output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
                       use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
-                      cu_seqlens=None, gate_mode=None, out=None, final_state_out=None):
+                      cu_seqlens=None, gate_mode=None, out=None, final_state_out=None, out_gate=None,
+                      out_gate_eps=None):
     """kda_chunk_fwd_noalloc: the chunked forward with its workspace in the
     library's own device array (no device allocation by the library).  With
     ``out`` and (if requested) ``final_state_out`` given, this call allocates
@@ -172,6 +191,7 @@ def chunk_kda_noalloc(q, k, v, g, beta, *, A_log=None, dt_bias=None, scale=None,
     a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
                                              output_final_state, use_qk_l2norm_in_kernel, gm,
                                              use_beta_sigmoid_in_kernel, lower_bound, chunk_size, cu_seqlens)
+    _set_out_gate(a, out_gate, out_gate_eps, B, T, H, V, dev)
     lib = _lib.load()
     o = out if out is not None else torch.empty(B, T, H, V, dtype=q.dtype, device=dev)
     _need(o, "out", q.dtype, dev)
@@ -446,7 +466,7 @@ class ChunkOp:
                  output_final_state=False, use_qk_l2norm_in_kernel=False, use_gate_in_kernel=False,
                  use_beta_sigmoid_in_kernel=False, safe_gate=False, lower_bound=None, chunk_size=64,
                  cu_seqlens=None, gate_mode=None, dO=None, d_final_state=None, need_d_initial_state=True,
-                 keep_for_backward=False):
+                 keep_for_backward=False, out_gate=None, out_gate_eps=None):
         gm = _gate_mode(use_gate_in_kernel, safe_gate, gate_mode)
         self._keep = [q, k, v, g, beta, A_log, dt_bias, initial_state, cu_seqlens, dO, d_final_state]
         a, (B, T, H, K, V, N, dev) = _chunk_args(q, k, v, g, beta, A_log, dt_bias, scale, initial_state,
@@ -454,7 +474,11 @@ class ChunkOp:
                                                  use_beta_sigmoid_in_kernel, lower_bound, chunk_size, cu_seqlens)
         if keep_for_backward and dO is None:
             raise ValueError("keep_for_backward needs dO")
+        if out_gate is not None and dO is not None:
+            raise ValueError("the fused output gate is a forward-only (inference) epilogue")
         a.keep_for_backward = int(bool(keep_for_backward))
+        self._keep.append(out_gate)
+        _set_out_gate(a, out_gate, out_gate_eps, B, T, H, V, dev)
         lib = _lib.load()
         self.lib = lib
         self.o = torch.empty(B, T, H, V, dtype=q.dtype, device=dev)

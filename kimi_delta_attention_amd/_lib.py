@@ -37,6 +37,7 @@ class ChunkArgs(ctypes.Structure):
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("stream", _vp),
         ("keep_for_backward", ctypes.c_int),
+        ("out_gate", _vp), ("out_gate_dtype", ctypes.c_int), ("out_gate_eps", ctypes.c_float),
     ]
 
 

@@ -68,6 +68,16 @@ kda_status check_chunk(const kda_chunk_args* a, kda::ChunkParams& p, bool forwar
     const int64_t bound = a->cu_seqlens ? nc_dense + N : nc_dense * N;
     if (bound * a->H > INT32_MAX / 2) return KDA_ERR_UNSUPPORTED;
     p.keep = a->keep_for_backward != 0;
+    if (a->out_gate) {
+        // the fused output gate is an inference epilogue of the forward
+        if (!forward || p.keep) return KDA_ERR_INVALID_ARG;
+        if (a->out_gate_dtype != KDA_F32 && a->out_gate_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+        if (!(std::isnan(a->out_gate_eps) || a->out_gate_eps >= 0.f)) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(a->out_gate)) return KDA_ERR_INVALID_ARG;
+        p.out_gate = a->out_gate;
+        p.out_gate_bf16 = a->out_gate_dtype == KDA_BF16;
+        p.out_gate_eps = std::isnan(a->out_gate_eps) ? kGateEpsDefault : a->out_gate_eps;
+    }
     p.max_chunks = static_cast<int>(nc_dense);
     p.total_chunks_bound = static_cast<int>(bound);
     return KDA_OK;

@@ -1988,15 +1988,6 @@ __device__ __forceinline__ f32x4 mma16_f32_rb_acc(const float* A, int lda, int m
     return acc;
 }
 
-// Sum over each row of 16 lanes, in every lane of the row (DPP row rotations).
-__device__ __forceinline__ float row16_sum(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xf, 0xf, false));
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xf, 0xf, false));
-    return v;
-}
-
 constexpr int kKlocW8Threads = 512;
 
 __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(ChunkParams p, ChunkGrads gr,

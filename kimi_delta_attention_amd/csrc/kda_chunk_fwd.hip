@@ -42,6 +42,28 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
             hipLaunchKernelGGL((chunk_prep_kernel<K, BF, KEEP, V>), dim3(prep_grid<K, BF, KEEP, V>(nblk)),
                                dim3(prep_threads(K)), 0, st, p, chunk_off, prep, sb, nblk);
     }
+    if ((stage < 0 || stage == 1) && p.out_gate) {
+        // the output gate fused into the state pass: one workgroup per head
+        if constexpr (!KEEP) {
+            const int chains = p.N * p.H;
+            if constexpr (K == 128 && V == 128 && BF) {
+                if (chains > 0) {
+                    if (p.out_gate_bf16)
+                        hipLaunchKernelGGL((chunk_state_fwd_gate_kernel<true>), dim3(chains), dim3(kGateStateThreads),
+                                           0, st, p, chunk_off, prep, sb);
+                    else
+                        hipLaunchKernelGGL((chunk_state_fwd_gate_kernel<false>), dim3(chains),
+                                           dim3(kGateStateThreads), 0, st, p, chunk_off, prep, sb);
+                }
+            } else {
+                const int grid = chain_grid(chains, 1);
+                if (grid > 0)
+                    hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, V, BF, false, true, kThreads, true>), dim3(grid),
+                                       dim3(kThreads), 0, st, p, chunk_off, prep, sb);
+            }
+        }
+        return hipGetLastError();
+    }
     if (stage < 0 || stage == 1) {
         // few chains (no more workgroups than CUs): 8 waves per chain shorten
         // each chunk step; otherwise 4 waves let two chains share a CU

@@ -870,7 +870,12 @@ struct Seg {
 // STORE writes each chunk's entry state (BwdExtra::kS, transposed, element type ET) for
 // the backward; WRITE_O computes and stores the output.  The next chunk's
 // operands are prefetched into registers while the current chunk computes.
-template <int K, int V, int BV, bool BF, bool STORE, bool WRITE_O, int NT = kThreads>
+//
+// GATE (with BV = V and 4 waves, so that a wave holds whole output rows)
+// applies the full-rank output gate of the "atlas_core/kimi_k3/kda.rs" page
+// (full_rank_output_gate) to each output row before it is stored: y =
+// sigmoid(g) o / sqrt(mean_v(o^2) + eps), g the gate input p.out_gate.
+template <int K, int V, int BV, bool BF, bool STORE, bool WRITE_O, int NT = kThreads, bool GATE = false>
 __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, const int32_t* chunk_off,
                                                              uint8_t* ws, int64_t slot_bytes) {
     using MM = Mma<BF>;
@@ -888,6 +893,8 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
     constexpr int TW = (NCT + CSTEP - 1) / CSTEP;  // column tiles per wave
     constexpr int NVB = V / BV;
     constexpr int QR = WRITE_O ? kChunk : 0;  // rows of QE ahead of W in QW
+    static_assert(!GATE || (BV == V && NT == kThreads && WRITE_O && !STORE),
+                  "the gated output needs whole rows per wave");
 
     __shared__ __attribute__((aligned(16))) ET QW[QR + kChunk][LDK];   // [QE;] W
     __shared__ __attribute__((aligned(16))) ET KDt[K][LDC];
@@ -1014,6 +1021,16 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
                 }
             }
             const int rbase = jc * kChunk;
+            float rinv[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (GATE) {  // each wave holds its 16 rows' whole V values
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int m = 0; m < TW; ++m) ss += oq[m][r] * oq[m][r];
+                    rinv[r] = rsqrtf(row16_sum(ss) * (1.0f / V) + p.out_gate_eps);
+                }
+            }
 #pragma unroll
             for (int m = 0; m < TW; ++m) {
                 const int ct = cw + CSTEP * m;
@@ -1021,9 +1038,16 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int row = 16 * rw + 4 * (lane >> 4) + r;
-                        if (rbase + row < len)
-                            Elem<IT>::store(og, ((start + rbase + row) * H + h) * V + v0 + 16 * ct + (lane & 15),
-                                            oq[m][r]);
+                        if (rbase + row < len) {
+                            const int64_t oi = ((start + rbase + row) * H + h) * V + v0 + 16 * ct + (lane & 15);
+                            float y = oq[m][r];
+                            if constexpr (GATE) {
+                                const float gi = p.out_gate_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.out_gate)[oi])
+                                                                 : static_cast<const float*>(p.out_gate)[oi];
+                                y = sigmoidf_(gi) * y * rinv[r];
+                            }
+                            Elem<IT>::store(og, oi, y);
+                        }
                     }
             }
         }
@@ -1351,6 +1375,292 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
         for (int t = 0; t < 8; ++t)
 #pragma unroll
             for (int r = 0; r < 4; ++r) p.ht[sbase + (16 * t + 4 * lg + r) * V + v0 + 16 * w + m] = S[t][r];
+    }
+}
+
+// ------------------------------------------------------------------ state pass with the output gate
+// Forward state pass for K = V = 128 in bf16 that applies the full-rank output
+// gate of the "atlas_core/kimi_k3/kda.rs" page (full_rank_output_gate: per
+// head, y = sigmoid(g) * o / sqrt(mean(o^2) + eps) over the head's V values) to
+// every output row before it leaves the chip, so that o never makes a round
+// trip through HBM.  The norm of a row needs all 128 value columns, so one
+// workgroup owns a whole head (sequence, head): 4 waves, wave w the 32 value
+// columns 32 w .. 32 w + 31 of the fp32 state (two 16-column strips over all
+// 128 key rows, in MFMA accumulators, as the consumers of
+// chunk_state_fwd_pc_kernel), so that every operand fragment read from LDS
+// serves two strips.  There are no producer waves: each wave issues its share
+// of the next chunk's direct global -> LDS copies (they hold no registers) at
+// the start of a step and waits for them at its end, and requests the next
+// chunk's gate inputs into registers.  Per chunk step:
+//   O = QE S + MS D  (D = U - W S),  s_i = sum_v O_iv^2 over the four waves
+//   (row sums in registers, exchanged through LDS), y = sigmoid(g) O / sqrt(s / 128 + eps),
+//   S' = GC * S + KD^T D.
+// Inference only: no entry state is stored for a backward.
+struct StateGateFwd {
+    static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oU = 57344, oGC = 73728;
+    static constexpr int kBuf = 74240;  // one chunk's operand tiles (U: [64][128] swizzled)
+};
+constexpr int kGateStateThreads = 256;
+
+template <bool GBF>  // gate input in bf16 (else fp32)
+__global__ __launch_bounds__(kGateStateThreads) void chunk_state_fwd_gate_kernel(ChunkParams p,
+                                                                                  const int32_t* chunk_off,
+                                                                                  uint8_t* ws, int64_t slot_bytes) {
+    using Z = StateGateFwd;
+    using L = PrepLayout<128, true>;
+    using GT = typename std::conditional<GBF, uint16_t, float>::type;
+    constexpr int K = 128, V = 128, NWV = kGateStateThreads / 64;
+    // 128-byte lines of one chunk's operands (QE, W, KD, MS, U, GC) warmed in
+    // L2 kWarmAhead chunks ahead, NWARM loads per lane
+    constexpr int NL = 384 + 64 + 128 + 4;
+    constexpr int NWARM = (NL + kGateStateThreads - 1) / kGateStateThreads;
+    __shared__ __attribute__((aligned(1024))) uint8_t smb[2 * Z::kBuf];
+    __shared__ __attribute__((aligned(16))) float red[kChunk][NWV];  // per row: each wave's sum of squares
+    __shared__ __attribute__((aligned(256))) uint8_t smj[256];
+
+    const int chain = blockIdx.x;
+    if (chain >= p.N * p.H) return;
+    const int H = p.H;
+    const int n = chain / H, h = chain % H;
+    int64_t start;
+    int len;
+    seq_bounds(p, n, start, len);
+    const int nc = chain_chunks(p, chunk_off, n, len);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int lg = lane >> 4, m = lane & 15;
+    const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
+    auto slot = [&](int jc) { return ws + ((slot0 + jc) * H + h) * slot_bytes; };
+    const GT* gate = static_cast<const GT*>(p.out_gate);
+    uint16_t* og = static_cast<uint16_t*>(p.o);
+    // this lane's value columns: strip j of the wave, column 16 (2 w + j) + m
+
+    // ---- this wave's share of chunk jc's direct copies into buffer jc & 1:
+    // pieces w, w + 4, w + 8, w + 12 of W, KD, QE and U, pieces w and w + 4 of
+    // MS, and (wave 0) GC
+    auto fetch = [&](int jc) {
+        const uint8_t* base = slot(jc);
+        uint8_t* buf = smb + (jc & 1) * Z::kBuf;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+            const int q = w + NWV * qq;
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kW), K, buf + Z::oW, q, lane);
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kKD), K, buf + Z::oKD, q, lane);
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kQE), K, buf + Z::oQE, q, lane);
+            dma_tile_piece<128>(reinterpret_cast<const uint16_t*>(base + L::kU), V, buf + Z::oU, q, lane);
+        }
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq)
+            dma_tile_piece<64>(reinterpret_cast<const uint16_t*>(base + L::kMS), kChunk, buf + Z::oMS, w + NWV * qq,
+                               lane);
+        if (w == 0 && lane < 32) dma16(base + L::kGC + 16 * lane, buf + Z::oGC);
+    };
+    // ---- one 4-byte copy per 128-byte line of chunk jc's operands (L2 warm-up)
+    auto warm = [&](int jc) {
+        const uint8_t* base = slot(jc);
+#pragma unroll
+        for (int i = 0; i < NWARM; ++i) {
+            int l = tid + kGateStateThreads * i;
+            l = l < NL ? l : NL - 1;
+            const uint8_t* a;
+            if (l < 384) a = base + L::kQE + 128 * l;  // QE, W, KD are contiguous
+            else if (l < 448) a = base + L::kMS + 128 * (l - 384);
+            else if (l < 576) a = base + L::kU + 128 * (l - 448);
+            else a = base + L::kGC + 128 * (l - 576);
+            __builtin_amdgcn_global_load_lds(a, (lds_void_t*)smj, 4, 0, 0);
+        }
+    };
+    // ---- chunk jc's gate inputs of this lane's 2 x 16 outputs (rows 16 rt +
+    // 4 lg + r, strips j); rows past the end read the last row again (their
+    // results are not stored)
+    auto gload = [&](int jc, GT (&gr)[2][4][4]) {
+        const int64_t row0 = start + static_cast<int64_t>(jc) * kChunk;
+        const int rows = min(kChunk, len - jc * kChunk);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * rt + 4 * lg + r;
+                const int ic = i < rows ? i : rows - 1;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) gr[j][rt][r] = gate[((row0 + ic) * H + h) * V + 16 * (2 * w + j) + m];
+            }
+    };
+
+    // ---- state strips: tile t = key rows 16 t + 4 lg + r, column 16 (2 w + j) + m
+    f32x4 S[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[j][t][r] = p.h0 ? p.h0[sbase + (16 * t + 4 * lg + r) * V + 16 * (2 * w + j) + m] : 0.f;
+        }
+    auto rdA = [](const uint8_t* tile, int off) { return *reinterpret_cast<const bf16x8*>(tile + off); };
+    auto rdT = [](const uint8_t* tile, int off0, int off1) {
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off0));
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off1));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+
+    GT gcur[2][4][4];
+    if (nc > 0) {
+        gload(0, gcur);
+        fetch(0);
+    }
+    wait_vmem_all();
+    __syncthreads();
+    for (int jc = 0; jc < nc; ++jc) {
+        // per-lane LDS offsets from an opaque copy of the lane id, so that they
+        // are recomputed per step rather than held in registers for the loop
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int mm = ln & 15, gg = ln >> 4;
+        auto offA = [&](int s) { return swz_off<128>(mm, 32 * s + 8 * gg); };
+        auto offM = [&](int s) { return swz_off<64>(mm, 32 * s + 8 * gg); };
+        auto offT = [&](int t, int hh) { return swz_off<128>(8 * gg + 4 * hh + (mm >> 2), 16 * t + 4 * (mm & 3)); };
+        const uint8_t* buf = smb + (jc & 1) * Z::kBuf;
+        const int64_t row0 = start + static_cast<int64_t>(jc) * kChunk;
+        const int rows = min(kChunk, len - jc * kChunk);
+        // the next chunk's gate inputs and operand copies, and the L2 warm-up
+        GT gnext[2][4][4];
+        if (jc + 1 < nc) {
+            gload(jc + 1, gnext);
+            fetch(jc + 1);
+        }
+        warm(jc + kWarmAhead < nc ? jc + kWarmAhead : jc);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // W S and QE S for both strips, one k-step of fragments ahead
+        bf16x8 fa[2][8];
+        auto load_a = [&](int s, bf16x8* f) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                f[rt] = rdA(buf + Z::oW + 4096 * rt, offA(s));
+                f[4 + rt] = rdA(buf + Z::oQE + 4096 * rt, offA(s));
+            }
+        };
+        f32x4 ws_[2][4], o[2][4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) ws_[j][rt] = o[j][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        load_a(0, fa[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            if (s < 3) load_a(s + 1, fa[(s + 1) & 1]);
+            const bf16x8 Sb0 = frag_acc_nat(S[0][2 * s], S[0][2 * s + 1]);
+            const bf16x8 Sb1 = frag_acc_nat(S[1][2 * s], S[1][2 * s + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                ws_[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][rt], Sb0, ws_[0][rt], 0, 0, 0);
+                ws_[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][rt], Sb1, ws_[1][rt], 0, 0, 0);
+                o[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][4 + rt], Sb0, o[0][rt], 0, 0, 0);
+                o[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[s & 1][4 + rt], Sb1, o[1][rt], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // D = U - W S;  O += MS D (MS lower triangular)
+        bf16x8 Db[2][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 d[4];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const bf16x4_t u = tr4<128>(buf + Z::oU, 16 * rt + 4 * gg, 16 * (2 * w + j), ln);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) d[rt][r] = static_cast<float>(u[r]) - ws_[j][rt][r];
+            }
+            Db[j][0] = frag_acc_nat(d[0], d[1]);
+            Db[j][1] = frag_acc_nat(d[2], d[3]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int s = 0; s <= (rt >> 1); ++s) {
+                const bf16x8 fm = rdA(buf + Z::oMS + 2048 * rt, offM(s));
+                o[0][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fm, Db[0][s], o[0][rt], 0, 0, 0);
+                o[1][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fm, Db[1][s], o[1][rt], 0, 0, 0);
+            }
+        // the rows' sums of squares over this wave's 32 columns; lane m records
+        // row 16 (m / 4) + 4 lg + m % 4 of its lane group
+        float mine = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ss = row16_sum(o[0][rt][r] * o[0][rt][r] + o[1][rt][r] * o[1][rt][r]);
+                mine = (m == 4 * rt + r) ? ss : mine;
+            }
+        red[16 * (m >> 2) + 4 * lg + (m & 3)][w] = mine;
+        barrier_lds();  // every wave's sums are in red
+        float rinv;
+        {
+            const float4 a4 = *reinterpret_cast<const float4*>(&red[16 * (m >> 2) + 4 * lg + (m & 3)][0]);
+            rinv = rsqrtf(((a4.x + a4.y) + (a4.z + a4.w)) * (1.0f / V) + p.out_gate_eps);
+        }
+        uint16_t yv[2][4][4];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ri = __shfl(rinv, 16 * lg + 4 * rt + r, 64);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float gi = GBF ? bf16_bits_to_f32(static_cast<uint16_t>(gcur[j][rt][r]))
+                                         : static_cast<float>(gcur[j][rt][r]);
+                    yv[j][rt][r] = f32_to_bf16_bits(sigmoidf_(gi) * o[j][rt][r] * ri);
+                }
+            }
+        // S' = GC S + KD^T D: each KD^T fragment serves both strips
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 g = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * gg));
+            bf16x8 fk[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) fk[s] = rdT(buf + Z::oKD + 8192 * s, offT(t, 0), offT(t, 1));
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[j][t][r] *= g[r];
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    S[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fk[s], Db[j][s], S[j][t], 0, 0, 0);
+            }
+        }
+        // this step's copies are done once at most its warm-up loads are
+        // outstanding (one in-order counter: the next chunk's gate loads and
+        // copies were issued before them); the row stores go out after that
+        // wait, so that no step waits for a store
+        wait_vmem<NWARM>();
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * rt + 4 * lg + r;
+                if (i < rows) {
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) og[((row0 + i) * H + h) * V + 16 * (2 * w + j) + m] = yv[j][rt][r];
+                }
+            }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) gcur[j][rt][r] = gnext[j][rt][r];
+        barrier_lds();
+    }
+    if (p.ht) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p.ht[sbase + (16 * t + 4 * lg + r) * V + 16 * (2 * w + j) + m] = S[j][t][r];
     }
 }
 

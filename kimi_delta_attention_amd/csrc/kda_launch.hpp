@@ -95,6 +95,9 @@ struct ChunkParams {
     int max_chunks;            // upper bound of chunks per sequence
     int total_chunks_bound;    // upper bound of sum over sequences of chunks
     bool keep;                 // forward writes the backward's slot layout; backward reuses it
+    const void* out_gate;      // [rows, H, V] gate input of the fused output gate, or nullptr
+    bool out_gate_bf16;        // its element type (bf16, else fp32)
+    float out_gate_eps;
 };
 
 struct ChunkGrads {

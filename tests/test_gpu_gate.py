@@ -1,5 +1,6 @@
 """GPU parity of the full-rank output gate (kda_output_gate, its reverse mode,
 and the gate fused into kda_recurrent_step) against the CPU oracle."""
+import numpy as np
 import pytest
 import torch
 
@@ -106,3 +107,91 @@ def test_decode_with_fused_output_gate(D, x_dtype):
         check(f"y[{t}]", y, want, TOL_F32)
     check("state", st, ost, TOL_F32)
     check("conv_state", cs, ocs, TOL_F32)
+
+
+def _fused(w, gate, eps, **over):
+    B, T, H, K = w["q"].shape
+    V = w["v"].shape[-1]
+    N = B if w["cu_seqlens"] is None else len(w["cu_seqlens"]) - 1
+    kw = dict(A_log=dev(w["A_log"]), dt_bias=dev(w["dt_bias"]), scale=w["scale"],
+              initial_state=dev(w["initial_state"]), output_final_state=True,
+              use_qk_l2norm_in_kernel=w["use_qk_l2norm"], gate_mode=w["gate_mode"],
+              use_beta_sigmoid_in_kernel=w["use_beta_sigmoid"], lower_bound=w["lower_bound"],
+              cu_seqlens=dev(w["cu_seqlens"]), out_gate=dev(gate), out_gate_eps=eps,
+              out=nan_full((B, T, H, V), w["q"].dtype), final_state_out=nan_full((N, H, K, V), torch.float32))
+    kw.update(over)
+    y, fs = kda.chunk_kda(dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["g"]), dev(w["beta"]), **kw)
+    torch.cuda.synchronize()
+    oo, ofs = oracle.chunk_fwd(w["q"], w["k"], w["v"], w["g"], w["beta"], A_log=w["A_log"], dt_bias=w["dt_bias"],
+                               scale=w["scale"], initial_state=w["initial_state"], use_qk_l2norm=w["use_qk_l2norm"],
+                               gate_mode=w["gate_mode"], use_beta_sigmoid=w["use_beta_sigmoid"],
+                               lower_bound=w["lower_bound"], cu_seqlens=w["cu_seqlens"])
+    want = oracle.output_gate(oo, gate, eps=1e-5 if eps is None else eps)
+    # the same kernels' plain output, gated by the oracle: isolates the epilogue
+    kw_plain = dict(kw)
+    for key in ("out_gate", "out_gate_eps", "out", "final_state_out"):
+        kw_plain.pop(key)
+    o_plain, _ = kda.chunk_kda(dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["g"]), dev(w["beta"]), **kw_plain)
+    torch.cuda.synchronize()
+    on_plain = oracle.output_gate(o_plain.float().cpu().double().numpy(), gate, eps=1e-5 if eps is None else eps)
+    return y, fs, want, ofs, on_plain, oo
+
+
+def _check_gated(tag, y, want, on_plain, oo, tol):
+    """The gated output against (1) the oracle's gate of the same kernels' plain
+    output, elementwise at tol, and (2) the oracle's gate of the oracle's
+    forward, with the forward's bar carried through the gate: the gate divides
+    row i by rms_i(o), so an error e in o becomes at most about 2 e / rms_i in y;
+    |y - y_ref| * rms_i(o_ref) / 2 must stay within tol * max|o_ref|."""
+    check(f"{tag} y vs gate(plain o)", y, on_plain, tol)
+    got = y.float().cpu().double().numpy()
+    assert np.isfinite(got).all(), f"{tag}: non-finite values"
+    rms = np.sqrt((oo ** 2).mean(axis=-1, keepdims=True) + 1e-5)
+    scale = max(float(np.abs(oo).max()), 1e-6)
+    md = float((np.abs(got - want) * rms / 2.0).max())
+    print(f"  {tag} y vs gate(oracle o), forward-equivalent: rel {md / scale:.3e} (tol {tol:.0e})", flush=True)
+    assert md <= tol * scale, f"{tag}: forward-equivalent error {md / scale:.3e} above {tol:.1e}"
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 130])
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.float32, 64, 64), (torch.bfloat16, 32, 32),
+                                       (torch.bfloat16, 64, 64), (torch.bfloat16, 128, 128),
+                                       (torch.float32, 32, 64), (torch.bfloat16, 32, 64)])
+def test_chunk_fwd_fused_output_gate(T, dtype, K, V):
+    """kda_chunk_fwd with out_gate: the output gate applied in the state pass
+    equals the oracle's gate of the oracle's forward, at lengths around the
+    64-row chunk, with a random initial state, every geometry and dtype."""
+    w = inputs.chunk_inputs(2, T, 3, K, V, seed=500 + T + K + V, dtype=dtype, h0_std=0.1)
+    g_dtype = torch.bfloat16 if (T % 2) else torch.float32
+    gate = inputs.gate_inputs(2 * T, 3, V, seed=600 + T, dtype=g_dtype)["g"].reshape(2, T, 3, V)
+    print(f"fused gate T={T} K={K} V={V} {dtype} gate {g_dtype}", flush=True)
+    y, fs, want, ofs, on_plain, oo = _fused(w, gate, None)
+    tol = tol_for(dtype)
+    _check_gated("fused", y, want, on_plain, oo, tol)
+    check("final_state", fs, ofs, tol)
+
+
+def test_chunk_fwd_fused_output_gate_packed_batch():
+    """The packed 1024/2048/1024/4096 batch, H16 K=V=128 bf16 with a bf16 gate
+    input: every element of the gated output, and empty and tiny sequences."""
+    w = inputs.workload("fwd_hybrid")
+    gate = inputs.gate_inputs(8192, 16, 128, seed=611, dtype=torch.bfloat16)["g"].reshape(1, 8192, 16, 128)
+    print("fused gate packed T8192 H16", flush=True)
+    y, fs, want, ofs, on_plain, oo = _fused(w, gate, 0.01)
+    _check_gated("packed", y, want, on_plain, oo, tol_for(torch.bfloat16))
+    check("final_state", fs, ofs, tol_for(torch.bfloat16))
+    cu = [0, 0, 1, 66, 66, 130, 200]
+    w = inputs.chunk_inputs(1, 200, 2, 128, 128, seed=612, dtype=torch.bfloat16, cu_seqlens=cu, h0_std=0.2)
+    gate = inputs.gate_inputs(200, 2, 128, seed=613, dtype=torch.float32)["g"].reshape(1, 200, 2, 128)
+    y, fs, want, ofs, on_plain, oo = _fused(w, gate, None)
+    _check_gated("varlen", y, want, on_plain, oo, tol_for(torch.bfloat16))
+    check("final_state varlen", fs, ofs, tol_for(torch.bfloat16))
+
+
+def test_chunk_fwd_fused_output_gate_refuses_saving():
+    w = inputs.chunk_inputs(1, 64, 2, 64, 64, seed=614, dtype=torch.bfloat16)
+    gate = torch.zeros(1, 64, 2, 64, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(1 << 24, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        kda.chunk_kda(dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["g"]), dev(w["beta"]), out_gate=gate,
+                      workspace=ws, keep_for_backward=True)
