@@ -174,6 +174,11 @@ def gate_bytes(rows, H, V, elt):
     return 3 * rows * H * V * elt
 
 
+def gate_bwd_bytes(rows, H, V, elt):
+    """Its reverse mode: o, g and dy read, dO and dg written once (elt bytes each)."""
+    return 5 * rows * H * V * elt
+
+
 def conv_bytes(rows, n_seq, H, D, W, elt):
     """x read once and q, k, v written once (elt bytes each); conv_w read; the
     conv state read and written once per sequence."""
@@ -277,16 +282,16 @@ def run_decode(steps, warmup, device):
         s = ins[t % n_in]
         kda.recurrent_step(s["x"], cw, cs, s["g"], s["beta"], st, out=o)
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record(stream)
     for t in range(steps):
         s = ins[(warmup + t) % n_in]
-        evs[t].record(stream)
         kda.recurrent_step(s["x"], cw, cs, s["g"], s["beta"], st, out=o)
-    evs[steps].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    kern_ms = sum(evs[t].elapsed_time(evs[t + 1]) for t in range(steps)) / steps
+    kern_ms = e0.elapsed_time(e1) / steps  # back-to-back launches: the average launch duration
     wall = (t1 - t0) / steps
     algo = decode_bytes(N, H, D, W, 2)
     # the same steps with the full-rank output gate fused into the step
@@ -296,14 +301,14 @@ def run_decode(steps, warmup, device):
         kda.recurrent_step(s["x"], cw, cs, s["g"], s["beta"], st, out=o, out_gate=gates[t % 2])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for t in range(steps):
         s = ins[(warmup + t) % n_in]
-        evs[t].record(stream)
         kda.recurrent_step(s["x"], cw, cs, s["g"], s["beta"], st, out=o, out_gate=gates[t % 2])
-    evs[steps].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    gk_ms = sum(evs[t].elapsed_time(evs[t + 1]) for t in range(steps)) / steps
+    gk_ms = e0.elapsed_time(e1) / steps
     galgo = algo + N * H * D * 2
     gated = {"value": N * steps / (t1 - t0), "unit": "seq/s", "kernel_ms": gk_ms, "algorithmic_bytes": galgo,
              "frac": galgo / (gk_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
@@ -314,7 +319,9 @@ def run_decode(steps, warmup, device):
         "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": algo / (kern_ms * 1e-3) / 1e9,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": stored_traffic("decode"),
-                     "algorithmic_bytes": algo, "kernel_ms": kern_ms},
+                     "algorithmic_bytes": algo, "kernel_ms": kern_ms,
+                     "timing": f"{steps} back-to-back steps between two events (state {N * H * D * D * 4 >> 20} MiB, "
+                               "above the Infinity Cache)"},
         "with_output_gate": gated,
     }
 
@@ -381,11 +388,39 @@ def run_prefill(steps, warmup, device):
     gate_ms = sum(e[3].elapsed_time(e[4]) for e in ev) / steps
     algo = conv_bytes(T_H, n_seq, H, D, W, 2)
     galgo = gate_bytes(T_H, H, D, 2)
+    gbalgo = gate_bwd_bytes(T_H, H, D, 2)
 
-    def roof(kernel, nbytes, ms, stage):
-        return {"bound": "hbm", "kernel": kernel, "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes": nbytes,
-                "traffic": stored_traffic(stage)}
+    # Each bandwidth kernel alone: back-to-back launches over R input/output
+    # sets (R x 200 MB, above the 256 MiB Infinity Cache), so that no launch
+    # finds the previous one's data cached and no event sits between launches.
+    R = 4
+    xs = [x] + [inputs.prefill_inputs(T_H, H, D, seed=inputs.SEEDS["decode"] + 20 + i)["x"].to(device)
+                for i in range(R - 1)]
+    css = [init["conv_state"].to(device) for _ in range(R)]
+    outs = [qkv] + [tuple(torch.empty_like(qkv[0]) for _ in range(3)) for _ in range(R - 1)]
+    gsets = []
+    for i in range(R):
+        gi = inputs.gate_inputs(T_H, H, D, seed=inputs.SEEDS["decode"] + 30 + i)
+        gsets.append({k: gi[k].to(device) for k in ("o", "g", "dy")})
+        gsets[-1].update(y=torch.empty_like(gsets[-1]["o"]), dO=torch.empty_like(gsets[-1]["o"]),
+                         dg=torch.empty_like(gsets[-1]["g"]))
+    n_loop = 8 * R
+    conv_cold = time_rotating(lambda i: kda.conv_prefill(xs[i], cw, H, D, conv_state=css[i], cu_seqlens=cu,
+                                                         out=outs[i]), R, n_loop, stream)
+    gate_cold = time_rotating(lambda i: kda.output_gate(gsets[i]["o"], gsets[i]["g"], out=gsets[i]["y"]),
+                              R, n_loop, stream)
+    gbwd_cold = time_rotating(lambda i: kda.output_gate_bwd(gsets[i]["o"], gsets[i]["g"], gsets[i]["dy"],
+                                                            out=(gsets[i]["dO"], gsets[i]["dg"])),
+                              R, n_loop, stream)
+    del xs, css, outs, gsets
+
+    def roof(kernel, nbytes, ms, stage, pipe_ms):
+        ach = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "kernel": kernel, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": nbytes, "kernel_ms": ms,
+                "traffic": stored_traffic(stage),
+                "timing": f"{n_loop} back-to-back launches over {R} rotating buffer sets",
+                "in_pipeline_ms": pipe_ms}
 
     return {
         "metric": "stateful prefill tokens/s", "unit": "tokens/s",
@@ -393,12 +428,60 @@ def run_prefill(steps, warmup, device):
         "workload": f"conv{W} prefill + chunk forward from decode states with the output gate fused, packed "
                     f"1024/2048/1024/4096 (T{T_H}), H{H} d{D}, bf16 x/q/k/v/o/gate, fp32 states",
         "conv_ms": conv_ms, "chunk_fwd_gated_ms": fwd_ms,
-        "conv_roofline": roof("conv_prefill_kernel", algo, conv_ms, "prefill.conv"),
+        "conv_roofline": roof("conv_prefill_kernel", algo, conv_cold, "prefill.conv", conv_ms),
+        "gate_roofline": roof("output_gate_kernel (forward)", galgo, gate_cold, "prefill.gate", gate_ms),
+        "gate_bwd_roofline": roof("output_gate_kernel (reverse)", gbalgo, gbwd_cold, "prefill.gate_bwd", None),
         "unfused": {"value": T_H / ((conv_ms + plain_ms + gate_ms) * 1e-3), "chunk_fwd_ms": plain_ms,
                     "gate_ms": gate_ms,
-                    "gate_roofline": roof("output_gate_kernel", galgo, gate_ms, "prefill.gate"),
                     "workload": "the same prefill with the plain forward and kda_output_gate as its own kernel"},
     }
+
+
+def time_rotating(fn, R, n, stream):
+    """Average duration (ms) of fn(i % R) over n back-to-back launches between two events."""
+    for i in range(2 * R):
+        fn(i % R)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        fn(i % R)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def hbm_ceiling(device, mib=1024, R=3, n=12):
+    """What HBM sustains for a kernel with nothing to compute: the streaming copy
+    and read of libkda_stream.so over R rotating mib-MiB buffers."""
+    import ctypes
+    from kimi_delta_attention_amd import build as kbuild
+    lib = ctypes.CDLL(kbuild.STREAM_LIB)
+    lib.kda_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.kda_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    nb = mib << 20
+    src = [torch.ones(nb // 4, device=device) for _ in range(R)]
+    dst = [torch.empty_like(t) for t in src]
+    sink = torch.zeros(256, device=device)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+
+    def call(f, *a):
+        rc = f(*a)
+        if rc:
+            raise RuntimeError(f"stream calibration kernel failed ({rc})")
+
+    t_copy = time_rotating(lambda i: call(lib.kda_stream_copy, src[i].data_ptr(), dst[i].data_ptr(), nb, sp),
+                           R, n, stream)
+    t_read = time_rotating(lambda i: call(lib.kda_stream_read, src[i].data_ptr(), sink.data_ptr(), nb, sp),
+                           R, n, stream)
+    del src, dst
+    copy_gbs = 2 * nb / (t_copy * 1e-3) / 1e9
+    read_gbs = nb / (t_read * 1e-3) / 1e9
+    return {"copy_GBs": copy_gbs, "copy_frac": copy_gbs / PEAK_HBM_GBS, "read_GBs": read_gbs,
+            "read_frac": read_gbs / PEAK_HBM_GBS,
+            "what": f"streaming copy (nontemporal 16-byte loads and stores) and streaming read of {mib} MiB "
+                    f"buffers, {R} rotating, {n} launches each"}
 
 
 def cpu_baseline(host):
@@ -625,6 +708,13 @@ def main():
         line["roofline"]["decode_hbm_frac"] = line["decode"]["roofline"]["frac"]
         _log("timing stateful prefill")
         line["prefill"] = run_prefill(max(args.steps // 2, 5), min(args.warmup, 3), device)
+        torch.cuda.empty_cache()
+        _log("timing the streaming copy and read (HBM ceiling)")
+        ceil = hbm_ceiling(device)
+        line["hbm_ceiling"] = ceil
+        for leg, key in ((line["decode"], "roofline"), (line["prefill"], "conv_roofline"),
+                         (line["prefill"], "gate_roofline"), (line["prefill"], "gate_bwd_roofline")):
+            leg[key]["frac_of_stream_copy"] = leg[key]["achieved"] / ceil["copy_GBs"]
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         _log("cpu baseline (oracle)")

@@ -1,4 +1,5 @@
-"""Build the HIP library ``libkda.so`` (gfx950) in-tree with hipcc.
+"""Build the HIP library ``libkda.so`` (gfx950) in-tree with hipcc, and the
+benchmark's bandwidth-calibration library ``libkda_stream.so`` beside it.
 
 Usage: ``python -m kimi_delta_attention_amd.build`` or ``build()`` from Python.
 Objects go to ``_build/`` at the repository root; the shared library is
@@ -17,6 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libkda.so")
+STREAM_LIB = os.path.join(HERE, "libkda_stream.so")
+STREAM_SOURCE = "stream_ceiling.hip"
 
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_conv.hip", "kda_gate.hip", "kda_chunk_fwd.hip", "kda_chunk_bwd.hip",
            "kda_noalloc.hip"]
@@ -44,18 +47,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out):
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + [STREAM_SOURCE]
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], STREAM_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", STREAM_LIB)
     return LIB
 
 

@@ -286,7 +286,9 @@ kda_status kda_conv_prefill(const kda_conv_args* a) {
     if (rows * C > (int64_t(1) << 40)) return KDA_ERR_UNSUPPORTED;
     const int64_t nb = (static_cast<int64_t>(a->T) + kda::kConvBlockRows - 1) / kda::kConvBlockRows;
     const int64_t block_bound = a->cu_seqlens ? nb + N : static_cast<int64_t>(N) * nb;
-    if (block_bound > INT32_MAX || (C / 4 + 255) / 256 > 65535 || N > 65535) return KDA_ERR_UNSUPPORTED;
+    if (block_bound * ((C / 4 + 255) / 256) > INT32_MAX || N > 65535) return KDA_ERR_UNSUPPORTED;
+    // a block's rows are addressed by 32-bit byte offsets from its first input
+    if (C * 4 * (kda::kConvBlockRows + 8) > INT32_MAX) return KDA_ERR_UNSUPPORTED;
     kda::ConvParams p{};
     p.B = a->B; p.T = a->T; p.H = a->H; p.D = a->D; p.W = a->W;
     p.N = N;

@@ -53,7 +53,7 @@ hipError_t launch_output_gate_bwd(const GateParams& p, hipStream_t st);
 
 // Stateful short-conv prefill.  Sizes are validated by the caller.
 // Rows of one sequence that one conv-prefill workgroup slides over.
-constexpr int kConvBlockRows = 64;
+constexpr int kConvBlockRows = 16;
 
 struct ConvParams {
     int B, T, H, D, W;
