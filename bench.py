@@ -318,7 +318,7 @@ def run_decode(steps, warmup, device):
         "ms_per_step": wall * 1e3, "workload": f"decode N{N} H{H} d{D} conv{W} bf16 x, fp32 state",
         "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": algo / (kern_ms * 1e-3) / 1e9,
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": stored_traffic("decode"),
+                     "frac": algo / (kern_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "traffic": stored_traffic("decode", "decode"),
                      "algorithmic_bytes": algo, "kernel_ms": kern_ms,
                      "timing": f"{steps} back-to-back steps between two events (state {N * H * D * D * 4 >> 20} MiB, "
                                "above the Infinity Cache)"},
@@ -418,7 +418,7 @@ def run_prefill(steps, warmup, device):
         ach = nbytes / (ms * 1e-3) / 1e9
         return {"bound": "hbm", "kernel": kernel, "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": ach / PEAK_HBM_GBS, "algorithmic_bytes": nbytes, "kernel_ms": ms,
-                "traffic": stored_traffic(stage),
+                "traffic": stored_traffic(stage, "prefill"),
                 "timing": f"{n_loop} back-to-back launches over {R} rotating buffer sets",
                 "in_pipeline_ms": pipe_ms}
 
@@ -510,17 +510,23 @@ def csrc_digest():
     return h.hexdigest()
 
 
-def stored_traffic(stage):
+# committed rocprofv3 summaries, one per leg (see the commands in their headers)
+PROFILE_SUFFIX = {"chunk": "chunk_fwdbwd_T8192_H16_D128", "gated": "chunk_softplus_T8192_H16_D128",
+                  "narrow": "chunk_narrow_B16_T2048_H8_K32_V64", "decode": "decode_N64_H96_D128",
+                  "prefill": "prefill_T8192_H16_D128"}
+
+
+def stored_traffic(stage, leg="chunk"):
     """HBM bytes per launch of `stage` from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summary, or None when there is none or the kernels changed since it was taken."""
-    return _stored("hbm_traffic_T8192_H16_D128.txt", f"hbm_bytes_per_launch[{stage}]")
+    summary of `leg`, or None when there is none or the kernels changed since it was taken."""
+    return _stored(f"hbm_traffic_{PROFILE_SUFFIX[leg]}.txt", f"hbm_bytes_per_launch[{stage}]")
 
 
-def stored_mfma_util(stage):
+def stored_mfma_util(stage, leg="chunk"):
     """MFMA busy fraction of `stage` from the committed rocprofv3 MFMA counter summary
     (SQ_VALU_MFMA_BUSY_CYCLES over the launch's cycles x 1,024 SIMDs), or None when
     there is none or the kernels changed since it was taken."""
-    return _stored("mfma_util_T8192_H16_D128.txt", f"mfma_util[{stage}]")
+    return _stored(f"mfma_util_{PROFILE_SUFFIX[leg]}.txt", f"mfma_util[{stage}]")
 
 
 def _stored(name, key):
@@ -597,7 +603,48 @@ def run_variant(B, T, H, K, V, cu, gate, steps, warmup, device, seed, what):
                                keep_for_backward=True))
     sec, per_stage, _ = time_chunk(ops, steps, warmup, True, _lib_stages())
     tokens = B * T if cu is None else cu[-1]
-    return {"workload": what, "tokens_per_s": tokens / sec, "ms_per_step": sec * 1e3, "stages_ms": per_stage}
+    leg = "narrow" if K != V else "gated"
+    counted = {}
+    for n, ms in per_stage.items():
+        tr = stored_traffic(n, leg)
+        counted[n] = {"kernel_ms": ms, "traffic": tr,
+                      "traffic_frac": None if tr is None else tr / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                      "mfma_util": stored_mfma_util(n, leg)}
+    return {"workload": what, "tokens_per_s": tokens / sec, "ms_per_step": sec * 1e3, "stages_ms": per_stage,
+            "stages_counted": counted}
+
+
+def run_leg(name, args, device):
+    """One leg of the benchmark other than the main chunk step."""
+    from kimi_delta_attention_amd import inputs
+    try:
+        if name == "train":
+            _log("timing chunk path (dense B8 x T4096)")
+            return run_train(max(args.steps // 2, 3), min(args.warmup, 3), device)
+        if name == "gated":
+            _log("timing chunk path (packed T8192) with the in-kernel softplus gate")
+            return run_variant(1, T_H, H_H, D_H, D_H, HYBRID_CU, inputs.GATE_SOFTPLUS, max(args.steps // 2, 5),
+                               min(args.warmup, 3), device, 1013,
+                               "chunk_kda fwd+bwd, packed 1024/2048/1024/4096 (T8192), H16, K=V=128, bf16, "
+                               "softplus gate and beta sigmoid in kernel, dA_log and d(dt_bias) produced")
+        if name == "narrow":
+            _log("timing chunk path, narrow-key geometry (K32, V64)")
+            return run_variant(16, 2048, 8, 32, 64, None, inputs.GATE_SOFTPLUS, max(args.steps // 2, 5),
+                               min(args.warmup, 3), device, 1015,
+                               "chunk_kda fwd+bwd, dense B16 x T2048, H8, K=32, V=64 (the 300M model's "
+                               "heads), bf16, softplus gate and beta sigmoid in kernel")
+        if name == "decode":
+            _log("timing decode")
+            return run_decode(max(args.steps, 10), args.warmup, device)
+        if name == "prefill":
+            _log("timing stateful prefill")
+            return run_prefill(max(args.steps // 2, 5), min(args.warmup, 3), device)
+        if name == "ceiling":
+            _log("timing the streaming copy and read (HBM ceiling)")
+            return hbm_ceiling(device)
+        raise ValueError(name)
+    finally:
+        torch.cuda.empty_cache()
 
 
 def _lib_stages():
@@ -617,6 +664,8 @@ def main():
                     help="skip the in-kernel gate and narrow-key (K32/V64) fwd+bwd legs")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--only", choices=["chunk", "train", "gated", "narrow", "decode", "prefill", "ceiling"],
+                    help="run one leg alone and print its object (profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the KDA operator needs no cross-GPU exchange and this build "
@@ -628,6 +677,10 @@ def main():
     _lib.load()
     if args.copy_probe_mib > 0:
         copy_probe(args.copy_probe_mib, device)
+
+    if args.only and args.only != "chunk":
+        print(json.dumps({"leg": args.only, **run_leg(args.only, args, device)}), flush=True)
+        return
 
     n_bwd = _lib_stages()
     _log("building inputs")
@@ -684,38 +737,23 @@ def main():
     }
     del ops, d0, d1
     torch.cuda.empty_cache()
+    if args.only == "chunk":
+        print(json.dumps({"leg": "chunk", **line}), flush=True)
+        return
     if not args.no_train:
-        _log("timing chunk path (dense B8 x T4096)")
-        line["train"] = run_train(max(args.steps // 2, 3), min(args.warmup, 3), device)
-        torch.cuda.empty_cache()
+        line["train"] = run_leg("train", args, device)
     if not args.no_variants:
-        from kimi_delta_attention_amd import inputs
-        _log("timing chunk path (packed T8192) with the in-kernel softplus gate")
-        line["gated"] = run_variant(1, T_H, H_H, D_H, D_H, HYBRID_CU, inputs.GATE_SOFTPLUS, max(args.steps // 2, 5),
-                                    min(args.warmup, 3), device, 1013,
-                                    "chunk_kda fwd+bwd, packed 1024/2048/1024/4096 (T8192), H16, K=V=128, bf16, "
-                                    "softplus gate and beta sigmoid in kernel, dA_log and d(dt_bias) produced")
-        torch.cuda.empty_cache()
-        _log("timing chunk path, narrow-key geometry (K32, V64)")
-        line["narrow_key"] = run_variant(16, 2048, 8, 32, 64, None, inputs.GATE_SOFTPLUS, max(args.steps // 2, 5),
-                                         min(args.warmup, 3), device, 1015,
-                                         "chunk_kda fwd+bwd, dense B16 x T2048, H8, K=32, V=64 (the 300M model's "
-                                         "heads), bf16, softplus gate and beta sigmoid in kernel")
-        torch.cuda.empty_cache()
+        line["gated"] = run_leg("gated", args, device)
+        line["narrow_key"] = run_leg("narrow", args, device)
     if not args.no_decode:
-        _log("timing decode")
-        line["decode"] = run_decode(max(args.steps, 10), args.warmup, device)
+        line["decode"] = run_leg("decode", args, device)
         line["roofline"]["decode_hbm_frac"] = line["decode"]["roofline"]["frac"]
-        _log("timing stateful prefill")
-        line["prefill"] = run_prefill(max(args.steps // 2, 5), min(args.warmup, 3), device)
-        torch.cuda.empty_cache()
-        _log("timing the streaming copy and read (HBM ceiling)")
-        ceil = hbm_ceiling(device)
+        line["prefill"] = run_leg("prefill", args, device)
+        ceil = run_leg("ceiling", args, device)
         line["hbm_ceiling"] = ceil
         for leg, key in ((line["decode"], "roofline"), (line["prefill"], "conv_roofline"),
                          (line["prefill"], "gate_roofline"), (line["prefill"], "gate_bwd_roofline")):
             leg[key]["frac_of_stream_copy"] = leg[key]["achieved"] / ceil["copy_GBs"]
-        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         _log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(host0)
