@@ -1164,8 +1164,7 @@ struct KlocMfmaSmem {
         struct {
             ET Tn[kChunk][LDC];
             ET Tt[kChunk][LDC];
-            ET dTt[kChunk][LDC];
-            ET Zn[kChunk][LDC];
+            ET dTt[kChunk][LDC];    // then Z = T^T dT
         } mm;
         struct {
             float dM[kChunk][LDD];  // scale * dMS (lower incl. diagonal)
@@ -1180,7 +1179,8 @@ struct KlocMfmaSmem {
     float dbc[4][kChunk];
     float dbr[kChunk];
     float dots[2][K / 16][kChunk];  // per-tile row dot products (q^.dq^, k^.dk^)
-    float ddt[K];
+    float ddt[2][K];                // per half of the rows (K = 32) or whole
+    float xch[K / 16][2][16];       // reverse-cumsum terms crossing the halves (K = 32)
     float gpa[4];
     int unsafe[4];
 };
@@ -1424,15 +1424,16 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 z[ct] = gemm<MM>(&s.x.mm.Tt[0][0], LDC, 16 * w, &s.x.mm.dTt[0][0], LDC, 16 * ct, 0, kChunk, z[ct],
                                  lane);
             }
+            __syncthreads();  // every wave is done reading dT: Z takes its place
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) tile_store<MM>(&s.x.mm.Zn[0][0], LDC, 16 * w, 16 * ct, z[ct], lane);
+            for (int ct = 0; ct < 4; ++ct) tile_store<MM>(&s.x.mm.dTt[0][0], LDC, 16 * w, 16 * ct, z[ct], lane);
         }
         __syncthreads();
         f32x4 da[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
             da[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-            da[ct] = gemm<MM>(&s.x.mm.Zn[0][0], LDC, 16 * w, &s.x.mm.Tn[0][0], LDC, 16 * ct, 0, kChunk, da[ct], lane);
+            da[ct] = gemm<MM>(&s.x.mm.dTt[0][0], LDC, 16 * w, &s.x.mm.Tn[0][0], LDC, 16 * ct, 0, kChunk, da[ct], lane);
         }
         __syncthreads();  // the score gradients below overlay T and Z
         {
@@ -1464,6 +1465,18 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         __syncthreads();
 
         // ---- 2. per column tile: score rule, element-wise terms, reverse cumsum, gate rule
+        // With two column tiles (K = 32) the four waves pair up: wave w takes
+        // tile w % 2 and the output rows of half w / 2 (sub-blocks 0-1 or 2-3),
+        // so that every SIMD has a share.  The score-rule B operands are built
+        // by both waves of a pair; the two terms of the reverse cumulative sum
+        // that cross the halves (the upper half's suffix sum at row 32, and the
+        // lower half's share of the row-63 term) are exchanged through LDS.
+        constexpr int HALVES = NKT < 4 ? 4 / NKT : 1;
+        constexpr int IPH = 4 / HALVES;  // output sub-blocks per wave
+        static_assert(HALVES == 1 || NKT * HALVES == 4, "tiles x halves = waves");
+        const int hf = HALVES > 1 ? w / NKT : 0;
+        const int I0 = IPH * hf, I1 = I0 + IPH;
+        auto mine = [&](int I) { return HALVES == 1 || (I >= I0 && I < I1); };
         const ET* gQE = reinterpret_cast<const ET*>(base + X::kDQE);
         const ET* gKE = reinterpret_cast<const ET*>(base + X::kDKE);
         const ET* gKD = reinterpret_cast<const ET*>(base + X::kDKD);
@@ -1476,7 +1489,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         // per wave and tile, 32 floats per lane (dq^ then dk^), lane-minor
         float* park = reinterpret_cast<float*>(base + X::kS) + w * 2 * 32 * 64 + lane;
 #pragma unroll 1
-        for (int ct = w; ct < NKT; ct += 4) {
+        for (int ct = HALVES > 1 ? w % NKT : w; ct < NKT; ct += 4) {
             const int c = 16 * ct + lc;     // this lane's channel
             // The tile's dQE, dKE, dKD (64 rows x 32 bytes each) are requested
             // now and staged in LDS after the P terms: vector v = lane + 64 hf
@@ -1526,6 +1539,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             // P terms: P_x[I] = a_I * sum_J f(J, I) dX_IJ (k b)_J
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
+                if (!mine(I)) continue;
                 f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int J = 0; J <= I; ++J) {
@@ -1583,6 +1597,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 const float* dX = pass == 0 ? &s.x.sc.dM[0][0] : &s.x.sc.dA[0][0];
 #pragma unroll
                 for (int J = 0; J < 4; ++J) {
+                    if (!mine(J)) continue;
 #pragma unroll
                     for (int I = J; I < 4; ++I) {
                         const float f = fac(J, I);
@@ -1595,6 +1610,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             }
 #pragma unroll
             for (int J = 0; J < 4; ++J) {
+                if (!mine(J)) continue;
                 const float Ge = s.G[kSub * J + kSub - 1][c];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -1616,7 +1632,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             if (any_unsafe) {
 #pragma unroll 1
                 for (int I = 0; I < 4; ++I) {
-                    if (!s.unsafe[I]) continue;  // uniform over the workgroup
+                    if (!s.unsafe[I] || !mine(I)) continue;  // uniform over the wave
                     const int b0 = kSub * I;
                     float gI[4], qI[4], kI[4];
 #pragma unroll
@@ -1720,7 +1736,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             const float Glast = s.G[kChunk - 1][c];
             float colp = 0.f;
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
+            for (int I = 0; I < 4; ++I) {
+                if (!mine(I)) continue;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
@@ -1736,14 +1753,18 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                     dG[I][r] += dqe * p.scale * q_ * E + dke * k_ * E - dkd * KD;
                     colp += dkd * KD;
                 }
+            }
             colp += __shfl_xor(colp, 16, 64);
             colp += __shfl_xor(colp, 32, 64);
-            if (lg == 3) dG[3][3] += colp + dgam[c] * __expf(Glast);
+            // the row-63 term: this wave's share of sum(dKD * KD) and d(G_last)
+            // (the lower half's share reaches every row as a constant below)
+            if (I1 == 4 && lg == 3) dG[3][3] += colp + dgam[c] * __expf(Glast);
 
             // reverse cumulative sum over the 64 rows of this column
             float carry = 0.f;
 #pragma unroll
             for (int I = 3; I >= 0; --I) {
+                if (!mine(I)) continue;
                 dG[I][2] += dG[I][3];
                 dG[I][1] += dG[I][2];
                 dG[I][0] += dG[I][1];
@@ -1758,6 +1779,16 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
 #pragma unroll
                 for (int r = 0; r < 4; ++r) dG[I][r] += add;
                 carry = __shfl(dG[I][0], lc, 64);  // suffix sum from row 16 I
+            }
+            if constexpr (HALVES > 1) {
+                // the lower half adds the upper half's suffix sum at row 32 and
+                // its own row-63 share; the upper half adds the lower half's share
+                if (lg == 0) s.xch[ct][hf][lc] = hf == 0 ? colp : carry;
+                __syncthreads();  // every wave of the workgroup is here once
+                const float add = hf == 0 ? colp + s.xch[ct][1][lc] : s.xch[ct][0][lc];
+#pragma unroll
+                for (int I = 0; I < 4; ++I)
+                    if (mine(I)) dG[I] += f32x4{add, add, add, add};
             }
 
             // gate chain rule.  Every gate input is requested before the first
@@ -1776,10 +1807,11 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         z[r] = p.g[((rbase + ic) * H + h) * K + c];
                     }
                 };
-                zload(0, zc);
+                zload(I0, zc);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
-                    if (I < 3) zload(I + 1, zn);
+                    if (!mine(I)) continue;
+                    if (I + 1 < I1) zload(I + 1, zn);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = kSub * I + 4 * lg + r;
@@ -1801,26 +1833,29 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         }
                         dG[I][r] = dx;
                     }
-                    if (I < 3) {
+                    if (I + 1 < I1) {
 #pragma unroll
                         for (int r = 0; r < 4; ++r) zc[r] = zn[r];
                     }
                 }
             }
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
+            for (int I = 0; I < 4; ++I) {
+                if (!mine(I)) continue;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
                     if (i < rows) gr.dg[((rbase + i) * H + h) * K + c] = dG[I][r];
                 }
+            }
             ddt += __shfl_xor(ddt, 16, 64);
             ddt += __shfl_xor(ddt, 32, 64);
-            if (lg == 0) s.ddt[c] = ddt;
+            if (lg == 0) s.ddt[hf][c] = ddt;
 
             // row dot products of the L2-norm rule
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
+            for (int I = 0; I < 4; ++I) {
+                if (!mine(I)) continue;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
@@ -1836,6 +1871,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         s.dots[1][ct][i] = vk;
                     }
                 }
+            }
             // with two tiles per wave, the tile's dq^, dk^ wait for the row
             // dot products in this lane's own strip of the slot's state
             // regions (read by the V-local kernel, free now), coalesced across
@@ -1872,7 +1908,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = kSub * I + 4 * lg + r;
-                        if (i >= rows) continue;
+                        if (i >= rows || !mine(I)) continue;
                         const float dotq = s.dots[0][0][i], dotk = s.dots[1][0][i];
                         float oq = tq[I][r], ok = tk[I][r];
                         if (p.use_qk_l2norm) {
@@ -1885,7 +1921,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                     }
             };
             if (!PARK) {
-                if (w < NKT) store_tile(w, dq, dk);
+                if (HALVES > 1) store_tile(w % NKT, dq, dk);
+                else if (w < NKT) store_tile(w, dq, dk);
             } else
 #pragma unroll 1
             for (int ct = w; ct < NKT; ct += 4) {
@@ -1911,7 +1948,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             if (lane == 0) s.gpa[w] = dal;
             __syncthreads();
             float* gp = reinterpret_cast<float*>(base + X::kGP);
-            for (int cc = t; cc < K; cc += kThreads) gp[cc] = s.ddt[cc];
+            for (int cc = t; cc < K; cc += kThreads) gp[cc] = HALVES > 1 ? s.ddt[0][cc] + s.ddt[1][cc] : s.ddt[0][cc];
             if (t == 0) gp[K] = s.gpa[0] + s.gpa[1] + s.gpa[2] + s.gpa[3];
         }
     }
@@ -2767,10 +2804,13 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                 hipLaunchKernelGGL(chunk_bwd_klocal_w8_kernel,
                                    dim3(static_cast<unsigned>(nblk < kPersistentGrid ? nblk : kPersistentGrid)),
                                    dim3(kKlocW8Threads), 0, st, p, gr, chunk_off, slots, sb, static_cast<int>(nblk));
-            else if constexpr (BF)
+            else if constexpr (BF) {
+                // at K = 32 the shared buffers fit two workgroups per CU
+                constexpr int grid = sizeof(KlocMfmaSmem<K>) <= 80 * 1024 ? 2 * kPersistentGrid : kPersistentGrid;
                 hipLaunchKernelGGL((chunk_bwd_klocal_mfma_kernel<K, V>),
-                                   dim3(static_cast<unsigned>(nblk < kPersistentGrid ? nblk : kPersistentGrid)),
-                                   dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb, static_cast<int>(nblk));
+                                   dim3(static_cast<unsigned>(nblk < grid ? nblk : grid)), dim3(kThreads), 0, st, p,
+                                   gr, chunk_off, slots, sb, static_cast<int>(nblk));
+            }
             else
                 hipLaunchKernelGGL((chunk_bwd_klocal_kernel<K, BF, V>), dim3(static_cast<unsigned>(nblk)),
                                    dim3(kThreads), 0, st, p, gr, chunk_off, slots, sb);
