@@ -262,7 +262,7 @@ struct PrepSmem {
     } u;
     float A[kChunk][kChunk + 4];  // 16-byte aligned rows (MFMA A operand)
     float M[kChunk][kChunk + 1];
-    float Ak[BWD ? kChunk : 1][kChunk + 1];  // un-scaled k-k scores (backward only)
+    ET Ak[BWD ? kChunk : 1][kChunk + 1];  // un-scaled k-k scores (backward only), as stored
     float P[4][K];     // exp(G_end(I) - G_ref(I)): decay across sub-block I
     float invP[4][K];  // 1 / P (finite where the block is factorised)
     float Er[4][K];    // exp(G_ref(I))
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             if (hh == 0 ? a_ == b_ : level_pair(a_, b_, hh)) {
                 s.M[rowg][colg] = accM[r];
                 s.A[rowg][colg] = accA[r] * s.beta[rowg];  // 0 on the diagonal
-                if (BWD) s.Ak[rowg][colg] = accA[r];
+                if (BWD) s.Ak[rowg][colg] = MM::from_f32(accA[r]);
             }
         }
     };
@@ -638,7 +638,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
             } else {
                 if (J == I && col >= row) v = 0.f;
                 s.A[row][col] = v * s.beta[row];
-                if (BWD) s.Ak[row][col] = v;
+                if (BWD) s.Ak[row][col] = MM::from_f32(v);
             }
         }
     }
@@ -732,7 +732,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         for (int x = 0; x < EPT; ++x) {
             const int b = b7 + x;
             tt[x] = b > a7 ? 0.f : s.u.T[a7][b];
-            ak[x] = b >= a7 ? 0.f : s.Ak[a7][b];
+            ak[x] = b >= a7 ? 0.f : MM::to_f32(s.Ak[a7][b]);
         }
         store_row<EPT>(reinterpret_cast<ET*>(out + X::kT) + e7, tt);
         store_row<EPT>(reinterpret_cast<ET*>(out + X::kAK) + e7, ak);
