@@ -1157,6 +1157,11 @@ struct KlocMfmaSmem {
     static constexpr int LDG = K + 4;       // G rows: 16-byte aligned, column reads conflict-free
     static constexpr int LDD = kChunk + 4;  // fp32 score-gradient rows, 16-byte aligned
     static constexpr int LDF = kChunk + 4;  // fp32 rows of a tile's score-rule B operand
+    // dQE, dKE, dKD staged per wave at K = 64; at K = 32 (two waves per tile)
+    // each wave reads its rows' values from the slot where it uses them, and
+    // the buffers shrink to a stub, so that two workgroups fit a CU
+    static constexpr bool EW_LDS = K / 16 >= 4;
+    static constexpr int EWW = EW_LDS ? 4 : 1, EWR = EW_LDS ? kChunk : 1;
     ET qh[kChunk][LDE];             // normalised q
     ET kh[kChunk][LDE];             // normalised k
     float G[kChunk][LDG];           // inclusive cumulative log-decay
@@ -1172,7 +1177,7 @@ struct KlocMfmaSmem {
         } sc;
     } x;
     float op[4][16][LDF];           // per wave: (k b)^T, (q a)^T or (k a)^T of its tile
-    ET ew[4][3][kChunk][16];        // per wave: the tile's dQE, dKE, dKD
+    ET ew[EWW][3][EWR][16];         // per wave: the tile's dQE, dKE, dKD
     float P[4][K], invP[4][K];
     float F20[K], F30[K], F31[K];
     float beta[kChunk], rq[kChunk], rk[kChunk];
@@ -1483,7 +1488,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         const float* dgam = reinterpret_cast<const float*>(base + X::kDGAM);
         const bool any_unsafe = s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3];
         float (*opw)[LDF] = s.op[w];
-        ET (*eww)[kChunk][16] = s.ew[w];
+        constexpr bool EW_LDS = SM::EW_LDS;
+        ET (*eww)[SM::EWR][16] = s.ew[EW_LDS ? w : 0];
         float dal = 0.f;
         f32x4 dq[4], dk[4];
         // per wave and tile, 32 floats per lane (dq^ then dk^), lane-minor
@@ -1495,13 +1501,15 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             // now and staged in LDS after the P terms: vector v = lane + 64 hf
             // holds row v / 2, columns 8 (v % 2) .. +7.
             uint4 ewv[6];
+            if constexpr (EW_LDS) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int v = lane + 64 * hf;
-                const int off = (v >> 1) * K + 16 * ct + 8 * (v & 1);
-                ewv[hf] = *reinterpret_cast<const uint4*>(gQE + off);
-                ewv[2 + hf] = *reinterpret_cast<const uint4*>(gKE + off);
-                ewv[4 + hf] = *reinterpret_cast<const uint4*>(gKD + off);
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int v = lane + 64 * hf;
+                    const int off = (v >> 1) * K + 16 * ct + 8 * (v & 1);
+                    ewv[hf] = *reinterpret_cast<const uint4*>(gQE + off);
+                    ewv[2 + hf] = *reinterpret_cast<const uint4*>(gKE + off);
+                    ewv[4 + hf] = *reinterpret_cast<const uint4*>(gKD + off);
+                }
             }
             // sub-block factors f(J, I) of this lane's column
             float invp[4];
@@ -1566,12 +1574,14 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 }
             }
             // stage the element-wise operands (requested at the tile start)
+            if constexpr (EW_LDS) {
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                const int v = lane + 64 * hf;
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int v = lane + 64 * hf;
 #pragma unroll
-                for (int a3 = 0; a3 < 3; ++a3)
-                    *reinterpret_cast<uint4*>(&eww[a3][v >> 1][8 * (v & 1)]) = ewv[2 * a3 + hf];
+                    for (int a3 = 0; a3 < 3; ++a3)
+                        *reinterpret_cast<uint4*>(&eww[a3][v >> 1][8 * (v & 1)]) = ewv[2 * a3 + hf];
+                }
             }
 
             // R terms: (q a)^T against dM, then (k a)^T against dA, a_i = e^(G_i - G_ref(I))
@@ -1744,9 +1754,16 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                     const float Gi = Gc[4 * I + r];
                     const float E = __expf(Gi), Ed = __expf(Glast - Gi);
                     const float q_ = MM::to_f32(s.qh[i][c]), k_ = MM::to_f32(s.kh[i][c]);
-                    const float dqe = MM::to_f32(eww[0][i][lc]);
-                    const float dke = MM::to_f32(eww[1][i][lc]);
-                    const float dkd = MM::to_f32(eww[2][i][lc]);
+                    float dqe, dke, dkd;
+                    if constexpr (EW_LDS) {
+                        dqe = MM::to_f32(eww[0][i][lc]);
+                        dke = MM::to_f32(eww[1][i][lc]);
+                        dkd = MM::to_f32(eww[2][i][lc]);
+                    } else {
+                        dqe = MM::to_f32(gQE[i * K + c]);
+                        dke = MM::to_f32(gKE[i * K + c]);
+                        dkd = MM::to_f32(gKD[i * K + c]);
+                    }
                     const float KD = k_ * Ed;
                     dq[I][r] += p.scale * dqe * E;
                     dk[I][r] += dke * E + dkd * Ed;
