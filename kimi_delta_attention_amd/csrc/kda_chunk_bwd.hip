@@ -1186,6 +1186,7 @@ struct KlocMfmaSmem {
     float dots[2][K / 16][kChunk];  // per-tile row dot products (q^.dq^, k^.dk^)
     float ddt[2][K];                // per half of the rows (K = 32) or whole
     float xch[K / 16][2][16];       // reverse-cumsum terms crossing the halves (K = 32)
+    uint32_t lvm[4][2][2][64];      // per lane: level 8 >> lv masks of the P and R rules (level_words)
     float gpa[4];
     int unsafe[4];
 };
@@ -1279,6 +1280,14 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
     const int lg = lane >> 4, lc = lane & 15;
     const int H = p.H;
 
+    {  // the level masks of every lane, once (they depend on the lane only)
+        const int lv = t >> 6, hh = 8 >> lv;
+        const u32x2 mp = level_words(lc, 4 * lg, hh, true), mr = level_words(lc, 4 * lg, hh, false);
+        s.lvm[lv][0][0][lane] = mp[0];
+        s.lvm[lv][0][1][lane] = mp[1];
+        s.lvm[lv][1][0][lane] = mr[0];
+        s.lvm[lv][1][1][lane] = mr[1];
+    }
     for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
         const int slot = blk / H;
         const int h = blk % H;
@@ -1684,8 +1693,8 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                             later[r] = (4 * lg + r) & hh;
                             f[r] = __expf(later[r] ? gI[r] - gref : gref - gI[r]);
                         }
-                        const u32x2 wP = level_words(lc, 4 * lg, hh, true);
-                        const u32x2 wR = level_words(lc, 4 * lg, hh, false);
+                        const u32x2 wP = {s.lvm[lv][0][0][lane], s.lvm[lv][0][1][lane]};
+                        const u32x2 wR = {s.lvm[lv][1][0][lane], s.lvm[lv][1][1][lane]};
                         float b4[4];
                         u32x2 bh, bl;
                         // P terms (dM carries the scale)
