@@ -329,10 +329,11 @@ def run_decode(steps, warmup, device):
 def run_prefill(steps, warmup, device):
     """Stateful prefill of the packed batch: the short conv from a conv state
     (kda_conv_prefill), then the chunk forward from a decode state with the
-    final states out and the full-rank output gate fused into its state pass
-    (kda_chunk_fwd with out_gate) -- the prime that hands over to decode.  The
-    same prefill with the gate as its own kernel (kda_output_gate after the
-    plain forward) is timed beside it for comparison."""
+    final states out and the full-rank output gate (kda_chunk_fwd with
+    out_gate; at these 64 chains the library gates o in place right after the
+    state pass) -- the prime that hands over to decode.  The same prefill with
+    the gate as a call of its own (kda_output_gate after the plain forward) is
+    timed beside it for comparison."""
     import kimi_delta_attention_amd as kda
     from kimi_delta_attention_amd import inputs
     H, D, W = H_H, D_H, 4
@@ -425,7 +426,7 @@ def run_prefill(steps, warmup, device):
     return {
         "metric": "stateful prefill tokens/s", "unit": "tokens/s",
         "value": T_H / ((conv_ms + fwd_ms) * 1e-3),
-        "workload": f"conv{W} prefill + chunk forward from decode states with the output gate fused, packed "
+        "workload": f"conv{W} prefill + chunk forward from decode states with the output gate in the same call, packed "
                     f"1024/2048/1024/4096 (T{T_H}), H{H} d{D}, bf16 x/q/k/v/o/gate, fp32 states",
         "conv_ms": conv_ms, "chunk_fwd_gated_ms": fwd_ms,
         "conv_roofline": roof("conv_prefill_kernel", algo, conv_cold, "prefill.conv", conv_ms),
@@ -433,7 +434,7 @@ def run_prefill(steps, warmup, device):
         "gate_bwd_roofline": roof("output_gate_kernel (reverse)", gbalgo, gbwd_cold, "prefill.gate_bwd", None),
         "unfused": {"value": T_H / ((conv_ms + plain_ms + gate_ms) * 1e-3), "chunk_fwd_ms": plain_ms,
                     "gate_ms": gate_ms,
-                    "workload": "the same prefill with the plain forward and kda_output_gate as its own kernel"},
+                    "workload": "the same prefill with the plain forward and kda_output_gate as a call of its own"},
     }
 
 

@@ -134,13 +134,16 @@ typedef struct {
     /* Fused full-rank output gate (forward only; the "atlas_core/kimi_k3/kda.rs"
      * page, full_rank_output_gate).  With out_gate given, o receives, per row
      * and head, y = sigmoid(out_gate) * o / sqrt(mean_v(o^2) + eps) over the
-     * head's V values -- kda_output_gate applied to the output -- computed in
-     * the state pass before the row is stored, so that o never makes a round
-     * trip through memory.  out_gate is [rows, H, V] in out_gate_dtype,
-     * 16-byte aligned.  Inference only: keep_for_backward must be 0 and
-     * kda_chunk_bwd rejects a set out_gate (KDA_ERR_INVALID_ARG); training
-     * calls the forward without it and kda_output_gate / kda_output_gate_bwd.
-     * The state pass then runs one workgroup per (sequence, head). */
+     * head's V values -- kda_output_gate applied to the output.  With at least
+     * 256 (sequence, head) chains the state pass computes it before each row
+     * is stored (one workgroup per chain, o never written ungated); with
+     * fewer, the state pass writes o and the gate runs over it in place within
+     * the same call (the split state pass fills the chip better; o is then
+     * rounded to its element type before the gate, as with kda_output_gate).
+     * out_gate is [rows, H, V] in out_gate_dtype, 16-byte aligned.  Inference
+     * only: keep_for_backward must be 0 and kda_chunk_bwd rejects a set
+     * out_gate (KDA_ERR_INVALID_ARG); training calls the forward without it
+     * and kda_output_gate / kda_output_gate_bwd. */
     const void *out_gate;     /* [rows, H, V] gate input, or NULL (o is the plain output) */
     int out_gate_dtype;       /* kda_dtype of out_gate */
     float out_gate_eps;       /* NaN means 1e-5; must be >= 0 */

@@ -49,6 +49,9 @@ struct GateParams {
 };
 
 hipError_t launch_output_gate(const GateParams& p, hipStream_t st);
+// Chains (sequences x heads) from which the chunk forward gates its output in
+// the state pass rather than in a pass over o after it.
+constexpr int kFusedGateMinChains = 256;
 hipError_t launch_output_gate_bwd(const GateParams& p, hipStream_t st);
 
 // Stateful short-conv prefill.  Sizes are validated by the caller.

@@ -171,6 +171,22 @@ def test_chunk_fwd_fused_output_gate(T, dtype, K, V):
     check("final_state", fs, ofs, tol)
 
 
+@pytest.mark.parametrize("dtype,K,V,B,H", [(torch.bfloat16, 128, 128, 16, 16), (torch.bfloat16, 32, 64, 32, 8),
+                                           (torch.float32, 64, 64, 16, 16)])
+def test_chunk_fwd_output_gate_in_state_pass(dtype, K, V, B, H):
+    """With at least 256 (sequence, head) chains the gate is applied inside the
+    state pass, one workgroup per chain (below that, by a pass over o in the
+    same call): the same bar, a ragged tail chunk, a random initial state."""
+    T = 70
+    w = inputs.chunk_inputs(B, T, H, K, V, seed=620 + K + V, dtype=dtype, h0_std=0.1)
+    gate = inputs.gate_inputs(B * T, H, V, seed=621, dtype=torch.bfloat16)["g"].reshape(B, T, H, V)
+    print(f"gate in state pass B{B} H{H} K={K} V={V} {dtype}", flush=True)
+    y, fs, want, ofs, on_plain, oo = _fused(w, gate, None)
+    tol = tol_for(dtype)
+    _check_gated("in state pass", y, want, on_plain, oo, tol)
+    check("final_state", fs, ofs, tol)
+
+
 def test_chunk_fwd_fused_output_gate_packed_batch():
     """The packed 1024/2048/1024/4096 batch, H16 K=V=128 bf16 with a bf16 gate
     input: every element of the gated output, and empty and tiny sequences."""
