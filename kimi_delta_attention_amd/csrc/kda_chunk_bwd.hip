@@ -1050,8 +1050,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_kernel(ChunkParams 
                         dx = dge * base_ * rate;
                         dal += dge * base_ * rate * z;
                     } else {
-                        dx = -dge * rate * sigmoidf_(z);
-                        dal += -dge * rate * softplusf_(z);
+                        float sp, sg;
+                        softplus_sigmoid(z, sp, sg);
+                        dx = -dge * rate * sg;
+                        dal += -dge * rate * sp;
                     }
                     ddt += dx;
                 }
@@ -1850,8 +1852,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                             dx = dge * b_ * rate;
                             da = dx * z;
                         } else {
-                            dx = -dge * rate * sigmoidf_(z);
-                            da = -dge * rate * softplusf_(z);
+                            float sp, sg;
+                            softplus_sigmoid(z, sp, sg);
+                            dx = -dge * rate * sg;
+                            da = -dge * rate * sp;
                         }
                         if (i < rows) {
                             ddt += dx;
@@ -2611,8 +2615,10 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                             dx = dge * b_ * rate;
                             da = dx * z;
                         } else {
-                            dx = -dge * rate * sigmoidf_(z);
-                            da = -dge * rate * softplusf_(z);
+                            float sp, sg;
+                            softplus_sigmoid(z, sp, sg);
+                            dx = -dge * rate * sg;
+                            da = -dge * rate * sp;
                         }
                         if (i < rows) {
                             ddt += dx;

@@ -67,6 +67,16 @@ __device__ __forceinline__ float softplusf_(float x) {
     return fmaxf(x, 0.0f) + log1p_unit(__expf(-fabsf(x)));
 }
 
+// softplus(z) and sigmoid(z) from one exponential t = e^-|z|: sigmoid(z) is
+// 1 / (1 + t) for z >= 0 and t / (1 + t) below, softplus(z) = max(z, 0) +
+// log1p(t) (the softplus gate's chain rule needs both).
+__device__ __forceinline__ void softplus_sigmoid(float z, float& sp, float& sg) {
+    const float t = __expf(-fabsf(z));
+    const float r = __builtin_amdgcn_rcpf(1.0f + t);
+    sg = z >= 0.0f ? r : t * r;
+    sp = fmaxf(z, 0.0f) + log1p_unit(t);
+}
+
 // Per-channel log-decay from the raw gate input (see kda_gate_mode in kda.h).
 __device__ __forceinline__ float gate_eff(int mode, float x, float rate, float bias, float lb) {
     if (mode == GATE_LOGDECAY) return x;
