@@ -527,7 +527,7 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
             if (n >= p.N) return l;
         }
         l.ok = true;
-        l.h = static_cast<int>(item % H);
+        l.h = item_head(item, H, GS, p.gate_mode != GATE_LOGDECAY);
         l.rows = min(kChunk, len - j * kChunk);
         l.rbase = start + static_cast<int64_t>(j) * kChunk;
         l.base = ws + (static_cast<int64_t>(slot) * H + l.h) * slot_bytes;
@@ -1292,7 +1292,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
     }
     for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
         const int slot = blk / H;
-        const int h = blk % H;
+        const int h = item_head(blk, H, gridDim.x, p.gate_mode != GATE_LOGDECAY);
         int n, j;
         int64_t start;
         int len;
@@ -2086,7 +2086,7 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
         const int lg = lane >> 4, lc = lane & 15;
         const int c = 16 * w + lc;  // this lane's channel in the tile phase
         const int slot = blk / H;
-        const int h = blk % H;
+        const int h = item_head(blk, H, gridDim.x, p.gate_mode != GATE_LOGDECAY);
         int n, j;
         int64_t start;
         int len;

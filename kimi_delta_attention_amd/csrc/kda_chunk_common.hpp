@@ -258,6 +258,23 @@ __device__ __forceinline__ bool chain_of_block(int bid, int n_chains, int nvb, i
     return chain < n_chains;
 }
 
+// Head of item `item` (item = slot * H + position among the slot's heads) in
+// the persistent loops over (slot, head) items.  With rotate, the heads of a
+// slot are rotated by slot / max(1, grid / H), so that a workgroup walking
+// items b, b + grid, b + 2 grid, ... meets a different head at each step
+// rather than one head throughout: with the in-kernel gates the work per slot
+// differs several-fold between fast- and slow-decaying heads (the level paths
+// of over-wide sub-blocks), and a fixed head per workgroup leaves the kernel
+// waiting on the workgroups of the fast heads.  A bijection on the heads of
+// each slot, so every (slot, head) is still taken exactly once.  Without
+// rotate (the log-decay gate, uniform work), the plain order measured slightly
+// faster.
+__host__ __device__ __forceinline__ int item_head(int64_t item, int H, int64_t grid, bool rotate) {
+    if (!rotate) return static_cast<int>(item % H);
+    const int64_t c = grid / H > 1 ? grid / H : 1;
+    return static_cast<int>((item % H + (item / H) / c) % H);
+}
+
 __host__ __device__ constexpr int chain_grid(int n_chains, int nvb) {
     return ((n_chains + 7) / 8) * 8 * nvb;
 }

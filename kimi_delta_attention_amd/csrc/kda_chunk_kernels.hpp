@@ -379,7 +379,8 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
         const bool ok0 = decode(blockIdx.x, mcur, n0, j0, st0, len0);
         const int i0 = static_cast<int>(threadIdx.x) / TPR, pq0 = static_cast<int>(threadIdx.x) % TPR;
         const int rows0 = ok0 ? min(kChunk, len0 - j0 * kChunk) : 0;
-        const int64_t rowh0 = (st0 + static_cast<int64_t>(j0) * kChunk + i0) * H + blockIdx.x % H;
+        const int64_t rowh0 = (st0 + static_cast<int64_t>(j0) * kChunk + i0) * H +
+                              item_head(blockIdx.x, H, GS, p.gate_mode != GATE_LOGDECAY);
         fetch_qkgb(ok0, rowh0, i0, pq0, rows0);
         fetch_v(ok0, rowh0, i0, pq0, rows0);
 #pragma unroll
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     int len;
     if (!decode(item, mcur, n, j, start, len)) break;  // items past the last chunk are all empty
     const int slot = static_cast<int>(item / H);
-    const int h = static_cast<int>(item % H);
+    const int h = item_head(item, H, GS, p.gate_mode != GATE_LOGDECAY);
     const int rows = min(kChunk, len - j * kChunk);  // >= 1 by construction
 
     // thread coordinates from an opaque copy of the thread id, so that the
@@ -473,7 +474,8 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     int64_t stn = 0;
     const bool okn = decode(item + GS, mnext, nn, jn, stn, lenn);
     const int rowsn = okn ? min(kChunk, lenn - jn * kChunk) : 0;
-    const int64_t rowhn = (stn + static_cast<int64_t>(jn) * kChunk + i) * H + static_cast<int>((item + GS) % H);
+    const int64_t rowhn = (stn + static_cast<int64_t>(jn) * kChunk + i) * H +
+                          item_head(item + GS, H, GS, p.gate_mode != GATE_LOGDECAY);
     const int4 mnext2 = map_entry(item + 2 * GS);
     fetch_qkgb(okn, rowhn, i, pq, rowsn);
     asm volatile("" ::: "memory");  // keeps the requests here (not sunk to the loop's end)
