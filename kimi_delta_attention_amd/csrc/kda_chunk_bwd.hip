@@ -1174,7 +1174,7 @@ struct KlocMfmaSmem {
             ET dTt[kChunk][LDC];    // then Z = T^T dT
         } mm;
         struct {
-            float dM[kChunk][LDD];  // scale * dMS (lower incl. diagonal)
+            float dM[kChunk][LDD];  // dMS (lower incl. diagonal), unscaled: exact in bf16
             float dA[kChunk][LDD];  // diag(beta) dA (strictly lower)
         } sc;
     } x;
@@ -1261,7 +1261,7 @@ __device__ __forceinline__ u32x2 level_words(int pos, int base, int h, bool row_
 }
 
 template <int K, int V = K>
-__global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkParams p, ChunkGrads gr,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_bwd_klocal_mfma_kernel(ChunkParams p, ChunkGrads gr,
                                                                          const int32_t* chunk_off, uint8_t* ws,
                                                                          int64_t slot_bytes, int nblk) {
     using MM = Mma<true>;
@@ -1278,11 +1278,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                   "parked tiles must fit the state regions");
     __shared__ __attribute__((aligned(16))) SM s;
 
-    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-    const int lg = lane >> 4, lc = lane & 15;
     const int H = p.H;
 
     {  // the level masks of every lane, once (they depend on the lane only)
+        const int t = threadIdx.x, lane = t & 63, lg = lane >> 4, lc = lane & 15;
         const int lv = t >> 6, hh = 8 >> lv;
         const u32x2 mp = level_words(lc, 4 * lg, hh, true), mr = level_words(lc, 4 * lg, hh, false);
         s.lvm[lv][0][0][lane] = mp[0];
@@ -1291,6 +1290,13 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         s.lvm[lv][1][1][lane] = mr[1];
     }
     for (int blk = blockIdx.x; blk < nblk; blk += gridDim.x) {
+        // The thread index passes through an empty asm each slot, so the
+        // per-lane LDS addresses derived from it are recomputed per slot
+        // rather than hoisted out of the loop and kept live across it.
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        const int lane = t & 63, w = t >> 6;
+        const int lg = lane >> 4, lc = lane & 15;
         const int slot = blk / H;
         const int h = item_head(blk, H, gridDim.x, p.gate_mode != GATE_LOGDECAY);
         int n, j;
@@ -1475,7 +1481,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int a = (t >> 6) + 4 * e, b = t & 63;
-                s.x.sc.dM[a][b] = (b <= a) ? p.scale * MM::to_f32(msv[e]) : 0.f;
+                s.x.sc.dM[a][b] = (b <= a) ? MM::to_f32(msv[e]) : 0.f;  // the scale is applied to the products
             }
         }
         __syncthreads();
@@ -1497,7 +1503,10 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
         const ET* gKE = reinterpret_cast<const ET*>(base + X::kDKE);
         const ET* gKD = reinterpret_cast<const ET*>(base + X::kDKD);
         const float* dgam = reinterpret_cast<const float*>(base + X::kDGAM);
-        const bool any_unsafe = s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3];
+        // sub-blocks whose diagonal block takes the level decomposition (bit I)
+        const int umask = __builtin_amdgcn_readfirstlane(s.unsafe[0] | s.unsafe[1] << 1 | s.unsafe[2] << 2 |
+                                                         s.unsafe[3] << 3);
+        auto unsafe = [&](int I) { return (umask >> I & 1) != 0; };
         float (*opw)[LDF] = s.op[w];
         constexpr bool EW_LDS = SM::EW_LDS;
         ET (*eww)[SM::EWR][16] = s.ew[EW_LDS ? w : 0];
@@ -1525,7 +1534,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             // sub-block factors f(J, I) of this lane's column
             float invp[4];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) invp[I] = s.unsafe[I] ? 0.f : s.invP[I][c];
+            for (int I = 0; I < 4; ++I) invp[I] = unsafe(I) ? 0.f : s.invP[I][c];
             const float f20 = s.F20[c], f30 = s.F30[c], f31 = s.F31[c];
             auto fac = [&](int J, int I) -> float {
                 if (J == I) return invp[I];
@@ -1562,6 +1571,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int J = 0; J <= I; ++J) {
+                    if (J == I && unsafe(I)) continue;  // the level decomposition below
                     const float f = fac(J, I);
                     const f32x4 aq = mma16_f32<false>(&s.x.sc.dM[0][0], SM::LDD, kSub * I, &opw[0][0], LDF, 0,
                                                       kSub * J, lane);
@@ -1578,7 +1588,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 for (int r = 0; r < 4; ++r) {
                     const int i = kSub * I + 4 * lg + r;
                     const float a_ = __expf(Gc[4 * I + r] - Gr);
-                    const float Pq = a_ * pq[r], Pk = a_ * pk[r];
+                    const float Pq = a_ * p.scale * pq[r], Pk = a_ * pk[r];
                     dq[I][r] += Pq;
                     dk[I][r] += Pk;
                     dG[I][r] += MM::to_f32(s.qh[i][c]) * Pq + MM::to_f32(s.kh[i][c]) * Pk;
@@ -1604,15 +1614,16 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                 {
                     const int ir = lane, I = ir / kSub;
                     const ET* xr = pass == 0 ? &s.qh[ir][16 * ct] : &s.kh[ir][16 * ct];
+                    const float sc = pass == 0 ? p.scale : 1.f;  // dM holds dMS unscaled
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float4 g4 = *reinterpret_cast<const float4*>(&s.G[ir][16 * ct + 4 * q]);
                         float4 r4 = {0.f, 0.f, 0.f, 0.f};
                         if (I > 0) r4 = *reinterpret_cast<const float4*>(&s.G[kSub * I - 1][16 * ct + 4 * q]);
-                        opw[4 * q + 0][ir] = MM::to_f32(xr[4 * q + 0]) * __expf(g4.x - r4.x);
-                        opw[4 * q + 1][ir] = MM::to_f32(xr[4 * q + 1]) * __expf(g4.y - r4.y);
-                        opw[4 * q + 2][ir] = MM::to_f32(xr[4 * q + 2]) * __expf(g4.z - r4.z);
-                        opw[4 * q + 3][ir] = MM::to_f32(xr[4 * q + 3]) * __expf(g4.w - r4.w);
+                        opw[4 * q + 0][ir] = sc * MM::to_f32(xr[4 * q + 0]) * __expf(g4.x - r4.x);
+                        opw[4 * q + 1][ir] = sc * MM::to_f32(xr[4 * q + 1]) * __expf(g4.y - r4.y);
+                        opw[4 * q + 2][ir] = sc * MM::to_f32(xr[4 * q + 2]) * __expf(g4.z - r4.z);
+                        opw[4 * q + 3][ir] = sc * MM::to_f32(xr[4 * q + 3]) * __expf(g4.w - r4.w);
                     }
                 }
                 const float* dX = pass == 0 ? &s.x.sc.dM[0][0] : &s.x.sc.dA[0][0];
@@ -1621,6 +1632,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                     if (!mine(J)) continue;
 #pragma unroll
                     for (int I = J; I < 4; ++I) {
+                        if (I == J && unsafe(J)) continue;  // the level decomposition below
                         const float f = fac(J, I);
                         const f32x4 acc =
                             mma16_f32<true>(dX, SM::LDD, kSub * J, &opw[0][0], LDF, 0, kSub * I, lane);
@@ -1645,15 +1657,15 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
             // diagonal sub-blocks too wide to factorise through one reference row:
             // the level decomposition (kda_chunk_common.hpp), every factor <= 1, as
             // 16 x 16 x 16 bf16 products over the block's own 16 rows with the fp32
-            // score gradients and the B values (each lane's own rows of the
-            // block) split into bf16 high and low parts, the A entries of other
-            // levels masked; the diagonal entries directly.  Block values are
-            // selected into registers and the contributions added back by
+            // dA and the B values (each lane's own rows of the block) split into
+            // bf16 high and low parts (dMS is exact in bf16), the A entries of
+            // other levels masked; the diagonal entries directly.  Block values
+            // are selected into registers and the contributions added back by
             // selection (no run-time register indexing).
-            if (any_unsafe) {
+            if (umask) {
 #pragma unroll 1
                 for (int I = 0; I < 4; ++I) {
-                    if (!s.unsafe[I] || !mine(I)) continue;  // uniform over the wave
+                    if (!unsafe(I) || !mine(I)) continue;  // uniform over the wave
                     const int b0 = kSub * I;
                     float gI[4], qI[4], kI[4];
 #pragma unroll
@@ -1679,7 +1691,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         }
                     }
                     u32x2 amh, aml, akh, akl, tmh, tml, tkh, tkl;
-                    split_hi_lo4(am, amh, aml);
+                    split_hi_lo4(am, amh, aml);  // aml and tml are zero
                     split_hi_lo4(ak, akh, akl);
                     split_hi_lo4(tm, tmh, tml);
                     split_hi_lo4(tk, tkh, tkl);
@@ -1699,25 +1711,23 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         const u32x2 wR = {s.lvm[lv][1][0][lane], s.lvm[lv][1][1][lane]};
                         float b4[4];
                         u32x2 bh, bl;
-                        // P terms (dM carries the scale)
+                        // P terms (the scale is applied to the q products)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) b4[r] = later[r] ? 0.f : kI[r] * f[r];
                         split_hi_lo4(b4, bh, bl);
                         f32x4 pq = {0.f, 0.f, 0.f, 0.f}, pk = {0.f, 0.f, 0.f, 0.f};
                         pq = mfma16x16x16(amh & wP, bh, pq);
                         pq = mfma16x16x16(amh & wP, bl, pq);
-                        pq = mfma16x16x16(aml & wP, bh, pq);
                         pk = mfma16x16x16(akh & wP, bh, pk);
                         pk = mfma16x16x16(akh & wP, bl, pk);
                         pk = mfma16x16x16(akl & wP, bh, pk);
                         // R terms: q against dM, then k against dA
                         f32x4 rr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? qI[r] * f[r] : 0.f;
+                        for (int r = 0; r < 4; ++r) b4[r] = later[r] ? p.scale * qI[r] * f[r] : 0.f;
                         split_hi_lo4(b4, bh, bl);
                         rr = mfma16x16x16(tmh & wR, bh, rr);
                         rr = mfma16x16x16(tmh & wR, bl, rr);
-                        rr = mfma16x16x16(tml & wR, bh, rr);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) b4[r] = later[r] ? kI[r] * f[r] : 0.f;
                         split_hi_lo4(b4, bh, bl);
@@ -1726,7 +1736,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
                         rr = mfma16x16x16(tkl & wR, bh, rr);
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
-                            const float Pq = later[r] ? f[r] * pq[r] : 0.f;
+                            const float Pq = later[r] ? f[r] * p.scale * pq[r] : 0.f;
                             const float Pk = later[r] ? f[r] * pk[r] : 0.f;
                             const float R = later[r] ? 0.f : f[r] * rr[r];
                             dqI[r] += Pq;
@@ -1739,7 +1749,7 @@ __global__ __launch_bounds__(kThreads) void chunk_bwd_klocal_mfma_kernel(ChunkPa
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = b0 + 4 * lg + r;
-                        const float dmii = s.x.sc.dM[i][i];
+                        const float dmii = p.scale * s.x.sc.dM[i][i];
                         dqI[r] += dmii * kI[r];
                         dkI[r] += dmii * qI[r];
                     }
@@ -2307,12 +2317,16 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                     qo[4 * I + r] = MM::to_f32(s.qh[i][c]);
                     ko[4 * I + r] = MM::to_f32(s.kh[i][c]);
                 }
+            // sub-blocks whose diagonal block takes the level decomposition (bit I)
+            const int umask = __builtin_amdgcn_readfirstlane(s.unsafe[0] | s.unsafe[1] << 1 | s.unsafe[2] << 2 |
+                                                             s.unsafe[3] << 3);
+            auto unsafe = [&](int I) { return (umask >> I & 1) != 0; };
             float Ge[4], Gr[4], invp[4];
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 Ge[I] = s.G[kSub * I + kSub - 1][c];
                 Gr[I] = I == 0 ? 0.f : s.G[kSub * I - 1][c];
-                invp[I] = s.unsafe[I] ? 0.f : s.invP[I][c];
+                invp[I] = unsafe(I) ? 0.f : s.invP[I][c];
             }
             const float f20 = s.F20[c], f30 = s.F30[c], f31 = s.F31[c];
             auto fac = [&](int J, int I) -> float {
@@ -2355,6 +2369,7 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int Jp = 0; Jp <= I; Jp += 2) {
+                    if (Jp == I && unsafe(I)) continue;  // only the diagonal block, taken below
                     MM::Frag bh, bl;
                     pair_b(fac(Jp, I), Jp, Jp + 1 <= I ? fac(Jp + 1, I) : 0.f, Jp + 1, bh, bl);
                     const auto am = load_ap<MM>(&s.x.sc.dM[0][0], LDC, kSub * I, kSub * Jp, lane);
@@ -2395,6 +2410,7 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
 #pragma unroll
                     for (int Ip = 0; Ip < 4; Ip += 2) {
                         if (Ip + 1 < J) continue;
+                        if (Ip + 1 == J && unsafe(J)) continue;  // only the diagonal block, taken below
                         MM::Frag bh, bl;
                         pair_b(Ip >= J ? fac(J, Ip) : 0.f, Ip, fac(J, Ip + 1), Ip + 1, bh, bl);
                         if (pass == 0) {
@@ -2427,10 +2443,10 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
             // code serves every block: the block's register values are selected
             // in and its contributions added back by selection, so that no
             // register array is indexed at run time.
-            if (s.unsafe[0] | s.unsafe[1] | s.unsafe[2] | s.unsafe[3]) {
+            if (umask) {
 #pragma unroll 1
                 for (int I = 0; I < 4; ++I) {
-                    if (!s.unsafe[I]) continue;  // uniform over the workgroup
+                    if (!unsafe(I)) continue;  // uniform over the workgroup
                     float gI[4], qI[4], kI[4];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
