@@ -1830,13 +1830,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
 
             // gate chain rule.  Every gate input is requested before the first
-            // d(gate) store, one sub-block ahead of its use: loads and stores
-            // share one in-order counter, so a load issued behind a store would
-            // also wait for that store.  dG becomes d(gate input) in place.
+            // d(gate) store (loads and stores share one in-order counter, so a
+            // load issued behind a store would also wait for that store), each
+            // sub-block's at its use: a request one sub-block ahead would be
+            // waited for at once and spilled at this register budget.  dG
+            // becomes d(gate input) in place.
             const float bias = (p.dt_bias && p.gate_mode != GATE_LOGDECAY) ? p.dt_bias[h * K + c] : 0.f;
             float ddt = 0.f;
             if (p.gate_mode != GATE_LOGDECAY) {
-                float zc[4], zn[4];
+                float zc[4];
                 auto zload = [&](int I, float (&z)[4]) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -1845,11 +1847,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                         z[r] = p.g[((rbase + ic) * H + h) * K + c];
                     }
                 };
-                zload(I0, zc);
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     if (!mine(I)) continue;
-                    if (I + 1 < I1) zload(I + 1, zn);
+                    zload(I, zc);
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int i = kSub * I + 4 * lg + r;
@@ -1872,10 +1873,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                             dal += da;
                         }
                         dG[I][r] = dx;
-                    }
-                    if (I + 1 < I1) {
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) zc[r] = zn[r];
                     }
                 }
             }
