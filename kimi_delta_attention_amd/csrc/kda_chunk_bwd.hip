@@ -1252,6 +1252,17 @@ __device__ __forceinline__ void split_hi_lo4(const float (&x)[4], u32x2& hi, u32
     lo = u32x2{__builtin_bit_cast(uint32_t, l0), __builtin_bit_cast(uint32_t, l1)};
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// The products f b0, f b1 as bf16 high parts (one conversion for the pair)
+// and bf16 remainders f b - hi, taken of the exact products (fused).
+__device__ __forceinline__ void split_prod2(float f, float b0, float b1, uint32_t& hi, uint32_t& lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{f * b0, f * b1}, bf16x2_t));
+    const float r0 = fmaf(f, b0, -__uint_as_float(hi << 16));
+    const float r1 = fmaf(f, b1, -__uint_as_float(hi & 0xffff0000u));
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{r0, r1}, bf16x2_t));
+}
+
 // AND masks over four bf16 entries (two per word) that keep the entries e of
 // level_keep(pos, base, h, row_is_later) and clear the others.
 __device__ __forceinline__ u32x2 level_words(int pos, int base, int h, bool row_is_later) {
@@ -2348,16 +2359,21 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
             // of load_ap): the lane's B values are its own rows of both.  B is
             // split into bf16 high and low parts, and so is dA (dMS is exact in
             // bf16), so that the products keep about 16 bits of their operands.
-            auto pair_b = [&](float f0, int b0, float f1, int b1, MM::Frag& hi, MM::Frag& lo) {
-                u16x8 uh, ul;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x_ = e < 4 ? f0 * bv[4 * b0 + e] : f1 * bv[4 * b1 + e - 4];
-                    uh[e] = MM::from_f32(x_);
-                    ul[e] = MM::from_f32(x_ - MM::to_f32(uh[e]));
+            // A half whose sub-block lies outside the product (has0 / has1
+            // false, known at compile time) is zero without arithmetic.
+            auto pair_b = [&](float f0, int b0, bool has0, float f1, int b1, bool has1, MM::Frag& hi,
+                              MM::Frag& lo) {
+                uint32_t h[4] = {0u, 0u, 0u, 0u}, l[4] = {0u, 0u, 0u, 0u};
+                if (has0) {
+                    split_prod2(f0, bv[4 * b0], bv[4 * b0 + 1], h[0], l[0]);
+                    split_prod2(f0, bv[4 * b0 + 2], bv[4 * b0 + 3], h[1], l[1]);
                 }
-                hi = __builtin_bit_cast(MM::Frag, uh);
-                lo = __builtin_bit_cast(MM::Frag, ul);
+                if (has1) {
+                    split_prod2(f1, bv[4 * b1], bv[4 * b1 + 1], h[2], l[2]);
+                    split_prod2(f1, bv[4 * b1 + 2], bv[4 * b1 + 3], h[3], l[3]);
+                }
+                hi = __builtin_bit_cast(MM::Frag, u32x4_t{h[0], h[1], h[2], h[3]});
+                lo = __builtin_bit_cast(MM::Frag, u32x4_t{l[0], l[1], l[2], l[3]});
             };
             f32x4 pq[4], pk[4];
 #pragma unroll
@@ -2368,7 +2384,7 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                 for (int Jp = 0; Jp <= I; Jp += 2) {
                     if (Jp == I && unsafe(I)) continue;  // only the diagonal block, taken below
                     MM::Frag bh, bl;
-                    pair_b(fac(Jp, I), Jp, Jp + 1 <= I ? fac(Jp + 1, I) : 0.f, Jp + 1, bh, bl);
+                    pair_b(fac(Jp, I), Jp, true, Jp + 1 <= I ? fac(Jp + 1, I) : 0.f, Jp + 1, Jp + 1 <= I, bh, bl);
                     const auto am = load_ap<MM>(&s.x.sc.dM[0][0], LDC, kSub * I, kSub * Jp, lane);
                     const auto ah = load_ap<MM>(&s.x.sc.dA[0][0], LDC, kSub * I, kSub * Jp, lane);
                     const auto al = load_ap<MM>(&s.x.sc.dAl[0][0], LDC, kSub * I, kSub * Jp, lane);
@@ -2409,7 +2425,7 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
                         if (Ip + 1 < J) continue;
                         if (Ip + 1 == J && unsafe(J)) continue;  // only the diagonal block, taken below
                         MM::Frag bh, bl;
-                        pair_b(Ip >= J ? fac(J, Ip) : 0.f, Ip, fac(J, Ip + 1), Ip + 1, bh, bl);
+                        pair_b(Ip >= J ? fac(J, Ip) : 0.f, Ip, Ip >= J, fac(J, Ip + 1), Ip + 1, true, bh, bl);
                         if (pass == 0) {
                             const auto am = load_kn<MM>(&s.x.sc.dM[0][0], LDC, kSub * Ip, kSub * J, lane);
                             rr[J] = MM::mma(am, bh, rr[J]);
