@@ -660,19 +660,23 @@ __global__ __launch_bounds__(prep_threads(K)) void chunk_prep_kernel(ChunkParams
     __syncthreads();
 
     // ---- 6. T = (I + A)^-1: diagonal sub-blocks by forward substitution ...
-    // (T above the diagonal is never read before step 7, which masks it)
+    // (T above the diagonal is never read before step 7, which masks it).
+    // Lane jc solves column jc: x_r = [r == jc] - sum_{m < r} A_rm x_m.  The
+    // sums are formed column by column (each x_m, once known, enters every
+    // later row's sum at once), so the dependent chain is one product per
+    // row rather than the whole sum; every sum still adds its terms in the
+    // order m = 0, 1, ...
     if (w < 4 && lane < kSub) {
         const int I = w;
         const int jc = lane;
-        float x[kSub];
+        float x[kSub], acc[kSub];
 #pragma unroll
-        for (int m = 0; m < kSub; ++m) x[m] = (m == jc) ? 1.f : 0.f;
+        for (int r = 0; r < kSub; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int r = 1; r < kSub; ++r) {
-            float acc = 0.f;
+        for (int m = 0; m < kSub; ++m) {
+            x[m] = m < jc ? 0.f : (m == jc ? 1.f : -acc[m]);
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc += s.A[kSub * I + r][kSub * I + m] * x[m];
-            if (r > jc) x[r] = -acc;
+            for (int r = m + 1; r < kSub; ++r) acc[r] += s.A[kSub * I + r][kSub * I + m] * x[m];
         }
 #pragma unroll
         for (int r = 0; r < kSub; ++r) s.u.T[kSub * I + r][kSub * I + jc] = x[r];
