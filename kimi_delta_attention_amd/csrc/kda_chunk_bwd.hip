@@ -1317,13 +1317,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         const int rows = min(kChunk, len - j * kChunk);
         uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
         const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
-        const float rate = (p.gate_mode == GATE_LOGDECAY) ? 0.f : __expf(p.A_log[h]);
+        float rate = 0.f;  // e^(A_log[h]), requested in the prologue with the row inputs
         __syncthreads();  // the previous slot is done with the shared buffers
 
         // ---- 0. prologue (row-wise), cumulative sum, sub-block factors
         {
             const int i = t >> 2, c0 = (t & 3) * CPT;
             const bool valid = i < rows;
+            // the gate parameters first, so that the waits for the rows
+            // below cover them (one wait, not one per element)
+            float bias[CPT];
+            if (p.gate_mode != GATE_LOGDECAY && p.dt_bias) {
+                load_row<CPT>(p.dt_bias + h * K + c0, bias);
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) bias[c] = 0.f;
+            }
+            // rate = e^alog is taken at use.  The request is unconditional (a
+            // valid word of beta stands in without an in-kernel gate) and its
+            // per-lane address (min(t, 0) is 0, which the compiler cannot see)
+            // keeps the value in a vector register, so that its wait falls at
+            // the use, with the rows'.
+            const bool gated = p.gate_mode != GATE_LOGDECAY;
+            const float alog = (gated ? p.A_log : p.beta)[(gated ? h : 0) + min(t, 0)];
             float qv[CPT], kv[CPT], gv[CPT];
             float braw = 0.f;
             if (valid) {
@@ -1353,10 +1369,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
             }
             if (!valid) rq = rk = 0.f;
             if (p.gate_mode != GATE_LOGDECAY) {
-                const float* bias = p.dt_bias ? p.dt_bias + h * K + c0 : nullptr;
+                rate = __expf(alog);
 #pragma unroll 4
                 for (int c = 0; c < CPT; ++c)
-                    gv[c] = valid ? gate_eff(p.gate_mode, gv[c], rate, bias ? bias[c] : 0.f, p.lower_bound) : 0.f;
+                    gv[c] = valid ? gate_eff(p.gate_mode, gv[c], rate, bias[c], p.lower_bound) : 0.f;
             }
 #pragma unroll
             for (int v = 0; v < CPT / 8; ++v) {
@@ -2112,7 +2128,7 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
         const int rows = min(kChunk, len - j * kChunk);
         uint8_t* base = ws + (static_cast<int64_t>(slot) * H + h) * slot_bytes;
         const int64_t rbase = start + static_cast<int64_t>(j) * kChunk;
-        const float rate = (p.gate_mode == GATE_LOGDECAY) ? 0.f : __expf(p.A_log[h]);
+        float rate = 0.f;  // e^(A_log[h]), requested in the prologue with the row inputs
         __syncthreads();  // the previous slot is done with the shared buffers
 
         // stage 1's operands are requested first, so that their latency
@@ -2141,6 +2157,22 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
         {
             const int i = t / TPR, c0 = (t % TPR) * CPT;
             const bool valid = i < rows;
+            // the gate parameters first, so that the waits for the rows
+            // below cover them (one wait, not one per element)
+            float bias[CPT];
+            if (p.gate_mode != GATE_LOGDECAY && p.dt_bias) {
+                load_row<CPT>(p.dt_bias + h * K + c0, bias);
+            } else {
+#pragma unroll
+                for (int cc = 0; cc < CPT; ++cc) bias[cc] = 0.f;
+            }
+            // rate = e^alog is taken at use.  The request is unconditional (a
+            // valid word of beta stands in without an in-kernel gate) and its
+            // per-lane address (min(t, 0) is 0, which the compiler cannot see)
+            // keeps the value in a vector register, so that its wait falls at
+            // the use, with the rows'.
+            const bool gated = p.gate_mode != GATE_LOGDECAY;
+            const float alog = (gated ? p.A_log : p.beta)[(gated ? h : 0) + min(t, 0)];
             float qv[CPT], kv[CPT], gv[CPT];
             float braw = 0.f;
             if (valid) {
@@ -2171,10 +2203,10 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
             }
             if (!valid) rq = rk = 0.f;
             if (p.gate_mode != GATE_LOGDECAY) {
-                const float* bias = p.dt_bias ? p.dt_bias + h * K + c0 : nullptr;
+                rate = __expf(alog);
 #pragma unroll 4
                 for (int cc = 0; cc < CPT; ++cc)
-                    gv[cc] = valid ? gate_eff(p.gate_mode, gv[cc], rate, bias ? bias[cc] : 0.f, p.lower_bound) : 0.f;
+                    gv[cc] = valid ? gate_eff(p.gate_mode, gv[cc], rate, bias[cc], p.lower_bound) : 0.f;
             }
 #pragma unroll
             for (int v = 0; v < CPT / 8; ++v) {
