@@ -1271,10 +1271,13 @@ __device__ __forceinline__ u32x2 level_words(int pos, int base, int h, bool row_
                  ((m & 4u) ? 0x0000FFFFu : 0u) | ((m & 8u) ? 0xFFFF0000u : 0u)};
 }
 
+// Two waves per SIMD are requested from the register allocator: at K = 32 the
+// LDS (80.9 KB) holds two workgroups per CU, which the register budget then
+// allows too (a few spills, outside the per-slot loops); at K = 64 the LDS
+// holds one workgroup and the request has no effect.
 template <int K, int V = K>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_bwd_klocal_mfma_kernel(ChunkParams p, ChunkGrads gr,
-                                                                         const int32_t* chunk_off, uint8_t* ws,
-                                                                         int64_t slot_bytes, int nblk) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void chunk_bwd_klocal_mfma_kernel(
+    ChunkParams p, ChunkGrads gr, const int32_t* chunk_off, uint8_t* ws, int64_t slot_bytes, int nblk) {
     using MM = Mma<true>;
     using ET = uint16_t;
     using X = BwdExtra<K, true, V>;
