@@ -431,7 +431,11 @@ __host__ __device__ constexpr int vlocal_threads(bool bf) { return bf ? 512 : 25
 // Per V-column block of BV columns: Y = v - KE S, dD = KD dS' + MS^T dO,
 // D = TB Y, dY = TB^T dD (= dv), and the V-summed products dQE, dKE, dKD,
 // dMS, dTB, dgam accumulate over the blocks.  The next block's S, dS', dO and
-// v are requested before the current block's products.  Every operand stays
+// v are requested before the current block's products.  dgam (per key, the
+// sum over the value columns of S dS') is formed from the blocks' S and dS'
+// vectors while they are in registers: each thread keeps the partial sums of
+// its vector's keys, and the BV threads that hold one key vector's columns
+// add theirs at the end of the item, within their wave.  Every operand stays
 // in LDS in the layout it arrives in: products that need a transposed operand
 // (MS^T, TB^T, and S, dS', dO, Y, dD as [k][n] B operands) read it through
 // the transposing LDS read (load_kn).
@@ -645,12 +649,36 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
     for (int c = 0; c < AW; ++c) aQE[c] = aKE[c] = aKD[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < CW; ++c) aMS[c] = aTB[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float dgam = 0.f;
+    float dgp[PS][VE];  // dgam partials: keys of the thread's S / dS' vectors, its columns, blocks so far
+#pragma unroll
+    for (int m = 0; m < PS; ++m)
+#pragma unroll
+        for (int q = 0; q < VE; ++q) dgp[m][q] = 0.f;
     const int klo = (16 * rt / MM::KS) * MM::KS;
 
     for (int vb = 0; vb < V / BV; ++vb) {
         const int v0 = vb * BV;
         stage(t);
+        // dgam partials from the vectors just staged (bf16 products are exact in fp32)
+#pragma unroll
+        for (int m = 0; m < PS; ++m) {
+            const int e = t + m * NT;
+            if (NVS % NT == 0 || e < NVS) {
+                if constexpr (BF) {
+                    // bf16 pairs: the low half is the earlier key
+                    const u32x4_t a = __builtin_bit_cast(u32x4_t, rS[m]), b = __builtin_bit_cast(u32x4_t, rD[m]);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        dgp[m][2 * q] += __uint_as_float(a[q] << 16) * __uint_as_float(b[q] << 16);
+                        dgp[m][2 * q + 1] +=
+                            __uint_as_float(a[q] & 0xffff0000u) * __uint_as_float(b[q] & 0xffff0000u);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) dgp[m][q] += rS[m][q] * rD[m][q];
+                }
+            }
+        }
         float vcur[TW][4];
 #pragma unroll
         for (int m = 0; m < TW; ++m)
@@ -706,13 +734,16 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
                 dy = MM::mma(load_kn<MM>(&TBn[0][0], LDC, k0, 16 * rt, lane),
                              load_kn<MM>(&dDn[0][0], LDB, k0, 16 * ct, lane), dy);
             tile_store<MM>(&dYn[0][0], LDB, 16 * rt, 16 * ct, dy, lane);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * rt + 4 * (lane >> 4) + r;
-                if (i < rows) Elem<IT>::store(dvg, ((rbase + i) * H + h) * V + v0 + 16 * ct + (lane & 15), dy[r]);
-            }
         }
         __syncthreads();
+
+        // dv = dY, the block's rows from LDS as 16-byte vectors
+        for (int e = t; e < kChunk * VPR; e += NT) {
+            const int i = e / VPR, c = (e % VPR) * VE;
+            if (i < rows)
+                *reinterpret_cast<f32x4*>(dvg + ((rbase + i) * H + h) * V + v0 + c) =
+                    *reinterpret_cast<const f32x4*>(&dYn[i][c]);
+        }
 
         // V-summed products over this column block (contraction over the block's
         // value columns; S and dS' enter as [v][key] B operands)
@@ -734,9 +765,6 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
             aMS[m] = gemm<MM>(&dOn[0][0], LDB, 16 * rt, &Dn[0][0], LDB, 16 * c, 0, BV, aMS[m], lane);
             aTB[m] = gemm<MM>(&dDn[0][0], LDB, 16 * rt, &Yn[0][0], LDB, 16 * c, 0, BV, aTB[m], lane);
         }
-        for (int key = t; key < K; key += NT)
-#pragma unroll 4
-            for (int c = 0; c < BV; ++c) dgam += MM::to_f32(St[c][key]) * MM::to_f32(dSt[c][key]);
         __syncthreads();
     }
 
@@ -762,7 +790,32 @@ __global__ __launch_bounds__(vlocal_threads(BF)) void chunk_bwd_vlocal_kernel(Ch
             gMS[i * kChunk + col] = MM::from_f32(aMS[m][r]);
             gTB[i * kChunk + col] = MM::from_f32(aTB[m][r]);
         }
-    for (int key = t; key < K; key += NT) reinterpret_cast<float*>(base + X::kDGAM)[key] = dgam;
+    // dgam: the BV threads of a key vector (aligned lanes of one wave) add
+    // their partials, rows of 16 lanes first, then row pairs (the swap of
+    // rows 1 and 0, 3 and 2); the thread of column 0 stores the keys
+    static_assert(BV == 16 || BV == 32, "a key vector's columns span one or two 16-lane rows");
+#pragma unroll
+    for (int m = 0; m < PS; ++m) {
+        const int e = t + m * NT;
+#pragma unroll
+        for (int q = 0; q < VE; ++q) {
+            float v = row16_sum(dgp[m][q]);
+            if constexpr (BV == 32) {
+                // the pair's elements go through integer copies: a bit cast
+                // applied to an element of the returned vector reads element 0
+                const uint32_t u = __builtin_bit_cast(uint32_t, v);
+                const auto pr = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+                const uint32_t x = pr[0], y = pr[1];
+                v = __uint_as_float(x) + __uint_as_float(y);
+            }
+            dgp[m][q] = v;
+        }
+        if ((NVS % NT == 0 || e < NVS) && e % BV == 0) {
+            float* gd = reinterpret_cast<float*>(base + X::kDGAM) + (e / BV) * VE;
+#pragma unroll
+            for (int q = 0; q < VE; ++q) gd[q] = dgp[m][q];
+        }
+    }
     lc = ln;
     mnext = mnext2;
     }  // items

@@ -68,6 +68,22 @@ def test_bwd_boundary_lengths(T, dtype, K, V):
     _compare(w, f"T={T} K={K} V={V}")
 
 
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.float32, 64, 64), (torch.bfloat16, 64, 64),
+                                       (torch.bfloat16, 128, 128), (torch.float32, 32, 64),
+                                       (torch.bfloat16, 32, 64)])
+def test_bwd_weak_decay(dtype, K, V):
+    """Log-decay drawn in [-0.02, 0] per step (a chunk decays the state by about
+    e^-0.6), with a final-state cotangent: the state gradient carries back
+    through every chunk boundary, and the gate gradient's state-decay term
+    (per key, the sum over the value columns of the entry state times the
+    exit state's gradient, scaled by the chunk's total decay) is of the order
+    of the rest of dg.  With the default [-5, 0] draw that term is scaled by
+    about e^-160 in every whole chunk."""
+    w = inputs.chunk_inputs(2, 320, 3, K, V, seed=600 + K + V, dtype=dtype, lower_bound=-0.02, h0_std=0.1,
+                            with_grad_out=True, dfinal_std=0.1)
+    _compare(w, f"weak decay K={K} V={V}")
+
+
 @pytest.mark.parametrize("mode", [inputs.GATE_SAFE, inputs.GATE_SOFTPLUS])
 @pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.bfloat16, 128, 128), (torch.bfloat16, 32, 64)])
 def test_bwd_in_kernel_gates(mode, dtype, K, V):

@@ -80,6 +80,17 @@ def test_fwd_boundary_lengths(T, dtype, K, V):
     _compare(w, f"T={T} K={K} V={V}")
 
 
+@pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.float32, 64, 64), (torch.bfloat16, 64, 64),
+                                       (torch.bfloat16, 128, 128), (torch.bfloat16, 32, 64)])
+def test_fwd_weak_decay(dtype, K, V):
+    """Log-decay drawn in [-0.02, 0] per step: a chunk decays the state by about
+    e^-0.6, so the state carries through every chunk boundary.  With the
+    default [-5, 0] draw a chunk decays it by about e^-160, and only the first
+    rows of a chunk see the state it enters with."""
+    w = inputs.chunk_inputs(2, 320, 3, K, V, seed=500 + K + V, dtype=dtype, lower_bound=-0.02, h0_std=0.1)
+    _compare(w, f"weak decay K={K} V={V}")
+
+
 @pytest.mark.parametrize("mode", [inputs.GATE_SAFE, inputs.GATE_SOFTPLUS])
 @pytest.mark.parametrize("dtype,K,V", [(torch.float32, 32, 32), (torch.bfloat16, 128, 128), (torch.bfloat16, 32, 64)])
 def test_fwd_in_kernel_gates(mode, dtype, K, V):
