@@ -2839,16 +2839,17 @@ __global__ __launch_bounds__(kKlocW8Threads) void chunk_bwd_klocal_w8_kernel(Chu
 
 // d(A_log) and d(dt_bias): deterministic sums of the per-chunk shares.  One
 // workgroup per head; thread (slot lane sl, column lane cl) sums the slots
-// sl, sl + 8, ... of its columns with four requests in flight, and the eight
+// sl, sl + SL, ... of its columns with eight requests in flight, and the SL
 // slot lanes' sums are added in a fixed order, so results are run-to-run
-// identical without atomics.
+// identical without atomics.  At K <= 64 the K + 1 columns take 64 column
+// lanes, so that 16 slot lanes share the slots.
 constexpr int kGateReduceThreads = 1024;
 template <int K>
 __global__ __launch_bounds__(kGateReduceThreads) void gate_param_reduce_kernel(ChunkParams p, ChunkGrads gr,
                                                                               const int32_t* chunk_off,
                                                                               const uint8_t* ws, int64_t slot_bytes,
                                                                               size_t gp_off) {
-    constexpr int CL = 128;                      // column lanes
+    constexpr int CL = K >= 128 ? 128 : 64;      // column lanes
     constexpr int SL = kGateReduceThreads / CL;  // slot lanes
     constexpr int NCOL = K + 1;                  // K d(dt_bias) shares and the d(A_log) share
     constexpr int CPL = (NCOL + CL - 1) / CL;    // columns per column lane
@@ -2866,12 +2867,12 @@ __global__ __launch_bounds__(kGateReduceThreads) void gate_param_reduce_kernel(C
                 return reinterpret_cast<const float*>(ws + (static_cast<int64_t>(s_) * H + h) * slot_bytes + gp_off)[c];
             };
             int s_ = sl;
-            for (; s_ + 3 * SL < nslots; s_ += 4 * SL) {
-                const float a0 = share(s_), a1 = share(s_ + SL), a2 = share(s_ + 2 * SL), a3 = share(s_ + 3 * SL);
-                acc += a0;
-                acc += a1;
-                acc += a2;
-                acc += a3;
+            for (; s_ + 7 * SL < nslots; s_ += 8 * SL) {
+                float a[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) a[u] = share(s_ + u * SL);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) acc += a[u];
             }
             for (; s_ < nslots; s_ += SL) acc += share(s_);
         }
