@@ -41,14 +41,19 @@ namespace kda {
 
 // ------------------------------------------------------------------ plan
 // The plan of a packed call (layout at plan_map_offset): chunk_off by a
-// block-wide scan of the sequences' chunk counts, then the slot map.  One
-// workgroup of kPlanThreads; sequence offsets are clamped into [0, T] as in
-// seq_bounds.
+// block-wide scan of the sequences' chunk counts (kPlanThreads per round:
+// shuffle scans within each wave, then the waves' totals), then the slot map,
+// each slot's sequence found by a binary search over the offsets (read from
+// LDS up to kPlanLdsSeqs sequences, from chunk_off beyond).  One workgroup of
+// kPlanThreads; sequence offsets are clamped into [0, T] as in seq_bounds.
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanLdsSeqs = 4096;
 static __global__ __launch_bounds__(kPlanThreads) void plan_chunks_kernel(const int32_t* cu, int N, int T,
                                                                           int32_t* chunk_off, int bound) {
-    __shared__ int part[kPlanThreads];
-    const int t = threadIdx.x;
+    constexpr int NW = kPlanThreads / 64;
+    __shared__ int wsum[NW];
+    __shared__ int offs[kPlanLdsSeqs + 1];
+    const int t = threadIdx.x, lane = t & 63, w = t >> 6;
     auto clamp_seq = [&](int n, int& a, int& b) {
         a = cu[n];
         b = cu[n + 1];
@@ -64,20 +69,36 @@ static __global__ __launch_bounds__(kPlanThreads) void plan_chunks_kernel(const 
             clamp_seq(n, a, b);
             c = n_chunks(b - a);
         }
-        part[t] = c;
-        __syncthreads();
-        for (int o = 1; o < kPlanThreads; o <<= 1) {  // inclusive scan
-            const int v = t >= o ? part[t - o] : 0;
-            __syncthreads();
-            part[t] += v;
-            __syncthreads();
+        int v = c;  // inclusive scan within the wave
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int u = __shfl_up(v, o, 64);
+            if (lane >= o) v += u;
         }
-        if (n < N) chunk_off[n] = carry + part[t] - c;
-        carry += part[kPlanThreads - 1];
+        if (lane == 63) wsum[w] = v;
         __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) {
+            const int s_ = wsum[q];
+            if (q < w) before += s_;
+            total += s_;
+        }
+        if (n < N) {
+            const int off = carry + before + v - c;
+            chunk_off[n] = off;
+            if (n < kPlanLdsSeqs) offs[n] = off;
+        }
+        carry += total;
+        __syncthreads();  // wsum is rewritten by the next round
     }
-    if (t == 0) chunk_off[N] = carry;
-    __syncthreads();  // chunk_off is read back below by other threads of this workgroup
+    if (t == 0) {
+        chunk_off[N] = carry;
+        if (N <= kPlanLdsSeqs) offs[N] = carry;
+    }
+    __syncthreads();  // the offsets are read back below by other threads of this workgroup
+    const bool in_lds = N <= kPlanLdsSeqs;
+    auto off_at = [&](int m) { return in_lds ? offs[m] : chunk_off[m]; };
     int4* map = reinterpret_cast<int4*>(reinterpret_cast<uint8_t*>(chunk_off) + plan_map_offset(N));
     for (int c = t; c < bound; c += kPlanThreads) {
         int4 e = {-1, 0, 0, 0};
@@ -85,11 +106,11 @@ static __global__ __launch_bounds__(kPlanThreads) void plan_chunks_kernel(const 
             int lo = 0, hi = N - 1;  // last n with chunk_off[n] <= c
             while (lo < hi) {
                 const int mid = (lo + hi + 1) >> 1;
-                if (chunk_off[mid] <= c) lo = mid; else hi = mid - 1;
+                if (off_at(mid) <= c) lo = mid; else hi = mid - 1;
             }
             int a, b;
             clamp_seq(lo, a, b);
-            e = int4{lo, c - chunk_off[lo], a, b - a};
+            e = int4{lo, c - off_at(lo), a, b - a};
         }
         map[c] = e;
     }

@@ -105,6 +105,18 @@ def test_fwd_varlen_with_empty_and_tiny_sequences():
     _compare(w, "varlen")
 
 
+def test_fwd_more_sequences_than_the_plans_lds_offsets():
+    """4,500 packed sequences of 0..12 tokens (above the 4,096 whose chunk
+    offsets the plan kernel keeps in LDS for its slot search, so the search
+    reads them from the workspace), H1 K=V=32 bf16."""
+    gen = torch.Generator().manual_seed(71)
+    lens = torch.randint(0, 13, (4500,), generator=gen)
+    lens[::101] = 0
+    cu = [0] + torch.cumsum(lens, 0).tolist()
+    w = inputs.chunk_inputs(1, cu[-1], 1, 32, 32, seed=72, dtype=torch.bfloat16, cu_seqlens=cu, h0_std=0.1)
+    _compare(w, f"N={len(cu) - 1} T={cu[-1]}")
+
+
 def test_fwd_no_l2norm_and_plain_scale():
     w = inputs.chunk_inputs(1, 96, 2, 32, 32, seed=8)
     # unit-norm keys supplied by the caller, so the chunk form stays well conditioned
