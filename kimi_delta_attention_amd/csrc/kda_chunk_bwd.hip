@@ -396,8 +396,10 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
         }
     }
     __syncthreads();
-    for (int jc = nc - 1; jc >= 0; --jc) {
-        if (prod) {
+    // One loop per role (each wave passes the same nc barriers): a shared loop
+    // body makes the compiler keep both roles' values live at once.
+    if (prod) {
+        for (int jc = nc - 1; jc >= 0; --jc) {
             // staging reads before this step's copies (the compiler would wait
             // for the copies before later LDS reads); the warm-up loads are
             // issued last and are the only ones allowed to stay in flight
@@ -407,10 +409,13 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
             warm(jc >= kWarmAhead ? jc - kWarmAhead : jc);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmem<NWARM>();
-        } else {
-            step(jc);
+            barrier_lds();
         }
-        barrier_lds();
+    } else {
+        for (int jc = nc - 1; jc >= 0; --jc) {
+            step(jc);
+            barrier_lds();
+        }
     }
     if (prod) {
         if (nc > 0) drain(0);
@@ -2928,10 +2933,14 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                dim3(prep_threads(K)), 0, st, p, chunk_off, slots, sb, nblk);
     }
     if (want(1) && cgrid > 0) {
-        if constexpr (K == 128 && V == 128 && BF)
-            hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<true, false>), dim3(cgrid), dim3(256), 0, st, p, chunk_off,
-                               slots, sb);
-        else if (cgrid <= kPersistentGrid)  // few chains: 8 waves per chain (see the forward)
+        if constexpr (K == 128 && V == 128 && BF) {
+            if (state_pc_bv(p.N * p.H) == 32)
+                hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<true, false, 32>), dim3(cgrid),
+                                   dim3(state_pc_threads(32)), 0, st, p, chunk_off, slots, sb);
+            else
+                hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<true, false, 64>), dim3(chain_grid(p.N * p.H, 2)),
+                                   dim3(state_pc_threads(64)), 0, st, p, chunk_off, slots, sb);
+        } else if (cgrid <= kPersistentGrid)  // few chains: 8 waves per chain (see the forward)
             hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, true, false, 512>), dim3(cgrid), dim3(512), 0,
                                st, p, chunk_off, slots, sb);
         else

@@ -71,9 +71,14 @@ static hipError_t run_fwd(const ChunkParams& p, void* ws, hipStream_t st, int st
         // each chunk step; otherwise 4 waves let two chains share a CU
         const int grid = chain_grid(p.N * p.H, V / BV);
         if constexpr (K == 128 && V == 128 && BF) {
-            if (grid > 0)
-                hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<KEEP, true>), dim3(grid), dim3(256), 0, st, p, chunk_off,
-                                   prep, sb);
+            if (state_pc_bv(p.N * p.H) == 32) {
+                if (grid > 0)
+                    hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<KEEP, true, 32>), dim3(grid),
+                                       dim3(state_pc_threads(32)), 0, st, p, chunk_off, prep, sb);
+            } else {
+                hipLaunchKernelGGL((chunk_state_fwd_pc_kernel<KEEP, true, 64>), dim3(chain_grid(p.N * p.H, 2)),
+                                   dim3(state_pc_threads(64)), 0, st, p, chunk_off, prep, sb);
+            }
         } else if (grid > 0 && grid <= kPersistentGrid)
             hipLaunchKernelGGL((chunk_state_fwd_kernel<K, V, BV, BF, KEEP, true, 512>), dim3(grid), dim3(512), 0,
                                st, p, chunk_off, prep, sb);

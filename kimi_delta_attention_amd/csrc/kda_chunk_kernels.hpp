@@ -1111,30 +1111,56 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
 }
 
 // ------------------------------------------------------------------ state (producer/consumer)
-// Forward state pass for K = V = 128 in bf16, 32 value columns per workgroup,
-// 256 threads.  Waves 0-1 (consumers) each own a 16-column strip of the fp32
-// state over all 128 rows, in MFMA accumulators.  Every product of a chunk
+// Forward state pass for K = V = 128 in bf16, BV value columns per workgroup
+// (32 or 64), 64 (BV / 16 + 2) threads.  Waves 0 .. BV/16 - 1 (consumers) each
+// own a 16-column strip of the fp32 state over all 128 rows, in MFMA
+// accumulators.  Every product of a chunk
 // step takes its B operand from registers: S itself, or D = U - W S formed
 // in registers.  Its A operand is one of the chunk's operand tiles in LDS, read
 // row-wise or transposed.  A consumer thus needs no other wave within a step.
-// Waves 2-3 (producers) do all global memory traffic: the next chunk's operand
-// tiles go straight into the other half of a double-buffered LDS area, and the
-// previous chunk's output rows and entry state go out from LDS staging.
+// The last two waves (producers) do the global memory traffic: the next
+// chunk's operand tiles go straight into the other half of a double-buffered
+// LDS area, and the previous chunk's output rows (and, at BV = 32, its entry
+// state) go out from LDS staging.  At BV = 64 the staged state would not fit
+// the LDS beside the operand buffers, so each consumer stores its strip of the
+// entry state itself, as 16-byte pieces of the transposed rows.  BV = 64 halves
+// the workgroups per chain: when chains x 4 exceed the CUs, 32-column blocks
+// would run in several rounds of workgroups, each as long as the chain.
 // There is one barrier per chunk.
 // Chunks ahead of use that the state passes warm L2 for.
 constexpr int kWarmAhead = 4;
+#ifndef KDA_WARM64
+#define KDA_WARM64 2
+#endif
 
+template <int BV>
 struct StatePcFwd {
-    static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oU = 57344, oGC = 61440;
-    static constexpr int kBuf = 61952;  // one chunk's operand tiles
+    static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oU = 57344, oGC = oU + 128 * BV;
+    static constexpr int kBuf = oGC + 512;  // one chunk's operand tiles
 };
 
-template <bool STORE, bool WRITE_O>
-__global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, const int32_t* chunk_off,
-                                                                 uint8_t* ws, int64_t slot_bytes) {
-    using Z = StatePcFwd;
+// Threads of the producer/consumer state passes with BV value columns per workgroup.
+__host__ __device__ constexpr int state_pc_threads(int BV) { return 64 * (BV / 16 + 2); }
+// Value columns per workgroup of the producer/consumer state passes for
+// `chains` (sequence, head) chains: 32 while four blocks per chain fit the
+// CUs at one workgroup each (shorter chunk steps), else 64 (half as many
+// rounds of workgroups, each as long as the whole chain).
+#ifdef KDA_PC_BV32
+__host__ __device__ constexpr int state_pc_bv(int) { return 32; }
+#else
+__host__ __device__ constexpr int state_pc_bv(int chains) { return chains * 4 <= kPersistentGrid ? 32 : 64; }
+#endif
+
+template <bool STORE, bool WRITE_O, int BV = 32>
+__global__ __launch_bounds__(state_pc_threads(BV)) void chunk_state_fwd_pc_kernel(ChunkParams p,
+                                                                                  const int32_t* chunk_off,
+                                                                                  uint8_t* ws, int64_t slot_bytes) {
+    static_assert(BV == 32 || BV == 64, "32- or 64-column blocks");
+    using Z = StatePcFwd<BV>;
     using L = PrepLayout<128, true>;
-    constexpr int K = 128, V = 128, BV = 32, NVB = V / BV;
+    constexpr int K = 128, V = 128, NVB = V / BV, NCW = BV / 16;
+    constexpr bool STAGE_S = STORE && BV == 32;  // entry state staged for the producers
+    constexpr int WA = BV == 32 ? kWarmAhead : KDA_WARM64;
     // L2 warm-up kWarmAhead chunks ahead (HBM latency exceeds a chunk step),
     // 128-byte lines split over the chain's
     // NVB workgroups, NWARM loads per producer lane
@@ -1144,8 +1170,8 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
     // separate arrays, so that the compiler knows the staging and operand
     // reads do not alias the warm-up copies
     __shared__ __attribute__((aligned(1024))) uint8_t smb[2 * Z::kBuf];
-    __shared__ __attribute__((aligned(1024))) uint8_t sms[2 * 8192];  // S^T staging [32][128] per parity
-    __shared__ __attribute__((aligned(1024))) uint8_t smo[2 * 4096];  // O^T staging [32][64] per parity
+    __shared__ __attribute__((aligned(1024))) uint8_t sms[STAGE_S ? 2 * 8192 : 16];  // S^T staging [32][128] per parity
+    __shared__ __attribute__((aligned(1024))) uint8_t smo[2 * 128 * BV];  // O^T staging [BV][64] per parity
     __shared__ __attribute__((aligned(256))) uint8_t smj[256];
 
     int chain, vb;
@@ -1161,11 +1187,11 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
     const int v0 = vb * BV;
     const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
-    const bool prod = w >= 2;
-    const int pw = w - 2;
+    const bool prod = w >= NCW;
+    const int pw = w - NCW;
     auto slot = [&](int jc) { return ws + ((slot0 + jc) * H + h) * slot_bytes; };
 
-    // ---- producer: chunk jc's operand tiles into buffer jc & 1 (61 pieces of 1 KB)
+    // ---- producer: chunk jc's operand tiles into buffer jc & 1 (57 + BV / 8 pieces of 1 KB)
     auto fetch = [&](int jc) {
         const uint8_t* base = slot(jc);
         uint8_t* buf = smb + (jc & 1) * Z::kBuf;
@@ -1183,8 +1209,8 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
                 dma_tile_piece<64>(reinterpret_cast<const uint16_t*>(base + L::kMS), kChunk, buf + Z::oMS, 2 * qq + pw,
                                     lane);
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-            dma_tile_piece<32>(reinterpret_cast<const uint16_t*>(base + L::kU) + v0, V, buf + Z::oU, 2 * qq + pw, lane);
+        for (int qq = 0; qq < BV / 16; ++qq)
+            dma_tile_piece<BV>(reinterpret_cast<const uint16_t*>(base + L::kU) + v0, V, buf + Z::oU, 2 * qq + pw, lane);
         if (pw == 1 && lane < 32) dma16(base + L::kGC + 16 * lane, buf + Z::oGC);
     };
     // ---- producer: chunk jc's entry state and output rows from staging jc & 1
@@ -1194,21 +1220,24 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
         // whole transposed rows (column v of S: 128 values, 256 bytes); the
         // output as 64-byte row segments, its staging read transposed twice
         // per lane for 8 columns.
+        constexpr int NH = BV / 32;  // 32-column halves of the block
         const uint8_t* sts = sms + (jc & 1) * 8192;
-        const uint8_t* sto = smo + (jc & 1) * 4096;
-        bf16x8 xs[4], xo[2];
-        if (STORE)
+        const uint8_t* sto = smo + (jc & 1) * (128 * BV);
+        bf16x8 xs[4], xo[2][NH];
+        if (STAGE_S)
 #pragma unroll
             for (int q = 0; q < 4; ++q)  // S^T rows 16 pw + 4 q + lane / 16, 16-byte chunk lane % 16
                 xs[q] = *reinterpret_cast<const bf16x8*>(sts + swz_off<128>(16 * pw + 4 * q + lg, 8 * m));
         if (WRITE_O)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {  // token rows 32 pw + 16 q + m, columns 8 lg .. 8 lg + 7
-                const bf16x4_t lo = tr4<64>(sto, 8 * lg, 32 * pw + 16 * q, lane);
-                const bf16x4_t hi = tr4<64>(sto, 8 * lg + 4, 32 * pw + 16 * q, lane);
-                xo[q] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-        if (STORE) {
+            for (int q = 0; q < 2; ++q)  // token rows 32 pw + 16 q + m, columns 32 hb + 8 lg .. + 7
+#pragma unroll
+                for (int hb = 0; hb < NH; ++hb) {
+                    const bf16x4_t lo = tr4<64>(sto, 32 * hb + 8 * lg, 32 * pw + 16 * q, lane);
+                    const bf16x4_t hi = tr4<64>(sto, 32 * hb + 8 * lg + 4, 32 * pw + 16 * q, lane);
+                    xo[q][hb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+        if (STAGE_S) {
             uint16_t* gS = reinterpret_cast<uint16_t*>(slot(jc) + BwdExtra<128, true>::kS) + v0 * K;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -1218,7 +1247,11 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int row = jc * kChunk + 32 * pw + 16 * q + m;
-                if (row < len) *reinterpret_cast<bf16x8*>(og + ((start + row) * H + h) * V + v0 + 8 * lg) = xo[q];
+                if (row < len)
+#pragma unroll
+                    for (int hb = 0; hb < NH; ++hb)
+                        *reinterpret_cast<bf16x8*>(og + ((start + row) * H + h) * V + v0 + 32 * hb + 8 * lg) =
+                            xo[q][hb];
             }
         }
     };
@@ -1253,7 +1286,14 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
     for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) offT[t][hh] = swz_off<128>(8 * lg + 4 * hh + (m >> 2), 16 * t + 4 * (m & 3));
-    const int offU = (4 * lg + (m >> 2)) * 64 + 32 * w + 8 * (m & 3);
+    // At BV = 64 two waves share a SIMD, so a wave has 256 registers: column
+    // tile t's offsets are formed from tile 0's (the tile index enters the
+    // swizzled chunk index only through an exclusive or with 2 t), and the
+    // decay factors are read a tile pair ahead instead of all at once.
+    auto offTt = [&](int t, int hh) { return BV == 32 ? offT[t][hh] : (offT[0][hh] ^ (32 * t)); };
+    // likewise the row fragments' k-steps (chunk index 4 s + lg)
+    auto offAs = [&](int s) { return BV == 32 ? offA[s] : (offA[0] ^ (64 * s)); };
+    auto offMs = [&](int s) { return BV == 32 ? offM[s] : (offM[0] ^ (64 * s)); };
     auto rdA = [](const uint8_t* tile, int off) { return *reinterpret_cast<const bf16x8*>(tile + off); };
     auto rdT = [](const uint8_t* tile, int off0, int off1) {
         const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(tile + off0));
@@ -1263,14 +1303,19 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
     auto step = [&](int jc) {
         const uint8_t* buf = smb + (jc & 1) * Z::kBuf;
         uint8_t* sts = sms + (jc & 1) * 8192;
-        uint8_t* sto = smo + (jc & 1) * 4096;
+        uint8_t* sto = smo + (jc & 1) * (128 * BV);
         bf16x8 Sb[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) Sb[s] = frag_acc_nat(S[2 * s], S[2 * s + 1]);
-        if (STORE) {  // S^T staging: lane group lg of fragment s holds k = 32 s + 8 lg .. +7
+        // lane group lg of fragment s holds k = 32 s + 8 lg .. +7 of column 16 w + m
+        if (STAGE_S) {  // S^T staging
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 *reinterpret_cast<bf16x8*>(sts + swz_off<128>(16 * w + m, 32 * s + 8 * lg)) = Sb[s];
+        } else if (STORE) {  // straight to the slot's transposed entry state
+            uint16_t* gS = reinterpret_cast<uint16_t*>(slot(jc) + BwdExtra<128, true>::kS) + (v0 + 16 * w + m) * K;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(gS + 32 * s + 8 * lg) = Sb[s];
         }
         // The LDS reads are issued in batches ahead of the products that use
         // them (scheduling barriers keep that order), so that their latency
@@ -1281,8 +1326,8 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
         auto load_a = [&](int s, bf16x8* f) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
-                f[rt] = rdA(buf + Z::oW + 4096 * rt, offA[s]);
-                if (WRITE_O) f[4 + rt] = rdA(buf + Z::oQE + 4096 * rt, offA[s]);
+                f[rt] = rdA(buf + Z::oW + 4096 * rt, offAs(s));
+                if (WRITE_O) f[4 + rt] = rdA(buf + Z::oQE + 4096 * rt, offAs(s));
             }
         };
         f32x4 ws_[4], o[4];
@@ -1305,22 +1350,22 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
         // factors, and the first KD^T fragments
         bf16x4_t u[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            u[rt] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(buf + Z::oU + 1024 * rt + offU));
+        for (int rt = 0; rt < 4; ++rt) u[rt] = tr4<BV>(buf + Z::oU, 16 * rt + 4 * lg, 16 * w, lane);
         bf16x8 fm[6];
         if (WRITE_O) {
 #pragma unroll
             for (int rt = 0, q = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int s = 0; s <= (rt >> 1); ++s, ++q) fm[q] = rdA(buf + Z::oMS + 2048 * rt, offM[s]);
+                for (int s = 0; s <= (rt >> 1); ++s, ++q) fm[q] = rdA(buf + Z::oMS + 2048 * rt, offMs(s));
         }
         f32x4 g[8];
+        auto load_g = [&](int t) { g[t] = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg)); };
 #pragma unroll
-        for (int t = 0; t < 8; ++t) g[t] = *reinterpret_cast<const f32x4*>(buf + Z::oGC + 4 * (16 * t + 4 * lg));
+        for (int t = 0; t < (BV == 32 ? 8 : 2); ++t) load_g(t);
         bf16x8 fk[2][4];  // KD^T fragments of two column tiles, k-steps 0 and 1
         auto load_k = [&](int t, bf16x8* f) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) f[s] = rdT(buf + Z::oKD + 8192 * s, offT[t][0], offT[t][1]);
+            for (int s = 0; s < 2; ++s) f[s] = rdT(buf + Z::oKD + 8192 * s, offTt(t, 0), offTt(t, 1));
         };
         load_k(0, &fk[0][0]);
         load_k(1, &fk[0][2]);
@@ -1350,6 +1395,10 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
             if (tp < 3) {
                 load_k(2 * tp + 2, &fk[(tp + 1) & 1][0]);
                 load_k(2 * tp + 3, &fk[(tp + 1) & 1][2]);
+                if (BV == 64) {
+                    load_g(2 * tp + 2);
+                    load_g(2 * tp + 3);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1379,21 +1428,29 @@ __global__ __launch_bounds__(256) void chunk_state_fwd_pc_kernel(ChunkParams p, 
         }
     }
     __syncthreads();
-    for (int jc = 0; jc < nc; ++jc) {
-        if (prod) {
+    // One loop per role (each wave passes the same nc barriers).  A shared
+    // loop body makes the compiler keep both roles' values live at once
+    // (288 registers against 194), and at BV = 64 it waited at the top of a
+    // consumer's step for the producers' loads, and so for the consumer's own
+    // state stores of the step before.
+    if (prod) {
+        for (int jc = 0; jc < nc; ++jc) {
             // staging reads before this step's copies (the compiler would wait
             // for the copies before any later LDS read); the warm-up loads are
             // issued last and are the only ones allowed to stay in flight
             if (jc > 0) drain(jc - 1);
             if (jc + 1 < nc) fetch(jc + 1);
             __builtin_amdgcn_sched_barrier(0);
-            warm(jc + kWarmAhead < nc ? jc + kWarmAhead : jc);
+            warm(jc + WA < nc ? jc + WA : jc);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmem<NWARM>();
-        } else {
-            step(jc);
+            barrier_lds();
         }
-        barrier_lds();
+    } else {
+        for (int jc = 0; jc < nc; ++jc) {
+            step(jc);
+            barrier_lds();
+        }
     }
     if (prod) {
         if (nc > 0) drain(nc - 1);

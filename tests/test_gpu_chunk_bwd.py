@@ -202,6 +202,33 @@ def test_bwd_reuses_saved_forward(case):
             check(f"saved {name}", got[name], o[name], tol_for(w["q"].dtype))
 
 
+@pytest.mark.parametrize("case", ["packed_h4", "dense_b17_h4"])
+def test_bwd_many_chains_64_column_state_blocks(case):
+    """K = V = 128 bf16 with 80 and 68 (sequence, head) chains, where the state
+    passes run 64-column blocks: every gradient against the oracle, both from
+    the recomputing backward and from a forward that saved for it (bit-identical)."""
+    from test_gpu_chunk_fwd import many_chain_cu
+    if case == "packed_h4":
+        cu = many_chain_cu()
+        w = inputs.chunk_inputs(1, cu[-1], 4, 128, 128, seed=83, dtype=torch.bfloat16, cu_seqlens=cu, h0_std=0.1,
+                                with_grad_out=True, dfinal_std=0.1)
+    else:
+        w = inputs.chunk_inputs(17, 150, 4, 128, 128, seed=84, dtype=torch.bfloat16, h0_std=0.1,
+                                with_grad_out=True, dfinal_std=0.1)
+    _compare(w, case)
+    kw = dict(scale=w["scale"], initial_state=dev(w["initial_state"]), use_qk_l2norm_in_kernel=True,
+              gate_mode=w["gate_mode"], lower_bound=w["lower_bound"], cu_seqlens=dev(w["cu_seqlens"]))
+    q, k, v, g, beta, dO = (dev(w[n]) for n in ("q", "k", "v", "g", "beta", "dO"))
+    ws = torch.empty(kda.chunk_bwd_workspace_bytes(q, k, v, g, beta, **kw), dtype=torch.uint8, device="cuda")
+    ref = kda.chunk_kda_bwd(q, k, v, g, beta, dO, d_final_state=dev(w["d_final_state"]), **kw)
+    kda.chunk_kda(q, k, v, g, beta, output_final_state=True, workspace=ws, keep_for_backward=True, **kw)
+    got = kda.chunk_kda_bwd(q, k, v, g, beta, dO, d_final_state=dev(w["d_final_state"]), workspace=ws,
+                            keep_for_backward=True, **kw)
+    torch.cuda.synchronize()
+    for name in NAMES:
+        assert torch.equal(ref[name], got[name]), name
+
+
 def test_bwd_many_short_sequences():
     """1,500 packed sequences of 0..70 tokens (more than the 1,024 the plan
     kernel's scan takes per round, empty ones among them), H2 K=V=32 bf16:

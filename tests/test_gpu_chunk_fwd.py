@@ -117,6 +117,33 @@ def test_fwd_more_sequences_than_the_plans_lds_offsets():
     _compare(w, f"N={len(cu) - 1} T={cu[-1]}")
 
 
+# Lengths of a packed batch with more (sequence, head) chains than four
+# 32-column state blocks each can place on the chip at one workgroup per CU,
+# so that the K = V = 128 state passes take 64-column blocks: empty, one-row,
+# chunk-boundary and ragged sequences.
+MANY_CHAIN_LENS = [0, 1, 63, 64, 65, 127, 130, 200, 7, 0, 129, 64, 3, 191, 66, 100, 1, 250, 64, 31]
+
+
+def many_chain_cu():
+    cu = [0]
+    for n in MANY_CHAIN_LENS:
+        cu.append(cu[-1] + n)
+    return cu
+
+
+@pytest.mark.parametrize("case", ["packed_h4", "dense_b17_h4"])
+def test_fwd_many_chains_64_column_state_blocks(case):
+    """K = V = 128 bf16 with 80 and 68 (sequence, head) chains: the state pass
+    runs 64-column blocks (two per chain).  Ragged and empty packed sequences
+    with an initial state; a dense batch with a tail chunk."""
+    if case == "packed_h4":
+        cu = many_chain_cu()
+        w = inputs.chunk_inputs(1, cu[-1], 4, 128, 128, seed=81, dtype=torch.bfloat16, cu_seqlens=cu, h0_std=0.1)
+    else:
+        w = inputs.chunk_inputs(17, 150, 4, 128, 128, seed=82, dtype=torch.bfloat16, h0_std=0.1)
+    _compare(w, case)
+
+
 def test_fwd_no_l2norm_and_plain_scale():
     w = inputs.chunk_inputs(1, 96, 2, 32, 32, seed=8)
     # unit-norm keys supplied by the caller, so the chunk form stays well conditioned
