@@ -173,32 +173,40 @@ __global__ __launch_bounds__(kThreads) void chunk_state_bwd_kernel(ChunkParams p
     }
 }
 
-// Reverse state pass for K = V = 128 in bf16, 32 value columns per workgroup,
-// 256 threads: the producer/consumer form of chunk_state_fwd_pc_kernel.
-// Waves 0-1 (consumers) each own a 16-column strip of dS' over all 128 rows.
-// dD = KD dS' + MS^T dO takes dS' from registers as its B operand.  The
-// token-row products QE^T dO and W^T dD take dO, read transposed, and -dD,
-// formed in registers, as B.  Waves 2-3 (producers) copy each chunk's
-// operand tiles and dO block into LDS a chunk ahead, warm L2 kWarmAhead
-// chunks ahead, and store the staged dS' of the chunk before.
+// Reverse state pass for K = V = 128 in bf16, BV (32 or 64) value columns per
+// workgroup, state_pc_threads(BV) threads: the producer/consumer form of
+// chunk_state_fwd_pc_kernel.  Waves 0 .. BV/16 - 1 (consumers) each own a
+// 16-column strip of dS' over all 128 rows.  dD = KD dS' + MS^T dO takes dS'
+// from registers as its B operand.  The token-row products QE^T dO and W^T dD
+// take dO, read transposed, and -dD, formed in registers, as B.  The last two
+// waves (producers) copy each chunk's operand tiles and dO block into LDS a
+// chunk ahead, warm L2 a few chunks ahead, and at BV = 32 store the staged dS'
+// of the chunk before; at BV = 64 (the block count of state_pc_bv) the
+// consumers store their dS' strips themselves, since the staging would not
+// fit the LDS beside the operand buffers.
+template <int BV>
 struct StatePcBwd {
-    static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oDO = 57344, oGC = 61440;
-    static constexpr int kBuf = 61952;  // one chunk's operand tiles and dO block
+    static constexpr int oW = 0, oQE = 16384, oKD = 32768, oMS = 49152, oDO = 57344, oGC = oDO + 128 * BV;
+    static constexpr int kBuf = oGC + 512;  // one chunk's operand tiles and dO block
 };
 
-__global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, ChunkGrads gr,
-                                                                 const int32_t* chunk_off, uint8_t* ws,
-                                                                 int64_t slot_bytes) {
-    using Z = StatePcBwd;
+template <int BV>
+__global__ __launch_bounds__(state_pc_threads(BV)) void chunk_state_bwd_pc_kernel(ChunkParams p, ChunkGrads gr,
+                                                                                  const int32_t* chunk_off,
+                                                                                  uint8_t* ws, int64_t slot_bytes) {
+    static_assert(BV == 32 || BV == 64, "32- or 64-column blocks");
+    using Z = StatePcBwd<BV>;
     using L = PrepLayout<128, true>;
     using X = BwdExtra<128, true>;
-    constexpr int K = 128, V = 128, BV = 32, NVB = V / BV;
+    constexpr int K = 128, V = 128, NVB = V / BV, NCW = BV / 16;
+    constexpr bool STAGE = BV == 32;  // dS' staged for the producers
+    constexpr int WA = BV == 32 ? kWarmAhead : kWarmAhead64;
     // L2 warm-up lines of a chunk: QE, W, KD (contiguous), MS, GC, then the
     // dO rows (two lines per head row), split over the chain's NVB workgroups
     constexpr int NL = 384 + 64 + 4 + 128;
     constexpr int NWARM = (NL + NVB * 128 - 1) / (NVB * 128);
     __shared__ __attribute__((aligned(1024))) uint8_t smb[2 * Z::kBuf];
-    __shared__ __attribute__((aligned(1024))) uint8_t sms[2 * 8192];  // dS'^T staging [32][128] per parity
+    __shared__ __attribute__((aligned(1024))) uint8_t sms[STAGE ? 2 * 8192 : 16];  // dS'^T staging [32][128] per parity
     __shared__ __attribute__((aligned(256))) uint8_t smj[256];
 
     int chain, vb;
@@ -214,8 +222,8 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
     const int v0 = vb * BV;
     const int64_t slot0 = chunk_slot(p, chunk_off, n, 0);
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * K * V;
-    const bool prod = w >= 2;
-    const int pw = w - 2;
+    const bool prod = w >= NCW;
+    const int pw = w - NCW;
     const uint16_t* dOg = static_cast<const uint16_t*>(gr.dO);
     auto slot = [&](int jc) { return ws + ((slot0 + jc) * H + h) * slot_bytes; };
     auto rows_in = [&](int jc) { return min(kChunk, len - jc * kChunk); };  // >= 1 for jc < nc
@@ -237,8 +245,8 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
                                 lane);
         const uint16_t* dO0 = dOg + ((start + static_cast<int64_t>(jc) * kChunk) * H + h) * V + v0;
 #pragma unroll
-        for (int qq = 0; qq < 2; ++qq)
-            dma_tile_piece<32>(dO0, static_cast<int64_t>(H) * V, buf + Z::oDO, 2 * qq + pw, lane, rows_in(jc));
+        for (int qq = 0; qq < BV / 16; ++qq)
+            dma_tile_piece<BV>(dO0, static_cast<int64_t>(H) * V, buf + Z::oDO, 2 * qq + pw, lane, rows_in(jc));
         if (pw == 1 && lane < 32) dma16(base + L::kGC + 16 * lane, buf + Z::oGC);
     };
     // ---- producer: chunk jc's dS' from staging jc & 1, as whole transposed
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
     int offA[4];      // [64][128] row fragment, k-step s, row tile 0 (+4096 per row tile)
     int offT[8][2];   // [64][128] transposed fragment halves, column tile t, k-step 0 (+8192 per k-step)
     int offMT[4][2];  // [64][64] transposed fragment halves, column tile j, k-step 0 (+4096 per k-step)
-    int offD[2];      // [64][32] dO, transposed halves, k-step 0 (+2048 per k-step)
+    int offD[2];      // [64][BV] dO, transposed halves, k-step 0 (+64 BV per k-step)
 #pragma unroll
     for (int s = 0; s < 4; ++s) offA[s] = swz_off<128>(m, 32 * s + 8 * lg);
 #pragma unroll
@@ -288,7 +296,7 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
         for (int t = 0; t < 8; ++t) offT[t][hh] = swz_off<128>(r, 16 * t + 4 * (m & 3));
 #pragma unroll
         for (int j = 0; j < 4; ++j) offMT[j][hh] = swz_off<64>(r, 16 * j + 4 * (m & 3));
-        offD[hh] = swz_off<32>(r, 16 * w + 4 * (m & 3));
+        offD[hh] = swz_off<BV>(r, 16 * w + 4 * (m & 3));
     }
     auto rdA = [](const uint8_t* tile, int off) { return *reinterpret_cast<const bf16x8*>(tile + off); };
     auto rdT = [](const uint8_t* tile, int off0, int off1) {
@@ -299,11 +307,16 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
     auto step = [&](int jc) {
         const uint8_t* buf = smb + (jc & 1) * Z::kBuf;
         uint8_t* st = sms + (jc & 1) * 8192;
-        bf16x8 Sb[4];  // dS' as the B operand over state rows; also staged for the store
+        bf16x8 Sb[4];  // dS' as the B operand over state rows; also stored (lane group lg: k = 32 s + 8 lg ..)
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             Sb[s] = frag_acc_nat(dS[2 * s], dS[2 * s + 1]);
-            *reinterpret_cast<bf16x8*>(st + swz_off<128>(16 * w + m, 32 * s + 8 * lg)) = Sb[s];
+            if (STAGE) *reinterpret_cast<bf16x8*>(st + swz_off<128>(16 * w + m, 32 * s + 8 * lg)) = Sb[s];
+        }
+        if (!STAGE) {  // straight to the slot's transposed dS'
+            uint16_t* gD = reinterpret_cast<uint16_t*>(slot(jc) + X::kDS) + (v0 + 16 * w + m) * K;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) *reinterpret_cast<bf16x8*>(gD + 32 * s + 8 * lg) = Sb[s];
         }
         // The LDS reads are issued in batches ahead of the products that use
         // them (scheduling barriers keep that order).
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
         // end), the MS^T fragments, the decay factors and the first KD fragments
         bf16x8 dOb[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) dOb[s] = rdT(buf + Z::oDO + 2048 * s, offD[0], offD[1]);
+        for (int s = 0; s < 2; ++s) dOb[s] = rdT(buf + Z::oDO + 64 * BV * s, offD[0], offD[1]);
         bf16x8 fm[6];
 #pragma unroll
         for (int jt = 0, q = 0; jt < 4; ++jt)
@@ -403,10 +416,10 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
             // staging reads before this step's copies (the compiler would wait
             // for the copies before later LDS reads); the warm-up loads are
             // issued last and are the only ones allowed to stay in flight
-            if (jc + 1 < nc) drain(jc + 1);
+            if (STAGE && jc + 1 < nc) drain(jc + 1);
             if (jc > 0) fetch(jc - 1);
             __builtin_amdgcn_sched_barrier(0);
-            warm(jc >= kWarmAhead ? jc - kWarmAhead : jc);
+            warm(jc >= WA ? jc - WA : jc);
             __builtin_amdgcn_sched_barrier(0);
             wait_vmem<NWARM>();
             barrier_lds();
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(256) void chunk_state_bwd_pc_kernel(ChunkParams p, 
         }
     }
     if (prod) {
-        if (nc > 0) drain(0);
+        if (STAGE && nc > 0) drain(0);
     } else if (gr.dh0) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
@@ -2948,9 +2961,14 @@ static hipError_t run_bwd(const ChunkParams& p, const ChunkGrads& gr, void* ws, 
                                st, p, chunk_off, slots, sb);
     }
     if (want(2) && cgrid > 0) {
-        if constexpr (K == 128 && V == 128 && BF)
-            hipLaunchKernelGGL(chunk_state_bwd_pc_kernel, dim3(cgrid), dim3(256), 0, st, p, gr, chunk_off, slots, sb);
-        else
+        if constexpr (K == 128 && V == 128 && BF) {
+            if (state_pc_bv(p.N * p.H) == 32)
+                hipLaunchKernelGGL(chunk_state_bwd_pc_kernel<32>, dim3(cgrid), dim3(state_pc_threads(32)), 0, st, p, gr,
+                                   chunk_off, slots, sb);
+            else
+                hipLaunchKernelGGL(chunk_state_bwd_pc_kernel<64>, dim3(chain_grid(p.N * p.H, 2)),
+                                   dim3(state_pc_threads(64)), 0, st, p, gr, chunk_off, slots, sb);
+        } else
             hipLaunchKernelGGL((chunk_state_bwd_kernel<K, V, BV, BF>), dim3(cgrid), dim3(kThreads), 0, st, p, gr,
                                chunk_off, slots, sb);
     }

@@ -1129,9 +1129,10 @@ __global__ __launch_bounds__(NT) void chunk_state_fwd_kernel(ChunkParams p, cons
 // There is one barrier per chunk.
 // Chunks ahead of use that the state passes warm L2 for.
 constexpr int kWarmAhead = 4;
-#ifndef KDA_WARM64
-#define KDA_WARM64 2
-#endif
+// With 64-column blocks twice as many chains share each XCD's L2, and four
+// chunks ahead no longer fit it (B8 x T4096 forward state: 213 us at two
+// chunks ahead, 228 at one, 231 at three, 237 at four).
+constexpr int kWarmAhead64 = 2;
 
 template <int BV>
 struct StatePcFwd {
@@ -1145,11 +1146,7 @@ __host__ __device__ constexpr int state_pc_threads(int BV) { return 64 * (BV / 1
 // `chains` (sequence, head) chains: 32 while four blocks per chain fit the
 // CUs at one workgroup each (shorter chunk steps), else 64 (half as many
 // rounds of workgroups, each as long as the whole chain).
-#ifdef KDA_PC_BV32
-__host__ __device__ constexpr int state_pc_bv(int) { return 32; }
-#else
 __host__ __device__ constexpr int state_pc_bv(int chains) { return chains * 4 <= kPersistentGrid ? 32 : 64; }
-#endif
 
 template <bool STORE, bool WRITE_O, int BV = 32>
 __global__ __launch_bounds__(state_pc_threads(BV)) void chunk_state_fwd_pc_kernel(ChunkParams p,
@@ -1160,7 +1157,7 @@ __global__ __launch_bounds__(state_pc_threads(BV)) void chunk_state_fwd_pc_kerne
     using L = PrepLayout<128, true>;
     constexpr int K = 128, V = 128, NVB = V / BV, NCW = BV / 16;
     constexpr bool STAGE_S = STORE && BV == 32;  // entry state staged for the producers
-    constexpr int WA = BV == 32 ? kWarmAhead : KDA_WARM64;
+    constexpr int WA = BV == 32 ? kWarmAhead : kWarmAhead64;
     // L2 warm-up kWarmAhead chunks ahead (HBM latency exceeds a chunk step),
     // 128-byte lines split over the chain's
     // NVB workgroups, NWARM loads per producer lane
