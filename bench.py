@@ -500,12 +500,13 @@ def cpu_baseline(host):
 
 
 def csrc_digest():
-    """SHA-256 over the kernel sources, to tell whether stored counter readings still apply."""
+    """SHA-256 over the KDA kernel sources, to tell whether stored counter readings still apply
+    (the calibration kernels of libkda_stream.so are not among them)."""
     import hashlib
     d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kimi_delta_attention_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".cpp")):
+        if f.endswith((".hip", ".hpp", ".cpp")) and f != "stream_ceiling.hip":
             with open(os.path.join(d, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
